@@ -1,0 +1,169 @@
+/*
+ * fp4lin.h - C ABI of the MI355X (gfx950) FP4 quantized linear-layer forward
+ *
+ *      Y = dequant(Aq . Wq) + dA . W
+ *
+ * The method is the forward pass of the FP4 linear layer described on the pages about
+ * "Optimizing Large Language Model Training Using FP4 Quantization":
+ *   - QbitAI report, quantization-format paragraph: E2M1 (1 sign, 2 exponent, 1 mantissa
+ *     bit);
+ *   - QbitAI report, granularity paragraph: W quantized per output channel (column), A per
+ *     token (row), chosen so the GEMM needs no extra transpose;
+ *   - QbitAI report, forward-quantization paragraph: at the start of each forward, W and A
+ *     of every linear layer are scaled into the FP4 range (scale+shift, per-layer ranges)
+ *     and rounded to the nearest FP4 value by table lookup;
+ *   - QbitAI report, outlier paragraph, and the paper abstract: outliers of A are found by
+ *     a quantile search, clamped to a threshold (A_clamped), and compensated by the sparse
+ *     matrix dA that is non-zero only where clamping happened.
+ *
+ * Readings fixed by this library where the pages are silent (the CPU oracle takes the
+ * same ones):
+ *   - scale: r = fl32(6 / amax) per row of A_clamped and per column of W, dequantization
+ *     scale s = fl32(amax / 6); a vector with amax < 2^-120 gets r = s = 0;
+ *   - rounding: nearest E2M1 value, ties to the even code, saturation at 6, sign copied;
+ *   - threshold: T = the (k+1)-th smallest |a| over all M*K entries, k = floor(q*(M*K-1))
+ *     in IEEE double; an outlier is |a| > T strictly; delta = fl32(a - copysign(T, a));
+ *   - product: acc = sum_k value(Aq) * value(Wq), exact in fp32 for K <= 65536;
+ *     Y_main = fl32(fl32(acc * sA[m]) * sW[n]);
+ *   - compensation uses the original W: Y = Y_main + sum over row m's dA entries of
+ *     delta * W[k][n], accumulated in fp32 in ascending k.
+ *
+ * Layouts (all row-major, dense, base pointers 16-byte aligned):
+ *   A   M x K activations (tokens x in-features), fp32 or bf16
+ *   W   K x N weights (in x out), same dtype as A
+ *   Aq  M x K/2 bytes: code of A[m][k] in byte (m, k/2), low nibble for even k
+ *   Wq  N x K/2 bytes: code of W[k][n] in byte (n, k/2), low nibble for even k
+ *       (K-contiguous per output channel: both GEMM operands are K-contiguous)
+ *   sA  fp32[M], sW fp32[N]
+ *   dA  COO sorted by (row, col): coo_row/coo_col int32[nnz], coo_val fp32[nnz],
+ *       row_ptr int32[M+1] (CSR row offsets of the same list)
+ *   Y   M x N, fp32 or bf16 (bf16 = round-to-nearest-even of the fp32 result)
+ *
+ * Ownership and threading: the caller owns every buffer (device memory unless stated).
+ * The library never allocates, frees or synchronizes, and never copies device data to
+ * the host: each call only validates its arguments on the host and enqueues kernels on
+ * the caller's HIP stream (hipStream_t passed as void*, NULL = default stream); results
+ * are ready when that stream reaches them.  No mutable global state: calls on different
+ * streams are independent as long as their buffers do not overlap.
+ *
+ * Errors: every argument check runs on the host before the first HIP call and returns a
+ * status; nothing is enqueued then.  FP4_ERR_DEVICE: the current device is not gfx950.
+ * FP4_ERR_HIP: a launch failed (the stream may hold part of the work).  Inputs must be
+ * finite; NaN or Inf give unspecified codes and outputs.
+ */
+#ifndef FP4LIN_H
+#define FP4LIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fp4_status;
+enum {
+    FP4_OK = 0,
+    FP4_ERR_NULL = 1,      /* a required pointer is NULL */
+    FP4_ERR_SHAPE = 2,     /* a size is out of range (see each call) */
+    FP4_ERR_DTYPE = 3,     /* unknown dtype or axis code */
+    FP4_ERR_QUANTILE = 4,  /* q is NaN or outside [0, 1] */
+    FP4_ERR_CAPACITY = 5,  /* COO capacity below fp4_outlier_capacity() */
+    FP4_ERR_WORKSPACE = 6, /* workspace smaller than the size query returns */
+    FP4_ERR_DEVICE = 7,    /* current HIP device is not gfx950 */
+    FP4_ERR_HIP = 8,       /* a HIP runtime call or launch failed */
+    FP4_ERR_ALIGN = 9      /* a pointer is not 16-byte aligned */
+};
+enum { FP4_F32 = 0, FP4_BF16 = 1 };          /* element types of A, W, X, Y */
+enum { FP4_PER_ROW = 0, FP4_PER_COL = 1 };   /* token-wise (A) / channel-wise (W) */
+
+/* Limits shared by all calls: 32 <= K <= 65536 and K % 32 == 0 (contraction length:
+ * two codes per byte, 16-byte vector lanes, and the fp32 accumulator stays exact);
+ * 1 <= M and M * K < 2^32; 1 <= N and N % 8 == 0. */
+
+/* Quantize one matrix X (R x C) to E2M1 codes and fp32 scales.
+ * QbitAI report, granularity and forward-quantization paragraphs.
+ *   axis FP4_PER_ROW: one scale per row (token-wise, as for A); needs C % 32 == 0,
+ *                     32 <= C <= 65536; codes R x C/2, scales fp32[R].
+ *   axis FP4_PER_COL: one scale per column (channel-wise, as for W with R = K, C = N);
+ *                     needs R % 32 == 0, 32 <= R <= 65536, C % 8 == 0; codes C x R/2
+ *                     (transposed: R-contiguous per column), scales fp32[C].  The scales
+ *                     buffer also serves as the column-maximum scratch during the call.
+ *   clamp_T: NULL, or a device fp32[1] holding T: each |x| > T is replaced by
+ *            copysign(T, x) before scaling (the clamp of the outlier paragraph).
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,ALIGN,DEVICE,HIP}. */
+fp4_status fp4_quantize(const void *X, int32_t x_dtype, int64_t R, int64_t C, int32_t axis,
+                        const float *clamp_T, uint8_t *codes, float *scales, void *stream);
+
+/* Host-only: the largest possible nnz of dA for an M x K input and quantile q,
+ * M*K - 1 - floor(q * (M*K - 1)); -1 if the arguments are invalid. */
+int64_t fp4_outlier_capacity(int64_t M, int64_t K, double q);
+
+/* Host-only: workspace bytes fp4_outlier_clamp needs for an M x K input of a_dtype
+ * (0 if the arguments are invalid). */
+size_t fp4_outlier_workspace_bytes(int64_t M, int64_t K, int32_t a_dtype, double q);
+
+/* Outlier clamping and compensation (QbitAI report, outlier paragraph; abstract):
+ * T = quantile q of |A| over the whole tensor; dA = A - clamp(A, -T, T) in COO order.
+ *   T        device fp32[1] (out)
+ *   coo_row, coo_col, coo_val  device arrays of `capacity` entries (out; the first *nnz
+ *            are written).  capacity >= fp4_outlier_capacity(M, K, q) is required.
+ *   row_ptr  device int32[M+1] (out), nnz  device int64[1] (out)
+ *   workspace device scratch of at least fp4_outlier_workspace_bytes() bytes.
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,QUANTILE,CAPACITY,WORKSPACE,ALIGN,DEVICE,HIP}. */
+fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t K, double q,
+                             float *T, int32_t *coo_row, int32_t *coo_col, float *coo_val,
+                             int64_t capacity, int32_t *row_ptr, int64_t *nnz, void *workspace,
+                             size_t ws_bytes, void *stream);
+
+/* The FP4 GEMM with dequantization and the sparse compensation fused into its output
+ * (QbitAI report, GEMM-kernel paragraph: the product of the two FP4 operands, here on
+ * CDNA4 FP4 matrix cores with fp32 accumulation; granularity paragraph: sA and sW factor
+ * out of the K-sum).
+ *   Aq M x K/2, sA fp32[M], Wq N x K/2, sW fp32[N] (as produced by fp4_quantize)
+ *   row_ptr, coo_col, coo_val: dA as produced by fp4_outlier_clamp, or all three NULL for
+ *            no compensation term; W (K x N, w_dtype) is then unused and may be NULL.
+ *   Y        M x N of y_dtype (out)
+ *   acc_out  NULL, or device fp32[M*N] receiving the raw accumulator acc (a check aid).
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,ALIGN,DEVICE,HIP}. */
+fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW,
+                    int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
+                    const int32_t *coo_col, const float *coo_val, const void *W, int32_t w_dtype,
+                    void *Y, int32_t y_dtype, float *acc_out, void *stream);
+
+/* Byte offsets of the intermediates inside the fp4_linear_forward workspace, so a caller
+ * can read T, the COO list, the codes and the scales after a forward. */
+struct fp4_ws_layout {
+    size_t total;                 /* bytes needed */
+    size_t T;                     /* fp32[1] */
+    size_t nnz;                   /* int64[1] */
+    size_t row_ptr;               /* int32[M+1] */
+    size_t coo_row, coo_col, coo_val; /* capacity entries each */
+    size_t Aq, sA, Wq, sW;        /* codes and scales */
+    size_t scratch;               /* internal */
+    int64_t capacity;             /* fp4_outlier_capacity(M, K, q) */
+};
+
+/* Host-only: workspace layout / size of fp4_linear_forward (returns FP4_OK or an
+ * argument error; size 0 on error). */
+fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q,
+                              struct fp4_ws_layout *out);
+size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q);
+
+/* The whole forward of one FP4 linear layer (QbitAI report, forward-quantization and
+ * outlier paragraphs): quantile and clamp of A with dA, token-wise quantization of
+ * A_clamped, channel-wise quantization of W, FP4 GEMM, dequantization, compensation.
+ *   A  M x K, W  K x N, both of in_dtype; Y  M x N of y_dtype (out)
+ *   workspace: at least fp4_forward_workspace_bytes() bytes (layout: fp4_forward_layout).
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,QUANTILE,WORKSPACE,ALIGN,DEVICE,HIP}. */
+fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, int64_t M,
+                              int64_t K, int64_t N, double q, void *Y, int32_t y_dtype,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *fp4_status_string(fp4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4LIN_H */

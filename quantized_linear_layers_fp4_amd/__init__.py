@@ -1,0 +1,214 @@
+"""MI355X (gfx950) FP4 quantized linear-layer forward: Python binding of libfp4lin.so.
+
+Argument marshalling only: torch supplies device memory and the current HIP stream,
+and every step of the forward runs in the library's HIP kernels (include/fp4lin.h is
+the ABI).  There is no CPU fallback: without the built library every call raises.
+
+    Y = linear_forward(A, W, q)            # A: M x K, W: K x N (cuda, bf16 or fp32)
+
+The method (quantization of A per token and W per output channel into E2M1, outlier
+clamping at a quantile of |A| with sparse compensation dA) follows the pages on
+"Optimizing Large Language Model Training Using FP4 Quantization" (QbitAI report:
+granularity, forward-quantization and outlier paragraphs).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4lin.so")
+
+FP4_F32, FP4_BF16 = 0, 1
+FP4_PER_ROW, FP4_PER_COL = 0, 1
+
+EXPORTS = (
+    "fp4_quantize", "fp4_outlier_capacity", "fp4_outlier_workspace_bytes", "fp4_outlier_clamp",
+    "fp4_gemm", "fp4_forward_layout", "fp4_forward_workspace_bytes", "fp4_linear_forward",
+    "fp4_status_string",
+)
+
+
+class WsLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("total", "T", "nnz", "row_ptr", "coo_row", "coo_col", "coo_val",
+                                          "Aq", "sA", "Wq", "sW", "scratch")] + [("capacity", C.c_int64)]
+
+
+class Fp4Error(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """Load libfp4lin.so from the package directory (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise Fp4Error(f"{LIB_PATH} is missing: build it with `python -m quantized_linear_layers_fp4_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    vp, i64, i32, dbl, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_double, C.c_size_t
+    sig = {
+        "fp4_quantize": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp]),
+        "fp4_outlier_capacity": (i64, [i64, i64, dbl]),
+        "fp4_outlier_workspace_bytes": (sz, [i64, i64, i32, dbl]),
+        "fp4_outlier_clamp": (i32, [vp, i32, i64, i64, dbl, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
+        "fp4_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32, vp, i32, vp, vp]),
+        "fp4_forward_layout": (i32, [i64, i64, i64, i32, dbl, C.POINTER(WsLayout)]),
+        "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, dbl]),
+        "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
+        "fp4_status_string": (C.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise Fp4Error(f"fp4 status {status}: {lib().fp4_status_string(status).decode()}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FP4_BF16
+    if t.dtype == torch.float32:
+        return FP4_F32
+    raise TypeError(f"expected bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on a HIP device")
+
+
+def _out_dtype_code(d: torch.dtype) -> int:
+    return {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[d]
+
+
+# --------------------------------------------------------------------------- calls
+def quantize(X: torch.Tensor, axis: int = FP4_PER_ROW, clamp_T: torch.Tensor | None = None):
+    """E2M1 codes and fp32 scales of X (R x C).  PER_ROW: codes R x C/2, scales R.
+    PER_COL: codes C x R/2 (transposed), scales C."""
+    _need_cuda(X, clamp_T)
+    R, Cn = X.shape
+    if axis == FP4_PER_ROW:
+        codes = torch.empty((R, Cn // 2), dtype=torch.uint8, device=X.device)
+        scales = torch.empty(R, dtype=torch.float32, device=X.device)
+    else:
+        codes = torch.empty((Cn, R // 2), dtype=torch.uint8, device=X.device)
+        scales = torch.empty(Cn, dtype=torch.float32, device=X.device)
+    _check(lib().fp4_quantize(_ptr(X), _dt(X), R, Cn, axis, _ptr(clamp_T), _ptr(codes), _ptr(scales), _stream(X)))
+    return codes, scales
+
+
+def outlier_capacity(M: int, K: int, q: float) -> int:
+    return int(lib().fp4_outlier_capacity(M, K, float(q)))
+
+
+def outlier_clamp(A: torch.Tensor, q: float, trim: bool = True) -> dict:
+    """Threshold T and the COO list of dA for A (M x K).  With trim=True the COO arrays
+    are cut to nnz (this reads nnz back and synchronizes)."""
+    _need_cuda(A)
+    M, K = A.shape
+    L = lib()
+    cap = int(L.fp4_outlier_capacity(M, K, float(q)))
+    if cap < 0:
+        _check(2)
+    dev = A.device
+    capn = max(cap, 1)
+    T = torch.empty(4, dtype=torch.float32, device=dev)
+    coo_row = torch.empty(capn, dtype=torch.int32, device=dev)
+    coo_col = torch.empty(capn, dtype=torch.int32, device=dev)
+    coo_val = torch.empty(capn, dtype=torch.float32, device=dev)
+    row_ptr = torch.empty(M + 1, dtype=torch.int32, device=dev)
+    nnz = torch.empty(2, dtype=torch.int64, device=dev)
+    wsb = int(L.fp4_outlier_workspace_bytes(M, K, _dt(A), float(q)))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check(L.fp4_outlier_clamp(_ptr(A), _dt(A), M, K, float(q), _ptr(T), _ptr(coo_row), _ptr(coo_col),
+                               _ptr(coo_val), capn, _ptr(row_ptr), _ptr(nnz), _ptr(ws), wsb, _stream(A)))
+    out = dict(T=T[:1], row_ptr=row_ptr, nnz=nnz[:1], coo_row=coo_row, coo_col=coo_col, coo_val=coo_val)
+    if trim:
+        n = int(nnz[0].item())
+        out.update(coo_row=coo_row[:n], coo_col=coo_col[:n], coo_val=coo_val[:n])
+    return out
+
+
+def gemm(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, K: int,
+         row_ptr: torch.Tensor | None = None, coo_col: torch.Tensor | None = None,
+         coo_val: torch.Tensor | None = None, W: torch.Tensor | None = None,
+         out_dtype: torch.dtype = torch.bfloat16, acc_out: bool = False):
+    """Y = fl(fl(acc * sA) * sW) (+ dA . W when the COO arrays and W are given)."""
+    _need_cuda(Aq, sA, Wq, sW, row_ptr, coo_col, coo_val, W)
+    M, N = Aq.shape[0], Wq.shape[0]
+    Y = torch.empty((M, N), dtype=out_dtype, device=Aq.device)
+    acc = torch.empty((M, N), dtype=torch.float32, device=Aq.device) if acc_out else None
+    wdt = _dt(W) if W is not None else FP4_BF16
+    _check(lib().fp4_gemm(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, _ptr(row_ptr), _ptr(coo_col),
+                          _ptr(coo_val), _ptr(W), wdt, _ptr(Y), _out_dtype_code(out_dtype), _ptr(acc), _stream(Aq)))
+    return (Y, acc) if acc_out else Y
+
+
+def forward_layout(M: int, K: int, N: int, dtype: torch.dtype, q: float) -> WsLayout:
+    lay = WsLayout()
+    _check(lib().fp4_forward_layout(M, K, N, _out_dtype_code(dtype), float(q), C.byref(lay)))
+    return lay
+
+
+def workspace(A: torch.Tensor, N: int, q: float) -> torch.Tensor:
+    """A workspace tensor sized for linear_forward(A, W (K x N), q)."""
+    M, K = A.shape
+    lay = forward_layout(M, K, N, A.dtype, q)
+    return torch.empty(lay.total, dtype=torch.uint8, device=A.device)
+
+
+def linear_forward(A: torch.Tensor, W: torch.Tensor, q: float, out_dtype: torch.dtype | None = None,
+                   ws: torch.Tensor | None = None, Y: torch.Tensor | None = None) -> torch.Tensor:
+    """FP4 linear forward Y = dequant(Aq . Wq) + dA . W on the current stream."""
+    _need_cuda(A, W, ws, Y)
+    if A.dtype != W.dtype:
+        raise TypeError("A and W must share a dtype")
+    M, K = A.shape
+    N = W.shape[1]
+    out_dtype = out_dtype or A.dtype
+    if ws is None:
+        ws = workspace(A, N, q)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    _check(lib().fp4_linear_forward(_ptr(A), _ptr(W), _dt(A), M, K, N, float(q), _ptr(Y), _dt(Y), _ptr(ws),
+                                    ws.numel(), _stream(A)))
+    return Y
+
+
+def forward_intermediates(ws: torch.Tensor, M: int, K: int, N: int, dtype: torch.dtype, q: float) -> dict:
+    """Views of T, nnz, the COO list, codes and scales inside a forward workspace."""
+    lay = forward_layout(M, K, N, dtype, q)
+    cap = max(int(lay.capacity), 1)
+
+    def view(off, count, dt, shape=None):
+        nbytes = count * torch.tensor([], dtype=dt).element_size()
+        t = ws[off:off + nbytes].view(dt)
+        return t.view(shape) if shape else t
+
+    return dict(
+        T=view(lay.T, 1, torch.float32), nnz=view(lay.nnz, 1, torch.int64),
+        row_ptr=view(lay.row_ptr, M + 1, torch.int32), coo_row=view(lay.coo_row, cap, torch.int32),
+        coo_col=view(lay.coo_col, cap, torch.int32), coo_val=view(lay.coo_val, cap, torch.float32),
+        Aq=view(lay.Aq, M * (K // 2), torch.uint8, (M, K // 2)), sA=view(lay.sA, M, torch.float32),
+        Wq=view(lay.Wq, N * (K // 2), torch.uint8, (N, K // 2)), sW=view(lay.sW, N, torch.float32),
+        capacity=int(lay.capacity))

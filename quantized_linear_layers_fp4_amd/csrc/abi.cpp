@@ -1,0 +1,271 @@
+// C ABI of the FP4 linear forward (declared in include/fp4lin.h): host-side argument
+// validation, workspace carving and stream-ordered kernel launches.  Every check runs
+// before the first HIP call; the library never allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "fp4_launch.h"
+#include "fp4lin.h"
+
+using namespace fp4;
+
+namespace {
+
+constexpr int64_t K_MAX = 65536;
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int32_t d) { return d == FP4_F32 || d == FP4_BF16; }
+bool q_ok(double q) { return q >= 0.0 && q <= 1.0; }  // false for NaN
+int dt_of(int32_t d) { return d == FP4_BF16 ? DT_BF16 : DT_F32; }
+
+bool k_ok(int64_t K) { return K >= 32 && K <= K_MAX && K % 32 == 0; }
+bool mk_ok(int64_t M, int64_t K) { return M >= 1 && k_ok(K) && M <= (int64_t)0xFFFFFFFF / K; }
+bool n_ok(int64_t N) { return N >= 1 && N % 8 == 0 && N <= (int64_t)1 << 30; }
+
+int64_t capacity_of(int64_t M, int64_t K, double q) {
+    const int64_t n = M * K;
+    const int64_t k = (int64_t)std::floor(q * (double)(n - 1));
+    return n - 1 - k;
+}
+
+// The current device must be gfx950; its CU count sizes the histogram grid.
+struct DevInfo {
+    bool known = false;
+    bool ok = false;
+    int cus = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+fp4_status device_check(int *cus) {
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return FP4_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DevInfo &info = g_dev[d];
+    if (!info.known) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, d) != hipSuccess) return FP4_ERR_HIP;
+        info.ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        info.cus = p.multiProcessorCount;
+        info.known = true;
+    }
+    if (!info.ok) return FP4_ERR_DEVICE;
+    *cus = info.cus;
+    return FP4_OK;
+}
+
+// Scratch of one outlier pass.  [state, hist, hist_lo) is zero-filled per call.
+struct OutlierWs {
+    size_t state, hist, hist_lo, zero_end, rowmax, row_cnt, stage, total;
+};
+
+OutlierWs outlier_ws(int64_t M, int32_t dtype, int64_t cap) {
+    OutlierWs w;
+    size_t off = 0;
+    w.state = off;
+    off += align_up(sizeof(State));
+    w.hist = off;
+    off += align_up((size_t)HIST_BINS * 4);
+    w.hist_lo = off;
+    if (dtype == FP4_F32) off += align_up((size_t)HIST_LO_BINS * 4);
+    w.zero_end = off;
+    w.rowmax = off;
+    off += align_up((size_t)M * 4);
+    w.row_cnt = off;
+    off += align_up((size_t)M * 4);
+    w.stage = off;
+    off += align_up((size_t)(cap > 0 ? cap : 1) * sizeof(StageEntry));
+    w.total = off;
+    return w;
+}
+
+fp4_status hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
+
+// Enqueue the outlier pass: zero, histogram + row maxima, select T, then rows (clamp,
+// optional codes, staging of dA), then the COO scan + scatter.
+fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, double q, uint8_t *ws,
+                        const OutlierWs &w, int cus, float *T, int32_t *coo_row, int32_t *coo_col,
+                        float *coo_val, int64_t cap, int32_t *row_ptr, int64_t *nnz, uint8_t *Aq,
+                        float *sA, hipStream_t s) {
+    State *st = reinterpret_cast<State *>(ws + w.state);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + w.hist);
+    uint32_t *hist_lo = reinterpret_cast<uint32_t *>(ws + w.hist_lo);
+    uint32_t *rowmax = reinterpret_cast<uint32_t *>(ws + w.rowmax);
+    int32_t *row_cnt = reinterpret_cast<int32_t *>(ws + w.row_cnt);
+    StageEntry *stage = reinterpret_cast<StageEntry *>(ws + w.stage);
+    const int dt = dt_of(dtype);
+    const int64_t n = M * K;
+    const uint64_t k = (uint64_t)std::floor(q * (double)(n - 1));
+    hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(ws + w.state), (int64_t)(w.zero_end - w.state) / 4, s);
+    if (e == hipSuccess) e = launch_hist_rowmax(A, dt, M, K, hist, rowmax, cus, s);
+    if (e == hipSuccess) e = launch_select(A, dt, n, hist, hist_lo, st, T, k, s);
+    const bool codes = Aq != nullptr;
+    if (e == hipSuccess)
+        e = launch_quant_rows(A, dt, M, K, codes ? rowmax : nullptr, T, Aq, sA, row_cnt, stage, cap, st,
+                              /*emit=*/true, /*write_codes=*/codes, s);
+    if (e == hipSuccess) e = launch_coo(row_cnt, M, row_ptr, nnz, stage, st, cap, coo_row, coo_col, coo_val, s);
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *fp4_status_string(fp4_status s) {
+    switch (s) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_NULL: return "a required pointer is NULL";
+    case FP4_ERR_SHAPE: return "a size is out of range";
+    case FP4_ERR_DTYPE: return "unknown dtype or axis code, or unsupported combination";
+    case FP4_ERR_QUANTILE: return "q is NaN or outside [0, 1]";
+    case FP4_ERR_CAPACITY: return "COO capacity below fp4_outlier_capacity()";
+    case FP4_ERR_WORKSPACE: return "workspace smaller than required";
+    case FP4_ERR_DEVICE: return "current HIP device is not gfx950";
+    case FP4_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case FP4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+fp4_status fp4_quantize(const void *X, int32_t x_dtype, int64_t R, int64_t C, int32_t axis,
+                        const float *clamp_T, uint8_t *codes, float *scales, void *stream) {
+    if (!X || !codes || !scales) return FP4_ERR_NULL;
+    if (!dtype_ok(x_dtype) || (axis != FP4_PER_ROW && axis != FP4_PER_COL)) return FP4_ERR_DTYPE;
+    if (axis == FP4_PER_COL && clamp_T) return FP4_ERR_DTYPE;  // W is never clamped
+    if (axis == FP4_PER_ROW) {
+        if (!mk_ok(R, C)) return FP4_ERR_SHAPE;
+    } else {
+        if (!mk_ok(C, R) || !n_ok(C)) return FP4_ERR_SHAPE;
+    }
+    if (!aligned16(X) || !aligned16(codes) || !aligned16(scales)) return FP4_ERR_ALIGN;
+    int cus;
+    fp4_status st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (axis == FP4_PER_ROW)
+        return hip_status(launch_quant_rows(X, dt_of(x_dtype), R, C, nullptr, clamp_T, codes, scales, nullptr,
+                                            nullptr, 0, nullptr, false, true, s));
+    return hip_status(launch_quant_cols(X, dt_of(x_dtype), R, C, scales, codes, s));
+}
+
+int64_t fp4_outlier_capacity(int64_t M, int64_t K, double q) {
+    if (!mk_ok(M, K) || !q_ok(q)) return -1;
+    return capacity_of(M, K, q);
+}
+
+size_t fp4_outlier_workspace_bytes(int64_t M, int64_t K, int32_t a_dtype, double q) {
+    if (!mk_ok(M, K) || !q_ok(q) || !dtype_ok(a_dtype)) return 0;
+    return outlier_ws(M, a_dtype, capacity_of(M, K, q)).total;
+}
+
+fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t K, double q, float *T,
+                             int32_t *coo_row, int32_t *coo_col, float *coo_val, int64_t capacity,
+                             int32_t *row_ptr, int64_t *nnz, void *workspace, size_t ws_bytes, void *stream) {
+    if (!A || !T || !coo_row || !coo_col || !coo_val || !row_ptr || !nnz || !workspace) return FP4_ERR_NULL;
+    if (!dtype_ok(a_dtype)) return FP4_ERR_DTYPE;
+    if (!mk_ok(M, K)) return FP4_ERR_SHAPE;
+    if (!q_ok(q)) return FP4_ERR_QUANTILE;
+    const int64_t cap = capacity_of(M, K, q);
+    if (capacity < cap) return FP4_ERR_CAPACITY;
+    const OutlierWs w = outlier_ws(M, a_dtype, cap);
+    if (ws_bytes < w.total) return FP4_ERR_WORKSPACE;
+    if (!aligned16(A) || !aligned16(workspace) || !aligned16(T) || !aligned16(row_ptr)) return FP4_ERR_ALIGN;
+    int cus;
+    fp4_status st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    // nnz <= cap always (T is the (k+1)-th smallest |a|), so the staging area and the COO
+    // positions are bounded by the computed cap, which the workspace was sized for.
+    return run_outliers(A, a_dtype, M, K, q, static_cast<uint8_t *>(workspace), w, cus, T, coo_row, coo_col,
+                        coo_val, cap, row_ptr, nnz, nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
+}
+
+fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
+                    int64_t K, const int32_t *row_ptr, const int32_t *coo_col, const float *coo_val, const void *W,
+                    int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *stream) {
+    if (!Aq || !sA || !Wq || !sW || !Y) return FP4_ERR_NULL;
+    const int ncomp = (row_ptr != nullptr) + (coo_col != nullptr) + (coo_val != nullptr);
+    if (ncomp != 0 && ncomp != 3) return FP4_ERR_NULL;
+    if (ncomp == 3 && !W) return FP4_ERR_NULL;
+    if (!dtype_ok(y_dtype) || (ncomp == 3 && !dtype_ok(w_dtype))) return FP4_ERR_DTYPE;
+    if (!mk_ok(M, K) || !n_ok(N) || M > (int64_t)1 << 30) return FP4_ERR_SHAPE;
+    if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(Y) || (W && !aligned16(W)) || (acc_out && !aligned16(acc_out)))
+        return FP4_ERR_ALIGN;
+    int cus;
+    fp4_status st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, ncomp ? row_ptr : nullptr, coo_col, coo_val, W,
+                                  dt_of(w_dtype), Y, dt_of(y_dtype), acc_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q,
+                              struct fp4_ws_layout *out) {
+    if (!out) return FP4_ERR_NULL;
+    std::memset(out, 0, sizeof(*out));
+    if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
+    if (!mk_ok(M, K) || !n_ok(N) || M > (int64_t)1 << 30) return FP4_ERR_SHAPE;
+    if (!q_ok(q)) return FP4_ERR_QUANTILE;
+    const int64_t cap = capacity_of(M, K, q);
+    const size_t capn = (size_t)(cap > 0 ? cap : 1);
+    size_t off = 0;
+    out->T = off; off += ALIGN;
+    out->nnz = off; off += ALIGN;
+    out->row_ptr = off; off += align_up((size_t)(M + 1) * 4);
+    out->coo_row = off; off += align_up(capn * 4);
+    out->coo_col = off; off += align_up(capn * 4);
+    out->coo_val = off; off += align_up(capn * 4);
+    out->Aq = off; off += align_up((size_t)M * (size_t)(K / 2));
+    out->sA = off; off += align_up((size_t)M * 4);
+    out->Wq = off; off += align_up((size_t)N * (size_t)(K / 2));
+    out->sW = off; off += align_up((size_t)N * 4);
+    out->scratch = off; off += outlier_ws(M, in_dtype, cap).total;
+    out->total = off;
+    out->capacity = cap;
+    return FP4_OK;
+}
+
+size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q) {
+    fp4_ws_layout l;
+    return fp4_forward_layout(M, K, N, in_dtype, q, &l) == FP4_OK ? l.total : 0;
+}
+
+fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N,
+                              double q, void *Y, int32_t y_dtype, void *workspace, size_t ws_bytes, void *stream) {
+    if (!A || !W || !Y || !workspace) return FP4_ERR_NULL;
+    if (!dtype_ok(in_dtype) || !dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
+    fp4_ws_layout l;
+    fp4_status st = fp4_forward_layout(M, K, N, in_dtype, q, &l);
+    if (st != FP4_OK) return st;
+    if (ws_bytes < l.total) return FP4_ERR_WORKSPACE;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace)) return FP4_ERR_ALIGN;
+    int cus;
+    st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    float *T = reinterpret_cast<float *>(ws + l.T);
+    int64_t *nnz = reinterpret_cast<int64_t *>(ws + l.nnz);
+    int32_t *row_ptr = reinterpret_cast<int32_t *>(ws + l.row_ptr);
+    int32_t *coo_row = reinterpret_cast<int32_t *>(ws + l.coo_row);
+    int32_t *coo_col = reinterpret_cast<int32_t *>(ws + l.coo_col);
+    float *coo_val = reinterpret_cast<float *>(ws + l.coo_val);
+    uint8_t *Aq = ws + l.Aq;
+    float *sA = reinterpret_cast<float *>(ws + l.sA);
+    uint8_t *Wq = ws + l.Wq;
+    float *sW = reinterpret_cast<float *>(ws + l.sW);
+    const OutlierWs w = outlier_ws(M, in_dtype, l.capacity);
+    st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, T, coo_row, coo_col, coo_val, l.capacity,
+                      row_ptr, nnz, Aq, sA, s);
+    if (st != FP4_OK) return st;
+    hipError_t e = launch_quant_cols(W, dt_of(in_dtype), K, N, sW, Wq, s);
+    if (e == hipSuccess)
+        e = launch_gemm(Aq, sA, Wq, sW, M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype), Y, dt_of(y_dtype),
+                        nullptr, s);
+    return hip_status(e);
+}
+
+}  // extern "C"

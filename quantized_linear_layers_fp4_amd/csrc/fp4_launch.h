@@ -1,0 +1,32 @@
+// Host-side launchers of the gfx950 kernels (internal; the C ABI is include/fp4lin.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4_common.h"
+
+namespace fp4 {
+
+hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s);
+hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist,
+                              uint32_t *rowmax_key, int num_cus, hipStream_t s);
+hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint32_t *ghist_lo,
+                         State *st, float *T_out, uint64_t k, hipStream_t s);
+hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const uint32_t *rowmax_key,
+                             const float *T_src, uint8_t *codes, float *scales, int32_t *row_cnt,
+                             StageEntry *stage, int64_t stage_cap, State *st, bool emit, bool write_codes,
+                             hipStream_t s);
+hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out,
+                      const StageEntry *stage, const State *st, int64_t cap, int32_t *coo_row,
+                      int32_t *coo_col, float *coo_val, hipStream_t s);
+hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
+                             uint8_t *codes, hipStream_t s);
+
+// FP4 GEMM + dequantization + compensation.  comp arrays NULL = no compensation term.
+hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
+                       int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
+                       const float *coo_val, const void *W, int w_dt, void *Y, int y_dt, float *acc_out,
+                       hipStream_t s);
+
+}  // namespace fp4

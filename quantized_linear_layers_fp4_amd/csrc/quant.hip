@@ -1,0 +1,494 @@
+// gfx950 kernels of the bandwidth-bound half of the FP4 linear forward:
+//   - |A| histogram + raw row maxima, order-statistic select of the quantile threshold T
+//     (outlier paragraph of the QbitAI report on "Optimizing Large Language Model Training
+//     Using FP4 Quantization": outliers are found by a quantile search over A);
+//   - clamp of A to [-T, T], token-wise E2M1 quantization and staging of dA in column order
+//     (granularity, forward-quantization and outlier paragraphs of the same report);
+//   - exclusive scan + scatter that turns the staging into the (row, col)-sorted COO list;
+//   - channel-wise column maxima and transposed E2M1 packing of W (granularity paragraph).
+#include "fp4_common.h"
+#include "fp4_launch.h"
+
+namespace fp4 {
+
+// ----------------------------------------------------------------------------- zero fill
+__global__ void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+// ----------------------------------------------------------------------------- histogram
+// One workgroup of 1024 threads per CU holds a 32768-bin histogram of key >> 16 in LDS
+// (128 KiB); a wave owns one row at a time and also reduces the row's maximum key.
+// Rows [r0, r1) of the block are contiguous.  Non-empty bins are merged with global atomics.
+template <int DT>
+__global__ __launch_bounds__(1024) void k_hist_rowmax(const void *__restrict__ A, int64_t M, int64_t K,
+                                                      uint32_t *__restrict__ ghist,
+                                                      uint32_t *__restrict__ rowmax_key) {
+    __shared__ uint32_t h[HIST_BINS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < HIST_BINS; i += 1024) h[i] = 0u;
+    __syncthreads();
+    const int64_t rows_per = (M + gridDim.x - 1) / gridDim.x;
+    const int64_t r0 = blockIdx.x * rows_per;
+    const int64_t r1 = min(M, r0 + rows_per);
+    const int64_t nchunk = K / 8;  // 8 elements per chunk
+    for (int64_t row = r0 + wave; row < r1; row += 16) {
+        const int64_t base = row * K;
+        uint32_t mx = 0;
+        for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * 4) {
+            float v[4][8];
+            uint32_t key[4][8], sg[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                int64_t c = c0 + u * 64 + lane;
+                if (c < nchunk) load8<DT>(A, base + c * 8, v[u], key[u], sg[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                int64_t c = c0 + u * 64 + lane;
+                if (c < nchunk) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        atomicAdd(&h[key[u][e] >> 16], 1u);
+                        mx = max(mx, key[u][e]);
+                    }
+                }
+            }
+        }
+        mx = wave_max_u32(mx);
+        if (lane == 0) rowmax_key[row] = mx;
+    }
+    __syncthreads();
+    for (int i = tid; i < HIST_BINS; i += 1024) {
+        uint32_t c = h[i];
+        if (c) atomicAdd(&ghist[i], c);
+    }
+}
+
+// Second level for fp32 inputs: among the entries whose key >> 16 is the selected bin,
+// histogram the low 16 bits (few entries: global atomics).
+__global__ __launch_bounds__(256) void k_hist_lo(const uint32_t *__restrict__ A, int64_t n,
+                                                 const State *__restrict__ st,
+                                                 uint32_t *__restrict__ ghist_lo) {
+    const uint32_t hi = st->hi_bin;
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+        uint32_t k = key_of_f32(A[i]);
+        if ((k >> 16) == hi) atomicAdd(&ghist_lo[k & 0xFFFFu], 1u);
+    }
+}
+
+// Select the bin holding rank k (0-based) of a histogram of NB bins with one workgroup.
+// level 1: k = k_level1 (computed on the host) over the 32768 high bins; level 2: k = st->k_rem over the 65536 low
+// bins of the selected high bin.  final_level says which level fixes T.
+template <int NB>
+__global__ __launch_bounds__(1024) void k_select(const uint32_t *__restrict__ hist, State *__restrict__ st,
+                                                 int level, int final_level, float *__restrict__ T_out,
+                                                 uint64_t k_level1) {
+    constexpr int PER = NB / 1024;
+    __shared__ uint64_t part[1024];
+    const int tid = threadIdx.x;
+    uint64_t local = 0;
+    for (int i = 0; i < PER; ++i) local += hist[tid * PER + i];
+    part[tid] = local;
+    __syncthreads();
+    // inclusive Hillis-Steele scan over 1024 partial sums
+    for (int off = 1; off < 1024; off <<= 1) {
+        uint64_t x = (tid >= off) ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += x;
+        __syncthreads();
+    }
+    const uint64_t incl = part[tid], excl = incl - local, total = part[1023];
+    const uint64_t k = (level == 1) ? k_level1 : st->k_rem;
+    if (excl <= k && k < incl) {
+        uint64_t cum = excl;
+        int b = tid * PER;
+        for (int i = 0; i < PER; ++i) {
+            uint32_t c = hist[tid * PER + i];
+            if (k < cum + c) {
+                b = tid * PER + i;
+                break;
+            }
+            cum += c;
+        }
+        const uint32_t cnt = hist[b];
+        const uint64_t above = total - (cum + cnt);  // entries in later bins
+        if (level == 1) {
+            st->hi_bin = (uint32_t)b;
+            st->hi_count = cnt;
+            st->k_rem = k - cum;
+            st->nnz_hist = above;
+            if (final_level == 1) {
+                st->T_key = (uint32_t)b << 16;
+                st->T = __uint_as_float((uint32_t)b << 16);
+                *T_out = st->T;
+            }
+        } else {
+            const uint32_t key = (st->hi_bin << 16) | (uint32_t)b;
+            st->T_key = key;
+            st->T = __uint_as_float(key);
+            st->nnz_hist += above;
+            *T_out = st->T;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- rows (A)
+// One wave per row.  Optionally clamps to [-T, T] (T from *T_src), writes the row's E2M1
+// codes and scale, and stages the clamped-away residuals dA in ascending column order.
+//   HAVE_ROWMAX: the raw row maximum key comes from rowmax_key (histogram pass); otherwise
+//                a first sweep over the row computes it.
+template <int DT, bool CLAMP, bool HAVE_ROWMAX, bool CODES, bool EMIT>
+__global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, int64_t R, int64_t C,
+                                                    const uint32_t *__restrict__ rowmax_key,
+                                                    const float *__restrict__ T_src,
+                                                    uint8_t *__restrict__ codes, float *__restrict__ scales,
+                                                    int32_t *__restrict__ row_cnt,
+                                                    StageEntry *__restrict__ stage, int64_t stage_cap,
+                                                    State *__restrict__ st) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= R) return;  // whole wave exits together
+    const int64_t base = row * C;
+    const int64_t nchunk = C / 8;
+    const uint32_t tkey = CLAMP ? key_of_f32(__float_as_uint(*T_src)) : 0xFFFFFFFFu;
+
+    uint32_t mx = 0;
+    if constexpr (HAVE_ROWMAX) {
+        mx = rowmax_key[row];
+    } else if constexpr (CODES) {
+        for (int64_t c = lane; c < nchunk; c += 64) {
+            float v[8];
+            uint32_t key[8], sg[8];
+            load8<DT>(X, base + c * 8, v, key, sg);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = max(mx, key[e]);
+        }
+        mx = wave_max_u32(mx);
+    }
+    mx = min(mx, tkey);  // max |clamp(a)| = min(max |a|, T)
+    float r = 0.0f, s = 0.0f;
+    if constexpr (CODES) {
+        vector_scale(__uint_as_float(mx), r, s);
+        if (lane == 0) scales[row] = s;
+    }
+    uint32_t running = 0;  // outliers of this row emitted so far
+    for (int64_t c0 = 0; c0 < nchunk; c0 += 64) {
+        const int64_t c = c0 + lane;
+        const bool valid = c < nchunk;
+        float v[8];
+        uint32_t key[8], sg[8];
+        if (valid) load8<DT>(X, base + c * 8, v, key, sg);
+        uint32_t omask = 0;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool out = valid && key[e] > tkey;
+            omask |= (uint32_t)out << e;
+            const float ac = out ? __uint_as_float(sg[e] | tkey) : v[e];
+            y[e] = ac * r;
+        }
+        if constexpr (CODES) {
+            if (valid) *reinterpret_cast<uint32_t *>(codes + row * (C / 2) + c * 4) = e2m1_pack8(y);
+        }
+        if constexpr (EMIT) {
+            const uint32_t cnt = __popc(omask);
+            if (__ballot(cnt != 0)) {
+                const uint32_t incl = wave_incl_scan(cnt, lane);
+                const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+                unsigned long long b0 = 0;
+                if (lane == 0) b0 = atomicAdd(&st->stage_count, (unsigned long long)total);
+                b0 = (unsigned long long)__shfl((long long)b0, 0, 64);
+                uint32_t rank = running + incl - cnt;
+                unsigned long long slot = b0 + (incl - cnt);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (omask & (1u << e)) {
+                        if (slot < (unsigned long long)stage_cap) {
+                            StageEntry ent;
+                            ent.row = (int32_t)row;
+                            ent.rank = (int32_t)rank;
+                            ent.col = (int32_t)(c * 8 + e);
+                            ent.val = v[e] - __uint_as_float(sg[e] | tkey);
+                            stage[slot] = ent;
+                        }
+                        ++rank;
+                        ++slot;
+                    }
+                }
+                running += total;
+            }
+        }
+    }
+    if constexpr (EMIT) {
+        if (lane == 0) row_cnt[row] = (int32_t)running;
+    }
+}
+
+// ----------------------------------------------------------------------------- COO
+// Exclusive scan of the per-row outlier counts (one workgroup of 1024 threads).
+__global__ __launch_bounds__(1024) void k_coo_scan(const int32_t *__restrict__ row_cnt, int64_t M,
+                                                   int32_t *__restrict__ row_ptr,
+                                                   int64_t *__restrict__ nnz_out) {
+    constexpr int ITEMS = 8;
+    __shared__ uint32_t part[1024];
+    __shared__ uint32_t carry_s;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry_s = 0;
+    __syncthreads();
+    for (int64_t b0 = 0; b0 < M; b0 += 1024 * ITEMS) {
+        uint32_t c[ITEMS], local = 0;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            int64_t r = b0 + (int64_t)tid * ITEMS + i;
+            c[i] = (r < M) ? (uint32_t)row_cnt[r] : 0u;
+            local += c[i];
+        }
+        part[tid] = local;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            uint32_t x = (tid >= off) ? part[tid - off] : 0u;
+            __syncthreads();
+            part[tid] += x;
+            __syncthreads();
+        }
+        uint32_t run = carry_s + part[tid] - local;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            int64_t r = b0 + (int64_t)tid * ITEMS + i;
+            if (r < M) row_ptr[r] = (int32_t)run;
+            run += c[i];
+        }
+        __syncthreads();
+        if (tid == 1023) carry_s += part[1023];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        row_ptr[M] = (int32_t)carry_s;
+        *nnz_out = (int64_t)carry_s;
+    }
+}
+
+// Move each staged entry to row_ptr[row] + rank.
+__global__ __launch_bounds__(256) void k_coo_scatter(const StageEntry *__restrict__ stage,
+                                                     const State *__restrict__ st,
+                                                     const int32_t *__restrict__ row_ptr, int64_t cap,
+                                                     int32_t *__restrict__ coo_row, int32_t *__restrict__ coo_col,
+                                                     float *__restrict__ coo_val) {
+    const int64_t n = min((int64_t)st->stage_count, cap);
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+        StageEntry e = stage[i];
+        int64_t pos = (int64_t)row_ptr[e.row] + e.rank;
+        if (pos < cap) {
+            if (coo_row) coo_row[pos] = e.row;
+            coo_col[pos] = e.col;
+            coo_val[pos] = e.val;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- columns (W)
+// Column maxima of K x N W (keys), merged with atomicMax into colmax_key (zeroed before).
+// Block: 256 threads = 4 waves over the same 512 columns (8 per lane), rows split by wave.
+template <int DT>
+__global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int64_t K, int64_t N,
+                                                int rows_per_block, uint32_t *__restrict__ colmax_key) {
+    __shared__ uint32_t red[4][512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = min(K, r0 + rows_per_block);
+    uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (col < N) {
+        int64_t r = r0 + wave;
+        for (; r + 12 < r1; r += 16) {
+            float v[4][8];
+            uint32_t key[4][8], sg[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) load8<DT>(W, (r + 4 * u) * N + col, v[u], key[u], sg[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mx[e] = max(mx[e], key[u][e]);
+        }
+        for (; r < r1; r += 4) {
+            float v[8];
+            uint32_t key[8], sg[8];
+            load8<DT>(W, r * N + col, v, key, sg);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx[e] = max(mx[e], key[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = mx[e];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 512; i += 256) {
+        uint32_t m = max(max(red[0][i], red[1][i]), max(red[2][i], red[3][i]));
+        int64_t c = (int64_t)blockIdx.x * 512 + i;
+        if (c < N && m) atomicMax(&colmax_key[c], m);
+    }
+}
+
+// Quantize a 256 (k) x 64 (n) tile of W with the finished column maxima and write it
+// transposed: Wq[n][k/2].  Loads: 8 threads per row (16 bytes = 8 columns each), two rows
+// (k, k+1) per thread per pass so each output byte (pair of k) is formed in registers; the
+// transpose goes through a 64 x 128-byte LDS tile.
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, int64_t K, int64_t N,
+                                                    const uint32_t *__restrict__ colmax_key,
+                                                    uint8_t *__restrict__ codes) {
+    __shared__ float rs[64];
+    __shared__ uint8_t tile[64][128 + 4];
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 256;
+    if (tid < 64) {
+        float r = 0.0f, s;
+        if (n0 + tid < N) vector_scale(__uint_as_float(colmax_key[n0 + tid]), r, s);
+        rs[tid] = r;
+    }
+    __syncthreads();
+    const int c8 = tid & 7;           // columns n0 + 8*c8 .. +7
+    const int64_t col = n0 + c8 * 8;
+    float r8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r8[e] = rs[c8 * 8 + e];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int j = (tid >> 3) + 32 * p;  // row pair: rows 2j, 2j+1 of the tile
+        const int64_t k = k0 + 2 * j;
+        uint32_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (col < N && k < K) {  // K % 32 == 0: both rows of a pair are in range together
+            float v0[8], v1[8];
+            uint32_t key0[8], key1[8], sg0[8], sg1[8];
+            load8<DT>(W, k * N + col, v0, key0, sg0);
+            load8<DT>(W, (k + 1) * N + col, v1, key1, sg1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = e2m1_pack2<0>(0u, v0[e] * r8[e], v1[e] * r8[e]) & 0xFFu;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[c8 * 8 + e][j] = (uint8_t)b[e];
+    }
+    __syncthreads();
+    // write out: n = tid / 4, 32 bytes (64 k) per thread
+    const int nl = tid >> 2, part = tid & 3;
+    const int64_t n = n0 + nl;
+    const int64_t kb = k0 / 2 + part * 32;  // byte offset within the row of Wq
+    if (n < N) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (kb + h * 16 < K / 2) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int o = part * 32 + h * 16 + i * 4;
+                    w[i] = (uint32_t)tile[nl][o] | ((uint32_t)tile[nl][o + 1] << 8) |
+                           ((uint32_t)tile[nl][o + 2] << 16) | ((uint32_t)tile[nl][o + 3] << 24);
+                }
+                *reinterpret_cast<uint4 *>(codes + n * (K / 2) + kb + h * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
+// Column maxima keys -> dequantization scales, in place.
+__global__ void k_col_scales(uint32_t *__restrict__ colmax_key_then_scale, int64_t N) {
+    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < N) {
+        float r, s;
+        vector_scale(__uint_as_float(colmax_key_then_scale[i]), r, s);
+        colmax_key_then_scale[i] = __float_as_uint(s);
+    }
+}
+
+// ----------------------------------------------------------------------------- launchers
+static inline int blocks_for(int64_t n, int threads, int cap) {
+    int64_t b = (n + threads - 1) / threads;
+    if (b > cap) b = cap;
+    return (int)(b < 1 ? 1 : b);
+}
+
+hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_u32, dim3(blocks_for(n, 256, 1024)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist,
+                              uint32_t *rowmax_key, int num_cus, hipStream_t s) {
+    int blocks = (int)(M < (int64_t)num_cus ? M : (int64_t)num_cus);
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(k_hist_rowmax<DT_BF16>, dim3(blocks), dim3(1024), 0, s, A, M, K, ghist, rowmax_key);
+    else
+        hipLaunchKernelGGL(k_hist_rowmax<DT_F32>, dim3(blocks), dim3(1024), 0, s, A, M, K, ghist, rowmax_key);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint32_t *ghist_lo,
+                         State *st, float *T_out, uint64_t k, hipStream_t s) {
+    const int final_level = (dt == DT_BF16) ? 1 : 2;
+    hipLaunchKernelGGL(k_select<HIST_BINS>, dim3(1), dim3(1024), 0, s, ghist, st, 1, final_level, T_out, k);
+    if (dt == DT_F32) {
+        hipLaunchKernelGGL(k_hist_lo, dim3(blocks_for(n, 256, 2048)), dim3(256), 0, s,
+                           (const uint32_t *)A, n, st, ghist_lo);
+        hipLaunchKernelGGL(k_select<HIST_LO_BINS>, dim3(1), dim3(1024), 0, s, ghist_lo, st, 2, 2, T_out, k);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const uint32_t *rowmax_key,
+                             const float *T_src, uint8_t *codes, float *scales, int32_t *row_cnt,
+                             StageEntry *stage, int64_t stage_cap, State *st, bool emit, bool write_codes,
+                             hipStream_t s) {
+    dim3 grid((unsigned)((R + 3) / 4)), block(256);
+    const bool clamp = T_src != nullptr;
+    const bool have_rm = rowmax_key != nullptr;
+#define QR(DT, CL, HR, CO, EM)                                                                      \
+    hipLaunchKernelGGL((k_quant_rows<DT, CL, HR, CO, EM>), grid, block, 0, s, X, R, C, rowmax_key, T_src, \
+                       codes, scales, row_cnt, stage, stage_cap, st)
+    if (dt == DT_BF16) {
+        if (emit && write_codes && have_rm) QR(DT_BF16, true, true, true, true);
+        else if (emit && !write_codes) QR(DT_BF16, true, false, false, true);
+        else if (clamp) QR(DT_BF16, true, false, true, false);
+        else QR(DT_BF16, false, false, true, false);
+    } else {
+        if (emit && write_codes && have_rm) QR(DT_F32, true, true, true, true);
+        else if (emit && !write_codes) QR(DT_F32, true, false, false, true);
+        else if (clamp) QR(DT_F32, true, false, true, false);
+        else QR(DT_F32, false, false, true, false);
+    }
+#undef QR
+    return hipGetLastError();
+}
+
+hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out,
+                      const StageEntry *stage, const State *st, int64_t cap, int32_t *coo_row,
+                      int32_t *coo_col, float *coo_val, hipStream_t s) {
+    hipLaunchKernelGGL(k_coo_scan, dim3(1), dim3(1024), 0, s, row_cnt, M, row_ptr, nnz_out);
+    hipLaunchKernelGGL(k_coo_scatter, dim3(blocks_for(cap, 256, 4096)), dim3(256), 0, s, stage, st, row_ptr,
+                       cap, coo_row, coo_col, coo_val);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
+                             uint8_t *codes, hipStream_t s) {
+    uint32_t *keys = reinterpret_cast<uint32_t *>(scales_as_keys);
+    hipError_t e = launch_zero(keys, N, s);
+    if (e != hipSuccess) return e;
+    const int rows_per_block = 256;
+    dim3 g1((unsigned)((N + 511) / 512), (unsigned)((K + rows_per_block - 1) / rows_per_block));
+    dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
+    if (dt == DT_BF16) {
+        hipLaunchKernelGGL(k_colmax<DT_BF16>, g1, dim3(256), 0, s, W, K, N, rows_per_block, keys);
+        hipLaunchKernelGGL(k_quant_cols<DT_BF16>, g2, dim3(256), 0, s, W, K, N, keys, codes);
+    } else {
+        hipLaunchKernelGGL(k_colmax<DT_F32>, g1, dim3(256), 0, s, W, K, N, rows_per_block, keys);
+        hipLaunchKernelGGL(k_quant_cols<DT_F32>, g2, dim3(256), 0, s, W, K, N, keys, codes);
+    }
+    hipLaunchKernelGGL(k_col_scales, dim3(blocks_for(N, 256, 1 << 20)), dim3(256), 0, s, keys, N);
+    return hipGetLastError();
+}
+
+}  // namespace fp4

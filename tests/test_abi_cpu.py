@@ -1,0 +1,131 @@
+"""The C ABI on the host: the library loads, exports what include/fp4lin.h declares, and
+rejects invalid arguments before any HIP call (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle
+import quantized_linear_layers_fp4_amd as fp4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4lin.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EQ, ECAP, EWS, EDEV, EHIP, EALIGN = range(10)
+FAKE = C.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp4_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_symbols() == sorted(fp4.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fp4.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = fp4.lib()
+    for s in range(10):
+        assert L.fp4_status_string(s)
+    assert L.fp4_status_string(99) == b"unknown status"
+
+
+def test_capacity_matches_oracle():
+    L = fp4.lib()
+    for (M, K, q) in [(128, 256, 0.99), (8192, 2048, 0.99), (16384, 4096, 0.999), (16384, 13824, 0.99),
+                      (7, 32, 0.0), (7, 32, 1.0), (1, 32, 0.5)]:
+        assert L.fp4_outlier_capacity(M, K, q) == oracle.capacity(M, K, q)
+    assert L.fp4_outlier_capacity(16384, 4096, 0.999) == 67109
+    assert L.fp4_outlier_capacity(10, 33, 0.5) == -1          # K % 32
+    assert L.fp4_outlier_capacity(10, 32, float("nan")) == -1
+    assert L.fp4_outlier_capacity(10, 32, 1.5) == -1
+
+
+def test_forward_layout_is_disjoint_and_aligned():
+    lay = fp4.WsLayout()
+    L = fp4.lib()
+    assert L.fp4_forward_layout(300, 512, 264, fp4.FP4_BF16, 0.99, C.byref(lay)) == OK
+    cap = lay.capacity
+    parts = [(lay.T, 4), (lay.nnz, 8), (lay.row_ptr, 301 * 4), (lay.coo_row, cap * 4), (lay.coo_col, cap * 4),
+             (lay.coo_val, cap * 4), (lay.Aq, 300 * 256), (lay.sA, 300 * 4), (lay.Wq, 264 * 256),
+             (lay.sW, 264 * 4), (lay.scratch, 1)]
+    parts.sort()
+    for (a, na), (b, _) in zip(parts, parts[1:]):
+        assert a % 256 == 0 and a + na <= b
+    assert parts[-1][0] < lay.total
+    assert L.fp4_forward_workspace_bytes(300, 512, 264, fp4.FP4_BF16, 0.99) == lay.total
+    assert L.fp4_forward_workspace_bytes(300, 500, 264, fp4.FP4_BF16, 0.99) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_A", ENULL), ("bad_dtype", EDTYPE), ("bad_ydtype", EDTYPE), ("k_not_32", ESHAPE), ("k_too_big", ESHAPE),
+    ("k_small", ESHAPE), ("n_not_8", ESHAPE), ("m_zero", ESHAPE), ("q_nan", EQ), ("q_neg", EQ), ("ws_small", EWS),
+    ("misaligned", EALIGN),
+])
+def test_linear_forward_rejects(case, expect):
+    L = fp4.lib()
+    args = dict(A=FAKE, W=FAKE, dt=fp4.FP4_BF16, M=64, K=128, N=64, q=0.99, Y=FAKE, ydt=fp4.FP4_BF16,
+                ws=FAKE, wsb=1 << 40)
+    if case == "null_A": args["A"] = None
+    if case == "bad_dtype": args["dt"] = 7
+    if case == "bad_ydtype": args["ydt"] = -1
+    if case == "k_not_32": args["K"] = 100
+    if case == "k_too_big": args["K"] = 65536 + 32
+    if case == "k_small": args["K"] = 0
+    if case == "n_not_8": args["N"] = 100
+    if case == "m_zero": args["M"] = 0
+    if case == "q_nan": args["q"] = float("nan")
+    if case == "q_neg": args["q"] = -0.01
+    if case == "ws_small": args["wsb"] = 1024
+    if case == "misaligned": args["Y"] = C.c_void_p(0x100004)
+    st = L.fp4_linear_forward(args["A"], args["W"], args["dt"], args["M"], args["K"], args["N"], args["q"],
+                              args["Y"], args["ydt"], args["ws"], args["wsb"], None)
+    assert st == expect
+
+
+def test_quantize_rejects():
+    L = fp4.lib()
+    c = C.c_void_p
+    assert L.fp4_quantize(None, 1, 4, 64, 0, None, FAKE, FAKE, None) == ENULL
+    assert L.fp4_quantize(FAKE, 1, 4, 64, 2, None, FAKE, FAKE, None) == EDTYPE
+    assert L.fp4_quantize(FAKE, 1, 4, 48, 0, None, FAKE, FAKE, None) == ESHAPE   # C % 32
+    assert L.fp4_quantize(FAKE, 1, 48, 64, 1, None, FAKE, FAKE, None) == ESHAPE  # R % 32 for PER_COL
+    assert L.fp4_quantize(FAKE, 1, 64, 12, 1, None, FAKE, FAKE, None) == ESHAPE  # C % 8 for PER_COL
+    assert L.fp4_quantize(FAKE, 1, 64, 64, 1, FAKE, FAKE, FAKE, None) == EDTYPE  # W is never clamped
+    assert L.fp4_quantize(c(0x100002), 1, 4, 64, 0, None, FAKE, FAKE, None) == EALIGN
+
+
+def test_outlier_clamp_rejects():
+    L = fp4.lib()
+    M, K, q = 64, 128, 0.99
+    cap = L.fp4_outlier_capacity(M, K, q)
+    wsb = L.fp4_outlier_workspace_bytes(M, K, fp4.FP4_BF16, q)
+    assert wsb > 0
+    call = lambda **kw: L.fp4_outlier_clamp(kw.get("A", FAKE), kw.get("dt", 1), M, K, kw.get("q", q), FAKE, FAKE,
+                                            FAKE, FAKE, kw.get("cap", cap), FAKE, FAKE, FAKE, kw.get("wsb", wsb), None)
+    assert call(A=None) == ENULL
+    assert call(dt=3) == EDTYPE
+    assert call(q=2.0) == EQ
+    assert call(cap=cap - 1) == ECAP
+    assert call(wsb=wsb - 1) == EWS
+
+
+def test_gemm_rejects():
+    L = fp4.lib()
+    g = lambda **kw: L.fp4_gemm(kw.get("Aq", FAKE), FAKE, FAKE, FAKE, kw.get("M", 64), kw.get("N", 64),
+                                kw.get("K", 128), kw.get("rp", None), kw.get("cc", None), kw.get("cv", None),
+                                kw.get("W", None), 1, FAKE, kw.get("ydt", 1), None, None)
+    assert g(Aq=None) == ENULL
+    assert g(rp=FAKE) == ENULL            # partial compensation arguments
+    assert g(rp=FAKE, cc=FAKE, cv=FAKE) == ENULL  # compensation without W
+    assert g(ydt=5) == EDTYPE
+    assert g(K=96 + 16) == ESHAPE
+    assert g(N=0) == ESHAPE

@@ -1,0 +1,343 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
+
+Bit-exact: E2M1 codes, scales, T, nnz, the COO list of dA, row_ptr and the raw
+accumulator.  Y (fp32) within the tolerance in parity_util.REL; bf16 Y a correct
+rounding of a value within that tolerance.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_linear_layers_fp4_amd as fp4
+from parity_util import (assert_bf16_close, assert_y_close, bf16_to_f64, oracle_inputs, to_np)
+from workloads import CONFIGS, as_numpy_bits, make_custom, make_layer
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dt(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+# ----------------------------------------------------------------------------- codec
+def test_codec_every_bf16_pattern():
+    # every bf16 magnitude up to 6, both signs, in rows whose maximum is exactly 6 so the
+    # multiplier r = fl(6/6) = 1 and the codes are the plain E2M1 rounding of the input
+    _say("codec sweep bf16")
+    pats = np.arange(0, 0x40C1, dtype=np.uint16)
+    vals = np.concatenate([pats, pats | 0x8000]).astype(np.uint16)
+    per_row = 511
+    nrows = -(-vals.size // per_row)
+    X = np.zeros((nrows, 512), dtype=np.uint16)
+    flat = np.zeros(nrows * per_row, dtype=np.uint16)
+    flat[:vals.size] = vals
+    X[:, 1:] = flat.reshape(nrows, per_row)
+    X[:, 0] = 0x40C0  # 6.0
+    Xt = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(DEV)
+    codes, scales = fp4.quantize(Xt, fp4.FP4_PER_ROW)
+    ref_c, ref_s = oracle.quant_rows(X)
+    assert np.array_equal(to_np(scales), ref_s)
+    assert np.array_equal(to_np(codes), ref_c)
+
+
+def test_codec_fp32_sweep():
+    _say("codec sweep fp32")
+    rng = np.random.default_rng(2)
+    pats = np.arange(0, 0x40C00001, 9973, dtype=np.uint32).view(np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+    near = np.concatenate([np.nextafter(mids, np.float32(0)), mids, np.nextafter(mids, np.float32(9))])
+    vals = np.concatenate([pats, near, rng.uniform(0, 6, 100000).astype(np.float32)])
+    vals = np.concatenate([vals, -vals])
+    per_row = 1023
+    nrows = -(-vals.size // per_row)
+    X = np.zeros((nrows, 1024), dtype=np.float32)
+    flat = np.zeros(nrows * per_row, dtype=np.float32)
+    flat[:vals.size] = vals
+    X[:, 1:] = flat.reshape(nrows, per_row)
+    X[:, 0] = 6.0
+    codes, scales = fp4.quantize(torch.from_numpy(X).to(DEV), fp4.FP4_PER_ROW)
+    ref_c, ref_s = oracle.quant_rows(X)
+    assert np.array_equal(to_np(scales), ref_s)
+    assert np.array_equal(to_np(codes), ref_c)
+
+
+# ----------------------------------------------------------------------------- quantizers
+ROW_SHAPES = [(1, 32), (37, 96), (257, 1056), (300, 4096), (4, 65536)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_quantize_rows(dtype, shape):
+    R, C = shape
+    _say(f"quantize rows {dtype} {shape}")
+    rng = np.random.default_rng(R * 7 + C)
+    X = (rng.standard_normal((R, C)) * rng.lognormal(0, 2, (R, 1))).astype(np.float32)
+    if R > 3:
+        X[1] = 0.0  # all-zero row: scale 0, sign-only codes
+        X[2, : C // 2] = -0.0
+    Xt = torch.from_numpy(X).to(_dt(dtype))
+    codes, scales = fp4.quantize(Xt.to(DEV), fp4.FP4_PER_ROW)
+    ref_c, ref_s = oracle.quant_rows(as_numpy_bits(Xt))
+    assert np.array_equal(to_np(scales), ref_s)
+    assert np.array_equal(to_np(codes), ref_c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_rows_clamped(dtype):
+    R, C = 130, 512
+    _say(f"quantize rows clamped {dtype}")
+    A, _ = make_custom(R, C, 8, dtype=dtype, seed=5)
+    Anp = as_numpy_bits(A)
+    T = oracle.abs_quantile(Anp, 0.99)
+    Tt = torch.tensor([T], dtype=torch.float32, device=DEV)
+    codes, scales = fp4.quantize(A.to(DEV), fp4.FP4_PER_ROW, clamp_T=Tt)
+    Ac = oracle.clamp_coo(Anp, T)["A_clamped"]
+    ref_c, ref_s = oracle.quant_rows(Ac)
+    assert np.array_equal(to_np(scales), ref_s)
+    assert np.array_equal(to_np(codes), ref_c)
+
+
+COL_SHAPES = [(32, 8), (96, 264), (1056, 520), (4096, 1000), (288, 4104)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("shape", COL_SHAPES)
+def test_quantize_cols(dtype, shape):
+    K, N = shape
+    _say(f"quantize cols {dtype} {shape}")
+    rng = np.random.default_rng(K + 3 * N)
+    W = (rng.standard_normal((K, N)) * rng.lognormal(-3, 1, (1, N))).astype(np.float32)
+    W[:, 3] = 0.0
+    Wt = torch.from_numpy(W).to(_dt(dtype))
+    codes, scales = fp4.quantize(Wt.to(DEV), fp4.FP4_PER_COL)
+    ref_c, ref_s = oracle.quant_cols(as_numpy_bits(Wt))
+    assert np.array_equal(to_np(scales), ref_s)
+    assert np.array_equal(to_np(codes), ref_c)
+
+
+# ----------------------------------------------------------------------------- outliers
+OUT_CASES = [
+    ("bf16", 64, 128, 0.99, "student_t"), ("bf16", 300, 1056, 0.99, "normal_sparse_outliers"),
+    ("bf16", 1000, 4096, 0.999, "normal_sparse_outliers"), ("fp32", 128, 256, 0.99, "normal_sparse_outliers"),
+    ("fp32", 333, 512, 0.9, "student_t"), ("bf16", 17, 64, 0.0, "plain"), ("bf16", 40, 96, 1.0, "plain"),
+    ("fp32", 9, 32, 0.5, "plain"), ("bf16", 2000, 2048, 0.5, "student_t"),
+]
+
+
+@pytest.mark.parametrize("dtype,M,K,q,kind", OUT_CASES)
+def test_outlier_clamp(dtype, M, K, q, kind):
+    _say(f"outlier clamp {dtype} {M}x{K} q={q} {kind}")
+    A, _ = make_custom(M, K, 8, dtype=dtype, seed=M + K, kind=kind)
+    out = fp4.outlier_clamp(A.to(DEV), q)
+    Anp = as_numpy_bits(A)
+    T = oracle.abs_quantile(Anp, q)
+    ref = oracle.clamp_coo(Anp, T, want_clamped=False)
+    assert float(out["T"].item()) == T
+    assert int(out["nnz"].item()) == ref["nnz"] <= oracle.capacity(M, K, q)
+    assert np.array_equal(to_np(out["row_ptr"]), ref["row_ptr"])
+    assert np.array_equal(to_np(out["coo_row"]), ref["coo_row"])
+    assert np.array_equal(to_np(out["coo_col"]), ref["coo_col"])
+    assert np.array_equal(to_np(out["coo_val"]), ref["coo_val"])
+
+
+# ----------------------------------------------------------------------------- GEMM
+def _random_codes(rng, R, K):
+    return rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+
+
+GEMM_SHAPES = [(256, 256, 256), (300, 264, 320), (513, 776, 1056), (64, 8, 32), (1, 520, 4096), (777, 1032, 2080)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_accumulator_exact(M, N, K):
+    _say(f"gemm acc {M}x{N}x{K}")
+    rng = np.random.default_rng(M * N + K)
+    Aq, Wq = _random_codes(rng, M, K), _random_codes(rng, N, K)
+    sA = rng.lognormal(-2, 1, M).astype(np.float32)
+    sW = rng.lognormal(-4, 1, N).astype(np.float32)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    Y, acc = fp4.gemm(t(Aq), t(sA), t(Wq), t(sW), K, out_dtype=torch.float32, acc_out=True)
+    ref_acc = oracle.accumulate(Aq, Wq, K)
+    assert np.array_equal(to_np(acc), ref_acc)
+    ref_y, denom = oracle.output(ref_acc, sA, sW, None, None, None, np.zeros((K, N), dtype=np.float32))
+    assert np.array_equal(to_np(Y), ref_y)  # no compensation: the dequantized product is bit-exact
+
+
+def test_gemm_accumulator_extremes():
+    # every product +-36 over the longest K: |acc| = 36 * 65536, still exact in fp32
+    M, N, K = 40, 24, 65536
+    _say("gemm acc extremes K=65536")
+    Aq = np.full((M, K // 2), 0x77, dtype=np.uint8)
+    Aq[1::2] = 0xFF
+    Wq = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    Wq[::3] = 0xF7  # alternating +-6 along k
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    ones_m = torch.ones(M, device=DEV)
+    ones_n = torch.ones(N, device=DEV)
+    _, acc = fp4.gemm(t(Aq), ones_m, t(Wq), ones_n, K, out_dtype=torch.float32, acc_out=True)
+    assert np.array_equal(to_np(acc), oracle.accumulate(Aq, Wq, K))
+    assert to_np(acc)[0, 1] == 36.0 * K and to_np(acc)[1, 1] == -36.0 * K
+
+
+@pytest.mark.parametrize("M,N,K,wdt", [(300, 264, 512, "bf16"), (513, 520, 1056, "fp32"), (64, 8, 96, "bf16")])
+def test_gemm_with_compensation(M, N, K, wdt):
+    _say(f"gemm comp {M}x{N}x{K} {wdt}")
+    A, W = make_custom(M, K, N, dtype=wdt, seed=11)
+    Anp, Wnp = oracle_inputs(A, W)
+    q = 0.98
+    ref = oracle.forward(Anp, Wnp, q)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    args = (t(ref["Aq"]), t(ref["sA"]), t(ref["Wq"]), t(ref["sW"]), K)
+    kw = dict(row_ptr=t(ref["row_ptr"]), coo_col=t(ref["coo_col"]), coo_val=t(ref["coo_val"]), W=W.to(DEV))
+    Y32 = fp4.gemm(*args, **kw, out_dtype=torch.float32)
+    Y16 = fp4.gemm(*args, **kw, out_dtype=torch.bfloat16)
+    assert_y_close(to_np(Y32), ref["Y"], ref["denom"])
+    # the bf16 output is the round-to-nearest-even of the same fp32 result
+    assert np.array_equal(to_np(Y16), to_np(Y32.to(torch.bfloat16)))
+
+
+# ----------------------------------------------------------------------------- forward
+def _check_forward_small(A, W, q, out_dtype):
+    M, K = A.shape
+    N = W.shape[1]
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    ws = fp4.workspace(Ad, N, q)
+    Y = fp4.linear_forward(Ad, Wd, q, out_dtype=out_dtype, ws=ws)
+    torch.cuda.synchronize()
+    inter = fp4.forward_intermediates(ws, M, K, N, A.dtype, q)
+    Anp, Wnp = oracle_inputs(A, W)
+    ref = oracle.forward(Anp, Wnp, q)
+    nnz = int(inter["nnz"].item())
+    assert float(inter["T"].item()) == ref["T"]
+    assert nnz == ref["nnz"]
+    assert np.array_equal(to_np(inter["row_ptr"]), ref["row_ptr"])
+    assert np.array_equal(to_np(inter["coo_row"][:nnz]), ref["coo_row"])
+    assert np.array_equal(to_np(inter["coo_col"][:nnz]), ref["coo_col"])
+    assert np.array_equal(to_np(inter["coo_val"][:nnz]), ref["coo_val"])
+    assert np.array_equal(to_np(inter["Aq"]), ref["Aq"])
+    assert np.array_equal(to_np(inter["sA"]), ref["sA"])
+    assert np.array_equal(to_np(inter["Wq"]), ref["Wq"])
+    assert np.array_equal(to_np(inter["sW"]), ref["sW"])
+    if out_dtype == torch.float32:
+        return assert_y_close(to_np(Y), ref["Y"], ref["denom"])
+    assert_bf16_close(to_np(Y), ref["Y"], ref["denom"])
+    return None
+
+
+def test_forward_config1_tiny():
+    _say("forward config 1")
+    A, W, L = make_layer(1)
+    err = _check_forward_small(A, W, L.q, torch.float32)
+    _say(f"config 1 max rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("dtype,M,K,N,q,out", [
+    ("bf16", 300, 512, 264, 0.99, "fp32"), ("bf16", 513, 1056, 776, 0.999, "bf16"),
+    ("fp32", 257, 288, 136, 0.95, "fp32"), ("bf16", 1, 32, 8, 0.5, "fp32"), ("bf16", 64, 64, 64, 1.0, "bf16"),
+    ("bf16", 520, 2048, 264, 0.9, "fp32"),
+])
+def test_forward_small(dtype, M, K, N, q, out):
+    _say(f"forward {dtype} {M}x{K}x{N} q={q} out={out}")
+    A, W = make_custom(M, K, N, dtype=dtype, seed=M + N)
+    _check_forward_small(A, W, q, _dt(out))
+
+
+def test_forward_zero_rows_and_columns():
+    _say("forward zero rows/cols")
+    A, W = make_custom(96, 256, 72, dtype="bf16", seed=3)
+    A[5] = 0
+    A[7, :100] = -0.0
+    W[:, 9] = 0
+    _check_forward_small(A, W, 0.99, torch.float32)
+
+
+def test_forward_is_deterministic():
+    _say("determinism")
+    A, W = make_custom(1024, 2048, 1032, dtype="bf16", seed=9, kind="student_t")
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    q = 0.99
+    ws1, ws2 = fp4.workspace(Ad, 1032, q).zero_(), fp4.workspace(Ad, 1032, q).zero_()
+    Y1 = fp4.linear_forward(Ad, Wd, q, out_dtype=torch.float32, ws=ws1)
+    Y2 = fp4.linear_forward(Ad, Wd, q, out_dtype=torch.float32, ws=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+    lay = fp4.forward_layout(1024, 2048, 1032, A.dtype, q)
+    assert torch.equal(ws1[: lay.scratch], ws2[: lay.scratch])
+
+
+# ----------------------------------------------------------------------------- full sizes
+def _sample_pairs(rng, M, N, row_ptr, count=3000):
+    ms = list(rng.integers(0, M, count))
+    ns = list(rng.integers(0, N, count))
+    busy = np.argsort(np.diff(row_ptr))[-16:]  # rows with the most outliers
+    for m in busy:
+        for n in rng.integers(0, N, 8):
+            ms.append(int(m))
+            ns.append(int(n))
+    for (m, n) in [(0, 0), (M - 1, N - 1), (0, N - 1), (M - 1, 0)]:
+        ms.append(m)
+        ns.append(n)
+    return np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
+
+
+FULL = [(c, li) for c in (2, 3, 4, 5) for li in range(len(CONFIGS[c]))]
+
+
+@pytest.mark.parametrize("cfg,li", FULL, ids=[f"cfg{c}-{CONFIGS[c][li].name}" for c, li in FULL])
+def test_forward_full_size(cfg, li):
+    """The workload sizes, in the launch configuration the benchmark times: every
+    intermediate compared in full, the accumulator and Y at sampled outputs."""
+    L = CONFIGS[cfg][li]
+    _say(f"full size {L.name} M={L.M} K={L.K} N={L.N} q={L.q}")
+    A, W, _ = make_layer(cfg, li)
+    M, K, N = L.M, L.K, L.N
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    ws = fp4.workspace(Ad, N, L.q)
+    Y = fp4.linear_forward(Ad, Wd, L.q, out_dtype=_dt(L.out_dtype), ws=ws)
+    inter = fp4.forward_intermediates(ws, M, K, N, A.dtype, L.q)
+    nnz = int(inter["nnz"].item())
+    Anp, Wnp = oracle_inputs(A, W)
+    T = oracle.abs_quantile(Anp, L.q)
+    assert float(inter["T"].item()) == T
+    cl = oracle.clamp_coo(Anp, T, want_clamped=True, cap=oracle.capacity(M, K, L.q))
+    assert nnz == cl["nnz"]
+    assert np.array_equal(to_np(inter["row_ptr"]), cl["row_ptr"])
+    assert np.array_equal(to_np(inter["coo_row"][:nnz]), cl["coo_row"])
+    assert np.array_equal(to_np(inter["coo_col"][:nnz]), cl["coo_col"])
+    assert np.array_equal(to_np(inter["coo_val"][:nnz]), cl["coo_val"])
+    Aq, sA = oracle.quant_rows(cl.pop("A_clamped"))
+    assert np.array_equal(to_np(inter["sA"]), sA)
+    assert np.array_equal(to_np(inter["Aq"]), Aq)
+    Wq, sW = oracle.quant_cols(Wnp)
+    assert np.array_equal(to_np(inter["sW"]), sW)
+    assert np.array_equal(to_np(inter["Wq"]), Wq)
+    _say(f"  intermediates bit-exact (T={T} nnz={nnz})")
+    # fp32 output and raw accumulator from the same codes
+    Y32, acc = fp4.gemm(inter["Aq"], inter["sA"], inter["Wq"], inter["sW"], K, row_ptr=inter["row_ptr"],
+                        coo_col=inter["coo_col"], coo_val=inter["coo_val"], W=Wd, out_dtype=torch.float32,
+                        acc_out=True)
+    if L.out_dtype == "bf16":
+        assert torch.equal(Y.view(torch.int16), Y32.to(torch.bfloat16).view(torch.int16))
+    rng = np.random.default_rng(cfg * 10 + li)
+    ms, ns = _sample_pairs(rng, M, N, cl["row_ptr"])
+    idx = torch.from_numpy(ms * N + ns).to(DEV)
+    g_acc = acc.view(-1)[idx].cpu().numpy()
+    g_y = Y32.view(-1)[idx].cpu().numpy()
+    r_acc = oracle.accumulate_pairs(Aq, Wq, K, ms, ns)
+    assert np.array_equal(g_acc, r_acc)
+    r_y, denom = oracle.output_pairs(r_acc, sA, sW, ms, ns, cl["row_ptr"], cl["coo_col"], cl["coo_val"], Wnp)
+    err = assert_y_close(g_y, r_y, denom)
+    if L.out_dtype == "bf16":
+        assert_bf16_close(to_np(Y.view(-1)[idx]), r_y, denom)
+    _say(f"  sampled acc bit-exact, Y max rel err {err:.3e}")
