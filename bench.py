@@ -1,0 +1,240 @@
+"""Benchmark of the FP4 quantized linear forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
+
+A step is one fp4_linear_forward (quantile + clamp + dA, token-wise quantization of A,
+channel-wise quantization of W, FP4 GEMM with dequantization and compensation) over one
+batch of seeded synthetic input already resident in HBM.  Default workload: the
+LLaMA-7B FFN gate+up projection (M=16384 tokens, K=4096, N=22016, bf16 in and out,
+clamp quantile 0.999).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import quantized_linear_layers_fp4_amd as fp4  # noqa: E402
+from workloads import CONFIGS, make_layer  # noqa: E402
+
+METRIC = "FP4 quantized-linear TFLOPS & % dense FP4 MFMA peak; quantizer HBM GB/s"
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak (10.1 PFLOP/s)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fp4_gemm_llama7b_gate_up.json")
+GEMM_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "gemm.hip")
+
+
+def b_in(dtype: torch.dtype) -> int:
+    return 2 if dtype == torch.bfloat16 else 4
+
+
+def quantizer_bytes(M, K, N, bi, nnz) -> int:
+    """Algorithmic HBM bytes of the quantizer stages: A read twice (histogram pass, then
+    clamp+quantize: T must be known before any code), codes, scales, dA; W read once,
+    codes, scales."""
+    a = 2 * M * K * bi + M * K // 2 + 4 * M + 12 * nnz + 4 * (M + 1)
+    w = K * N * bi + K * N // 2 + 4 * N
+    return a + w
+
+
+def time_on_stream(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds of fn() over `steps` calls, HIP events on the current stream
+    (the stream every launch of fn goes to)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def gemm_src_sha() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(launch_bytes_alg: float):
+    """HBM bytes per GEMM launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current GEMM source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_src_sha") != gemm_src_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, W, L, rows: int = 32) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload: every
+    quantizer step at full size, the accumulator/dequant/compensation on `rows` sampled
+    rows x all N columns, extrapolated linearly to M rows."""
+    import oracle
+    from workloads import as_numpy_bits
+    Anp, Wnp = as_numpy_bits(A), as_numpy_bits(W)
+    M, K, N = L.M, L.K, L.N
+    t0 = time.perf_counter()
+    T = oracle.abs_quantile(Anp, L.q)
+    cl = oracle.clamp_coo(Anp, T, want_clamped=True, cap=oracle.capacity(M, K, L.q))
+    Aq, sA = oracle.quant_rows(cl.pop("A_clamped"))
+    Wq, sW = oracle.quant_cols(Wnp)
+    t1 = time.perf_counter()
+    rs = np.sort(np.random.default_rng(0).choice(M, rows, replace=False))
+    ms = np.repeat(rs, N).astype(np.int64)
+    ns = np.tile(np.arange(N, dtype=np.int64), rows)
+    acc = oracle.accumulate_pairs(Aq, Wq, K, ms, ns)
+    oracle.output_pairs(acc, sA, sW, ms, ns, cl["row_ptr"], cl["coo_col"], cl["coo_val"], Wnp)
+    t2 = time.perf_counter()
+    t_full = (t1 - t0) + (t2 - t1) * M / rows
+    return {
+        "value": round(2.0 * M * N * K / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{L.name}: quantile, clamp+dA and A/W quantization at full size ({t1 - t0:.2f} s); "
+                   f"accumulator+dequant+compensation on {rows} of {M} rows x {N} cols ({t2 - t1:.2f} s), "
+                   f"extrapolated x{M // rows} to the full step ({t_full:.1f} s)"),
+        "host_cpu": _cpu_model(), "host_threads_available": os.cpu_count(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def run_copy(steps: int):
+    """Plain 1 GiB device copy: the calibration kernel for the HBM byte counters."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = time_on_stream(lambda: dst.copy_(src), steps, 2)
+    print(json.dumps({"copy_bytes": 1 << 30, "ms_per_copy": ms, "GB/s_read+write": 2 * (1 << 30) / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
+              "forward is described in DESIGN.md but not run.", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.mode == "copy":
+        run_copy(args.steps)
+        return
+
+    layers = [make_layer(args.config, li) for li in range(len(CONFIGS[args.config]))]
+    dev = torch.device("cuda:0")
+    runs = []
+    for A, W, L in layers:
+        Ad, Wd = A.to(dev), W.to(dev)
+        ws = fp4.workspace(Ad, L.N, L.q)
+        Y = torch.empty((L.M, L.N), dtype=torch.bfloat16 if L.out_dtype == "bf16" else torch.float32, device=dev)
+        runs.append((A, W, L, Ad, Wd, ws, Y))
+    torch.cuda.synchronize()
+
+    def step():
+        for _, _, L, Ad, Wd, ws, Y in runs:
+            fp4.linear_forward(Ad, Wd, L.q, ws=ws, Y=Y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(args.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    flops = sum(L.flops for _, _, L, *_ in runs)
+
+    if args.mode == "forward":
+        print(json.dumps({"ms_per_step": ms_step}))
+        return
+
+    # the dominant kernel (the GEMM) alone, same arguments as inside the forward
+    gemm_ms, qbytes, nnz_total = 0.0, 0, 0
+    per_layer = []
+    for A, W, L, Ad, Wd, ws, Y in runs:
+        it = fp4.forward_intermediates(ws, L.M, L.K, L.N, A.dtype, L.q)
+        nnz = int(it["nnz"].item())
+        g = lambda: fp4.lib().fp4_gemm(  # noqa: E731
+            fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K,
+            fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]), fp4._ptr(Wd), fp4._dt(Wd),
+            fp4._ptr(Y), fp4._dt(Y), None, fp4._stream(Ad))
+        ms_g = time_on_stream(g, args.steps, 2)
+        gemm_ms += ms_g
+        qb = quantizer_bytes(L.M, L.K, L.N, b_in(A.dtype), nnz)
+        qbytes += qb
+        nnz_total += nnz
+        per_layer.append({"layer": L.name, "M": L.M, "K": L.K, "N": L.N, "q": L.q, "nnz": nnz,
+                          "gemm_ms": round(ms_g, 4), "gemm_TFLOP/s": round(L.flops / ms_g / 1e9, 1)})
+
+    quant_ms = max(ms_step - gemm_ms, 1e-9)
+    gemm_tflops = flops / gemm_ms / 1e9
+    fwd_tflops = flops / ms_step / 1e9
+    quant_gbs = qbytes / quant_ms / 1e6
+    first = runs[0][2]
+    traffic = load_traffic(None) if (args.config == 3) else None
+    name = first.name if len(runs) == 1 else f"llama7b_layer_chain(x{len(runs)})"
+    out = {
+        "metric": METRIC,
+        "value": round(fwd_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4e2m1 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": name, "M": first.M, "K": first.K, "N": first.N, "in_dtype": first.dtype,
+                   "out_dtype": first.out_dtype, "q": first.q, "layers": len(runs), "parallelism": "none (1 GPU)"},
+        "forward_frac_of_fp4_peak": round(fwd_tflops / PEAK_FP4_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_fp4_gemm", "achieved": round(gemm_tflops, 1),
+                     "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+                     "traffic": traffic, "ms_per_launch": round(gemm_ms, 4)},
+        "quantizer": {"bound": "hbm", "achieved": round(quant_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(quant_gbs / PEAK_HBM_GBS, 4), "ms": round(quant_ms, 4),
+                      "algorithmic_bytes": qbytes},
+        "nnz": nnz_total,
+        "layers": per_layer,
+        "wall_s_timed": round(wall, 3),
+        "device": torch.cuda.get_device_properties(0).gcnArchName,
+    }
+    if not args.no_cpu_baseline:
+        A, W, L = runs[0][0], runs[0][1], runs[0][2]
+        out["cpu_baseline"] = cpu_baseline(A, W, L)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -61,11 +61,21 @@ fp4_status device_check(int *cus) {
 
 // Scratch of one outlier pass.  [state, hist, hist_lo) is zero-filled per call.
 struct OutlierWs {
-    size_t state, hist, hist_lo, zero_end, rowmax, row_cnt, stage, total;
+    size_t state, hist, hist_lo, zero_end, rowmax, row_cnt, slots, over, total;
+    int32_t S;  // staging slots per row
 };
 
-OutlierWs outlier_ws(int64_t M, int32_t dtype, int64_t cap) {
+// Slots per row: twice the mean outlier count per row that the capacity bound allows,
+// plus a margin, at most K.  Rows with more outliers spill into the overflow list.
+int32_t slots_per_row(int64_t M, int64_t K, int64_t cap) {
+    int64_t mean = (cap + M - 1) / M;
+    int64_t S = 2 * mean + 8;
+    return (int32_t)(S < K ? S : K);
+}
+
+OutlierWs outlier_ws(int64_t M, int64_t K, int32_t dtype, int64_t cap) {
     OutlierWs w;
+    w.S = slots_per_row(M, K, cap);
     size_t off = 0;
     w.state = off;
     off += align_up(sizeof(State));
@@ -78,8 +88,10 @@ OutlierWs outlier_ws(int64_t M, int32_t dtype, int64_t cap) {
     off += align_up((size_t)M * 4);
     w.row_cnt = off;
     off += align_up((size_t)M * 4);
-    w.stage = off;
-    off += align_up((size_t)(cap > 0 ? cap : 1) * sizeof(StageEntry));
+    w.slots = off;
+    off += align_up((size_t)M * (size_t)w.S * sizeof(SlotEntry));
+    w.over = off;
+    off += align_up((size_t)(cap > 0 ? cap : 1) * sizeof(OverEntry));
     w.total = off;
     return w;
 }
@@ -97,7 +109,11 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     uint32_t *hist_lo = reinterpret_cast<uint32_t *>(ws + w.hist_lo);
     uint32_t *rowmax = reinterpret_cast<uint32_t *>(ws + w.rowmax);
     int32_t *row_cnt = reinterpret_cast<int32_t *>(ws + w.row_cnt);
-    StageEntry *stage = reinterpret_cast<StageEntry *>(ws + w.stage);
+    Staging stg;
+    stg.slots = reinterpret_cast<SlotEntry *>(ws + w.slots);
+    stg.over = reinterpret_cast<OverEntry *>(ws + w.over);
+    stg.S = w.S;
+    stg.over_cap = cap > 0 ? cap : 1;
     const int dt = dt_of(dtype);
     const int64_t n = M * K;
     const uint64_t k = (uint64_t)std::floor(q * (double)(n - 1));
@@ -106,9 +122,9 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     if (e == hipSuccess) e = launch_select(A, dt, n, hist, hist_lo, st, T, k, s);
     const bool codes = Aq != nullptr;
     if (e == hipSuccess)
-        e = launch_quant_rows(A, dt, M, K, codes ? rowmax : nullptr, T, Aq, sA, row_cnt, stage, cap, st,
+        e = launch_quant_rows(A, dt, M, K, codes ? rowmax : nullptr, T, Aq, sA, row_cnt, stg, st,
                               /*emit=*/true, /*write_codes=*/codes, s);
-    if (e == hipSuccess) e = launch_coo(row_cnt, M, row_ptr, nnz, stage, st, cap, coo_row, coo_col, coo_val, s);
+    if (e == hipSuccess) e = launch_coo(row_cnt, M, row_ptr, nnz, stg, st, cap, coo_row, coo_col, coo_val, s);
     return hip_status(e);
 }
 
@@ -149,7 +165,7 @@ fp4_status fp4_quantize(const void *X, int32_t x_dtype, int64_t R, int64_t C, in
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (axis == FP4_PER_ROW)
         return hip_status(launch_quant_rows(X, dt_of(x_dtype), R, C, nullptr, clamp_T, codes, scales, nullptr,
-                                            nullptr, 0, nullptr, false, true, s));
+                                            Staging{nullptr, nullptr, 0, 0}, nullptr, false, true, s));
     return hip_status(launch_quant_cols(X, dt_of(x_dtype), R, C, scales, codes, s));
 }
 
@@ -160,7 +176,7 @@ int64_t fp4_outlier_capacity(int64_t M, int64_t K, double q) {
 
 size_t fp4_outlier_workspace_bytes(int64_t M, int64_t K, int32_t a_dtype, double q) {
     if (!mk_ok(M, K) || !q_ok(q) || !dtype_ok(a_dtype)) return 0;
-    return outlier_ws(M, a_dtype, capacity_of(M, K, q)).total;
+    return outlier_ws(M, K, a_dtype, capacity_of(M, K, q)).total;
 }
 
 fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t K, double q, float *T,
@@ -172,7 +188,7 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
     if (!q_ok(q)) return FP4_ERR_QUANTILE;
     const int64_t cap = capacity_of(M, K, q);
     if (capacity < cap) return FP4_ERR_CAPACITY;
-    const OutlierWs w = outlier_ws(M, a_dtype, cap);
+    const OutlierWs w = outlier_ws(M, K, a_dtype, cap);
     if (ws_bytes < w.total) return FP4_ERR_WORKSPACE;
     if (!aligned16(A) || !aligned16(workspace) || !aligned16(T) || !aligned16(row_ptr)) return FP4_ERR_ALIGN;
     int cus;
@@ -222,7 +238,7 @@ fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype,
     out->sA = off; off += align_up((size_t)M * 4);
     out->Wq = off; off += align_up((size_t)N * (size_t)(K / 2));
     out->sW = off; off += align_up((size_t)N * 4);
-    out->scratch = off; off += outlier_ws(M, in_dtype, cap).total;
+    out->scratch = off; off += outlier_ws(M, K, in_dtype, cap).total;
     out->total = off;
     out->capacity = cap;
     return FP4_OK;
@@ -257,7 +273,7 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
     float *sA = reinterpret_cast<float *>(ws + l.sA);
     uint8_t *Wq = ws + l.Wq;
     float *sW = reinterpret_cast<float *>(ws + l.sW);
-    const OutlierWs w = outlier_ws(M, in_dtype, l.capacity);
+    const OutlierWs w = outlier_ws(M, K, in_dtype, l.capacity);
     st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, T, coo_row, coo_col, coo_val, l.capacity,
                       row_ptr, nnz, Aq, sA, s);
     if (st != FP4_OK) return st;

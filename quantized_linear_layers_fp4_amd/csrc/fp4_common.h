@@ -23,7 +23,7 @@ constexpr int HIST_LO_BINS = 65536;  // level-2 histogram for fp32 keys: key & 0
 struct State {
     uint64_t k_rem;        // rank left inside the level-1 bin (fp32 inputs)
     uint64_t nnz_hist;     // #{|a| > T} counted from the histograms
-    unsigned long long stage_count;  // outlier staging reservations
+    unsigned long long over_count;  // outliers staged past their row's slots
     uint32_t T_key;        // key of T
     float T;               // T itself
     uint32_t hi_bin;       // selected level-1 bin
@@ -31,13 +31,24 @@ struct State {
 };
 static_assert(sizeof(State) == 40, "State layout");
 
-// One staged outlier: its row, its rank among the row's outliers (ascending column),
-// its column and delta = a - copysign(T, a).
-struct StageEntry {
+// Outlier staging.  Row m owns S slots; the outlier of rank j (ascending column) in row m
+// goes to slot m*S + j, and ranks >= S go to the shared overflow list (rare: S is twice the
+// mean count per row plus a margin).  No global atomic is touched unless a row overflows.
+struct SlotEntry {
+    int32_t col;
+    float val;   // delta = a - copysign(T, a)
+};
+struct OverEntry {
     int32_t row;
     int32_t rank;
     int32_t col;
     float val;
+};
+struct Staging {
+    SlotEntry *slots;
+    OverEntry *over;
+    int32_t S;
+    int64_t over_cap;
 };
 
 // Per-vector scales: r = fl(6 / amax) multiplies, s = fl(amax / 6) dequantizes; a vector

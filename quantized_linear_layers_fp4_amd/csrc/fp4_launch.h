@@ -15,11 +15,10 @@ hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint
                          State *st, float *T_out, uint64_t k, hipStream_t s);
 hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const uint32_t *rowmax_key,
                              const float *T_src, uint8_t *codes, float *scales, int32_t *row_cnt,
-                             StageEntry *stage, int64_t stage_cap, State *st, bool emit, bool write_codes,
-                             hipStream_t s);
-hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out,
-                      const StageEntry *stage, const State *st, int64_t cap, int32_t *coo_row,
-                      int32_t *coo_col, float *coo_val, hipStream_t s);
+                             const Staging &stg, State *st, bool emit, bool write_codes, hipStream_t s);
+hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
+                      const State *st, int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val,
+                      hipStream_t s);
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
                              uint8_t *codes, hipStream_t s);
 

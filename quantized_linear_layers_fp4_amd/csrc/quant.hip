@@ -145,8 +145,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, 
                                                     const uint32_t *__restrict__ rowmax_key,
                                                     const float *__restrict__ T_src,
                                                     uint8_t *__restrict__ codes, float *__restrict__ scales,
-                                                    int32_t *__restrict__ row_cnt,
-                                                    StageEntry *__restrict__ stage, int64_t stage_cap,
+                                                    int32_t *__restrict__ row_cnt, Staging stg,
                                                     State *__restrict__ st) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -198,24 +197,29 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, 
             if (__ballot(cnt != 0)) {
                 const uint32_t incl = wave_incl_scan(cnt, lane);
                 const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-                unsigned long long b0 = 0;
-                if (lane == 0) b0 = atomicAdd(&st->stage_count, (unsigned long long)total);
-                b0 = (unsigned long long)__shfl((long long)b0, 0, 64);
                 uint32_t rank = running + incl - cnt;
-                unsigned long long slot = b0 + (incl - cnt);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     if (omask & (1u << e)) {
-                        if (slot < (unsigned long long)stage_cap) {
-                            StageEntry ent;
-                            ent.row = (int32_t)row;
-                            ent.rank = (int32_t)rank;
-                            ent.col = (int32_t)(c * 8 + e);
-                            ent.val = v[e] - __uint_as_float(sg[e] | tkey);
-                            stage[slot] = ent;
+                        const int32_t col = (int32_t)(c * 8 + e);
+                        const float val = v[e] - __uint_as_float(sg[e] | tkey);
+                        if (rank < (uint32_t)stg.S) {
+                            SlotEntry se;
+                            se.col = col;
+                            se.val = val;
+                            stg.slots[row * stg.S + rank] = se;
+                        } else {
+                            const unsigned long long i = atomicAdd(&st->over_count, 1ull);
+                            if (i < (unsigned long long)stg.over_cap) {
+                                OverEntry oe;
+                                oe.row = (int32_t)row;
+                                oe.rank = (int32_t)rank;
+                                oe.col = col;
+                                oe.val = val;
+                                stg.over[i] = oe;
+                            }
                         }
                         ++rank;
-                        ++slot;
                     }
                 }
                 running += total;
@@ -228,64 +232,84 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, 
 }
 
 // ----------------------------------------------------------------------------- COO
-// Exclusive scan of the per-row outlier counts (one workgroup of 1024 threads).
+// Exclusive scan of the per-row outlier counts (one workgroup of 1024 threads, 16 rows
+// per thread per pass, wave scans + one cross-wave step).
 __global__ __launch_bounds__(1024) void k_coo_scan(const int32_t *__restrict__ row_cnt, int64_t M,
                                                    int32_t *__restrict__ row_ptr,
                                                    int64_t *__restrict__ nnz_out) {
-    constexpr int ITEMS = 8;
-    __shared__ uint32_t part[1024];
+    constexpr int ITEMS = 16;
+    __shared__ uint32_t wsum[16];
     __shared__ uint32_t carry_s;
-    const int tid = threadIdx.x;
-    if (tid == 0) carry_s = 0;
-    __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t carry = 0;
     for (int64_t b0 = 0; b0 < M; b0 += 1024 * ITEMS) {
         uint32_t c[ITEMS], local = 0;
+        const int64_t r0 = b0 + (int64_t)tid * ITEMS;
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            int64_t r = b0 + (int64_t)tid * ITEMS + i;
-            c[i] = (r < M) ? (uint32_t)row_cnt[r] : 0u;
+            c[i] = (r0 + i < M) ? (uint32_t)row_cnt[r0 + i] : 0u;
             local += c[i];
         }
-        part[tid] = local;
+        const uint32_t incl = wave_incl_scan(local, lane);
+        if (lane == 63) wsum[wave] = incl;
         __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {
-            uint32_t x = (tid >= off) ? part[tid - off] : 0u;
-            __syncthreads();
-            part[tid] += x;
-            __syncthreads();
+        if (wave == 0) {
+            uint32_t x = lane < 16 ? wsum[lane] : 0u;
+            const uint32_t xi = wave_incl_scan(x, lane);
+            if (lane < 16) wsum[lane] = xi - x;  // exclusive
+            if (lane == 15) carry_s = xi;          // total of this pass
         }
-        uint32_t run = carry_s + part[tid] - local;
+        __syncthreads();
+        uint32_t run = carry + wsum[wave] + incl - local;
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            int64_t r = b0 + (int64_t)tid * ITEMS + i;
-            if (r < M) row_ptr[r] = (int32_t)run;
+            if (r0 + i < M) row_ptr[r0 + i] = (int32_t)run;
             run += c[i];
         }
-        __syncthreads();
-        if (tid == 1023) carry_s += part[1023];
+        carry += carry_s;
         __syncthreads();
     }
     if (tid == 0) {
-        row_ptr[M] = (int32_t)carry_s;
-        *nnz_out = (int64_t)carry_s;
+        row_ptr[M] = (int32_t)carry;
+        *nnz_out = (int64_t)carry;
     }
 }
 
-// Move each staged entry to row_ptr[row] + rank.
-__global__ __launch_bounds__(256) void k_coo_scatter(const StageEntry *__restrict__ stage,
-                                                     const State *__restrict__ st,
-                                                     const int32_t *__restrict__ row_ptr, int64_t cap,
+// Move each staged entry to row_ptr[row] + rank: one wave per row for the slots; the
+// last OVER_BLOCKS workgroups move the overflow list.
+constexpr int OVER_BLOCKS = 16;
+__global__ __launch_bounds__(256) void k_coo_scatter(Staging stg, const State *__restrict__ st,
+                                                     const int32_t *__restrict__ row_cnt,
+                                                     const int32_t *__restrict__ row_ptr, int64_t M, int64_t cap,
                                                      int32_t *__restrict__ coo_row, int32_t *__restrict__ coo_col,
                                                      float *__restrict__ coo_val) {
-    const int64_t n = min((int64_t)st->stage_count, cap);
-    int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
-        StageEntry e = stage[i];
-        int64_t pos = (int64_t)row_ptr[e.row] + e.rank;
+    const int64_t row_blocks = (M + 3) / 4;
+    if ((int64_t)blockIdx.x < row_blocks) {
+        const int lane = threadIdx.x & 63;
+        const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+        if (row >= M) return;
+        const int32_t n = min(row_cnt[row], stg.S);
+        const int64_t base = row_ptr[row];
+        for (int32_t j = lane; j < n; j += 64) {
+            const SlotEntry se = stg.slots[row * stg.S + j];
+            const int64_t pos = base + j;
+            if (pos < cap) {
+                if (coo_row) coo_row[pos] = (int32_t)row;
+                coo_col[pos] = se.col;
+                coo_val[pos] = se.val;
+            }
+        }
+        return;
+    }
+    const int64_t n = min((int64_t)st->over_count, stg.over_cap);
+    const int64_t stride = (int64_t)OVER_BLOCKS * blockDim.x;
+    for (int64_t i = (blockIdx.x - row_blocks) * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+        const OverEntry oe = stg.over[i];
+        const int64_t pos = (int64_t)row_ptr[oe.row] + oe.rank;
         if (pos < cap) {
-            if (coo_row) coo_row[pos] = e.row;
-            coo_col[pos] = e.col;
-            coo_val[pos] = e.val;
+            if (coo_row) coo_row[pos] = oe.row;
+            coo_col[pos] = oe.col;
+            coo_val[pos] = oe.val;
         }
     }
 }
@@ -440,14 +464,13 @@ hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint
 
 hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const uint32_t *rowmax_key,
                              const float *T_src, uint8_t *codes, float *scales, int32_t *row_cnt,
-                             StageEntry *stage, int64_t stage_cap, State *st, bool emit, bool write_codes,
-                             hipStream_t s) {
+                             const Staging &stg, State *st, bool emit, bool write_codes, hipStream_t s) {
     dim3 grid((unsigned)((R + 3) / 4)), block(256);
     const bool clamp = T_src != nullptr;
     const bool have_rm = rowmax_key != nullptr;
 #define QR(DT, CL, HR, CO, EM)                                                                      \
     hipLaunchKernelGGL((k_quant_rows<DT, CL, HR, CO, EM>), grid, block, 0, s, X, R, C, rowmax_key, T_src, \
-                       codes, scales, row_cnt, stage, stage_cap, st)
+                       codes, scales, row_cnt, stg, st)
     if (dt == DT_BF16) {
         if (emit && write_codes && have_rm) QR(DT_BF16, true, true, true, true);
         else if (emit && !write_codes) QR(DT_BF16, true, false, false, true);
@@ -463,12 +486,13 @@ hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const 
     return hipGetLastError();
 }
 
-hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out,
-                      const StageEntry *stage, const State *st, int64_t cap, int32_t *coo_row,
-                      int32_t *coo_col, float *coo_val, hipStream_t s) {
+hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
+                      const State *st, int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val,
+                      hipStream_t s) {
     hipLaunchKernelGGL(k_coo_scan, dim3(1), dim3(1024), 0, s, row_cnt, M, row_ptr, nnz_out);
-    hipLaunchKernelGGL(k_coo_scatter, dim3(blocks_for(cap, 256, 4096)), dim3(256), 0, s, stage, st, row_ptr,
-                       cap, coo_row, coo_col, coo_val);
+    const int blocks = (int)((M + 3) / 4) + OVER_BLOCKS;
+    hipLaunchKernelGGL(k_coo_scatter, dim3(blocks), dim3(256), 0, s, stg, st, row_cnt, row_ptr, M, cap, coo_row,
+                       coo_col, coo_val);
     return hipGetLastError();
 }
 

@@ -151,6 +151,27 @@ def test_outlier_clamp(dtype, M, K, q, kind):
     assert np.array_equal(to_np(out["coo_val"]), ref["coo_val"])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_outlier_clamp_row_overflow(dtype):
+    # nearly every outlier in one row: the row's staging slots overflow into the shared list
+    M, K, q = 256, 512, 0.999
+    _say(f"outlier overflow {dtype}")
+    A, W = make_custom(M, K, 64, dtype=dtype, seed=77, kind="plain")
+    A[3] *= 100
+    A[200, 7] = 1000.0
+    out = fp4.outlier_clamp(A.to(DEV), q)
+    Anp = as_numpy_bits(A)
+    T = oracle.abs_quantile(Anp, q)
+    ref = oracle.clamp_coo(Anp, T, want_clamped=False)
+    assert ref["row_ptr"][4] - ref["row_ptr"][3] > 50  # far beyond the per-row slots
+    assert float(out["T"].item()) == T
+    assert np.array_equal(to_np(out["row_ptr"]), ref["row_ptr"])
+    assert np.array_equal(to_np(out["coo_col"]), ref["coo_col"])
+    assert np.array_equal(to_np(out["coo_val"]), ref["coo_val"])
+    assert np.array_equal(to_np(out["coo_row"]), ref["coo_row"])
+    _check_forward_small(A, W, q, torch.float32)
+
+
 # ----------------------------------------------------------------------------- GEMM
 def _random_codes(rng, R, K):
     return rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
