@@ -79,7 +79,11 @@ enum { FP4_PER_ROW = 0, FP4_PER_COL = 1 };   /* token-wise (A) / channel-wise (W
 
 /* Limits shared by all calls: 32 <= K <= 65536 and K % 32 == 0 (contraction length:
  * two codes per byte, 16-byte vector lanes, and the fp32 accumulator stays exact);
- * 1 <= M and M * K < 2^32; 1 <= N and N % 8 == 0. */
+ * 1 <= M and M * K < 2^32; 1 <= N and N % 8 == 0.  The product (fp4_gemm,
+ * fp4_linear_forward) also needs N * K < 2^32 and, when it adds the compensation term,
+ * K * N * sizeof(W element) < 2^31.  The outlier calls need the capacity bound
+ * M*K - 1 - floor(q * (M*K - 1)) <= 2^29 (int32 COO offsets); a smaller q is rejected with
+ * FP4_ERR_QUANTILE. */
 
 /* Quantize one matrix X (R x C) to E2M1 codes and fp32 scales.
  * QbitAI report, granularity and forward-quantization paragraphs.

@@ -26,6 +26,16 @@ int dt_of(int32_t d) { return d == FP4_BF16 ? DT_BF16 : DT_F32; }
 bool k_ok(int64_t K) { return K >= 32 && K <= K_MAX && K % 32 == 0; }
 bool mk_ok(int64_t M, int64_t K) { return M >= 1 && k_ok(K) && M <= (int64_t)0xFFFFFFFF / K; }
 bool n_ok(int64_t N) { return N >= 1 && N % 8 == 0 && N <= (int64_t)1 << 30; }
+// Shapes of the product: Wq (N x K/2) is addressed like Aq, and the compensation gathers
+// rows of the original W (K x N) with 32-bit byte offsets.
+bool gemm_ok(int64_t M, int64_t N, int64_t K) { return mk_ok(M, K) && n_ok(N) && mk_ok(N, K); }
+bool wcomp_ok(int64_t N, int64_t K, int32_t w_dtype) {
+    return K * N * (w_dtype == FP4_BF16 ? 2 : 4) <= (int64_t)0x7FFFFFFF;
+}
+
+// The COO list of dA is indexed with int32 (row_ptr), and the kernels address it with
+// 32-bit byte offsets: the capacity bound must stay below 2^29 entries.
+constexpr int64_t COO_MAX = (int64_t)1 << 29;
 
 int64_t capacity_of(int64_t M, int64_t K, double q) {
     const int64_t n = M * K;
@@ -187,6 +197,7 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
     if (!mk_ok(M, K)) return FP4_ERR_SHAPE;
     if (!q_ok(q)) return FP4_ERR_QUANTILE;
     const int64_t cap = capacity_of(M, K, q);
+    if (cap > COO_MAX) return FP4_ERR_QUANTILE;
     if (capacity < cap) return FP4_ERR_CAPACITY;
     const OutlierWs w = outlier_ws(M, K, a_dtype, cap);
     if (ws_bytes < w.total) return FP4_ERR_WORKSPACE;
@@ -208,7 +219,7 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
     if (ncomp != 0 && ncomp != 3) return FP4_ERR_NULL;
     if (ncomp == 3 && !W) return FP4_ERR_NULL;
     if (!dtype_ok(y_dtype) || (ncomp == 3 && !dtype_ok(w_dtype))) return FP4_ERR_DTYPE;
-    if (!mk_ok(M, K) || !n_ok(N) || M > (int64_t)1 << 30) return FP4_ERR_SHAPE;
+    if (!gemm_ok(M, N, K) || (ncomp == 3 && !wcomp_ok(N, K, w_dtype))) return FP4_ERR_SHAPE;
     if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(Y) || (W && !aligned16(W)) || (acc_out && !aligned16(acc_out)))
         return FP4_ERR_ALIGN;
     int cus;
@@ -223,9 +234,10 @@ fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype,
     if (!out) return FP4_ERR_NULL;
     std::memset(out, 0, sizeof(*out));
     if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
-    if (!mk_ok(M, K) || !n_ok(N) || M > (int64_t)1 << 30) return FP4_ERR_SHAPE;
+    if (!gemm_ok(M, N, K) || !wcomp_ok(N, K, in_dtype)) return FP4_ERR_SHAPE;
     if (!q_ok(q)) return FP4_ERR_QUANTILE;
     const int64_t cap = capacity_of(M, K, q);
+    if (cap > COO_MAX) return FP4_ERR_QUANTILE;
     const size_t capn = (size_t)(cap > 0 ? cap : 1);
     size_t off = 0;
     out->T = off; off += ALIGN;

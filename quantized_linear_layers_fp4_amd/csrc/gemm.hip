@@ -11,7 +11,14 @@
 // K advances 128 codes (64 bytes per row) per stage.  Operand tiles travel from global
 // memory straight into one of four LDS stage buffers (buffer loads with the LDS flag,
 // issued three stages ahead); rows or K chunks outside the matrices read as zero.  One
-// barrier per stage.
+// barrier per stage.  The row/column scales and the row pointers of dA for the tile are
+// fetched into LDS under the first stage loads.
+//
+// Epilogue: 32 rows at a time through an fp32 slab in LDS.  The tile's dA entries (sorted
+// by row, then column) stream through in rounds of 32 KiB of gathered W row segments:
+// the (column, delta) pairs of a round are copied into a small LDS ring one round before
+// its gather, and each gather is issued two rounds before it is applied, so the gathers'
+// latency runs under the application of the rounds before.
 #include "fp4_common.h"
 #include "fp4_launch.h"
 
@@ -24,7 +31,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-constexpr int BM = 256, BN = 256, NT = 512;
+constexpr int BM = 256, BN = 256, NW = 8, NT = 64 * NW;
 constexpr int BKB = 64;                    // bytes of K per row per stage (128 codes)
 constexpr int OPB = 256 * BKB;             // one operand tile per stage: 16 KiB
 constexpr int STB = 2 * OPB;               // A then B: 32 KiB per stage buffer
@@ -32,7 +39,8 @@ constexpr int UNIT_SCALE = 0x7F7F7F7F;     // E8M0 127 = 2^0 in every byte
 constexpr int BUF_FLAGS = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
 constexpr int OOB = 0x7FFFFFF0;            // an offset past every buffer: the load returns 0
 constexpr int SLAB = 32;                   // epilogue rows per pass (one 32-row MFMA tile)
-constexpr int RP_OFF = 0, KC_OFF = 264, DV_OFF = 264 + 192;  // bookkeeping layout (ints)
+constexpr int RING = 64;                   // (column, delta) pairs per ring slot
+constexpr int LPR = STB / 1024 / NW;       // gather loads per wave per round (4)
 
 // 16-byte slot of (row, chunk) in a 256-row x 4-chunk operand tile.  A 16-lane group
 // reading 16 consecutive rows of one chunk hits 16 distinct slots modulo 16.
@@ -52,7 +60,15 @@ struct TileArgs {
     void *Y;
     float *acc_out;
     int tilesM, tilesN, raster_group;
-    int pf_dist;   // stages ahead that the L2 warm-up touches (0: off)
+};
+
+// LDS bookkeeping of one tile.
+struct Book {
+    float sA[BM];
+    float sW[BN];
+    int32_t rp[BM + 4];        // row_ptr[m0 .. m0+256] (clamped to M)
+    int32_t kc[4][RING];       // ring of the dA entries' columns, one slot per round
+    float dv[4][RING];         // and their values
 };
 
 // One stage of DMA for this wave: 2 loads of A (rows 32w..32w+31) and 2 of B.  Lane i of
@@ -102,136 +118,66 @@ __device__ __forceinline__ void mfma_block(v16f (&acc)[4][2], const u32x4 (&a)[4
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
-// The rest of one epilogue slab, after its scaled products are in E: add the dA * W
-// compensation (W rows gathered into the freed stage buffers) and store 32 rows of Y.
-template <int YDT, int WDT, bool COMP>
-__device__ __forceinline__ void slab_finish(const TileArgs &p, int q, int m0, int n0, int tid, int wave, int lane,
-                                            float *E, const int32_t *rp_s, int32_t *kc_s, float *dv_s, uint8_t *sb1,
-                                            uint8_t *sb2, uint8_t *sb3, __amdgpu_buffer_rsrc_t rsW) {
-    constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
-    constexpr int ROW_BYTES = BN * ESZ;          // one gathered W row segment
-    constexpr int ROUND = 3 * STB / ROW_BYTES;   // entries gathered per round (3 buffers)
-    const int M = p.M, N = p.N;
-    const int g = tid >> 5;   // 16 row groups: rows g and g + 16 of the slab
-    const int c8 = tid & 31;  // columns n0 + 8*c8 .. +7
-    const int gn = n0 + c8 * 8;
-        __syncthreads();
-        if constexpr (COMP) {
-            const int e_lo = rp_s[q * SLAB], e_hi = rp_s[q * SLAB + SLAB];
-#pragma unroll 1
-            for (int cb = e_lo; cb < e_hi; cb += ROUND) {
-                const int n_e = min(ROUND, e_hi - cb);
-                for (int t = tid; t < n_e; t += NT) {
-                    kc_s[t] = p.coo_col[cb + t];
-                    dv_s[t] = p.coo_val[cb + t];
-                }
-                __syncthreads();
-                // gather W[k][n0 .. n0+255] of every entry into sb1..sb3 back to back; a load
-                // moves 1 KiB: lane i carries bytes 16i.. of it
-                const int loads = (n_e * ROW_BYTES + 1023) / 1024;
-                for (int L = wave; L < loads; L += NT / 64) {
-                    const int byte = L * 1024 + lane * 16;
-                    const int e = byte / ROW_BYTES;
-                    const int col = n0 + (byte % ROW_BYTES) / ESZ;
-                    int o = OOB;
-                    if (e < n_e && col < N) o = (kc_s[e] * N + col) * ESZ;
-                    const int bsel = (L * 1024) / STB, within = L * 1024 - bsel * STB;
-                    uint8_t *dst = bsel == 0 ? sb1 : (bsel == 1 ? sb2 : sb3);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, LDS_PTR(dst + within), 16, o, 0, 0, 0);
-                }
-                WAIT_VMCNT(0);
-                __syncthreads();
-                if (gn < N) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int lr = g + 16 * h;
-                        const int rel = q * SLAB + lr;
-                        const int a0 = max(rp_s[rel], cb) - cb;
-                        const int a1 = min(rp_s[rel + 1], cb + n_e) - cb;
-                        if (a0 >= a1) continue;
-                        float4 *ep0 = reinterpret_cast<float4 *>(&E[eidx(lr, c8 * 8)]);
-                        float4 *ep1 = reinterpret_cast<float4 *>(&E[eidx(lr, c8 * 8 + 4)]);
-                        float4 y0 = *ep0, y1 = *ep1;
-                        for (int e = a0; e < a1; ++e) {
-                            const int byte = e * ROW_BYTES + c8 * 8 * ESZ;
-                            const int bsel = byte / STB;
-                            const uint8_t *src = (bsel == 0 ? sb1 : (bsel == 1 ? sb2 : sb3)) + (byte - bsel * STB);
-                            float wf[8];
-                            if constexpr (WDT == DT_BF16) {
-                                const u32x4 q4 = *reinterpret_cast<const u32x4 *>(src);
-                                const uint32_t ws[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-                                for (int t = 0; t < 4; ++t) {
-                                    wf[2 * t] = bf16_to_f32(ws[t] & 0xFFFFu);
-                                    wf[2 * t + 1] = bf16_to_f32(ws[t] >> 16);
-                                }
-                            } else {
-                                const u32x4 q0 = *reinterpret_cast<const u32x4 *>(src);
-                                const u32x4 q1 = *reinterpret_cast<const u32x4 *>(src + 16);
-                                const uint32_t ws[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-                                for (int t = 0; t < 8; ++t) wf[t] = __uint_as_float(ws[t]);
-                            }
-                            const float d = dv_s[e];
-                            y0.x = __builtin_fmaf(d, wf[0], y0.x);
-                            y0.y = __builtin_fmaf(d, wf[1], y0.y);
-                            y0.z = __builtin_fmaf(d, wf[2], y0.z);
-                            y0.w = __builtin_fmaf(d, wf[3], y0.w);
-                            y1.x = __builtin_fmaf(d, wf[4], y1.x);
-                            y1.y = __builtin_fmaf(d, wf[5], y1.y);
-                            y1.z = __builtin_fmaf(d, wf[6], y1.z);
-                            y1.w = __builtin_fmaf(d, wf[7], y1.w);
-                        }
-                        *ep0 = y0;
-                        *ep1 = y1;
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        // store the slab: 32 rows x 32 chunks of 8 columns, 32 threads per row
-        if (gn < N) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int lr = g + 16 * h;
-                const int grow = m0 + q * SLAB + lr;
-                if (grow < M) {
-                    const float4 e0 = *reinterpret_cast<const float4 *>(&E[eidx(lr, c8 * 8)]);
-                    const float4 e1 = *reinterpret_cast<const float4 *>(&E[eidx(lr, c8 * 8 + 4)]);
-                    if constexpr (YDT == DT_BF16) {
-                        uint4 o;
-                        o.x = f32_to_bf16_bits(e0.x) | (f32_to_bf16_bits(e0.y) << 16);
-                        o.y = f32_to_bf16_bits(e0.z) | (f32_to_bf16_bits(e0.w) << 16);
-                        o.z = f32_to_bf16_bits(e1.x) | (f32_to_bf16_bits(e1.y) << 16);
-                        o.w = f32_to_bf16_bits(e1.z) | (f32_to_bf16_bits(e1.w) << 16);
-                        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.Y) + (size_t)grow * N + gn) = o;
-                    } else {
-                        float4 *yp = reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.Y) + (size_t)grow * N + gn);
-                        yp[0] = e0;
-                        yp[1] = e1;
-                    }
-                }
-            }
-        }
-        __syncthreads();
+// Gather buffer of round u (three LDS buffers in rotation).  A select between the LDS
+// arrays themselves keeps the accesses in the LDS address space.
+__device__ __forceinline__ uint8_t *gather_buf(int u, uint8_t *g0, uint8_t *g1, uint8_t *g2) {
+    const int b = u % 3;
+    return b == 0 ? g0 : (b == 1 ? g1 : g2);
 }
 
+// The dA stream of one tile: entries [E0, E0 + n) of the COO list, in rounds of RE entries
+// whose W row segments (BN columns each) fill one 32 KiB gather buffer.
+template <int WDT>
+struct Stream {
+    static constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
+    static constexpr int ROW_BYTES = BN * ESZ;
+    static constexpr int RE = STB / ROW_BYTES;   // 64 (bf16 W) or 32 (fp32 W) entries per round
+    static_assert(RE <= RING, "ring slot holds a round");
+    __amdgpu_buffer_rsrc_t rsK, rsV, rsW;        // the tile's columns and values, and W
+    int n;                                       // entries of the tile
+    int N, n0, wave, lane;
+
+    // (column, delta) pairs of round u into ring slot u%4: wave 0 copies the columns,
+    // wave 1 the values (one 4-byte load per lane; past the tile's entries they read 0).
+    __device__ __forceinline__ void issue_pairs(Book &bk, int u) const {
+        const int o = (u * RE + lane) * 4;
+        if (wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, LDS_PTR(&bk.kc[u & 3][0]), 4, o, 0, 0, 0);
+        else if (wave == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, LDS_PTR(&bk.dv[u & 3][0]), 4, o, 0, 0, 0);
+    }
+    // W[k][n0 .. n0+BN-1] of every entry of round u, back to back into buffer u%3.  A load
+    // moves 1 KiB: lane i carries bytes 16i.. of it.  Every wave issues LPR loads.
+    __device__ __forceinline__ void issue_gather(const Book &bk, int u, uint8_t *g0, uint8_t *g1, uint8_t *g2) const {
+        uint8_t *dst = gather_buf(u, g0, g1, g2);
+#pragma unroll
+        for (int j = 0; j < LPR; ++j) {
+            const int L = wave * LPR + j;
+            const int byte = L * 1024 + lane * 16;
+            const int el = byte / ROW_BYTES;
+            const int col = n0 + (byte % ROW_BYTES) / ESZ;
+            int o = OOB;
+            if (u * RE + el < n && col < N) o = (bk.kc[u & 3][el] * N + col) * ESZ;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, LDS_PTR(dst + L * 1024), 16, o, 0, 0, 0);
+        }
+    }
+};
+
 template <int YDT, int WDT, bool COMP, bool ACCOUT>
-__global__ __launch_bounds__(NT) void k_fp4_gemm(TileArgs p) {
+__global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sb0[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb1[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb2[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb3[STB];
-    __shared__ __attribute__((aligned(16))) int32_t sx[1024];  // epilogue bookkeeping
-    __shared__ __attribute__((aligned(16))) uint32_t sink[8 * 64];  // target of the L2 warm-up loads
+    __shared__ __attribute__((aligned(16))) Book bk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int M = p.M, N = p.N, K = p.K;
 
     // XCD-aware order: consecutive workgroup ids go to different XCDs, so give each XCD a
     // contiguous range of logical tiles; within it raster_group tile-rows sweep the
-    // tile-columns together, so the tiles an XCD runs at once share their W column strip
-    // (operand codes and the compensation's W rows) in its L2.
+    // tile-columns together, so the tiles an XCD runs at once share operand strips (and
+    // the compensation's W rows) in its L2.
     const int per_xcd = gridDim.x / 8;
     const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= p.tilesM * p.tilesN) return;
@@ -265,34 +211,40 @@ __global__ __launch_bounds__(NT) void k_fp4_gemm(TileArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // prologue: stage 0, the tile's scales and row pointers, then stages 1 and 2.  The
+    // bookkeeping loads are older than the later stages' loads, so the wait for stage 0
+    // covers them too.
     stage_dma(rsA, rsB, sb0, wave, offA, offB, 0, KB, lane_chunk16);
+    __builtin_amdgcn_sched_barrier(0);
+    float bA = 0.0f, bW = 0.0f;
+    int bR0 = 0, bR1 = 0;
+    if (tid < 256) {
+        if (m0 + tid < M) bA = p.sA[m0 + tid];
+        if (n0 + tid < N) bW = p.sW[n0 + tid];
+        if constexpr (COMP) bR0 = p.row_ptr[min(m0 + tid, M)];
+    } else if (COMP && tid < 260) {
+        bR1 = p.row_ptr[min(m0 + tid, M)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     stage_dma(rsA, rsB, sb1, wave, offA, offB, 1, KB, lane_chunk16);
     stage_dma(rsA, rsB, sb2, wave, offA, offB, 2, KB, lane_chunk16);
+    __builtin_amdgcn_sched_barrier(0);
     WAIT_VMCNT(8);
+    if (tid < 256) {
+        bk.sA[tid] = bA;
+        bk.sW[tid] = bW;
+        if constexpr (COMP) bk.rp[tid] = bR0;
+    } else if (COMP && tid < 260) {
+        bk.rp[tid] = bR1;
+    }
     __builtin_amdgcn_s_barrier();
-
-    // L2 warm-up: one 4-byte load per 64-byte line of stage kt + pf_dist (waves 0-3 cover
-    // the 256 A rows, waves 4-7 the 256 B rows), landing in a scratch LDS word.  It pulls
-    // the lines into the XCD's L2 ahead of the stage loads, which then hit.
-    const int pf_row = (wave & 3) * 64 + lane;
-    const int pf_base = (wave < 4) ? ((m0 + pf_row < M) ? (m0 + pf_row) * KB : OOB)
-                                   : ((n0 + pf_row < N) ? (n0 + pf_row) * KB : OOB);
-    const __amdgpu_buffer_rsrc_t rsPF = (wave < 4) ? rsA : rsB;
-    auto warm = [&](int kt) {
-        const int s = kt + p.pf_dist;
-        const int o = (p.pf_dist > 0 && pf_base != OOB && s * BKB < KB) ? pf_base + s * BKB : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsPF, LDS_PTR(sink + wave * 64), 4, o, 0, 0, 0);
-    };
 
     // Stage kt lives in buffer kt%4.  Its loads were issued at stage kt-3; each wave waits
     // for its own loads of stage kt+1 before the barrier that ends stage kt, so after that
-    // barrier stage kt+1 is complete and stage kt's buffer is free for stage kt+4.  Per
-    // stage a wave issues 4 stage loads then 1 warm-up load: 11 loads follow those of
-    // stage kt+1.
+    // barrier stage kt+1 is complete and stage kt's buffer is free for stage kt+4.
     auto step = [&](int kt, const uint8_t *cur, uint8_t *ahead) {
         __builtin_amdgcn_sched_barrier(0);
         stage_dma(rsA, rsB, ahead, wave, offA, offB, kt + 3, KB, lane_chunk16);
-        warm(kt);
         u32x4 a0[4], b0[2], a1[4], b1[2];
         frag_load(cur, wm, wn, lane, 0, a0, b0);
         frag_load(cur, wm, wn, lane, 1, a1, b1);
@@ -301,7 +253,7 @@ __global__ __launch_bounds__(NT) void k_fp4_gemm(TileArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
-        WAIT_VMCNT(11);
+        WAIT_VMCNT(8);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -319,44 +271,63 @@ __global__ __launch_bounds__(NT) void k_fp4_gemm(TileArgs p) {
     // ---- epilogue: Y = fl(fl(acc * sA) * sW), then + sum of delta * W[k][n] over the row's
     // dA entries in ascending k, 32 rows at a time through an fp32 slab in LDS.
     // MFMA 32x32 output layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, col l%32.
-    constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
-    constexpr int ROW_BYTES = BN * ESZ;                 // one gathered W row segment
-    constexpr int ROUND = 3 * STB / ROW_BYTES;          // entries gathered per round (3 buffers)
-    static_assert(ROUND <= 192, "bookkeeping holds 192 entries");
+    using S = Stream<WDT>;
+    constexpr int RE = S::RE, ROW_BYTES = S::ROW_BYTES, ESZ = S::ESZ;
     float *E = reinterpret_cast<float *>(sb0);
-    int32_t *rp_s = sx + RP_OFF;
-    int32_t *kc_s = sx + KC_OFF;
-    float *dv_s = reinterpret_cast<float *>(sx + DV_OFF);
-    if constexpr (COMP) {
-        for (int t = tid; t <= BM; t += NT) rp_s[t] = p.row_ptr[min(m0 + t, M)];
-    }
     float sw[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int gcol = n0 + wn * 64 + j * 32 + (lane & 31);
-        sw[j] = gcol < N ? p.sW[gcol] : 0.0f;
-    }
-    const __amdgpu_buffer_rsrc_t rsW =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p.Wc), 0, COMP ? K * N * ESZ : 0, BUF_FLAGS);
+    for (int j = 0; j < 2; ++j) sw[j] = bk.sW[wn * 64 + j * 32 + (lane & 31)];
+    const int g = tid >> 5;    // 16 row groups: slab rows g and g + 16
+    const int c8 = tid & 31;   // columns n0 + 8*c8 .. +7
+    const int gn = n0 + c8 * 8;
 
-    // slab q holds tile rows 32q..32q+31: MFMA tile q%4 of the waves with wm == q/4 (the
-    // tile index must be a compile-time constant, so the four tiles are unrolled)
-#pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
+    S st;
+    int visited = 0;           // rounds whose first application has started
+    int E0 = 0;
+    if constexpr (COMP) {
+        E0 = bk.rp[0];
+        st.n = bk.rp[BM] - E0;
+        st.N = N;
+        st.n0 = n0;
+        st.wave = wave;
+        st.lane = lane;
+        st.rsK = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p.coo_col + E0), 0, st.n * 4, BUF_FLAGS);
+        st.rsV = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.coo_val + E0), 0, st.n * 4, BUF_FLAGS);
+        st.rsW = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p.Wc), 0, K * N * ESZ, BUF_FLAGS);
+        if (st.n > 0) {
+            // prime: pairs of rounds 0..2 and the gathers of rounds 0 and 1.  In flight
+            // afterwards: gather 0, pairs 2, gather 1 (the order every later wait assumes).
+            st.issue_pairs(bk, 0);
+            WAIT_VMCNT(0);
+            __syncthreads();
+            st.issue_pairs(bk, 1);
+            st.issue_gather(bk, 0, sb1, sb2, sb3);
+            WAIT_VMCNT(LPR);
+            __syncthreads();
+            st.issue_pairs(bk, 2);
+            st.issue_gather(bk, 1, sb1, sb2, sb3);
+        }
+    }
+
+    // slab q holds tile rows 32q..32q+31: MFMA tile q%4 of the waves with wm == q/4.  The
+    // slabs go in ascending row order (the dA stream is sorted by row); the tile index must
+    // be a compile-time constant, so the four tiles of a half are unrolled.
 #pragma unroll 1
-        for (int qh = 0; qh < 2; ++qh) {
+    for (int qh = 0; qh < 2; ++qh) {
+#pragma unroll
+        for (int qi = 0; qi < 4; ++qi) {
             const int q = qh * 4 + qi;
             if (wm == qh) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const int grow = m0 + q * SLAB + lr;
-                    const float sa = grow < M ? p.sA[grow] : 0.0f;
+                    const float sa = bk.sA[q * SLAB + lr];
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const int lc = wn * 64 + j * 32 + (lane & 31);
                         const float a = acc[qi][j][r];
                         if constexpr (ACCOUT) {
+                            const int grow = m0 + q * SLAB + lr;
                             if (grow < M && n0 + lc < N) p.acc_out[(size_t)grow * N + n0 + lc] = a;
                         }
                         const float t = a * sa;
@@ -364,31 +335,124 @@ __global__ __launch_bounds__(NT) void k_fp4_gemm(TileArgs p) {
                     }
                 }
             }
-            slab_finish<YDT, WDT, COMP>(p, q, m0, n0, tid, wave, lane, E, rp_s, kc_s, dv_s, sb1, sb2, sb3, rsW);
+            __syncthreads();
+            if constexpr (COMP) {
+                const int e_lo = bk.rp[q * SLAB] - E0, e_hi = bk.rp[q * SLAB + SLAB] - E0;
+                if (e_hi > e_lo) {
+#pragma unroll 1
+                    for (int t = e_lo / RE; t <= (e_hi - 1) / RE; ++t) {
+                        if (t >= visited) {
+                            // first use of round t: its gather (issued two rounds ago) and the
+                            // pairs of round t+2 are complete once only gather t+1 is in flight
+                            WAIT_VMCNT(LPR);
+                            __syncthreads();
+                            st.issue_pairs(bk, t + 3);
+                            st.issue_gather(bk, t + 2, sb1, sb2, sb3);
+                            visited = t + 1;
+                        }
+                        const uint8_t *gb = gather_buf(t, sb1, sb2, sb3);
+                        const float *dvr = bk.dv[t & 3];
+                        // thread (g, c8) adds the round's entries of slab rows g and g+16 to
+                        // their 8 columns, ascending k; four entries' W segments and deltas are
+                        // read together, then applied in order
+                        if (gn < N) {
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const int lr = g + 16 * h;
+                                const int rel = q * SLAB + lr;
+                                const int a0 = max(bk.rp[rel] - E0, t * RE) - t * RE;
+                                const int a1 = min(bk.rp[rel + 1] - E0, t * RE + RE) - t * RE;
+                                if (a0 >= a1) continue;
+                                float4 *ep0 = reinterpret_cast<float4 *>(&E[eidx(lr, c8 * 8)]);
+                                float4 *ep1 = reinterpret_cast<float4 *>(&E[eidx(lr, c8 * 8 + 4)]);
+                                float y[8];
+                                {
+                                    const float4 y0 = *ep0, y1 = *ep1;
+                                    y[0] = y0.x; y[1] = y0.y; y[2] = y0.z; y[3] = y0.w;
+                                    y[4] = y1.x; y[5] = y1.y; y[6] = y1.z; y[7] = y1.w;
+                                }
+#pragma unroll 1
+                                for (int e = a0; e < a1; e += 4) {
+                                    float wf[4][8], d[4];
+#pragma unroll
+                                    for (int u = 0; u < 4; ++u) {
+                                        const int ee = min(e + u, a1 - 1);
+                                        const uint8_t *src = gb + ee * ROW_BYTES + c8 * 8 * ESZ;
+                                        d[u] = dvr[ee];
+                                        if constexpr (WDT == DT_BF16) {
+                                            const u32x4 q4 = *reinterpret_cast<const u32x4 *>(src);
+                                            const uint32_t ws[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+                                            for (int v = 0; v < 4; ++v) {
+                                                wf[u][2 * v] = bf16_to_f32(ws[v] & 0xFFFFu);
+                                                wf[u][2 * v + 1] = bf16_to_f32(ws[v] >> 16);
+                                            }
+                                        } else {
+                                            const u32x4 q0 = *reinterpret_cast<const u32x4 *>(src);
+                                            const u32x4 q1 = *reinterpret_cast<const u32x4 *>(src + 16);
+                                            const uint32_t ws[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+                                            for (int v = 0; v < 8; ++v) wf[u][v] = __uint_as_float(ws[v]);
+                                        }
+                                    }
+#pragma unroll
+                                    for (int u = 0; u < 4; ++u) {
+                                        const bool valid = e + u < a1;
+#pragma unroll
+                                        for (int v = 0; v < 8; ++v) {
+                                            const float f = __builtin_fmaf(d[u], wf[u][v], y[v]);
+                                            y[v] = valid ? f : y[v];
+                                        }
+                                    }
+                                }
+                                *ep0 = make_float4(y[0], y[1], y[2], y[3]);
+                                *ep1 = make_float4(y[4], y[5], y[6], y[7]);
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            // store the slab: 32 rows x 32 chunks of 8 columns, 32 threads per row
+            if (gn < N) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int lr = g + 16 * h;
+                    const int grow = m0 + q * SLAB + lr;
+                    if (grow < M) {
+                        const float4 e0 = *reinterpret_cast<const float4 *>(&E[eidx(lr, c8 * 8)]);
+                        const float4 e1 = *reinterpret_cast<const float4 *>(&E[eidx(lr, c8 * 8 + 4)]);
+                        if constexpr (YDT == DT_BF16) {
+                            uint4 o;
+                            o.x = f32_to_bf16_bits(e0.x) | (f32_to_bf16_bits(e0.y) << 16);
+                            o.y = f32_to_bf16_bits(e0.z) | (f32_to_bf16_bits(e0.w) << 16);
+                            o.z = f32_to_bf16_bits(e1.x) | (f32_to_bf16_bits(e1.y) << 16);
+                            o.w = f32_to_bf16_bits(e1.z) | (f32_to_bf16_bits(e1.w) << 16);
+                            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.Y) + (size_t)grow * N + gn) = o;
+                        } else {
+                            float4 *yp =
+                                reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.Y) + (size_t)grow * N + gn);
+                            yp[0] = e0;
+                            yp[1] = e1;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
         }
     }
+    if constexpr (COMP) WAIT_VMCNT(0);  // the look-ahead gathers land before the workgroup ends
 }
 
 // Tile-rows per column sweep within an XCD.  FP4_GEMM_RASTER overrides (tuning aid).
-static int raster_group_for(int tilesM) {
+static int raster_group_for(int tilesM, bool comp) {
     static int env = -2;
     if (env == -2) {
         const char *e = getenv("FP4_GEMM_RASTER");
         env = e ? atoi(e) : -1;
     }
-    const int g = env > 0 ? env : 32;
+    const int g = env > 0 ? env : (comp ? 32 : 8);
     return g < tilesM ? g : tilesM;
-}
-
-// Stages ahead of the one being multiplied that the L2 warm-up touches.  FP4_GEMM_PF
-// overrides (tuning aid; 0 disables).
-static int pf_dist_default() {
-    static int env = -2;
-    if (env == -2) {
-        const char *e = getenv("FP4_GEMM_PF");
-        env = e ? atoi(e) : -1;
-    }
-    return env >= 0 ? env : 8;
 }
 
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
@@ -411,11 +475,10 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
     p.acc_out = acc_out;
     p.tilesM = (int)((M + BM - 1) / BM);
     p.tilesN = (int)((N + BN - 1) / BN);
-    p.raster_group = raster_group_for(p.tilesM);
-    p.pf_dist = pf_dist_default();
+    const bool comp = row_ptr != nullptr;
+    p.raster_group = raster_group_for(p.tilesM, comp);
     const int64_t tiles = (int64_t)p.tilesM * p.tilesN;
     const int blocks = (int)((tiles + 7) / 8 * 8);
-    const bool comp = row_ptr != nullptr;
 #define G(YD, WD, CO, AO) hipLaunchKernelGGL((k_fp4_gemm<YD, WD, CO, AO>), dim3(blocks), dim3(NT), 0, s, p)
 #define G2(YD, WD)                                    \
     do {                                              \

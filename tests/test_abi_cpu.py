@@ -129,3 +129,6 @@ def test_gemm_rejects():
     assert g(ydt=5) == EDTYPE
     assert g(K=96 + 16) == ESHAPE
     assert g(N=0) == ESHAPE
+    # Wq (N x K/2) must stay below 2^31 bytes, and the compensation's W below 2^31 bytes
+    assert g(N=1 << 17, K=32768) == ESHAPE
+    assert g(N=1 << 15, K=32768, rp=FAKE, cc=FAKE, cv=FAKE, W=FAKE) == ESHAPE
