@@ -186,7 +186,8 @@ def main():
         nnz = int(it["nnz"].item())
         g = lambda: fp4.lib().fp4_gemm(  # noqa: E731
             fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K,
-            fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]), fp4._ptr(Wd), fp4._dt(Wd),
+            fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_row"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]),
+            fp4._ptr(Wd), fp4._dt(Wd),
             fp4._ptr(Y), fp4._dt(Y), None, fp4._stream(Ad))
         ms_g = time_on_stream(g, args.steps, 2)
         gemm_ms += ms_g

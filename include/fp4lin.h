@@ -125,13 +125,14 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
  * CDNA4 FP4 matrix cores with fp32 accumulation; granularity paragraph: sA and sW factor
  * out of the K-sum).
  *   Aq M x K/2, sA fp32[M], Wq N x K/2, sW fp32[N] (as produced by fp4_quantize)
- *   row_ptr, coo_col, coo_val: dA as produced by fp4_outlier_clamp, or all three NULL for
- *            no compensation term; W (K x N, w_dtype) is then unused and may be NULL.
+ *   row_ptr, coo_row, coo_col, coo_val: dA as produced by fp4_outlier_clamp (CSR row
+ *            offsets plus the COO list sorted by (row, col)), or all four NULL for no
+ *            compensation term; W (K x N, w_dtype) is then unused and may be NULL.
  *   Y        M x N of y_dtype (out)
  *   acc_out  NULL, or device fp32[M*N] receiving the raw accumulator acc (a check aid).
  * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,ALIGN,DEVICE,HIP}. */
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW,
-                    int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
+                    int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_row,
                     const int32_t *coo_col, const float *coo_val, const void *W, int32_t w_dtype,
                     void *Y, int32_t y_dtype, float *acc_out, void *stream);
 

@@ -57,7 +57,7 @@ def lib():
         "fp4_outlier_capacity": (i64, [i64, i64, dbl]),
         "fp4_outlier_workspace_bytes": (sz, [i64, i64, i32, dbl]),
         "fp4_outlier_clamp": (i32, [vp, i32, i64, i64, dbl, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
-        "fp4_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32, vp, i32, vp, vp]),
+        "fp4_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp]),
         "fp4_forward_layout": (i32, [i64, i64, i64, i32, dbl, C.POINTER(WsLayout)]),
         "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, dbl]),
         "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
@@ -150,17 +150,18 @@ def outlier_clamp(A: torch.Tensor, q: float, trim: bool = True) -> dict:
 
 
 def gemm(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, K: int,
-         row_ptr: torch.Tensor | None = None, coo_col: torch.Tensor | None = None,
-         coo_val: torch.Tensor | None = None, W: torch.Tensor | None = None,
+         row_ptr: torch.Tensor | None = None, coo_row: torch.Tensor | None = None,
+         coo_col: torch.Tensor | None = None, coo_val: torch.Tensor | None = None, W: torch.Tensor | None = None,
          out_dtype: torch.dtype = torch.bfloat16, acc_out: bool = False):
     """Y = fl(fl(acc * sA) * sW) (+ dA . W when the COO arrays and W are given)."""
-    _need_cuda(Aq, sA, Wq, sW, row_ptr, coo_col, coo_val, W)
+    _need_cuda(Aq, sA, Wq, sW, row_ptr, coo_row, coo_col, coo_val, W)
     M, N = Aq.shape[0], Wq.shape[0]
     Y = torch.empty((M, N), dtype=out_dtype, device=Aq.device)
     acc = torch.empty((M, N), dtype=torch.float32, device=Aq.device) if acc_out else None
     wdt = _dt(W) if W is not None else FP4_BF16
-    _check(lib().fp4_gemm(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, _ptr(row_ptr), _ptr(coo_col),
-                          _ptr(coo_val), _ptr(W), wdt, _ptr(Y), _out_dtype_code(out_dtype), _ptr(acc), _stream(Aq)))
+    _check(lib().fp4_gemm(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, _ptr(row_ptr), _ptr(coo_row),
+                          _ptr(coo_col), _ptr(coo_val), _ptr(W), wdt, _ptr(Y), _out_dtype_code(out_dtype), _ptr(acc),
+                          _stream(Aq)))
     return (Y, acc) if acc_out else Y
 
 

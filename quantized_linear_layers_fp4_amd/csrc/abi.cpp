@@ -212,20 +212,21 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
 }
 
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
-                    int64_t K, const int32_t *row_ptr, const int32_t *coo_col, const float *coo_val, const void *W,
+                    int64_t K, const int32_t *row_ptr, const int32_t *coo_row, const int32_t *coo_col,
+                    const float *coo_val, const void *W,
                     int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *stream) {
     if (!Aq || !sA || !Wq || !sW || !Y) return FP4_ERR_NULL;
-    const int ncomp = (row_ptr != nullptr) + (coo_col != nullptr) + (coo_val != nullptr);
-    if (ncomp != 0 && ncomp != 3) return FP4_ERR_NULL;
-    if (ncomp == 3 && !W) return FP4_ERR_NULL;
-    if (!dtype_ok(y_dtype) || (ncomp == 3 && !dtype_ok(w_dtype))) return FP4_ERR_DTYPE;
-    if (!gemm_ok(M, N, K) || (ncomp == 3 && !wcomp_ok(N, K, w_dtype))) return FP4_ERR_SHAPE;
+    const int ncomp = (row_ptr != nullptr) + (coo_row != nullptr) + (coo_col != nullptr) + (coo_val != nullptr);
+    if (ncomp != 0 && ncomp != 4) return FP4_ERR_NULL;
+    if (ncomp == 4 && !W) return FP4_ERR_NULL;
+    if (!dtype_ok(y_dtype) || (ncomp == 4 && !dtype_ok(w_dtype))) return FP4_ERR_DTYPE;
+    if (!gemm_ok(M, N, K) || (ncomp == 4 && !wcomp_ok(N, K, w_dtype))) return FP4_ERR_SHAPE;
     if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(Y) || (W && !aligned16(W)) || (acc_out && !aligned16(acc_out)))
         return FP4_ERR_ALIGN;
     int cus;
     fp4_status st = device_check(&cus);
     if (st != FP4_OK) return st;
-    return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, ncomp ? row_ptr : nullptr, coo_col, coo_val, W,
+    return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, ncomp ? row_ptr : nullptr, coo_row, coo_col, coo_val, W,
                                   dt_of(w_dtype), Y, dt_of(y_dtype), acc_out, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -291,7 +292,8 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
     if (st != FP4_OK) return st;
     hipError_t e = launch_quant_cols(W, dt_of(in_dtype), K, N, sW, Wq, s);
     if (e == hipSuccess)
-        e = launch_gemm(Aq, sA, Wq, sW, M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype), Y, dt_of(y_dtype),
+        e = launch_gemm(Aq, sA, Wq, sW, M, N, K, row_ptr, coo_row, coo_col, coo_val, W, dt_of(in_dtype), Y,
+                        dt_of(y_dtype),
                         nullptr, s);
     return hip_status(e);
 }

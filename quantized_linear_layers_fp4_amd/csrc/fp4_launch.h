@@ -24,7 +24,7 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
 
 // FP4 GEMM + dequantization + compensation.  comp arrays NULL = no compensation term.
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
+                       int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_row, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, void *Y, int y_dt, float *acc_out,
                        hipStream_t s);
 

@@ -11,7 +11,8 @@
 // K advances 128 codes (64 bytes per row) per stage.  Operand tiles travel from global
 // memory straight into one of four LDS stage buffers (buffer loads with the LDS flag,
 // issued three stages ahead); rows or K chunks outside the matrices read as zero.  One
-// barrier per stage.  The row/column scales and the row pointers of dA for the tile are
+// barrier per stage; the fragments of the next stage's first K-step are read before it, so
+// the matrix cores restart right after each barrier.  The row/column scales and the row pointers of dA for the tile are
 // fetched into LDS under the first stage loads.
 //
 // Epilogue: 32 rows at a time through an fp32 slab in LDS.  The tile's dA entries (sorted
@@ -54,7 +55,7 @@ struct TileArgs {
     const uint8_t *Aq, *Wq;
     const float *sA, *sW;
     int M, N, K;
-    const int32_t *row_ptr, *coo_col;
+    const int32_t *row_ptr, *coo_row, *coo_col;
     const float *coo_val;
     const void *Wc;
     void *Y;
@@ -62,14 +63,67 @@ struct TileArgs {
     int tilesM, tilesN, raster_group;
 };
 
-// LDS bookkeeping of one tile.
+// LDS bookkeeping of one tile (written with ordinary stores).
 struct Book {
     float sA[BM];
     float sW[BN];
     int32_t rp[BM + 4];        // row_ptr[m0 .. m0+256] (clamped to M)
-    int32_t kc[4][RING];       // ring of the dA entries' columns, one slot per round
-    float dv[4][RING];         // and their values
+    float X[NW][BN];           // first-row partial sums of each wave's share of a pass
+    int32_t Xrow[NW];          // (slab row of X[w], or -1)
 };
+
+// The dA entries of the rounds in flight, one slot per round (filled by buffer loads with
+// the LDS flag).
+struct Ring {
+    int32_t kc[4][RING];       // columns
+    float dv[4][RING];         // values
+    int32_t kr[4][RING];       // rows
+};
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)LDS_PTR(const_cast<void *>(p));
+}
+
+// Reads of LDS that buffer loads with the LDS flag fill.  The loads' completion is waited
+// for explicitly (vmcnt, then a barrier); these reads carry their own lgkmcnt wait, so the
+// compiler does not add a wait for every buffer load still in flight.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_read2_u32(uint32_t a, uint32_t b, uint32_t &x, uint32_t &y) {
+    asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(x), "=&v"(y)
+                 : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void lds_read4_u32(const uint32_t (&a)[4], uint32_t (&x)[4]) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+__device__ __forceinline__ void lds_read4_b64(const uint32_t (&a)[4], u32x2 (&x)[4]) {
+    asm volatile(
+        "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+__device__ __forceinline__ void lds_read4_b128(const uint32_t (&a)[4], u32x4 (&x)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes are done, then
+// s_barrier.  Buffer loads and global stores stay in flight (their waits are explicit).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 // One stage of DMA for this wave: 2 loads of A (rows 32w..32w+31) and 2 of B.  Lane i of
 // load j fills slot 64*(2w+j) + i: row 16*(2w+j) + i/4, at the swizzled position i%4.
@@ -133,31 +187,41 @@ struct Stream {
     static constexpr int ROW_BYTES = BN * ESZ;
     static constexpr int RE = STB / ROW_BYTES;   // 64 (bf16 W) or 32 (fp32 W) entries per round
     static_assert(RE <= RING, "ring slot holds a round");
-    __amdgpu_buffer_rsrc_t rsK, rsV, rsW;        // the tile's columns and values, and W
+    __amdgpu_buffer_rsrc_t rsK, rsV, rsR, rsW;   // the tile's columns, values and rows, and W
     int n;                                       // entries of the tile
     int N, n0, wave, lane;
 
-    // (column, delta) pairs of round u into ring slot u%4: wave 0 copies the columns,
-    // wave 1 the values (one 4-byte load per lane; past the tile's entries they read 0).
-    __device__ __forceinline__ void issue_pairs(Book &bk, int u) const {
+    // (column, delta, row) of the entries of round u into ring slot u%4: wave 0 copies the
+    // columns, wave 1 the values, wave 2 the rows (one 4-byte load per lane; past the
+    // tile's entries they read 0).
+    __device__ __forceinline__ void issue_pairs(Ring &rg, int u) const {
         const int o = (u * RE + lane) * 4;
         if (wave == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, LDS_PTR(&bk.kc[u & 3][0]), 4, o, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, LDS_PTR(&rg.kc[u & 3][0]), 4, o, 0, 0, 0);
         else if (wave == 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, LDS_PTR(&bk.dv[u & 3][0]), 4, o, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, LDS_PTR(&rg.dv[u & 3][0]), 4, o, 0, 0, 0);
+        else if (wave == 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, LDS_PTR(&rg.kr[u & 3][0]), 4, o, 0, 0, 0);
     }
     // W[k][n0 .. n0+BN-1] of every entry of round u, back to back into buffer u%3.  A load
     // moves 1 KiB: lane i carries bytes 16i.. of it.  Every wave issues LPR loads.
-    __device__ __forceinline__ void issue_gather(const Book &bk, int u, uint8_t *g0, uint8_t *g1, uint8_t *g2) const {
+    __device__ __forceinline__ void issue_gather(const Ring &rg, int u, uint8_t *g0, uint8_t *g1, uint8_t *g2) const {
         uint8_t *dst = gather_buf(u, g0, g1, g2);
+        uint32_t ka[LPR], kv[LPR];
+        int el[LPR], col[LPR];
+#pragma unroll
+        for (int j = 0; j < LPR; ++j) {
+            const int byte = (wave * LPR + j) * 1024 + lane * 16;
+            el[j] = byte / ROW_BYTES;
+            col[j] = n0 + (byte % ROW_BYTES) / ESZ;
+            ka[j] = lds_addr(&rg.kc[u & 3][el[j]]);
+        }
+        lds_read4_u32(ka, kv);
 #pragma unroll
         for (int j = 0; j < LPR; ++j) {
             const int L = wave * LPR + j;
-            const int byte = L * 1024 + lane * 16;
-            const int el = byte / ROW_BYTES;
-            const int col = n0 + (byte % ROW_BYTES) / ESZ;
             int o = OOB;
-            if (u * RE + el < n && col < N) o = (bk.kc[u & 3][el] * N + col) * ESZ;
+            if (u * RE + el[j] < n && col[j] < N) o = ((int)kv[j] * N + col[j]) * ESZ;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, LDS_PTR(dst + L * 1024), 16, o, 0, 0, 0);
         }
     }
@@ -170,6 +234,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sb2[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb3[STB];
     __shared__ __attribute__((aligned(16))) Book bk;
+    __shared__ __attribute__((aligned(16))) Ring rg;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int M = p.M, N = p.N, K = p.K;
@@ -212,8 +277,8 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // prologue: stage 0, the tile's scales and row pointers, then stages 1 and 2.  The
-    // bookkeeping loads are older than the later stages' loads, so the wait for stage 0
-    // covers them too.
+    // bookkeeping loads are older than the later stages' loads, so the wait for stages 0
+    // and 1 covers them too.
     stage_dma(rsA, rsB, sb0, wave, offA, offB, 0, KB, lane_chunk16);
     __builtin_amdgcn_sched_barrier(0);
     float bA = 0.0f, bW = 0.0f;
@@ -229,7 +294,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     stage_dma(rsA, rsB, sb1, wave, offA, offB, 1, KB, lane_chunk16);
     stage_dma(rsA, rsB, sb2, wave, offA, offB, 2, KB, lane_chunk16);
     __builtin_amdgcn_sched_barrier(0);
-    WAIT_VMCNT(8);
+    WAIT_VMCNT(4);
     if (tid < 256) {
         bk.sA[tid] = bA;
         bk.sW[tid] = bW;
@@ -239,31 +304,38 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     }
     __builtin_amdgcn_s_barrier();
 
-    // Stage kt lives in buffer kt%4.  Its loads were issued at stage kt-3; each wave waits
-    // for its own loads of stage kt+1 before the barrier that ends stage kt, so after that
-    // barrier stage kt+1 is complete and stage kt's buffer is free for stage kt+4.
-    auto step = [&](int kt, const uint8_t *cur, uint8_t *ahead) {
+    // Stage kt lives in buffer kt%4; its loads are issued at step kt-3.  At the start of
+    // step kt the K-step-0 fragments of stage kt are already in registers and stage kt+1 is
+    // complete; the step reads stage kt's K-step-1 fragments under the first eight MFMAs
+    // and stage kt+1's K-step-0 fragments under the second eight.  Each wave then waits for
+    // its own loads of stage kt+2 before the barrier that ends the step, so after it stage
+    // kt+2 is complete and stage kt-1's buffer (read last in step kt-1) takes stage kt+3.
+    u32x4 a0[4], b0[2];
+    __builtin_amdgcn_sched_barrier(0);
+    frag_load(sb0, wm, wn, lane, 0, a0, b0);
+    auto step = [&](int kt, const uint8_t *cur, const uint8_t *nxt, uint8_t *ahead) {
         __builtin_amdgcn_sched_barrier(0);
         stage_dma(rsA, rsB, ahead, wave, offA, offB, kt + 3, KB, lane_chunk16);
-        u32x4 a0[4], b0[2], a1[4], b1[2];
-        frag_load(cur, wm, wn, lane, 0, a0, b0);
+        u32x4 a1[4], b1[2];
         frag_load(cur, wm, wn, lane, 1, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, a0, b0);
         __builtin_amdgcn_sched_barrier(0);
+        frag_load(nxt, wm, wn, lane, 0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
-        WAIT_VMCNT(8);
+        WAIT_VMCNT(4);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
     // whole groups of four stages (a group may run past the last stage on zeros: one exit
     // keeps the accumulators in one set of registers)
     for (int kt = 0; kt < kstages; kt += 4) {
-        step(kt, sb0, sb3);
-        step(kt + 1, sb1, sb0);
-        step(kt + 2, sb2, sb1);
-        step(kt + 3, sb3, sb2);
+        step(kt, sb0, sb1, sb3);
+        step(kt + 1, sb1, sb2, sb0);
+        step(kt + 2, sb2, sb3, sb1);
+        step(kt + 3, sb3, sb0, sb2);
     }
     WAIT_VMCNT(0);  // look-ahead loads past the end (zeros) land before the buffers are reused
     __syncthreads();
@@ -293,19 +365,20 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
         st.lane = lane;
         st.rsK = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p.coo_col + E0), 0, st.n * 4, BUF_FLAGS);
         st.rsV = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.coo_val + E0), 0, st.n * 4, BUF_FLAGS);
+        st.rsR = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p.coo_row + E0), 0, st.n * 4, BUF_FLAGS);
         st.rsW = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p.Wc), 0, K * N * ESZ, BUF_FLAGS);
         if (st.n > 0) {
             // prime: pairs of rounds 0..2 and the gathers of rounds 0 and 1.  In flight
             // afterwards: gather 0, pairs 2, gather 1 (the order every later wait assumes).
-            st.issue_pairs(bk, 0);
+            st.issue_pairs(rg, 0);
             WAIT_VMCNT(0);
-            __syncthreads();
-            st.issue_pairs(bk, 1);
-            st.issue_gather(bk, 0, sb1, sb2, sb3);
+            lds_barrier();
+            st.issue_pairs(rg, 1);
+            st.issue_gather(rg, 0, sb1, sb2, sb3);
             WAIT_VMCNT(LPR);
-            __syncthreads();
-            st.issue_pairs(bk, 2);
-            st.issue_gather(bk, 1, sb1, sb2, sb3);
+            lds_barrier();
+            st.issue_pairs(rg, 2);
+            st.issue_gather(rg, 1, sb1, sb2, sb3);
         }
     }
 
@@ -335,7 +408,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             if constexpr (COMP) {
                 const int e_lo = bk.rp[q * SLAB] - E0, e_hi = bk.rp[q * SLAB + SLAB] - E0;
                 if (e_hi > e_lo) {
@@ -345,72 +418,133 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
                             // first use of round t: its gather (issued two rounds ago) and the
                             // pairs of round t+2 are complete once only gather t+1 is in flight
                             WAIT_VMCNT(LPR);
-                            __syncthreads();
-                            st.issue_pairs(bk, t + 3);
-                            st.issue_gather(bk, t + 2, sb1, sb2, sb3);
+                            lds_barrier();
+                            st.issue_pairs(rg, t + 3);
+                            st.issue_gather(rg, t + 2, sb1, sb2, sb3);
                             visited = t + 1;
                         }
                         const uint8_t *gb = gather_buf(t, sb1, sb2, sb3);
-                        const float *dvr = bk.dv[t & 3];
-                        // thread (g, c8) adds the round's entries of slab rows g and g+16 to
-                        // their 8 columns, ascending k; four entries' W segments and deltas are
-                        // read together, then applied in order
-                        if (gn < N) {
+
+                        // one pass: the round's entries of slab q split into NW contiguous
+                        // shares, wave w adding share w over all BN columns (4 per lane).
+                        // Entries are sorted by row, so a share owns its rows except the first,
+                        // which may continue the previous share's last row: that partial sum
+                        // goes to X[w] and is added after the barrier, shares in order.
+                        const int a = max(e_lo, t * RE) - t * RE;
+                        const int b = min(e_hi, t * RE + RE) - t * RE;
+                        const int pa = a + ((b - a) * wave) / NW, pb = a + ((b - a) * (wave + 1)) / NW;
+                        const int rbase = m0 + q * SLAB;
+                        // the share's rows and deltas: one LDS read per lane, then broadcast
+                        const int ns = pb - pa;   // at most RE / NW <= 8 entries
+                        int krl = 0;
+                        float dvl = 0.0f;
+                        {
+                            const int ei = pa + min(lane, max(ns - 1, 0));
+                            uint32_t kx, dx;
+                            lds_read2_u32(lds_addr(&rg.kr[t & 3][ei]), lds_addr(&rg.dv[t & 3][ei]), kx, dx);
+                            krl = ((int)kx - rbase) & (SLAB - 1);
+                            dvl = __uint_as_float(dx);
+                        }
+                        const int first_row = ns > 0 ? __builtin_amdgcn_readfirstlane(krl) : -1;
+                        if (lane == 0) bk.Xrow[wave] = first_row;
+                        float4 part = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                        int cur = first_row;
+                        auto add_to_E = [&](int row, const float4 &v) {
+                            float4 *ep = reinterpret_cast<float4 *>(&E[eidx(row, lane * 4)]);
+                            float4 y = *ep;
+                            y.x += v.x;
+                            y.y += v.y;
+                            y.z += v.z;
+                            y.w += v.w;
+                            *ep = y;
+                        };
+                        // four entries' W segments are read together, then added in order
 #pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                const int lr = g + 16 * h;
-                                const int rel = q * SLAB + lr;
-                                const int a0 = max(bk.rp[rel] - E0, t * RE) - t * RE;
-                                const int a1 = min(bk.rp[rel + 1] - E0, t * RE + RE) - t * RE;
-                                if (a0 >= a1) continue;
-                                float4 *ep0 = reinterpret_cast<float4 *>(&E[eidx(lr, c8 * 8)]);
-                                float4 *ep1 = reinterpret_cast<float4 *>(&E[eidx(lr, c8 * 8 + 4)]);
-                                float y[8];
-                                {
-                                    const float4 y0 = *ep0, y1 = *ep1;
-                                    y[0] = y0.x; y[1] = y0.y; y[2] = y0.z; y[3] = y0.w;
-                                    y[4] = y1.x; y[5] = y1.y; y[6] = y1.z; y[7] = y1.w;
+                        for (int i0 = 0; i0 < RE / NW; i0 += 4) {
+                            if (i0 >= ns) break;
+                            float wf[4][4];
+                            uint32_t wa[4];
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                wa[u] = lds_addr(gb + (pa + min(i0 + u, ns - 1)) * ROW_BYTES + lane * 4 * ESZ);
+                            if constexpr (WDT == DT_BF16) {
+                                u32x2 w2[4];
+                                lds_read4_b64(wa, w2);
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) {
+                                    wf[u][0] = bf16_to_f32(w2[u].x & 0xFFFFu);
+                                    wf[u][1] = bf16_to_f32(w2[u].x >> 16);
+                                    wf[u][2] = bf16_to_f32(w2[u].y & 0xFFFFu);
+                                    wf[u][3] = bf16_to_f32(w2[u].y >> 16);
                                 }
-#pragma unroll 1
-                                for (int e = a0; e < a1; e += 4) {
-                                    float wf[4][8], d[4];
+                            } else {
+                                u32x4 w4[4];
+                                lds_read4_b128(wa, w4);
 #pragma unroll
-                                    for (int u = 0; u < 4; ++u) {
-                                        const int ee = min(e + u, a1 - 1);
-                                        const uint8_t *src = gb + ee * ROW_BYTES + c8 * 8 * ESZ;
-                                        d[u] = dvr[ee];
-                                        if constexpr (WDT == DT_BF16) {
-                                            const u32x4 q4 = *reinterpret_cast<const u32x4 *>(src);
-                                            const uint32_t ws[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-                                            for (int v = 0; v < 4; ++v) {
-                                                wf[u][2 * v] = bf16_to_f32(ws[v] & 0xFFFFu);
-                                                wf[u][2 * v + 1] = bf16_to_f32(ws[v] >> 16);
-                                            }
-                                        } else {
-                                            const u32x4 q0 = *reinterpret_cast<const u32x4 *>(src);
-                                            const u32x4 q1 = *reinterpret_cast<const u32x4 *>(src + 16);
-                                            const uint32_t ws[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-                                            for (int v = 0; v < 8; ++v) wf[u][v] = __uint_as_float(ws[v]);
-                                        }
-                                    }
-#pragma unroll
-                                    for (int u = 0; u < 4; ++u) {
-                                        const bool valid = e + u < a1;
-#pragma unroll
-                                        for (int v = 0; v < 8; ++v) {
-                                            const float f = __builtin_fmaf(d[u], wf[u][v], y[v]);
-                                            y[v] = valid ? f : y[v];
-                                        }
-                                    }
+                                for (int u = 0; u < 4; ++u) {
+                                    wf[u][0] = __uint_as_float(w4[u].x);
+                                    wf[u][1] = __uint_as_float(w4[u].y);
+                                    wf[u][2] = __uint_as_float(w4[u].z);
+                                    wf[u][3] = __uint_as_float(w4[u].w);
                                 }
-                                *ep0 = make_float4(y[0], y[1], y[2], y[3]);
-                                *ep1 = make_float4(y[4], y[5], y[6], y[7]);
+                            }
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                if (i0 + u >= ns) break;
+                                const int row = __builtin_amdgcn_readlane(krl, i0 + u);
+                                const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                    __builtin_bit_cast(int, dvl), i0 + u));
+                                if (row != cur) {
+                                    // rows are sorted: cur is complete (only the first row of a
+                                    // share can continue the previous share's last row)
+                                    if (wave > 0 && cur == first_row)
+                                        *reinterpret_cast<float4 *>(&bk.X[wave][lane * 4]) = part;
+                                    else
+                                        add_to_E(cur, part);
+                                    cur = row;
+                                    part = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                                }
+                                part.x = __builtin_fmaf(d, wf[u][0], part.x);
+                                part.y = __builtin_fmaf(d, wf[u][1], part.y);
+                                part.z = __builtin_fmaf(d, wf[u][2], part.z);
+                                part.w = __builtin_fmaf(d, wf[u][3], part.w);
                             }
                         }
+                        if (ns > 0) {
+                            if (wave > 0 && cur == first_row)
+                                *reinterpret_cast<float4 *>(&bk.X[wave][lane * 4]) = part;
+                            else
+                                add_to_E(cur, part);
+                        }
+                        lds_barrier();
+                        if (wave == 0) {
+                            // the shares' first-row partial sums in share order; a run of one
+                            // row is summed first and added to E once
+                            const int xr = lane < NW ? bk.Xrow[lane] : -1;
+                            float4 x[NW];
+#pragma unroll
+                            for (int w = 1; w < NW; ++w) x[w] = *reinterpret_cast<const float4 *>(&bk.X[w][lane * 4]);
+                            int rr = -1;
+                            float4 run = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                            for (int w = 1; w < NW; ++w) {
+                                const int r = __builtin_amdgcn_readlane(xr, w);
+                                if (r < 0) continue;
+                                if (r == rr) {
+                                    run.x += x[w].x;
+                                    run.y += x[w].y;
+                                    run.z += x[w].z;
+                                    run.w += x[w].w;
+                                } else {
+                                    if (rr >= 0) add_to_E(rr, run);
+                                    rr = r;
+                                    run = x[w];
+                                }
+                            }
+                            if (rr >= 0) add_to_E(rr, run);
+                        }
+                        lds_barrier();
                     }
-                    __syncthreads();
                 }
             }
             // store the slab: 32 rows x 32 chunks of 8 columns, 32 threads per row
@@ -438,7 +572,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
     if constexpr (COMP) WAIT_VMCNT(0);  // the look-ahead gathers land before the workgroup ends
@@ -456,7 +590,7 @@ static int raster_group_for(int tilesM, bool comp) {
 }
 
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
+                       int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_row, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, void *Y, int y_dt, float *acc_out,
                        hipStream_t s) {
     TileArgs p;
@@ -468,6 +602,7 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
     p.N = (int)N;
     p.K = (int)K;
     p.row_ptr = row_ptr;
+    p.coo_row = coo_row;
     p.coo_col = coo_col;
     p.coo_val = coo_val;
     p.Wc = W;

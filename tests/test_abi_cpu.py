@@ -121,14 +121,16 @@ def test_outlier_clamp_rejects():
 def test_gemm_rejects():
     L = fp4.lib()
     g = lambda **kw: L.fp4_gemm(kw.get("Aq", FAKE), FAKE, FAKE, FAKE, kw.get("M", 64), kw.get("N", 64),
-                                kw.get("K", 128), kw.get("rp", None), kw.get("cc", None), kw.get("cv", None),
+                                kw.get("K", 128), kw.get("rp", None), kw.get("cr", None), kw.get("cc", None),
+                                kw.get("cv", None),
                                 kw.get("W", None), 1, FAKE, kw.get("ydt", 1), None, None)
     assert g(Aq=None) == ENULL
     assert g(rp=FAKE) == ENULL            # partial compensation arguments
-    assert g(rp=FAKE, cc=FAKE, cv=FAKE) == ENULL  # compensation without W
+    assert g(rp=FAKE, cc=FAKE, cv=FAKE) == ENULL  # coo_row missing
+    assert g(rp=FAKE, cr=FAKE, cc=FAKE, cv=FAKE) == ENULL  # compensation without W
     assert g(ydt=5) == EDTYPE
     assert g(K=96 + 16) == ESHAPE
     assert g(N=0) == ESHAPE
     # Wq (N x K/2) must stay below 2^31 bytes, and the compensation's W below 2^31 bytes
     assert g(N=1 << 17, K=32768) == ESHAPE
-    assert g(N=1 << 15, K=32768, rp=FAKE, cc=FAKE, cv=FAKE, W=FAKE) == ESHAPE
+    assert g(N=1 << 15, K=32768, rp=FAKE, cr=FAKE, cc=FAKE, cv=FAKE, W=FAKE) == ESHAPE
