@@ -40,8 +40,9 @@ constexpr int UNIT_SCALE = 0x7F7F7F7F;     // E8M0 127 = 2^0 in every byte
 constexpr int BUF_FLAGS = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
 constexpr int OOB = 0x7FFFFFF0;            // an offset past every buffer: the load returns 0
 constexpr int SLAB = 32;                   // epilogue rows per pass (one 32-row MFMA tile)
-constexpr int RING = 64;                   // (column, delta) pairs per ring slot
-constexpr int LPR = STB / 1024 / NW;       // gather loads per wave per round (4)
+constexpr int GBYTES = 3 * STB;            // gather space of one round: the three free stage buffers
+constexpr int RING = 192;                  // dA entries per ring slot
+constexpr int LPR = GBYTES / 1024 / NW;    // gather loads per wave per round (12)
 
 // 16-byte slot of (row, chunk) in a 256-row x 4-chunk operand tile.  A 16-lane group
 // reading 16 consecutive rows of one chunk hits 16 distinct slots modulo 16.
@@ -75,9 +76,9 @@ struct Book {
 // The dA entries of the rounds in flight, one slot per round (filled by buffer loads with
 // the LDS flag).
 struct Ring {
-    int32_t kc[4][RING];       // columns
-    float dv[4][RING];         // values
-    int32_t kr[4][RING];       // rows
+    int32_t kc[2][RING];       // columns
+    float dv[2][RING];         // values
+    int32_t kr[2][RING];       // rows
 };
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -172,11 +173,11 @@ __device__ __forceinline__ void mfma_block(v16f (&acc)[4][2], const u32x4 (&a)[4
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
-// Gather buffer of round u (three LDS buffers in rotation).  A select between the LDS
-// arrays themselves keeps the accesses in the LDS address space.
-__device__ __forceinline__ uint8_t *gather_buf(int u, uint8_t *g0, uint8_t *g1, uint8_t *g2) {
-    const int b = u % 3;
-    return b == 0 ? g0 : (b == 1 ? g1 : g2);
+// Byte `off` of the gather space, which spans the three free stage buffers in order.  A
+// select between the LDS arrays themselves keeps the accesses in the LDS address space.
+__device__ __forceinline__ uint8_t *gather_at(int off, uint8_t *g0, uint8_t *g1, uint8_t *g2) {
+    const int b = off / STB;
+    return (b == 0 ? g0 : (b == 1 ? g1 : g2)) + (off - b * STB);
 }
 
 // The dA stream of one tile: entries [E0, E0 + n) of the COO list, in rounds of RE entries
@@ -185,7 +186,7 @@ template <int WDT>
 struct Stream {
     static constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
     static constexpr int ROW_BYTES = BN * ESZ;
-    static constexpr int RE = STB / ROW_BYTES;   // 64 (bf16 W) or 32 (fp32 W) entries per round
+    static constexpr int RE = GBYTES / ROW_BYTES;   // 192 (bf16 W) or 96 (fp32 W) entries per round
     static_assert(RE <= RING, "ring slot holds a round");
     __amdgpu_buffer_rsrc_t rsK, rsV, rsR, rsW;   // the tile's columns, values and rows, and W
     int n;                                       // entries of the tile
@@ -195,18 +196,20 @@ struct Stream {
     // columns, wave 1 the values, wave 2 the rows (one 4-byte load per lane; past the
     // tile's entries they read 0).
     __device__ __forceinline__ void issue_pairs(Ring &rg, int u) const {
-        const int o = (u * RE + lane) * 4;
-        if (wave == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, LDS_PTR(&rg.kc[u & 3][0]), 4, o, 0, 0, 0);
-        else if (wave == 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, LDS_PTR(&rg.dv[u & 3][0]), 4, o, 0, 0, 0);
-        else if (wave == 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, LDS_PTR(&rg.kr[u & 3][0]), 4, o, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < (RE + 63) / 64; ++c) {
+            const int o = (u * RE + c * 64 + lane) * 4;
+            if (wave == 0)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, LDS_PTR(&rg.kc[u & 1][c * 64]), 4, o, 0, 0, 0);
+            else if (wave == 1)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, LDS_PTR(&rg.dv[u & 1][c * 64]), 4, o, 0, 0, 0);
+            else if (wave == 2)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsR, LDS_PTR(&rg.kr[u & 1][c * 64]), 4, o, 0, 0, 0);
+        }
     }
     // W[k][n0 .. n0+BN-1] of every entry of round u, back to back into buffer u%3.  A load
     // moves 1 KiB: lane i carries bytes 16i.. of it.  Every wave issues LPR loads.
     __device__ __forceinline__ void issue_gather(const Ring &rg, int u, uint8_t *g0, uint8_t *g1, uint8_t *g2) const {
-        uint8_t *dst = gather_buf(u, g0, g1, g2);
         uint32_t ka[LPR], kv[LPR];
         int el[LPR], col[LPR];
 #pragma unroll
@@ -214,15 +217,24 @@ struct Stream {
             const int byte = (wave * LPR + j) * 1024 + lane * 16;
             el[j] = byte / ROW_BYTES;
             col[j] = n0 + (byte % ROW_BYTES) / ESZ;
-            ka[j] = lds_addr(&rg.kc[u & 3][el[j]]);
+            ka[j] = lds_addr(&rg.kc[u & 1][el[j]]);
         }
-        lds_read4_u32(ka, kv);
+#pragma unroll
+        for (int j = 0; j < LPR; j += 4) {
+            const uint32_t a4[4] = {ka[j], ka[j + 1], ka[j + 2], ka[j + 3]};
+            uint32_t v4[4];
+            lds_read4_u32(a4, v4);
+            kv[j] = v4[0];
+            kv[j + 1] = v4[1];
+            kv[j + 2] = v4[2];
+            kv[j + 3] = v4[3];
+        }
 #pragma unroll
         for (int j = 0; j < LPR; ++j) {
             const int L = wave * LPR + j;
             int o = OOB;
             if (u * RE + el[j] < n && col[j] < N) o = ((int)kv[j] * N + col[j]) * ESZ;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, LDS_PTR(dst + L * 1024), 16, o, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, LDS_PTR(gather_at(L * 1024, g0, g1, g2)), 16, o, 0, 0, 0);
         }
     }
 };
@@ -368,17 +380,10 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
         st.rsR = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p.coo_row + E0), 0, st.n * 4, BUF_FLAGS);
         st.rsW = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p.Wc), 0, K * N * ESZ, BUF_FLAGS);
         if (st.n > 0) {
-            // prime: pairs of rounds 0..2 and the gathers of rounds 0 and 1.  In flight
-            // afterwards: gather 0, pairs 2, gather 1 (the order every later wait assumes).
+            // prime: the entries of round 0 in the ring
             st.issue_pairs(rg, 0);
             WAIT_VMCNT(0);
             lds_barrier();
-            st.issue_pairs(rg, 1);
-            st.issue_gather(rg, 0, sb1, sb2, sb3);
-            WAIT_VMCNT(LPR);
-            lds_barrier();
-            st.issue_pairs(rg, 2);
-            st.issue_gather(rg, 1, sb1, sb2, sb3);
         }
     }
 
@@ -415,15 +420,16 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
 #pragma unroll 1
                     for (int t = e_lo / RE; t <= (e_hi - 1) / RE; ++t) {
                         if (t >= visited) {
-                            // first use of round t: its gather (issued two rounds ago) and the
-                            // pairs of round t+2 are complete once only gather t+1 is in flight
-                            WAIT_VMCNT(LPR);
+                            // first use of round t: every wave is past round t-1, whose gather
+                            // space and ring slot are free; gather round t and copy the entries
+                            // of round t+1, then wait for both
                             lds_barrier();
-                            st.issue_pairs(rg, t + 3);
-                            st.issue_gather(rg, t + 2, sb1, sb2, sb3);
+                            st.issue_gather(rg, t, sb1, sb2, sb3);
+                            st.issue_pairs(rg, t + 1);
+                            WAIT_VMCNT(0);
+                            lds_barrier();
                             visited = t + 1;
                         }
-                        const uint8_t *gb = gather_buf(t, sb1, sb2, sb3);
 
                         // one pass: the round's entries of slab q split into NW contiguous
                         // shares, wave w adding share w over all BN columns (4 per lane).
@@ -435,13 +441,13 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
                         const int pa = a + ((b - a) * wave) / NW, pb = a + ((b - a) * (wave + 1)) / NW;
                         const int rbase = m0 + q * SLAB;
                         // the share's rows and deltas: one LDS read per lane, then broadcast
-                        const int ns = pb - pa;   // at most RE / NW <= 8 entries
+                        const int ns = pb - pa;   // at most RE / NW <= 24 entries
                         int krl = 0;
                         float dvl = 0.0f;
                         {
                             const int ei = pa + min(lane, max(ns - 1, 0));
                             uint32_t kx, dx;
-                            lds_read2_u32(lds_addr(&rg.kr[t & 3][ei]), lds_addr(&rg.dv[t & 3][ei]), kx, dx);
+                            lds_read2_u32(lds_addr(&rg.kr[t & 1][ei]), lds_addr(&rg.dv[t & 1][ei]), kx, dx);
                             krl = ((int)kx - rbase) & (SLAB - 1);
                             dvl = __uint_as_float(dx);
                         }
@@ -466,7 +472,8 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
                             uint32_t wa[4];
 #pragma unroll
                             for (int u = 0; u < 4; ++u)
-                                wa[u] = lds_addr(gb + (pa + min(i0 + u, ns - 1)) * ROW_BYTES + lane * 4 * ESZ);
+                                wa[u] = lds_addr(gather_at((pa + min(i0 + u, ns - 1)) * ROW_BYTES + lane * 4 * ESZ,
+                                                           sb1, sb2, sb3));
                             if constexpr (WDT == DT_BF16) {
                                 u32x2 w2[4];
                                 lds_read4_b64(wa, w2);
