@@ -113,7 +113,7 @@ fp4_status hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_
 fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, double q, uint8_t *ws,
                         const OutlierWs &w, int cus, float *T, int32_t *coo_row, int32_t *coo_col,
                         float *coo_val, int64_t cap, int32_t *row_ptr, int64_t *nnz, uint8_t *Aq,
-                        float *sA, hipStream_t s) {
+                        float *sA, uint32_t *zero2, int64_t n_zero2, hipStream_t s) {
     State *st = reinterpret_cast<State *>(ws + w.state);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + w.hist);
     uint32_t *hist_lo = reinterpret_cast<uint32_t *>(ws + w.hist_lo);
@@ -127,7 +127,8 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     const int dt = dt_of(dtype);
     const int64_t n = M * K;
     const uint64_t k = (uint64_t)std::floor(q * (double)(n - 1));
-    hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(ws + w.state), (int64_t)(w.zero_end - w.state) / 4, s);
+    hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(ws + w.state), (int64_t)(w.zero_end - w.state) / 4, zero2,
+                               n_zero2, s);
     if (e == hipSuccess) e = launch_hist_rowmax(A, dt, M, K, hist, rowmax, cus, s);
     if (e == hipSuccess) e = launch_select(A, dt, n, hist, hist_lo, st, T, k, s);
     const bool codes = Aq != nullptr;
@@ -176,7 +177,7 @@ fp4_status fp4_quantize(const void *X, int32_t x_dtype, int64_t R, int64_t C, in
     if (axis == FP4_PER_ROW)
         return hip_status(launch_quant_rows(X, dt_of(x_dtype), R, C, nullptr, clamp_T, codes, scales, nullptr,
                                             Staging{nullptr, nullptr, 0, 0}, nullptr, false, true, s));
-    return hip_status(launch_quant_cols(X, dt_of(x_dtype), R, C, scales, codes, s));
+    return hip_status(launch_quant_cols(X, dt_of(x_dtype), R, C, scales, codes, false, s));
 }
 
 int64_t fp4_outlier_capacity(int64_t M, int64_t K, double q) {
@@ -208,7 +209,7 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
     // nnz <= cap always (T is the (k+1)-th smallest |a|), so the staging area and the COO
     // positions are bounded by the computed cap, which the workspace was sized for.
     return run_outliers(A, a_dtype, M, K, q, static_cast<uint8_t *>(workspace), w, cus, T, coo_row, coo_col,
-                        coo_val, cap, row_ptr, nnz, nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
+                        coo_val, cap, row_ptr, nnz, nullptr, nullptr, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
 }
 
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
@@ -287,10 +288,11 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
     uint8_t *Wq = ws + l.Wq;
     float *sW = reinterpret_cast<float *>(ws + l.sW);
     const OutlierWs w = outlier_ws(M, K, in_dtype, l.capacity);
+    // the column-maximum keys of W (kept in sW) are zeroed with the outlier scratch
     st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, T, coo_row, coo_col, coo_val, l.capacity,
-                      row_ptr, nnz, Aq, sA, s);
+                      row_ptr, nnz, Aq, sA, reinterpret_cast<uint32_t *>(sW), N, s);
     if (st != FP4_OK) return st;
-    hipError_t e = launch_quant_cols(W, dt_of(in_dtype), K, N, sW, Wq, s);
+    hipError_t e = launch_quant_cols(W, dt_of(in_dtype), K, N, sW, Wq, true, s);
     if (e == hipSuccess)
         e = launch_gemm(Aq, sA, Wq, sW, M, N, K, row_ptr, coo_row, coo_col, coo_val, W, dt_of(in_dtype), Y,
                         dt_of(y_dtype),

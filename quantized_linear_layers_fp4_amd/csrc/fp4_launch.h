@@ -8,7 +8,8 @@
 
 namespace fp4 {
 
-hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s);
+// Zeroes p1[0..n1) and p2[0..n2) in one launch (n2 may be 0).
+hipError_t launch_zero(uint32_t *p1, int64_t n1, uint32_t *p2, int64_t n2, hipStream_t s);
 hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist,
                               uint32_t *rowmax_key, int num_cus, hipStream_t s);
 hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint32_t *ghist_lo,
@@ -19,8 +20,9 @@ hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const 
 hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
                       const State *st, int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val,
                       hipStream_t s);
+// keys_zeroed: the column-maximum keys (in the scales buffer) were zeroed by an earlier launch.
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
-                             uint8_t *codes, hipStream_t s);
+                             uint8_t *codes, bool keys_zeroed, hipStream_t s);
 
 // FP4 GEMM + dequantization + compensation.  comp arrays NULL = no compensation term.
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,

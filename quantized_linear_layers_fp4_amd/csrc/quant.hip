@@ -12,9 +12,13 @@
 namespace fp4 {
 
 // ----------------------------------------------------------------------------- zero fill
-__global__ void k_zero_u32(uint32_t *__restrict__ p, int64_t n) {
-    int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+// Zeroes p1[0..n1) and p2[0..n2) (n2 may be 0) in one launch.
+__global__ void k_zero_u32(uint32_t *__restrict__ p1, int64_t n1, uint32_t *__restrict__ p2, int64_t n2) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n1 + n2; i += stride) {
+        if (i < n1) p1[i] = 0u;
+        else p2[i - n1] = 0u;
+    }
 }
 
 // ----------------------------------------------------------------------------- histogram
@@ -33,25 +37,42 @@ __global__ __launch_bounds__(1024) void k_hist_rowmax(const void *__restrict__ A
     const int64_t r0 = blockIdx.x * rows_per;
     const int64_t r1 = min(M, r0 + rows_per);
     const int64_t nchunk = K / 8;  // 8 elements per chunk
+    constexpr int U = (DT == DT_BF16) ? 8 : 4;     // chunks per lane per memory round trip
+    constexpr int WPC = (DT == DT_BF16) ? 1 : 2;   // 16-byte words per chunk of 8 elements
     for (int64_t row = r0 + wave; row < r1; row += 16) {
         const int64_t base = row * K;
         uint32_t mx = 0;
-        for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * 4) {
-            float v[4][8];
-            uint32_t key[4][8], sg[4][8];
+        for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * U) {
+            uint4 raw[U][WPC];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                int64_t c = c0 + u * 64 + lane;
-                if (c < nchunk) load8<DT>(A, base + c * 8, v[u], key[u], sg[u]);
+            for (int u = 0; u < U; ++u) {
+                const int64_t c = c0 + u * 64 + lane;
+                if (c < nchunk) {
+                    const uint4 *src = reinterpret_cast<const uint4 *>(
+                        reinterpret_cast<const uint8_t *>(A) + (base + c * 8) * (DT == DT_BF16 ? 2 : 4));
+#pragma unroll
+                    for (int w = 0; w < WPC; ++w) raw[u][w] = src[w];
+                }
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                int64_t c = c0 + u * 64 + lane;
-                if (c < nchunk) {
+            for (int u = 0; u < U; ++u) {
+                if (c0 + u * 64 + lane < nchunk) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        atomicAdd(&h[key[u][e] >> 16], 1u);
-                        mx = max(mx, key[u][e]);
+                    for (int w = 0; w < WPC; ++w) {
+                        const uint32_t wd[4] = {raw[u][w].x, raw[u][w].y, raw[u][w].z, raw[u][w].w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (DT == DT_BF16) {
+                                const uint32_t k0 = key_of_bf16(wd[i] & 0xFFFFu), k1 = key_of_bf16(wd[i] >> 16);
+                                atomicAdd(&h[k0 >> 16], 1u);
+                                atomicAdd(&h[k1 >> 16], 1u);
+                                mx = max(mx, max(k0, k1));
+                            } else {
+                                const uint32_t k0 = key_of_f32(wd[i]);
+                                atomicAdd(&h[k0 >> 16], 1u);
+                                mx = max(mx, k0);
+                            }
+                        }
                     }
                 }
             }
@@ -87,20 +108,27 @@ __global__ __launch_bounds__(1024) void k_select(const uint32_t *__restrict__ hi
                                                  int level, int final_level, float *__restrict__ T_out,
                                                  uint64_t k_level1) {
     constexpr int PER = NB / 1024;
-    __shared__ uint64_t part[1024];
-    const int tid = threadIdx.x;
-    uint64_t local = 0;
-    for (int i = 0; i < PER; ++i) local += hist[tid * PER + i];
-    part[tid] = local;
-    __syncthreads();
-    // inclusive Hillis-Steele scan over 1024 partial sums
-    for (int off = 1; off < 1024; off <<= 1) {
-        uint64_t x = (tid >= off) ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += x;
-        __syncthreads();
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t total_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // every count and partial sum is at most M*K < 2^32
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(hist + tid * PER + i);
+        local += q.x + q.y + q.z + q.w;
     }
-    const uint64_t incl = part[tid], excl = incl - local, total = part[1023];
+    const uint32_t wincl = wave_incl_scan(local, lane);
+    if (lane == 63) wsum[wave] = wincl;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t x = lane < 16 ? wsum[lane] : 0u;
+        const uint32_t xi = wave_incl_scan(x, lane);
+        if (lane < 16) wsum[lane] = xi - x;  // exclusive prefix of the waves
+        if (lane == 15) total_s = xi;
+    }
+    __syncthreads();
+    const uint64_t incl = (uint64_t)wsum[wave] + wincl, excl = incl - local, total = total_s;
     const uint64_t k = (level == 1) ? k_level1 : st->k_rem;
     if (excl <= k && k < incl) {
         uint64_t cum = excl;
@@ -174,55 +202,96 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, 
         if (lane == 0) scales[row] = s;
     }
     uint32_t running = 0;  // outliers of this row emitted so far
-    for (int64_t c0 = 0; c0 < nchunk; c0 += 64) {
-        const int64_t c = c0 + lane;
-        const bool valid = c < nchunk;
-        float v[8];
-        uint32_t key[8], sg[8];
-        if (valid) load8<DT>(X, base + c * 8, v, key, sg);
-        uint32_t omask = 0;
-        float y[8];
+    // U chunks of 8 elements per lane are loaded before any is processed, so a row of
+    // 64*8*U elements costs one memory round trip.  Chunks are processed in ascending
+    // column order (the staging order of dA).
+    constexpr int U = (DT == DT_BF16) ? 8 : 4;
+    constexpr int WPC = (DT == DT_BF16) ? 1 : 2;  // 16-byte words per chunk
+    for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * U) {
+        uint4 raw[U][WPC];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bool out = valid && key[e] > tkey;
-            omask |= (uint32_t)out << e;
-            const float ac = out ? __uint_as_float(sg[e] | tkey) : v[e];
-            y[e] = ac * r;
-        }
-        if constexpr (CODES) {
-            if (valid) *reinterpret_cast<uint32_t *>(codes + row * (C / 2) + c * 4) = e2m1_pack8(y);
-        }
-        if constexpr (EMIT) {
-            const uint32_t cnt = __popc(omask);
-            if (__ballot(cnt != 0)) {
-                const uint32_t incl = wave_incl_scan(cnt, lane);
-                const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-                uint32_t rank = running + incl - cnt;
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + u * 64 + lane;
+            if (c < nchunk) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(
+                    reinterpret_cast<const uint8_t *>(X) + (base + c * 8) * (DT == DT_BF16 ? 2 : 4));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (omask & (1u << e)) {
-                        const int32_t col = (int32_t)(c * 8 + e);
-                        const float val = v[e] - __uint_as_float(sg[e] | tkey);
-                        if (rank < (uint32_t)stg.S) {
-                            SlotEntry se;
-                            se.col = col;
-                            se.val = val;
-                            stg.slots[row * stg.S + rank] = se;
-                        } else {
-                            const unsigned long long i = atomicAdd(&st->over_count, 1ull);
-                            if (i < (unsigned long long)stg.over_cap) {
-                                OverEntry oe;
-                                oe.row = (int32_t)row;
-                                oe.rank = (int32_t)rank;
-                                oe.col = col;
-                                oe.val = val;
-                                stg.over[i] = oe;
-                            }
-                        }
-                        ++rank;
-                    }
+                for (int w = 0; w < WPC; ++w) raw[u][w] = src[w];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = c0 + u * 64 + lane;
+            if (c0 + u * 64 >= nchunk) break;  // wave-uniform: no lane has chunk u
+            const bool valid = c < nchunk;
+            float v[8];
+            uint32_t key[8], sg[8];
+            if constexpr (DT == DT_BF16) {
+                const uint32_t wd[4] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = wd[i] & 0xFFFFu, hi = wd[i] >> 16;
+                    v[2 * i] = bf16_to_f32(lo);
+                    v[2 * i + 1] = bf16_to_f32(hi);
+                    key[2 * i] = key_of_bf16(lo);
+                    key[2 * i + 1] = key_of_bf16(hi);
+                    sg[2 * i] = (lo << 16) & 0x80000000u;
+                    sg[2 * i + 1] = (hi << 16) & 0x80000000u;
                 }
-                running += total;
+            } else {
+                const uint32_t wd[8] = {raw[u][0].x, raw[u][0].y, raw[u][0].z, raw[u][0].w,
+                                        raw[u][1].x, raw[u][1].y, raw[u][1].z, raw[u][1].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    v[i] = __uint_as_float(wd[i]);
+                    key[i] = key_of_f32(wd[i]);
+                    sg[i] = wd[i] & 0x80000000u;
+                }
+            }
+            uint32_t omask = 0;
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool out = valid && key[e] > tkey;
+                omask |= (uint32_t)out << e;
+                const float ac = out ? __uint_as_float(sg[e] | tkey) : v[e];
+                y[e] = ac * r;
+            }
+            if constexpr (CODES) {
+                if (valid) *reinterpret_cast<uint32_t *>(codes + row * (C / 2) + c * 4) = e2m1_pack8(y);
+            }
+            if constexpr (EMIT) {
+                const uint32_t cnt = __popc(omask);
+                if (__ballot(cnt != 0)) {
+                    const uint32_t incl = wave_incl_scan(cnt, lane);
+                    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+                    uint32_t rank = running + incl - cnt;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (omask & (1u << e)) {
+                            const int32_t col = (int32_t)(c * 8 + e);
+                            const float val = v[e] - __uint_as_float(sg[e] | tkey);
+                            if (rank < (uint32_t)stg.S) {
+                                SlotEntry se;
+                                se.col = col;
+                                se.val = val;
+                                stg.slots[row * stg.S + rank] = se;
+                            } else {
+                                const unsigned long long i = atomicAdd(&st->over_count, 1ull);
+                                if (i < (unsigned long long)stg.over_cap) {
+                                    OverEntry oe;
+                                    oe.row = (int32_t)row;
+                                    oe.rank = (int32_t)rank;
+                                    oe.col = col;
+                                    oe.val = val;
+                                    stg.over[i] = oe;
+                                }
+                            }
+                            ++rank;
+                        }
+                    }
+                    running += total;
+                }
             }
         }
     }
@@ -245,11 +314,22 @@ __global__ __launch_bounds__(1024) void k_coo_scan(const int32_t *__restrict__ r
     for (int64_t b0 = 0; b0 < M; b0 += 1024 * ITEMS) {
         uint32_t c[ITEMS], local = 0;
         const int64_t r0 = b0 + (int64_t)tid * ITEMS;
+        if (r0 + ITEMS <= M) {
+            // row_cnt is 16-byte aligned and r0 a multiple of 16: four 16-byte loads
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            c[i] = (r0 + i < M) ? (uint32_t)row_cnt[r0 + i] : 0u;
-            local += c[i];
+            for (int i = 0; i < ITEMS; i += 4) {
+                const int4 q = *reinterpret_cast<const int4 *>(row_cnt + r0 + i);
+                c[i] = (uint32_t)q.x;
+                c[i + 1] = (uint32_t)q.y;
+                c[i + 2] = (uint32_t)q.z;
+                c[i + 3] = (uint32_t)q.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) c[i] = (r0 + i < M) ? (uint32_t)row_cnt[r0 + i] : 0u;
         }
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) local += c[i];
         const uint32_t incl = wave_incl_scan(local, lane);
         if (lane == 63) wsum[wave] = incl;
         __syncthreads();
@@ -261,10 +341,20 @@ __global__ __launch_bounds__(1024) void k_coo_scan(const int32_t *__restrict__ r
         }
         __syncthreads();
         uint32_t run = carry + wsum[wave] + incl - local;
+        int32_t out[ITEMS];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            if (r0 + i < M) row_ptr[r0 + i] = (int32_t)run;
+            out[i] = (int32_t)run;
             run += c[i];
+        }
+        if (r0 + ITEMS <= M) {
+#pragma unroll
+            for (int i = 0; i < ITEMS; i += 4)
+                *reinterpret_cast<int4 *>(row_ptr + r0 + i) = make_int4(out[i], out[i + 1], out[i + 2], out[i + 3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i)
+                if (r0 + i < M) row_ptr[r0 + i] = out[i];
         }
         carry += carry_s;
         __syncthreads();
@@ -434,9 +524,9 @@ static inline int blocks_for(int64_t n, int threads, int cap) {
     return (int)(b < 1 ? 1 : b);
 }
 
-hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_zero_u32, dim3(blocks_for(n, 256, 1024)), dim3(256), 0, s, p, n);
+hipError_t launch_zero(uint32_t *p1, int64_t n1, uint32_t *p2, int64_t n2, hipStream_t s) {
+    if (n1 + n2 <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_u32, dim3(blocks_for(n1 + n2, 256, 1024)), dim3(256), 0, s, p1, n1, p2, n2);
     return hipGetLastError();
 }
 
@@ -497,10 +587,12 @@ hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64
 }
 
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
-                             uint8_t *codes, hipStream_t s) {
+                             uint8_t *codes, bool keys_zeroed, hipStream_t s) {
     uint32_t *keys = reinterpret_cast<uint32_t *>(scales_as_keys);
-    hipError_t e = launch_zero(keys, N, s);
-    if (e != hipSuccess) return e;
+    if (!keys_zeroed) {
+        hipError_t e = launch_zero(keys, N, nullptr, 0, s);
+        if (e != hipSuccess) return e;
+    }
     const int rows_per_block = 256;
     dim3 g1((unsigned)((N + 511) / 512), (unsigned)((K + rows_per_block - 1) / rows_per_block));
     dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
