@@ -119,6 +119,43 @@ def _cpu_model() -> str:
     return platform.processor()
 
 
+def _counter_per_dispatch(d: str, counter: str, kernel_pred) -> float:
+    """Mean over dispatches of one counter for the kernels kernel_pred accepts, from a
+    rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_pred(r["Kernel_Name"]):
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows in {d}")
+    return sum(vals) / len(vals)
+
+
+def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write: str):
+    """HBM bytes per k_fp4_gemm launch on the 7B gate+up shape: FETCH_SIZE and WRITE_SIZE
+    per dispatch, each scaled by the bytes a plain 1 GiB copy moves per unit of the same
+    counter.  Written with the hash of the GEMM source it was measured on."""
+    is_gemm = lambda n: "k_fp4_gemm" in n  # noqa: E731
+    is_copy = lambda n: "copyBuffer" in n  # noqa: E731
+    g_f = _counter_per_dispatch(gemm_fetch, "FETCH_SIZE", is_gemm)
+    g_w = _counter_per_dispatch(gemm_write, "WRITE_SIZE", is_gemm)
+    c_f = _counter_per_dispatch(copy_fetch, "FETCH_SIZE", is_copy)
+    c_w = _counter_per_dispatch(copy_write, "WRITE_SIZE", is_copy)
+    f_fetch, f_write = (1 << 30) / c_f, (1 << 30) / c_w
+    rec = {"gemm_src_sha": gemm_src_sha(), "workload": "llama7b_gate_up",
+           "fetch_size_per_launch": g_f, "write_size_per_launch": g_w,
+           "copy_fetch_size": c_f, "copy_write_size": c_w,
+           "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write,
+           "hbm_read_bytes_per_launch": g_f * f_fetch, "hbm_write_bytes_per_launch": g_w * f_write,
+           "hbm_bytes_per_launch": round(g_f * f_fetch + g_w * f_write)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 def run_copy(steps: int):
     """Plain 1 GiB device copy: the calibration kernel for the HBM byte counters."""
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -134,11 +171,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward"])
+    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic"])
+    ap.add_argument("--traffic-dirs", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="--mode traffic: rocprofv3 --pmc output directories of FETCH_SIZE and WRITE_SIZE for "
+                         "the full bench and for --mode copy")
     args = ap.parse_args()
+    if args.mode == "traffic":
+        write_traffic(*args.traffic_dirs)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
-              "forward is described in DESIGN.md but not run.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this forward is built and "
+              "measured on a single GPU; sharding it over several is a design note, not a run.", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.mode == "copy":
