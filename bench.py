@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
 
 A step is one fp4_linear_forward (quantile + clamp + dA, token-wise quantization of A,
-channel-wise quantization of W, FP4 GEMM with dequantization and compensation) over one
+channel-wise quantization of W, FP4 GEMM with dequantization, compensation pass) over one
 batch of seeded synthetic input already resident in HBM.  Default workload: the
 LLaMA-7B FFN gate+up projection (M=16384 tokens, K=4096, N=22016, bf16 in and out,
 clamp quantile 0.999).  Prints one JSON line.
@@ -45,6 +45,13 @@ def quantizer_bytes(M, K, N, bi, nnz) -> int:
     a = 2 * M * K * bi + M * K // 2 + 4 * M + 12 * nnz + 4 * (M + 1)
     w = K * N * bi + K * N // 2 + 4 * N
     return a + w
+
+
+def comp_bytes(M, N, b_out, nnz) -> int:
+    """Algorithmic HBM bytes of the compensation pass: Y_main (fp32) read and Y written,
+    plus the dA list; the W rows it gathers are counted as L2 traffic, not HBM (each row is
+    reused by every entry of its column)."""
+    return M * N * 4 + M * N * b_out + 8 * nnz + 4 * (M + 1)
 
 
 def time_on_stream(fn, steps: int, warmup: int) -> float:
@@ -221,26 +228,38 @@ def main():
         print(json.dumps({"ms_per_step": ms_step}))
         return
 
-    # the dominant kernel (the GEMM) alone, same arguments as inside the forward
-    gemm_ms, qbytes, nnz_total = 0.0, 0, 0
+    # The dominant kernel (the GEMM) alone, as the forward launches it: fp32 Y_main into the
+    # workspace (into Y itself for an fp32 Y).  Then GEMM + compensation pass together, the
+    # pass's time being the difference.
+    gemm_ms, comp_ms, qbytes, cbytes, nnz_total = 0.0, 0.0, 0, 0, 0
     per_layer = []
     for A, W, L, Ad, Wd, ws, Y in runs:
         it = fp4.forward_intermediates(ws, L.M, L.K, L.N, A.dtype, L.q)
+        lay = fp4.forward_layout(L.M, L.K, L.N, A.dtype, L.q)
         nnz = int(it["nnz"].item())
+        ymain = Y if Y.dtype == torch.float32 else ws[lay.ymain:]
+        wsb = ymain.numel() * ymain.element_size()
+        common = (fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K)
         g = lambda: fp4.lib().fp4_gemm(  # noqa: E731
-            fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K,
-            fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_row"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]),
-            fp4._ptr(Wd), fp4._dt(Wd),
-            fp4._ptr(Y), fp4._dt(Y), None, fp4._stream(Ad))
+            *common, None, None, None, None, fp4._dt(Wd), fp4._ptr(ymain), fp4.FP4_F32, None, None, 0,
+            fp4._stream(Ad))
+        gc = lambda: fp4.lib().fp4_gemm(  # noqa: E731
+            *common, fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]), fp4._ptr(Wd),
+            fp4._dt(Wd), fp4._ptr(Y), fp4._dt(Y), None, fp4._ptr(ymain), wsb, fp4._stream(Ad))
         ms_g = time_on_stream(g, args.steps, 2)
+        ms_c = max(time_on_stream(gc, args.steps, 2) - ms_g, 1e-9)
         gemm_ms += ms_g
+        comp_ms += ms_c
         qb = quantizer_bytes(L.M, L.K, L.N, b_in(A.dtype), nnz)
+        cb = comp_bytes(L.M, L.N, Y.element_size(), nnz)
         qbytes += qb
+        cbytes += cb
         nnz_total += nnz
         per_layer.append({"layer": L.name, "M": L.M, "K": L.K, "N": L.N, "q": L.q, "nnz": nnz,
-                          "gemm_ms": round(ms_g, 4), "gemm_TFLOP/s": round(L.flops / ms_g / 1e9, 1)})
+                          "gemm_ms": round(ms_g, 4), "gemm_TFLOP/s": round(L.flops / ms_g / 1e9, 1),
+                          "comp_ms": round(ms_c, 4), "comp_GB/s": round(cb / ms_c / 1e6, 1)})
 
-    quant_ms = max(ms_step - gemm_ms, 1e-9)
+    quant_ms = max(ms_step - gemm_ms - comp_ms, 1e-9)
     gemm_tflops = flops / gemm_ms / 1e9
     fwd_tflops = flops / ms_step / 1e9
     quant_gbs = qbytes / quant_ms / 1e6
@@ -266,6 +285,9 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k_fp4_gemm", "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(gemm_ms, 4)},
+        "compensation": {"bound": "hbm", "kernel": "k_comp_apply", "achieved": round(cbytes / comp_ms / 1e6, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(cbytes / comp_ms / 1e6 / PEAK_HBM_GBS, 4),
+                         "ms": round(comp_ms, 4), "algorithmic_bytes": cbytes},
         "quantizer": {"bound": "hbm", "achieved": round(quant_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(quant_gbs / PEAK_HBM_GBS, 4), "ms": round(quant_ms, 4),
                       "algorithmic_bytes": qbytes},

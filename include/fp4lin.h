@@ -120,21 +120,30 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
                              int64_t capacity, int32_t *row_ptr, int64_t *nnz, void *workspace,
                              size_t ws_bytes, void *stream);
 
-/* The FP4 GEMM with dequantization and the sparse compensation fused into its output
- * (QbitAI report, GEMM-kernel paragraph: the product of the two FP4 operands, here on
- * CDNA4 FP4 matrix cores with fp32 accumulation; granularity paragraph: sA and sW factor
- * out of the K-sum).
+/* Host-only: workspace bytes fp4_gemm needs: M * N * 4 (an fp32 copy of Y_main) when it
+ * adds the compensation term into a bf16 Y, else 0 (also 0 for invalid arguments). */
+size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t with_comp);
+
+/* The FP4 GEMM with dequantization, plus the sparse compensation term (QbitAI report,
+ * GEMM-kernel paragraph: the product of the two FP4 operands, here on CDNA4 FP4 matrix
+ * cores with fp32 accumulation; granularity paragraph: sA and sW factor out of the K-sum;
+ * outlier paragraph: the product of dA with the weights is added back).
  *   Aq M x K/2, sA fp32[M], Wq N x K/2, sW fp32[N] (as produced by fp4_quantize)
- *   row_ptr, coo_row, coo_col, coo_val: dA as produced by fp4_outlier_clamp (CSR row
- *            offsets plus the COO list sorted by (row, col)), or all four NULL for no
+ *   row_ptr, coo_col, coo_val: dA as produced by fp4_outlier_clamp (CSR row offsets and
+ *            the column/value lists sorted by (row, col)), or all three NULL for no
  *            compensation term; W (K x N, w_dtype) is then unused and may be NULL.
  *   Y        M x N of y_dtype (out)
  *   acc_out  NULL, or device fp32[M*N] receiving the raw accumulator acc (a check aid).
- * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,ALIGN,DEVICE,HIP}. */
+ *   workspace, ws_bytes: device scratch of at least fp4_gemm_workspace_bytes() bytes
+ *            (may be NULL when that is 0).  Y_main is written there in fp32 and the
+ *            compensation pass reads it back; with an fp32 Y it works in place in Y.
+ * Two kernels run on the stream: the GEMM, then (with dA) the compensation pass.
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW,
-                    int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_row,
+                    int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
                     const int32_t *coo_col, const float *coo_val, const void *W, int32_t w_dtype,
-                    void *Y, int32_t y_dtype, float *acc_out, void *stream);
+                    void *Y, int32_t y_dtype, float *acc_out, void *workspace, size_t ws_bytes,
+                    void *stream);
 
 /* Byte offsets of the intermediates inside the fp4_linear_forward workspace, so a caller
  * can read T, the COO list, the codes and the scales after a forward. */
@@ -145,6 +154,7 @@ struct fp4_ws_layout {
     size_t row_ptr;               /* int32[M+1] */
     size_t coo_row, coo_col, coo_val; /* capacity entries each */
     size_t Aq, sA, Wq, sW;        /* codes and scales */
+    size_t ymain;                 /* fp32[M*N]: Y_main before the compensation pass */
     size_t scratch;               /* internal */
     int64_t capacity;             /* fp4_outlier_capacity(M, K, q) */
 };

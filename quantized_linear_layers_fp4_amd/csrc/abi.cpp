@@ -212,23 +212,38 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
                         coo_val, cap, row_ptr, nnz, nullptr, nullptr, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
 }
 
+size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t with_comp) {
+    if (M < 1 || !n_ok(N) || !dtype_ok(y_dtype)) return 0;
+    return (with_comp && y_dtype == FP4_BF16) ? (size_t)M * (size_t)N * 4 : 0;
+}
+
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
-                    int64_t K, const int32_t *row_ptr, const int32_t *coo_row, const int32_t *coo_col,
-                    const float *coo_val, const void *W,
-                    int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *stream) {
+                    int64_t K, const int32_t *row_ptr, const int32_t *coo_col, const float *coo_val, const void *W,
+                    int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *workspace, size_t ws_bytes,
+                    void *stream) {
     if (!Aq || !sA || !Wq || !sW || !Y) return FP4_ERR_NULL;
-    const int ncomp = (row_ptr != nullptr) + (coo_row != nullptr) + (coo_col != nullptr) + (coo_val != nullptr);
-    if (ncomp != 0 && ncomp != 4) return FP4_ERR_NULL;
-    if (ncomp == 4 && !W) return FP4_ERR_NULL;
-    if (!dtype_ok(y_dtype) || (ncomp == 4 && !dtype_ok(w_dtype))) return FP4_ERR_DTYPE;
-    if (!gemm_ok(M, N, K) || (ncomp == 4 && !wcomp_ok(N, K, w_dtype))) return FP4_ERR_SHAPE;
-    if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(Y) || (W && !aligned16(W)) || (acc_out && !aligned16(acc_out)))
+    const int ncomp = (row_ptr != nullptr) + (coo_col != nullptr) + (coo_val != nullptr);
+    if (ncomp != 0 && ncomp != 3) return FP4_ERR_NULL;
+    const bool comp = ncomp == 3;
+    if (comp && !W) return FP4_ERR_NULL;
+    if (!dtype_ok(y_dtype) || (comp && !dtype_ok(w_dtype))) return FP4_ERR_DTYPE;
+    if (!gemm_ok(M, N, K) || (comp && !wcomp_ok(N, K, w_dtype))) return FP4_ERR_SHAPE;
+    const bool staged = comp && y_dtype == FP4_BF16;  // Y_main goes through the workspace
+    if (staged && !workspace) return FP4_ERR_NULL;
+    if (staged && ws_bytes < (size_t)M * (size_t)N * 4) return FP4_ERR_WORKSPACE;
+    if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(Y) || (comp && !aligned16(W)) ||
+        (acc_out && !aligned16(acc_out)) || (staged && !aligned16(workspace)))
         return FP4_ERR_ALIGN;
     int cus;
     fp4_status st = device_check(&cus);
     if (st != FP4_OK) return st;
-    return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, ncomp ? row_ptr : nullptr, coo_row, coo_col, coo_val, W,
-                                  dt_of(w_dtype), Y, dt_of(y_dtype), acc_out, reinterpret_cast<hipStream_t>(stream)));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!comp) return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, Y, dt_of(y_dtype), acc_out, s));
+    float *ymain = staged ? static_cast<float *>(workspace) : static_cast<float *>(Y);
+    hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, acc_out, s);
+    if (e == hipSuccess)
+        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype), s);
+    return hip_status(e);
 }
 
 fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q,
@@ -252,6 +267,7 @@ fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype,
     out->sA = off; off += align_up((size_t)M * 4);
     out->Wq = off; off += align_up((size_t)N * (size_t)(K / 2));
     out->sW = off; off += align_up((size_t)N * 4);
+    out->ymain = off; off += align_up((size_t)M * (size_t)N * 4);
     out->scratch = off; off += outlier_ws(M, K, in_dtype, cap).total;
     out->total = off;
     out->capacity = cap;
@@ -293,10 +309,11 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
                       row_ptr, nnz, Aq, sA, reinterpret_cast<uint32_t *>(sW), N, s);
     if (st != FP4_OK) return st;
     hipError_t e = launch_quant_cols(W, dt_of(in_dtype), K, N, sW, Wq, true, s);
+    // Y_main in fp32 (straight into Y when Y is fp32), then Y = Y_main + dA . W
+    float *ymain = y_dtype == FP4_F32 ? static_cast<float *>(Y) : reinterpret_cast<float *>(ws + l.ymain);
+    if (e == hipSuccess) e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, nullptr, s);
     if (e == hipSuccess)
-        e = launch_gemm(Aq, sA, Wq, sW, M, N, K, row_ptr, coo_row, coo_col, coo_val, W, dt_of(in_dtype), Y,
-                        dt_of(y_dtype),
-                        nullptr, s);
+        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype), s);
     return hip_status(e);
 }
 

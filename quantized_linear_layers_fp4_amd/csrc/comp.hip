@@ -1,0 +1,160 @@
+// gfx950 kernel of the sparse compensation term dA . W of the FP4 linear forward (outlier
+// paragraph of the QbitAI report on "Optimizing Large Language Model Training Using FP4
+// Quantization": the entries clamped away from A are kept as a sparse matrix and their
+// product with the weights is added back).  It runs after the FP4 GEMM has written the
+// dequantized product Y_main in fp32, and writes Y = Y_main + dA . W in the output type,
+// rounded once.
+//
+// One wave per (row, 512-column chunk) task; lane l owns the eight columns 8l..8l+7 of the
+// chunk.  The wave first issues its Y_main loads and the row's two CSR offsets together,
+// then takes the row's dA entries (ascending column k) 64 at a time, one (k, delta) pair
+// per lane, and walks them in groups of eight: the eight W row segments are loaded
+// together and added to the eight running sums in ascending k (one fp32 fma each).
+//
+// Task order: the tasks are dealt out to the eight XCDs in contiguous ranges (consecutive
+// workgroup ids go to different XCDs), chunk-major within a range, so each XCD streams all
+// rows over one chunk at a time and the W rows that chunk gathers stay in that XCD's L2.
+// Y_main and Y are streamed with non-temporal hints so they do not evict those rows.
+// Nothing here needs N * 4 or K * N * sizeof(W) beyond 2^31 - 1 bytes per descriptor:
+// Y_main is addressed per row.
+#include "fp4_common.h"
+#include "fp4_launch.h"
+
+namespace fp4 {
+
+constexpr int CCOLS = 8;             // columns per lane
+constexpr int CCHUNK = 64 * CCOLS;   // columns per task
+constexpr int CB = 8;                // W row segments in flight per lane
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// INPLACE: Y is the fp32 Y_main buffer itself; a row without entries is then left alone.
+template <int YDT, int WDT, bool INPLACE>
+__global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y, int M, int N, int K,
+                                                    int chunks, int per_xcd,
+                                                    const int32_t *__restrict__ row_ptr,
+                                                    const int32_t *__restrict__ coo_col,
+                                                    const float *__restrict__ coo_val, const void *__restrict__ W) {
+    const int lane = threadIdx.x & 63;
+    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    const int64_t task = (int64_t)logical * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (task >= (int64_t)chunks * M) return;  // whole wave
+    const int chunk = (int)(task / M);
+    const int row = (int)(task - (int64_t)chunk * M);
+    const int col = chunk * CCHUNK + lane * CCOLS;
+    const bool active = col < N;  // N % 8 == 0: a lane's eight columns are in range together
+    const size_t yoff = (size_t)row * N + col;
+
+    // The row's CSR offsets (lane l loads row_ptr[row + (l & 1)]) and the lane's Y_main
+    // segment, issued together and unconditionally; Y_main goes through a descriptor over
+    // the row, so a lane past N reads zeros.
+    const int32_t rp = row_ptr[row + (lane & 1)];
+    const __amdgpu_buffer_rsrc_t rsY =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(Ymain) + (size_t)row * N, 0, N * 4, 0x00020000);
+    v4i y0 = {0, 0, 0, 0}, y1 = y0;
+    if constexpr (!INPLACE) {
+        y0 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4, 0, 2);
+        y1 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4 + 16, 0, 2);
+    }
+    const int32_t e0 = __builtin_amdgcn_readlane(rp, 0);
+    const int32_t e1 = __builtin_amdgcn_readlane(rp, 1);
+    if constexpr (INPLACE) {
+        if (e0 == e1) return;
+        y0 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4, 0, 2);
+        y1 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4 + 16, 0, 2);
+    }
+    float y[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        y[c] = __int_as_float(y0[c]);
+        y[4 + c] = __int_as_float(y1[c]);
+    }
+
+    // W through a buffer descriptor.  Offsets are unsigned 32-bit: K*N*ESZ < 2^31, so the
+    // largest (a lane past N on the last row of W) stays below 2^32 and reads zeros; such a
+    // lane is never stored.
+    constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
+    constexpr int NH = CCOLS * ESZ / 16;  // 16-byte loads per segment
+    const __amdgpu_buffer_rsrc_t rsW =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(W), 0, (int)((int64_t)K * N * ESZ), 0x00020000);
+    const uint32_t row_bytes = (uint32_t)N * ESZ;
+    const uint32_t lane_off = (uint32_t)col * ESZ;
+    for (int32_t e = e0; e < e1; e += 64) {
+        int32_t kk = 0;
+        float dd = 0.0f;
+        if (e + lane < e1) {
+            kk = coo_col[e + lane];
+            dd = coo_val[e + lane];
+        }
+        const int nb = min(64, e1 - e);  // wave-uniform
+        for (int s = 0; s < nb; s += CB) {
+            v4i w[CB][NH];
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                const uint32_t k = (uint32_t)__builtin_amdgcn_readlane(kk, s + u);
+                const uint32_t off = k * row_bytes + lane_off;
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    w[u][h] = (s + u < nb) ? __builtin_amdgcn_raw_buffer_load_b128(rsW, (int)(off + 16 * h), 0, 0)
+                                           : v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                if (s + u < nb) {  // wave-uniform
+                    const float d = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int32_t, dd), s + u));
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        float wv;
+                        if constexpr (WDT == DT_BF16) {
+                            const uint32_t pr = (uint32_t)w[u][0][c >> 1];
+                            wv = bf16_to_f32((c & 1) ? (pr >> 16) : (pr & 0xFFFFu));
+                        } else {
+                            wv = __int_as_float(w[u][c >> 2][c & 3]);
+                        }
+                        y[c] = __builtin_fmaf(d, wv, y[c]);
+                    }
+                }
+            }
+        }
+    }
+    if (!active) return;
+    if constexpr (YDT == DT_BF16) {
+        v4i o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = (int)(f32_to_bf16_bits(y[2 * i]) | (f32_to_bf16_bits(y[2 * i + 1]) << 16));
+        __builtin_nontemporal_store(o, reinterpret_cast<v4i *>(reinterpret_cast<uint16_t *>(Y) + yoff));
+    } else {
+        f4 *yp = reinterpret_cast<f4 *>(reinterpret_cast<float *>(Y) + yoff);
+        __builtin_nontemporal_store(f4{y[0], y[1], y[2], y[3]}, yp);
+        __builtin_nontemporal_store(f4{y[4], y[5], y[6], y[7]}, yp + 1);
+    }
+}
+
+hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
+                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, hipStream_t s) {
+    const int chunks = (int)((N + CCHUNK - 1) / CCHUNK);
+    const int64_t tasks = (int64_t)chunks * M;
+    const int64_t blocks = (tasks + 3) / 4;
+    const int per_xcd = (int)((blocks + 7) / 8);
+    const dim3 grid((unsigned)per_xcd * 8u), block(256);
+    const bool inplace = static_cast<const void *>(Ymain) == Y;
+#define C(YD, WD, IP)                                                                                            \
+    hipLaunchKernelGGL((k_comp_apply<YD, WD, IP>), grid, block, 0, s, Ymain, Y, (int)M, (int)N, (int)K, chunks, \
+                       per_xcd, row_ptr, coo_col, coo_val, W)
+    if (y_dt == DT_BF16) {
+        if (w_dt == DT_BF16) C(DT_BF16, DT_BF16, false);
+        else C(DT_BF16, DT_F32, false);
+    } else if (inplace) {
+        if (w_dt == DT_BF16) C(DT_F32, DT_BF16, true);
+        else C(DT_F32, DT_F32, true);
+    } else {
+        if (w_dt == DT_BF16) C(DT_F32, DT_BF16, false);
+        else C(DT_F32, DT_F32, false);
+    }
+#undef C
+    return hipGetLastError();
+}
+
+}  // namespace fp4

@@ -24,10 +24,12 @@ hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
                              uint8_t *codes, bool keys_zeroed, hipStream_t s);
 
-// FP4 GEMM + dequantization + compensation.  comp arrays NULL = no compensation term.
+// FP4 GEMM + dequantization: Y = fl(fl(acc * sA) * sW) in y_dt.  acc_out: NULL or fp32[M*N].
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_row, const int32_t *coo_col,
-                       const float *coo_val, const void *W, int w_dt, void *Y, int y_dt, float *acc_out,
-                       hipStream_t s);
+                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s);
+// Y = Y_main + dA . W, accumulated in fp32 in ascending k from Y_main, rounded once to y_dt.
+// Y_main and Y may be the same fp32 buffer.
+hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
+                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, hipStream_t s);
 
 }  // namespace fp4

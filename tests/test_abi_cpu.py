@@ -56,7 +56,7 @@ def test_forward_layout_is_disjoint_and_aligned():
     cap = lay.capacity
     parts = [(lay.T, 4), (lay.nnz, 8), (lay.row_ptr, 301 * 4), (lay.coo_row, cap * 4), (lay.coo_col, cap * 4),
              (lay.coo_val, cap * 4), (lay.Aq, 300 * 256), (lay.sA, 300 * 4), (lay.Wq, 264 * 256),
-             (lay.sW, 264 * 4), (lay.scratch, 1)]
+             (lay.sW, 264 * 4), (lay.ymain, 300 * 264 * 4), (lay.scratch, 1)]
     parts.sort()
     for (a, na), (b, _) in zip(parts, parts[1:]):
         assert a % 256 == 0 and a + na <= b
@@ -120,17 +120,30 @@ def test_outlier_clamp_rejects():
 
 def test_gemm_rejects():
     L = fp4.lib()
+    comp = dict(rp=FAKE, cc=FAKE, cv=FAKE, W=FAKE)
     g = lambda **kw: L.fp4_gemm(kw.get("Aq", FAKE), FAKE, FAKE, FAKE, kw.get("M", 64), kw.get("N", 64),
-                                kw.get("K", 128), kw.get("rp", None), kw.get("cr", None), kw.get("cc", None),
-                                kw.get("cv", None),
-                                kw.get("W", None), 1, FAKE, kw.get("ydt", 1), None, None)
+                                kw.get("K", 128), kw.get("rp", None), kw.get("cc", None), kw.get("cv", None),
+                                kw.get("W", None), 1, FAKE, kw.get("ydt", 1), None, kw.get("ws", None),
+                                kw.get("wsb", 0), None)
     assert g(Aq=None) == ENULL
     assert g(rp=FAKE) == ENULL            # partial compensation arguments
-    assert g(rp=FAKE, cc=FAKE, cv=FAKE) == ENULL  # coo_row missing
-    assert g(rp=FAKE, cr=FAKE, cc=FAKE, cv=FAKE) == ENULL  # compensation without W
+    assert g(rp=FAKE, cc=FAKE) == ENULL
+    assert g(rp=FAKE, cc=FAKE, cv=FAKE) == ENULL  # compensation without W
+    assert g(**comp) == ENULL             # bf16 Y with compensation needs the fp32 workspace
+    assert g(**comp, ws=FAKE, wsb=64 * 64 * 4 - 1) == EWS
+    assert g(**comp, ws=C.c_void_p(0x100008), wsb=64 * 64 * 4) == EALIGN
     assert g(ydt=5) == EDTYPE
     assert g(K=96 + 16) == ESHAPE
     assert g(N=0) == ESHAPE
     # Wq (N x K/2) must stay below 2^31 bytes, and the compensation's W below 2^31 bytes
     assert g(N=1 << 17, K=32768) == ESHAPE
-    assert g(N=1 << 15, K=32768, rp=FAKE, cr=FAKE, cc=FAKE, cv=FAKE, W=FAKE) == ESHAPE
+    assert g(N=1 << 15, K=32768, **comp, ws=FAKE, wsb=1 << 40) == ESHAPE
+
+
+def test_gemm_workspace_bytes():
+    L = fp4.lib()
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 1) == 300 * 264 * 4
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 0) == 0
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 1) == 0   # fp32 Y is updated in place
+    assert L.fp4_gemm_workspace_bytes(0, 264, fp4.FP4_BF16, 1) == 0
+    assert L.fp4_gemm_workspace_bytes(300, 100, fp4.FP4_BF16, 1) == 0

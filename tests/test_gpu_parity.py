@@ -220,8 +220,7 @@ def test_gemm_with_compensation(M, N, K, wdt):
     ref = oracle.forward(Anp, Wnp, q)
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     args = (t(ref["Aq"]), t(ref["sA"]), t(ref["Wq"]), t(ref["sW"]), K)
-    kw = dict(row_ptr=t(ref["row_ptr"]), coo_row=t(ref["coo_row"]), coo_col=t(ref["coo_col"]),
-              coo_val=t(ref["coo_val"]), W=W.to(DEV))
+    kw = dict(row_ptr=t(ref["row_ptr"]), coo_col=t(ref["coo_col"]), coo_val=t(ref["coo_val"]), W=W.to(DEV))
     Y32 = fp4.gemm(*args, **kw, out_dtype=torch.float32)
     Y16 = fp4.gemm(*args, **kw, out_dtype=torch.bfloat16)
     assert_y_close(to_np(Y32), ref["Y"], ref["denom"])
@@ -347,7 +346,7 @@ def test_forward_full_size(cfg, li):
     _say(f"  intermediates bit-exact (T={T} nnz={nnz})")
     # fp32 output and raw accumulator from the same codes
     Y32, acc = fp4.gemm(inter["Aq"], inter["sA"], inter["Wq"], inter["sW"], K, row_ptr=inter["row_ptr"],
-                        coo_row=inter["coo_row"], coo_col=inter["coo_col"], coo_val=inter["coo_val"], W=Wd,
+                        coo_col=inter["coo_col"], coo_val=inter["coo_val"], W=Wd,
                         out_dtype=torch.float32, acc_out=True)
     if L.out_dtype == "bf16":
         assert torch.equal(Y.view(torch.int16), Y32.to(torch.bfloat16).view(torch.int16))
