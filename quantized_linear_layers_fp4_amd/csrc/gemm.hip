@@ -15,8 +15,8 @@
 // first K-step's MFMAs.  The row/column scales of the tile are fetched into LDS with the
 // first stage.
 //
-// Epilogue: Y = fl(fl(acc * sA) * sW), stored straight from the MFMA result registers
-// (each store instruction writes two 32-column row segments).  The sparse compensation
+// Epilogue: Y = fl(fl(acc * sA) * sW); each wave reorders its result tiles through a
+// private patch of LDS so that the stores are 16 bytes per lane along rows.  The sparse compensation
 // dA . W is a separate kernel (comp.hip) that runs on the fp32 result.
 #include "fp4_common.h"
 #include "fp4_launch.h"
@@ -28,6 +28,8 @@ namespace fp4 {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int BM = 256, BN = 128, NW = 4, NT = 64 * NW;
@@ -224,44 +226,91 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     }
     WAIT_VMCNT(0);  // look-ahead loads past the end (zeros) land before the workgroup ends
 
-    // ---- epilogue: Y = fl(fl(acc * sA) * sW) straight from the result registers.
+    // ---- epilogue: Y = fl(fl(acc * sA) * sW).  Each wave turns its 32 x 32 result tiles
+    // into row-major order through a private 4 KiB patch of LDS, so every store writes 16
+    // contiguous bytes per lane.  The patch lies in the buffer of the last real stage: all
+    // waves finished reading it before the last barrier, and no look-ahead load targets it.
     // MFMA 32x32 output layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, col l%32.
+    const int last = (kstages + 2) % 3;
+    uint8_t *stg = last == 0 ? sb0 : (last == 1 ? sb1 : sb2);
+    float *E = reinterpret_cast<float *>(stg + wave * 4096);
     float sw[2];
-    int gcol[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int lc = wn * 64 + j * 32 + (lane & 31);
-        sw[j] = bk.sW[lc];
-        gcol[j] = n0 + lc;
-    }
+    for (int j = 0; j < 2; ++j) sw[j] = bk.sW[wn * 64 + j * 32 + (lane & 31)];
     const bool full = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        float sa[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const int lr0 = wm * 128 + i * 32 + 8 * r4 + 4 * (lane >> 5);  // rows lr0 .. lr0+3
-            const float4 sa4 = *reinterpret_cast<const float4 *>(&bk.sA[lr0]);
-            const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+            const float4 v = *reinterpret_cast<const float4 *>(&bk.sA[wm * 128 + i * 32 + 8 * r4 + 4 * (lane >> 5)]);
+            sa[4 * r4] = v.x;
+            sa[4 * r4 + 1] = v.y;
+            sa[4 * r4 + 2] = v.z;
+            sa[4 * r4 + 3] = v.w;
+        }
+        const int row0 = m0 + wm * 128 + i * 32;  // first row of this 32-row tile
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int grow = m0 + lr0 + t;
-                const size_t rbase = (size_t)grow * N;
+        for (int j = 0; j < 2; ++j) {
+            const int col0 = n0 + wn * 64 + j * 32;
+            if constexpr (ACCOUT) {  // raw accumulator, a check aid: plain stores
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float a = acc[i][j][r4 * 4 + t];
-                    const float y = (a * sa[t]) * sw[j];
-                    if (full || (grow < M && gcol[j] < N)) {
-                        if constexpr (ACCOUT) p.acc_out[rbase + gcol[j]] = a;
-                        // streaming stores: Y is not read back soon enough to be worth caching,
-                        // and leaving it out of the caches keeps the operand strips there
-                        if constexpr (YDT == DT_BF16)
-                            __builtin_nontemporal_store((uint16_t)f32_to_bf16_bits(y),
-                                                        reinterpret_cast<uint16_t *>(p.Y) + rbase + gcol[j]);
-                        else
-                            __builtin_nontemporal_store(y, reinterpret_cast<float *>(p.Y) + rbase + gcol[j]);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int grow = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (full || (grow < M && col0 + (lane & 31) < N))
+                        p.acc_out[(size_t)grow * N + col0 + (lane & 31)] = acc[i][j][r];
                 }
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                E[lr * 32 + (lane & 31)] = (acc[i][j][r] * sa[r]) * sw[j];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // streaming stores: Y is not read back soon enough to be worth caching, and
+            // leaving it out of the caches keeps the operand strips there
+            // all of the patch is read back before the first store is issued
+            f4 e[4];
+            if constexpr (YDT == DT_BF16) {
+                // chunk c = 64k + lane: row c/4, columns 8(c%4) .. +7 (floats 8c .. 8c+7)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    e[2 * k] = *reinterpret_cast<const f4 *>(&E[8 * (k * 64 + lane)]);
+                    e[2 * k + 1] = *reinterpret_cast<const f4 *>(&E[8 * (k * 64 + lane) + 4]);
+                }
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int c = k * 64 + lane, lr = c >> 2, cc = (c & 3) * 8;
+                    const f4 e0 = e[2 * k], e1 = e[2 * k + 1];
+                    const int grow = row0 + lr, gcol = col0 + cc;
+                    if (full || (grow < M && gcol < N)) {
+                        v4i o;
+                        o[0] = (int)(f32_to_bf16_bits(e0[0]) | (f32_to_bf16_bits(e0[1]) << 16));
+                        o[1] = (int)(f32_to_bf16_bits(e0[2]) | (f32_to_bf16_bits(e0[3]) << 16));
+                        o[2] = (int)(f32_to_bf16_bits(e1[0]) | (f32_to_bf16_bits(e1[1]) << 16));
+                        o[3] = (int)(f32_to_bf16_bits(e1[2]) | (f32_to_bf16_bits(e1[3]) << 16));
+                        __builtin_nontemporal_store(
+                            o, reinterpret_cast<v4i *>(reinterpret_cast<uint16_t *>(p.Y) + (size_t)grow * N + gcol));
+                    }
+                }
+            } else {
+                // chunk c = 64k + lane: row c/8, columns 4(c%8) .. +3 (floats 4c .. 4c+3)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) e[k] = *reinterpret_cast<const f4 *>(&E[4 * (k * 64 + lane)]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int c = k * 64 + lane, lr = c >> 3, cc = (c & 7) * 4;
+                    const int grow = row0 + lr, gcol = col0 + cc;
+                    if (full || (grow < M && gcol < N))
+                        __builtin_nontemporal_store(
+                            e[k], reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.Y) + (size_t)grow * N + gcol));
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 }
