@@ -241,10 +241,11 @@ def main():
         wsb = ymain.numel() * ymain.element_size()
         common = (fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K)
         g = lambda: fp4.lib().fp4_gemm(  # noqa: E731
-            *common, None, None, None, None, fp4._dt(Wd), fp4._ptr(ymain), fp4.FP4_F32, None, None, 0,
+            *common, None, None, None, 0, None, fp4._dt(Wd), fp4._ptr(ymain), fp4.FP4_F32, None, None, 0,
             fp4._stream(Ad))
         gc = lambda: fp4.lib().fp4_gemm(  # noqa: E731
-            *common, fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]), fp4._ptr(Wd),
+            *common, fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]), lay.capacity,
+            fp4._ptr(Wd),
             fp4._dt(Wd), fp4._ptr(Y), fp4._dt(Y), None, fp4._ptr(ymain), wsb, fp4._stream(Ad))
         ms_g = time_on_stream(g, args.steps, 2)
         ms_c = max(time_on_stream(gc, args.steps, 2) - ms_g, 1e-9)

@@ -132,6 +132,8 @@ size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t w
  *   row_ptr, coo_col, coo_val: dA as produced by fp4_outlier_clamp (CSR row offsets and
  *            the column/value lists sorted by (row, col)), or all three NULL for no
  *            compensation term; W (K x N, w_dtype) is then unused and may be NULL.
+ *   capacity the number of entries the dA lists were sized for (fp4_outlier_capacity),
+ *            or 0 if unknown; it only picks the shape of the compensation kernel.
  *   Y        M x N of y_dtype (out)
  *   acc_out  NULL, or device fp32[M*N] receiving the raw accumulator acc (a check aid).
  *   workspace, ws_bytes: device scratch of at least fp4_gemm_workspace_bytes() bytes
@@ -141,9 +143,9 @@ size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t w
  * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW,
                     int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
-                    const int32_t *coo_col, const float *coo_val, const void *W, int32_t w_dtype,
-                    void *Y, int32_t y_dtype, float *acc_out, void *workspace, size_t ws_bytes,
-                    void *stream);
+                    const int32_t *coo_col, const float *coo_val, int64_t capacity, const void *W,
+                    int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *workspace,
+                    size_t ws_bytes, void *stream);
 
 /* Byte offsets of the intermediates inside the fp4_linear_forward workspace, so a caller
  * can read T, the COO list, the codes and the scales after a forward. */

@@ -58,7 +58,7 @@ def lib():
         "fp4_outlier_workspace_bytes": (sz, [i64, i64, i32, dbl]),
         "fp4_outlier_clamp": (i32, [vp, i32, i64, i64, dbl, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
         "fp4_gemm_workspace_bytes": (sz, [i64, i64, i32, i32]),
-        "fp4_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
+        "fp4_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, sz, vp]),
         "fp4_forward_layout": (i32, [i64, i64, i64, i32, dbl, C.POINTER(WsLayout)]),
         "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, dbl]),
         "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
@@ -153,7 +153,8 @@ def outlier_clamp(A: torch.Tensor, q: float, trim: bool = True) -> dict:
 def gemm(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, K: int,
          row_ptr: torch.Tensor | None = None, coo_col: torch.Tensor | None = None,
          coo_val: torch.Tensor | None = None, W: torch.Tensor | None = None,
-         out_dtype: torch.dtype = torch.bfloat16, acc_out: bool = False, ws: torch.Tensor | None = None):
+         out_dtype: torch.dtype = torch.bfloat16, acc_out: bool = False, ws: torch.Tensor | None = None,
+         capacity: int | None = None):
     """Y = fl(fl(acc * sA) * sW) (+ dA . W when row_ptr, coo_col, coo_val and W are given)."""
     _need_cuda(Aq, sA, Wq, sW, row_ptr, coo_col, coo_val, W, ws)
     M, N = Aq.shape[0], Wq.shape[0]
@@ -164,8 +165,9 @@ def gemm(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor,
     if ws is None:
         nbytes = lib().fp4_gemm_workspace_bytes(M, N, _out_dtype_code(out_dtype), with_comp)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=Aq.device) if nbytes else None
+    cap = capacity if capacity is not None else (coo_col.numel() if coo_col is not None else 0)
     _check(lib().fp4_gemm(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, _ptr(row_ptr), _ptr(coo_col),
-                          _ptr(coo_val), _ptr(W), wdt, _ptr(Y), _out_dtype_code(out_dtype), _ptr(acc), _ptr(ws),
+                          _ptr(coo_val), cap, _ptr(W), wdt, _ptr(Y), _out_dtype_code(out_dtype), _ptr(acc), _ptr(ws),
                           ws.numel() if ws is not None else 0, _stream(Aq)))
     return (Y, acc) if acc_out else Y
 

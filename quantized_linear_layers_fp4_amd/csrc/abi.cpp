@@ -218,9 +218,9 @@ size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t w
 }
 
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
-                    int64_t K, const int32_t *row_ptr, const int32_t *coo_col, const float *coo_val, const void *W,
-                    int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *workspace, size_t ws_bytes,
-                    void *stream) {
+                    int64_t K, const int32_t *row_ptr, const int32_t *coo_col, const float *coo_val,
+                    int64_t capacity, const void *W, int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out,
+                    void *workspace, size_t ws_bytes, void *stream) {
     if (!Aq || !sA || !Wq || !sW || !Y) return FP4_ERR_NULL;
     const int ncomp = (row_ptr != nullptr) + (coo_col != nullptr) + (coo_val != nullptr);
     if (ncomp != 0 && ncomp != 3) return FP4_ERR_NULL;
@@ -242,7 +242,8 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
     float *ymain = staged ? static_cast<float *>(workspace) : static_cast<float *>(Y);
     hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, acc_out, s);
     if (e == hipSuccess)
-        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype), s);
+        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype),
+                        capacity > 0 ? capacity : 0, s);
     return hip_status(e);
 }
 
@@ -313,7 +314,8 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
     float *ymain = y_dtype == FP4_F32 ? static_cast<float *>(Y) : reinterpret_cast<float *>(ws + l.ymain);
     if (e == hipSuccess) e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, nullptr, s);
     if (e == hipSuccess)
-        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype), s);
+        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype),
+                        l.capacity, s);
     return hip_status(e);
 }
 

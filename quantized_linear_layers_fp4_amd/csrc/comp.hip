@@ -5,31 +5,57 @@
 // dequantized product Y_main in fp32, and writes Y = Y_main + dA . W in the output type,
 // rounded once.
 //
-// One wave per (row, 512-column chunk) task; lane l owns the eight columns 8l..8l+7 of the
-// chunk.  The wave first issues its Y_main loads and the row's two CSR offsets together,
-// then takes the row's dA entries (ascending column k) 64 at a time, one (k, delta) pair
-// per lane, and walks them in groups of eight: the eight W row segments are loaded
-// together and added to the eight running sums in ascending k (one fp32 fma each).
+// One wave per (row, chunk of 64*CC columns) task; lane l owns the CC columns CC*l .. of
+// the chunk.  The wave first issues its Y_main loads and the row's two CSR offsets
+// together, then takes the row's dA entries (ascending column k) 64 at a time, one
+// (k, delta) pair per lane, and walks them in groups of eight: the eight W row segments are
+// loaded together and added to the running sums in ascending k (one fp32 fma each).
 //
 // Task order: the tasks are dealt out to the eight XCDs in contiguous ranges (consecutive
 // workgroup ids go to different XCDs), chunk-major within a range, so each XCD streams all
 // rows over one chunk at a time and the W rows that chunk gathers stay in that XCD's L2.
 // Y_main and Y are streamed with non-temporal hints so they do not evict those rows.
-// Nothing here needs N * 4 or K * N * sizeof(W) beyond 2^31 - 1 bytes per descriptor:
-// Y_main is addressed per row.
+// Two widths: CC = 8 (512-column chunks, more Y_main bytes in flight per wave) when the
+// rows hold few entries and the pass streams Y_main; CC = 4 (256-column chunks, half the
+// W strip per chunk) when many entries per row make it bound by its gathers.
 #include "fp4_common.h"
 #include "fp4_launch.h"
 
 namespace fp4 {
 
-constexpr int CCOLS = 8;             // columns per lane
-constexpr int CCHUNK = 64 * CCOLS;   // columns per task
-constexpr int CB = 8;                // W row segments in flight per lane
+constexpr int CB = 8;  // W row segments in flight per lane
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// CC consecutive elements of type WDT (bf16 or fp32) at byte offset off, raw, through a
+// buffer descriptor (out of range: zeros); nothing is loaded when !on.
+template <int WDT, int CC>
+__device__ __forceinline__ void load_seg(__amdgpu_buffer_rsrc_t rs, uint32_t off, bool on, v4i (&raw)[2]) {
+    constexpr int BYTES = CC * (WDT == DT_BF16 ? 2 : 4);
+    raw[0] = raw[1] = v4i{0, 0, 0, 0};
+    if (!on) return;
+    if constexpr (BYTES == 8) {
+        const v2i q = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
+        raw[0] = v4i{q.x, q.y, 0, 0};
+    } else {
+        raw[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+        if constexpr (BYTES == 32) raw[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off + 16, 0, 0);
+    }
+}
+// element c of such a segment as fp32
+template <int WDT>
+__device__ __forceinline__ float seg_elem(const v4i (&raw)[2], int c) {
+    if constexpr (WDT == DT_BF16) {
+        const uint32_t pr = (uint32_t)raw[c >> 3][(c >> 1) & 3];
+        return bf16_to_f32((c & 1) ? (pr >> 16) : (pr & 0xFFFFu));
+    } else {
+        return __int_as_float(raw[c >> 2][c & 3]);
+    }
+}
+
 // INPLACE: Y is the fp32 Y_main buffer itself; a row without entries is then left alone.
-template <int YDT, int WDT, bool INPLACE>
+template <int YDT, int WDT, bool INPLACE, int CC>
 __global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y, int M, int N, int K,
                                                     int chunks, int per_xcd,
                                                     const int32_t *__restrict__ row_ptr,
@@ -41,8 +67,8 @@ __global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y,
     if (task >= (int64_t)chunks * M) return;  // whole wave
     const int chunk = (int)(task / M);
     const int row = (int)(task - (int64_t)chunk * M);
-    const int col = chunk * CCHUNK + lane * CCOLS;
-    const bool active = col < N;  // N % 8 == 0: a lane's eight columns are in range together
+    const int col = chunk * (64 * CC) + lane * CC;
+    const bool active = col < N;  // N % 8 == 0: a lane's columns are in range together
     const size_t yoff = (size_t)row * N + col;
 
     // The row's CSR offsets (lane l loads row_ptr[row + (l & 1)]) and the lane's Y_main
@@ -51,30 +77,26 @@ __global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y,
     const int32_t rp = row_ptr[row + (lane & 1)];
     const __amdgpu_buffer_rsrc_t rsY =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(Ymain) + (size_t)row * N, 0, N * 4, 0x00020000);
-    v4i y0 = {0, 0, 0, 0}, y1 = y0;
-    if constexpr (!INPLACE) {
-        y0 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4, 0, 2);
-        y1 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4 + 16, 0, 2);
-    }
+    v4i yv[CC / 4];
+    auto load_y = [&]() {
+#pragma unroll
+        for (int h = 0; h < CC / 4; ++h) yv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4 + 16 * h, 0, 2);
+    };
+    if constexpr (!INPLACE) load_y();
     const int32_t e0 = __builtin_amdgcn_readlane(rp, 0);
     const int32_t e1 = __builtin_amdgcn_readlane(rp, 1);
     if constexpr (INPLACE) {
         if (e0 == e1) return;
-        y0 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4, 0, 2);
-        y1 = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4 + 16, 0, 2);
+        load_y();
     }
-    float y[8];
+    float y[CC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        y[c] = __int_as_float(y0[c]);
-        y[4 + c] = __int_as_float(y1[c]);
-    }
+    for (int c = 0; c < CC; ++c) y[c] = __int_as_float(yv[c >> 2][c & 3]);
 
     // W through a buffer descriptor.  Offsets are unsigned 32-bit: K*N*ESZ < 2^31, so the
     // largest (a lane past N on the last row of W) stays below 2^32 and reads zeros; such a
     // lane is never stored.
     constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
-    constexpr int NH = CCOLS * ESZ / 16;  // 16-byte loads per segment
     const __amdgpu_buffer_rsrc_t rsW =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(W), 0, (int)((int64_t)K * N * ESZ), 0x00020000);
     const uint32_t row_bytes = (uint32_t)N * ESZ;
@@ -88,15 +110,11 @@ __global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y,
         }
         const int nb = min(64, e1 - e);  // wave-uniform
         for (int s = 0; s < nb; s += CB) {
-            v4i w[CB][NH];
+            v4i w[CB][2];
 #pragma unroll
             for (int u = 0; u < CB; ++u) {
                 const uint32_t k = (uint32_t)__builtin_amdgcn_readlane(kk, s + u);
-                const uint32_t off = k * row_bytes + lane_off;
-#pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    w[u][h] = (s + u < nb) ? __builtin_amdgcn_raw_buffer_load_b128(rsW, (int)(off + 16 * h), 0, 0)
-                                           : v4i{0, 0, 0, 0};
+                load_seg<WDT, CC>(rsW, k * row_bytes + lane_off, s + u < nb, w[u]);
             }
 #pragma unroll
             for (int u = 0; u < CB; ++u) {
@@ -104,45 +122,42 @@ __global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y,
                     const float d = __builtin_bit_cast(
                         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int32_t, dd), s + u));
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        float wv;
-                        if constexpr (WDT == DT_BF16) {
-                            const uint32_t pr = (uint32_t)w[u][0][c >> 1];
-                            wv = bf16_to_f32((c & 1) ? (pr >> 16) : (pr & 0xFFFFu));
-                        } else {
-                            wv = __int_as_float(w[u][c >> 2][c & 3]);
-                        }
-                        y[c] = __builtin_fmaf(d, wv, y[c]);
-                    }
+                    for (int c = 0; c < CC; ++c) y[c] = __builtin_fmaf(d, seg_elem<WDT>(w[u], c), y[c]);
                 }
             }
         }
     }
     if (!active) return;
     if constexpr (YDT == DT_BF16) {
-        v4i o;
+        uint32_t o[CC / 2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[i] = (int)(f32_to_bf16_bits(y[2 * i]) | (f32_to_bf16_bits(y[2 * i + 1]) << 16));
-        __builtin_nontemporal_store(o, reinterpret_cast<v4i *>(reinterpret_cast<uint16_t *>(Y) + yoff));
+        for (int i = 0; i < CC / 2; ++i) o[i] = f32_to_bf16_bits(y[2 * i]) | (f32_to_bf16_bits(y[2 * i + 1]) << 16);
+        uint16_t *yp = reinterpret_cast<uint16_t *>(Y) + yoff;
+        if constexpr (CC == 8)
+            __builtin_nontemporal_store(v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]}, reinterpret_cast<v4i *>(yp));
+        else
+            __builtin_nontemporal_store(v2i{(int)o[0], (int)o[1]}, reinterpret_cast<v2i *>(yp));
     } else {
         f4 *yp = reinterpret_cast<f4 *>(reinterpret_cast<float *>(Y) + yoff);
-        __builtin_nontemporal_store(f4{y[0], y[1], y[2], y[3]}, yp);
-        __builtin_nontemporal_store(f4{y[4], y[5], y[6], y[7]}, yp + 1);
+#pragma unroll
+        for (int h = 0; h < CC / 4; ++h)
+            __builtin_nontemporal_store(f4{y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]}, yp + h);
     }
 }
 
-hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
-                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, hipStream_t s) {
-    const int chunks = (int)((N + CCHUNK - 1) / CCHUNK);
+template <int CC>
+static hipError_t launch_comp_w(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K,
+                                const int32_t *row_ptr, const int32_t *coo_col, const float *coo_val, const void *W,
+                                int w_dt, hipStream_t s) {
+    const int chunks = (int)((N + 64 * CC - 1) / (64 * CC));
     const int64_t tasks = (int64_t)chunks * M;
     const int64_t blocks = (tasks + 3) / 4;
     const int per_xcd = (int)((blocks + 7) / 8);
     const dim3 grid((unsigned)per_xcd * 8u), block(256);
     const bool inplace = static_cast<const void *>(Ymain) == Y;
-#define C(YD, WD, IP)                                                                                            \
-    hipLaunchKernelGGL((k_comp_apply<YD, WD, IP>), grid, block, 0, s, Ymain, Y, (int)M, (int)N, (int)K, chunks, \
-                       per_xcd, row_ptr, coo_col, coo_val, W)
+#define C(YD, WD, IP)                                                                                        \
+    hipLaunchKernelGGL((k_comp_apply<YD, WD, IP, CC>), grid, block, 0, s, Ymain, Y, (int)M, (int)N, (int)K, \
+                       chunks, per_xcd, row_ptr, coo_col, coo_val, W)
     if (y_dt == DT_BF16) {
         if (w_dt == DT_BF16) C(DT_BF16, DT_BF16, false);
         else C(DT_BF16, DT_F32, false);
@@ -155,6 +170,15 @@ hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t
     }
 #undef C
     return hipGetLastError();
+}
+
+hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
+                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, int64_t capacity,
+                       hipStream_t s) {
+    // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
+    // gathers and the narrower chunks keep more of each W strip in L2
+    if (capacity > 64 * M) return launch_comp_w<4>(Ymain, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
+    return launch_comp_w<8>(Ymain, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
 }
 
 }  // namespace fp4

@@ -28,8 +28,10 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
                        int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s);
 // Y = Y_main + dA . W, accumulated in fp32 in ascending k from Y_main, rounded once to y_dt.
-// Y_main and Y may be the same fp32 buffer.
+// Y_main and Y may be the same fp32 buffer.  capacity: what the dA list was sized for (picks
+// the kernel shape only; 0 if unknown).
 hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
-                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, hipStream_t s);
+                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, int64_t capacity,
+                       hipStream_t s);
 
 }  // namespace fp4

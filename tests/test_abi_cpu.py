@@ -122,7 +122,7 @@ def test_gemm_rejects():
     L = fp4.lib()
     comp = dict(rp=FAKE, cc=FAKE, cv=FAKE, W=FAKE)
     g = lambda **kw: L.fp4_gemm(kw.get("Aq", FAKE), FAKE, FAKE, FAKE, kw.get("M", 64), kw.get("N", 64),
-                                kw.get("K", 128), kw.get("rp", None), kw.get("cc", None), kw.get("cv", None),
+                                kw.get("K", 128), kw.get("rp", None), kw.get("cc", None), kw.get("cv", None), 0,
                                 kw.get("W", None), 1, FAKE, kw.get("ydt", 1), None, kw.get("ws", None),
                                 kw.get("wsb", 0), None)
     assert g(Aq=None) == ENULL

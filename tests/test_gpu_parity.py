@@ -211,16 +211,21 @@ def test_gemm_accumulator_extremes():
     assert to_np(acc)[0, 1] == 36.0 * K and to_np(acc)[1, 1] == -36.0 * K
 
 
-@pytest.mark.parametrize("M,N,K,wdt", [(300, 264, 512, "bf16"), (513, 520, 1056, "fp32"), (64, 8, 96, "bf16")])
-def test_gemm_with_compensation(M, N, K, wdt):
-    _say(f"gemm comp {M}x{N}x{K} {wdt}")
+@pytest.mark.parametrize("wide", [True, False], ids=["chunk512", "chunk256"])
+@pytest.mark.parametrize("M,N,K,wdt", [(300, 264, 512, "bf16"), (513, 520, 1056, "fp32"), (64, 8, 96, "bf16"),
+                                       (70, 776, 128, "fp32")])
+def test_gemm_with_compensation(M, N, K, wdt, wide):
+    """Both shapes of the compensation kernel (the capacity hint picks one: more than 64
+    entries per row selects the 256-column chunks)."""
+    _say(f"gemm comp {M}x{N}x{K} {wdt} {'wide' if wide else 'narrow'}")
     A, W = make_custom(M, K, N, dtype=wdt, seed=11)
     Anp, Wnp = oracle_inputs(A, W)
     q = 0.98
     ref = oracle.forward(Anp, Wnp, q)
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     args = (t(ref["Aq"]), t(ref["sA"]), t(ref["Wq"]), t(ref["sW"]), K)
-    kw = dict(row_ptr=t(ref["row_ptr"]), coo_col=t(ref["coo_col"]), coo_val=t(ref["coo_val"]), W=W.to(DEV))
+    kw = dict(row_ptr=t(ref["row_ptr"]), coo_col=t(ref["coo_col"]), coo_val=t(ref["coo_val"]), W=W.to(DEV),
+              capacity=0 if wide else 65 * M)
     Y32 = fp4.gemm(*args, **kw, out_dtype=torch.float32)
     Y16 = fp4.gemm(*args, **kw, out_dtype=torch.bfloat16)
     assert_y_close(to_np(Y32), ref["Y"], ref["denom"])
