@@ -54,20 +54,23 @@ def comp_bytes(M, N, b_out, nnz) -> int:
     return M * N * 4 + M * N * b_out + 8 * nnz + 4 * (M + 1)
 
 
-def time_on_stream(fn, steps: int, warmup: int) -> float:
-    """Average milliseconds of fn() over `steps` calls, HIP events on the current stream
-    (the stream every launch of fn goes to)."""
+def time_on_stream(fn, steps: int, warmup: int, rounds: int = 3) -> float:
+    """Average milliseconds of fn() per call, HIP events on the current stream (the stream
+    every launch of fn goes to): the median over `rounds` runs of `steps` back-to-back calls."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(steps):
-        fn()
-    e1.record(s)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    out = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return sorted(out)[len(out) // 2]
 
 
 def gemm_src_sha() -> str:
@@ -142,22 +145,25 @@ def _counter_per_dispatch(d: str, counter: str, kernel_pred) -> float:
 
 
 def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write: str):
-    """HBM bytes per k_fp4_gemm launch on the 7B gate+up shape: FETCH_SIZE and WRITE_SIZE
-    per dispatch, each scaled by the bytes a plain 1 GiB copy moves per unit of the same
-    counter.  Written with the hash of the GEMM source it was measured on."""
+    """HBM bytes per k_fp4_gemm launch (and per k_comp_apply launch) on the 7B gate+up shape:
+    FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the bytes a plain 1 GiB copy moves
+    per unit of the same counter.  Written with the hash of the GEMM source it was measured on."""
     is_gemm = lambda n: "k_fp4_gemm" in n  # noqa: E731
+    is_comp = lambda n: "k_comp_apply" in n  # noqa: E731
     is_copy = lambda n: "copyBuffer" in n  # noqa: E731
-    g_f = _counter_per_dispatch(gemm_fetch, "FETCH_SIZE", is_gemm)
-    g_w = _counter_per_dispatch(gemm_write, "WRITE_SIZE", is_gemm)
     c_f = _counter_per_dispatch(copy_fetch, "FETCH_SIZE", is_copy)
     c_w = _counter_per_dispatch(copy_write, "WRITE_SIZE", is_copy)
     f_fetch, f_write = (1 << 30) / c_f, (1 << 30) / c_w
     rec = {"gemm_src_sha": gemm_src_sha(), "workload": "llama7b_gate_up",
-           "fetch_size_per_launch": g_f, "write_size_per_launch": g_w,
            "copy_fetch_size": c_f, "copy_write_size": c_w,
-           "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write,
-           "hbm_read_bytes_per_launch": g_f * f_fetch, "hbm_write_bytes_per_launch": g_w * f_write,
-           "hbm_bytes_per_launch": round(g_f * f_fetch + g_w * f_write)}
+           "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write}
+    for name, pred in (("gemm", is_gemm), ("comp", is_comp)):
+        fs = _counter_per_dispatch(gemm_fetch, "FETCH_SIZE", pred)
+        ws = _counter_per_dispatch(gemm_write, "WRITE_SIZE", pred)
+        pre = "" if name == "gemm" else "comp_"
+        rec.update({f"{pre}fetch_size_per_launch": fs, f"{pre}write_size_per_launch": ws,
+                    f"{pre}hbm_read_bytes_per_launch": fs * f_fetch, f"{pre}hbm_write_bytes_per_launch": ws * f_write,
+                    f"{pre}hbm_bytes_per_launch": round(fs * f_fetch + ws * f_write)})
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
