@@ -243,8 +243,9 @@ def main():
         it = fp4.forward_intermediates(ws, L.M, L.K, L.N, A.dtype, L.q)
         lay = fp4.forward_layout(L.M, L.K, L.N, A.dtype, L.q)
         nnz = int(it["nnz"].item())
-        ymain = Y if Y.dtype == torch.float32 else ws[lay.ymain:]
-        wsb = ymain.numel() * ymain.element_size()
+        wsb = L.M * L.N * 4
+        ymain = Y if Y.dtype == torch.float32 else ws[lay.ymain:lay.ymain + wsb]
+        assert ymain.numel() * ymain.element_size() == wsb, "workspace has no Y_main region"
         common = (fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K)
         g = lambda: fp4.lib().fp4_gemm(  # noqa: E731
             *common, None, None, None, 0, None, fp4._dt(Wd), fp4._ptr(ymain), fp4.FP4_F32, None, None, 0,
