@@ -322,7 +322,7 @@ static int raster_group_for(int tilesM) {
         const char *e = getenv("FP4_GEMM_RASTER");
         env = e ? atoi(e) : -1;
     }
-    const int g = env > 0 ? env : 8;
+    const int g = env > 0 ? env : 4;
     return g < tilesM ? g : tilesM;
 }
 
