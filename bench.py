@@ -38,13 +38,13 @@ def b_in(dtype: torch.dtype) -> int:
     return 2 if dtype == torch.bfloat16 else 4
 
 
-def quantizer_bytes(M, K, N, bi, nnz) -> int:
+def quantizer_bytes(M, K, N, bi, nnz, with_w: bool = True) -> int:
     """Algorithmic HBM bytes of the quantizer stages: A read twice (histogram pass, then
     clamp+quantize: T must be known before any code), codes, scales, dA; W read once,
     codes, scales."""
     a = 2 * M * K * bi + M * K // 2 + 4 * M + 12 * nnz + 4 * (M + 1)
     w = K * N * bi + K * N // 2 + 4 * N
-    return a + w
+    return a + (w if with_w else 0)
 
 
 def comp_bytes(M, N, b_out, nnz) -> int:
@@ -184,6 +184,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wq", default="per-step", choices=["per-step", "cached", "overlap"],
+                    help="W quantization: inside every forward (the pages' scheme, default); once before the "
+                         "timed steps (fixed inference weights); or on a second stream, each layer's under the "
+                         "previous layer's forward")
     ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic"])
     ap.add_argument("--traffic-dirs", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="--mode traffic: rocprofv3 --pmc output directories of FETCH_SIZE and WRITE_SIZE for "
@@ -211,9 +215,48 @@ def main():
         runs.append((A, W, L, Ad, Wd, ws, Y))
     torch.cuda.synchronize()
 
+    # W's codes and scales, for --wq cached / overlap (per-step quantizes inside the forward)
+    wqs = []
+    for _, _, L, Ad, Wd, ws, Y in runs:
+        wqs.append((torch.empty((L.N, L.K // 2), dtype=torch.uint8, device=dev),
+                    torch.empty(L.N, dtype=torch.float32, device=dev)))
+
+    def quant_w(i):
+        _, _, L, _, Wd, _, _ = runs[i]
+        Wq, sW = wqs[i]
+        fp4._check(fp4.lib().fp4_quantize(fp4._ptr(Wd), fp4._dt(Wd), L.K, L.N, fp4.FP4_PER_COL, None,
+                                          fp4._ptr(Wq), fp4._ptr(sW), fp4._stream(Wd)))
+
+    def forward_wq(i):
+        _, _, L, Ad, Wd, ws, Y = runs[i]
+        Wq, sW = wqs[i]
+        fp4.linear_forward_wq(Ad, Wd, Wq, sW, L.q, ws=ws, Y=Y)
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=dev)  # default priority
+    if args.wq == "cached":
+        for i in range(len(runs)):
+            quant_w(i)
+
     def step():
-        for _, _, L, Ad, Wd, ws, Y in runs:
-            fp4.linear_forward(Ad, Wd, L.q, ws=ws, Y=Y)
+        if args.wq == "per-step":
+            for _, _, L, Ad, Wd, ws, Y in runs:
+                fp4.linear_forward(Ad, Wd, L.q, ws=ws, Y=Y)
+        elif args.wq == "cached":
+            for i in range(len(runs)):
+                forward_wq(i)
+        else:  # overlap: W of layer i+1 is quantized on a second stream under layer i's forward
+            side.wait_stream(main)
+            ready = []
+            with torch.cuda.stream(side):
+                for i in range(len(runs)):
+                    quant_w(i)
+                    ev = torch.cuda.Event()
+                    ev.record(side)
+                    ready.append(ev)
+            for i in range(len(runs)):
+                main.wait_event(ready[i])
+                forward_wq(i)
 
     for _ in range(args.warmup):
         step()
@@ -258,7 +301,7 @@ def main():
         ms_c = max(time_on_stream(gc, args.steps, 2) - ms_g, 1e-9)
         gemm_ms += ms_g
         comp_ms += ms_c
-        qb = quantizer_bytes(L.M, L.K, L.N, b_in(A.dtype), nnz)
+        qb = quantizer_bytes(L.M, L.K, L.N, b_in(A.dtype), nnz, with_w=args.wq != "cached")
         cb = comp_bytes(L.M, L.N, Y.element_size(), nnz)
         qbytes += qb
         cbytes += cb
@@ -288,7 +331,8 @@ def main():
         "dtype": "fp4e2m1 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": name, "M": first.M, "K": first.K, "N": first.N, "in_dtype": first.dtype,
-                   "out_dtype": first.out_dtype, "q": first.q, "layers": len(runs), "parallelism": "none (1 GPU)"},
+                   "out_dtype": first.out_dtype, "q": first.q, "layers": len(runs), "w_quant": args.wq,
+                   "parallelism": "none (1 GPU)"},
         "forward_frac_of_fp4_peak": round(fwd_tflops / PEAK_FP4_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "k_fp4_gemm", "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),

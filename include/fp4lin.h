@@ -177,6 +177,19 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
                               int64_t K, int64_t N, double q, void *Y, int32_t y_dtype,
                               void *workspace, size_t ws_bytes, void *stream);
 
+/* The same forward with W already quantized: Wq and sW as fp4_quantize(W, FP4_PER_COL)
+ * produced them (N x K/2 codes, fp32[N] scales) while W is unchanged, as when the weights
+ * of an inference layer are fixed.  The QbitAI report quantizes W at every forward
+ * (forward-quantization paragraph); the codes depend on W alone, so reusing them gives
+ * bit-identical results and skips the per-channel pass.  W itself is still read for the
+ * compensation term.  Workspace and layout as for fp4_linear_forward (its Wq and sW regions
+ * are left untouched).
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,QUANTILE,WORKSPACE,ALIGN,DEVICE,HIP}. */
+fp4_status fp4_linear_forward_wq(const void *A, const void *W, const uint8_t *Wq, const float *sW,
+                                 int32_t in_dtype, int64_t M, int64_t K, int64_t N, double q,
+                                 void *Y, int32_t y_dtype, void *workspace, size_t ws_bytes,
+                                 void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *fp4_status_string(fp4_status s);
 

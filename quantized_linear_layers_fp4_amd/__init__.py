@@ -27,6 +27,7 @@ FP4_PER_ROW, FP4_PER_COL = 0, 1
 EXPORTS = (
     "fp4_quantize", "fp4_outlier_capacity", "fp4_outlier_workspace_bytes", "fp4_outlier_clamp",
     "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_forward_layout", "fp4_forward_workspace_bytes", "fp4_linear_forward",
+    "fp4_linear_forward_wq",
     "fp4_status_string",
 )
 
@@ -62,6 +63,7 @@ def lib():
         "fp4_forward_layout": (i32, [i64, i64, i64, i32, dbl, C.POINTER(WsLayout)]),
         "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, dbl]),
         "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
+        "fp4_linear_forward_wq": (i32, [vp, vp, vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -200,6 +202,35 @@ def linear_forward(A: torch.Tensor, W: torch.Tensor, q: float, out_dtype: torch.
         Y = torch.empty((M, N), dtype=out_dtype, device=A.device)
     _check(lib().fp4_linear_forward(_ptr(A), _ptr(W), _dt(A), M, K, N, float(q), _ptr(Y), _dt(Y), _ptr(ws),
                                     ws.numel(), _stream(A)))
+    return Y
+
+
+def quantize_weights(W: torch.Tensor):
+    """(Wq, sW) of a K x N weight matrix: per-output-channel codes (N x K/2) and scales."""
+    _need_cuda(W)
+    K, N = W.shape
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    sW = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check(lib().fp4_quantize(_ptr(W), _dt(W), K, N, FP4_PER_COL, None, _ptr(Wq), _ptr(sW), _stream(W)))
+    return Wq, sW
+
+
+def linear_forward_wq(A: torch.Tensor, W: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, q: float,
+                      out_dtype: torch.dtype | None = None, ws: torch.Tensor | None = None,
+                      Y: torch.Tensor | None = None) -> torch.Tensor:
+    """The forward with W's codes and scales from quantize_weights(W) (W unchanged since)."""
+    _need_cuda(A, W, Wq, sW, ws, Y)
+    if A.dtype != W.dtype:
+        raise TypeError("A and W must share a dtype")
+    M, K = A.shape
+    N = W.shape[1]
+    out_dtype = out_dtype or A.dtype
+    if ws is None:
+        ws = workspace(A, N, q)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    _check(lib().fp4_linear_forward_wq(_ptr(A), _ptr(W), _ptr(Wq), _ptr(sW), _dt(A), M, K, N, float(q), _ptr(Y),
+                                       _dt(Y), _ptr(ws), ws.numel(), _stream(A)))
     return Y
 
 

@@ -141,6 +141,55 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
 
 }  // namespace
 
+namespace {
+// The forward; Wq_in/sW_in: W's codes and scales from an earlier fp4_quantize (W unchanged
+// since), or NULL to quantize W here.
+fp4_status forward_impl(const void *A, const void *W, const uint8_t *Wq_in, const float *sW_in, int32_t in_dtype,
+                        int64_t M, int64_t K, int64_t N, double q, void *Y, int32_t y_dtype, void *workspace,
+                        size_t ws_bytes, void *stream) {
+    if (!A || !W || !Y || !workspace) return FP4_ERR_NULL;
+    if (!dtype_ok(in_dtype) || !dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
+    fp4_ws_layout l;
+    fp4_status st = fp4_forward_layout(M, K, N, in_dtype, q, &l);
+    if (st != FP4_OK) return st;
+    if (ws_bytes < l.total) return FP4_ERR_WORKSPACE;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace)) return FP4_ERR_ALIGN;
+    int cus;
+    st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    float *T = reinterpret_cast<float *>(ws + l.T);
+    int64_t *nnz = reinterpret_cast<int64_t *>(ws + l.nnz);
+    int32_t *row_ptr = reinterpret_cast<int32_t *>(ws + l.row_ptr);
+    int32_t *coo_row = reinterpret_cast<int32_t *>(ws + l.coo_row);
+    int32_t *coo_col = reinterpret_cast<int32_t *>(ws + l.coo_col);
+    float *coo_val = reinterpret_cast<float *>(ws + l.coo_val);
+    uint8_t *Aq = ws + l.Aq;
+    float *sA = reinterpret_cast<float *>(ws + l.sA);
+    const bool wq_given = Wq_in != nullptr;
+    const uint8_t *Wq = wq_given ? Wq_in : ws + l.Wq;
+    const float *sW = wq_given ? sW_in : reinterpret_cast<float *>(ws + l.sW);
+    uint32_t *sW_keys = reinterpret_cast<uint32_t *>(ws + l.sW);  // column-max keys, then scales
+    const OutlierWs w = outlier_ws(M, K, in_dtype, l.capacity);
+    // the column-maximum keys of W (kept in the sW region) are zeroed with the outlier scratch
+    st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, T, coo_row, coo_col, coo_val, l.capacity,
+                      row_ptr, nnz, Aq, sA, wq_given ? nullptr : sW_keys, wq_given ? 0 : N, s);
+    if (st != FP4_OK) return st;
+    hipError_t e = hipSuccess;
+    if (!wq_given)
+        e = launch_quant_cols(W, dt_of(in_dtype), K, N, reinterpret_cast<float *>(sW_keys), ws + l.Wq, true, s);
+    // Y_main in fp32 (straight into Y when Y is fp32), then Y = Y_main + dA . W
+    float *ymain = y_dtype == FP4_F32 ? static_cast<float *>(Y) : reinterpret_cast<float *>(ws + l.ymain);
+    if (e == hipSuccess) e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, nullptr, s);
+    if (e == hipSuccess)
+        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype),
+                        l.capacity, s);
+    return hip_status(e);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *fp4_status_string(fp4_status s) {
@@ -282,41 +331,15 @@ size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_d
 
 fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N,
                               double q, void *Y, int32_t y_dtype, void *workspace, size_t ws_bytes, void *stream) {
-    if (!A || !W || !Y || !workspace) return FP4_ERR_NULL;
-    if (!dtype_ok(in_dtype) || !dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
-    fp4_ws_layout l;
-    fp4_status st = fp4_forward_layout(M, K, N, in_dtype, q, &l);
-    if (st != FP4_OK) return st;
-    if (ws_bytes < l.total) return FP4_ERR_WORKSPACE;
-    if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace)) return FP4_ERR_ALIGN;
-    int cus;
-    st = device_check(&cus);
-    if (st != FP4_OK) return st;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    float *T = reinterpret_cast<float *>(ws + l.T);
-    int64_t *nnz = reinterpret_cast<int64_t *>(ws + l.nnz);
-    int32_t *row_ptr = reinterpret_cast<int32_t *>(ws + l.row_ptr);
-    int32_t *coo_row = reinterpret_cast<int32_t *>(ws + l.coo_row);
-    int32_t *coo_col = reinterpret_cast<int32_t *>(ws + l.coo_col);
-    float *coo_val = reinterpret_cast<float *>(ws + l.coo_val);
-    uint8_t *Aq = ws + l.Aq;
-    float *sA = reinterpret_cast<float *>(ws + l.sA);
-    uint8_t *Wq = ws + l.Wq;
-    float *sW = reinterpret_cast<float *>(ws + l.sW);
-    const OutlierWs w = outlier_ws(M, K, in_dtype, l.capacity);
-    // the column-maximum keys of W (kept in sW) are zeroed with the outlier scratch
-    st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, T, coo_row, coo_col, coo_val, l.capacity,
-                      row_ptr, nnz, Aq, sA, reinterpret_cast<uint32_t *>(sW), N, s);
-    if (st != FP4_OK) return st;
-    hipError_t e = launch_quant_cols(W, dt_of(in_dtype), K, N, sW, Wq, true, s);
-    // Y_main in fp32 (straight into Y when Y is fp32), then Y = Y_main + dA . W
-    float *ymain = y_dtype == FP4_F32 ? static_cast<float *>(Y) : reinterpret_cast<float *>(ws + l.ymain);
-    if (e == hipSuccess) e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, nullptr, s);
-    if (e == hipSuccess)
-        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype),
-                        l.capacity, s);
-    return hip_status(e);
+    return forward_impl(A, W, nullptr, nullptr, in_dtype, M, K, N, q, Y, y_dtype, workspace, ws_bytes, stream);
+}
+
+fp4_status fp4_linear_forward_wq(const void *A, const void *W, const uint8_t *Wq, const float *sW, int32_t in_dtype,
+                                 int64_t M, int64_t K, int64_t N, double q, void *Y, int32_t y_dtype,
+                                 void *workspace, size_t ws_bytes, void *stream) {
+    if (!Wq || !sW) return FP4_ERR_NULL;
+    if (!aligned16(Wq)) return FP4_ERR_ALIGN;
+    return forward_impl(A, W, Wq, sW, in_dtype, M, K, N, q, Y, y_dtype, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -91,6 +91,22 @@ def test_linear_forward_rejects(case, expect):
     assert st == expect
 
 
+def test_linear_forward_wq_rejects():
+    """The pre-quantized-W forward checks its two extra pointers, then everything the plain
+    forward checks."""
+    L = fp4.lib()
+    lay = fp4.WsLayout()
+    assert L.fp4_forward_layout(64, 128, 64, fp4.FP4_BF16, 0.99, C.byref(lay)) == OK
+    call = lambda **kw: L.fp4_linear_forward_wq(  # noqa: E731
+        FAKE, FAKE, kw.get("Wq", FAKE), kw.get("sW", FAKE), fp4.FP4_BF16, 64, kw.get("K", 128), 64, 0.99, FAKE,
+        fp4.FP4_BF16, FAKE, kw.get("wsb", lay.total), None)
+    assert call(Wq=None) == ENULL
+    assert call(sW=None) == ENULL
+    assert call(Wq=C.c_void_p(0x100008)) == EALIGN
+    assert call(K=100) == ESHAPE
+    assert call(wsb=lay.total - 1) == EWS
+
+
 def test_quantize_rejects():
     L = fp4.lib()
     c = C.c_void_p

@@ -302,6 +302,30 @@ def test_forward_is_deterministic():
     assert torch.equal(ws1[: lay.scratch], ws2[: lay.scratch])
 
 
+@pytest.mark.parametrize("dtype,M,K,N,q,out", [
+    ("bf16", 300, 512, 264, 0.99, torch.bfloat16),
+    ("fp32", 130, 256, 72, 0.95, torch.float32),
+    ("bf16", 1024, 2048, 1032, 0.9, torch.float32),   # many entries per row: separate 256-column pass
+])
+def test_forward_with_cached_weights(dtype, M, K, N, q, out):
+    """W quantized once (fp4_quantize per column) and reused: the forward on those codes is
+    bit-identical to the forward that quantizes W itself, and both match the oracle."""
+    _say(f"forward_wq {dtype} {M}x{K}x{N} q={q}")
+    A, W = make_custom(M, K, N, dtype=dtype, seed=21)
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    Wq, sW = fp4.quantize_weights(Wd)
+    Y1 = fp4.linear_forward(Ad, Wd, q, out_dtype=out)
+    Y2 = fp4.linear_forward_wq(Ad, Wd, Wq, sW, q, out_dtype=out)
+    torch.cuda.synchronize()
+    bits = torch.int16 if out == torch.bfloat16 else torch.int32
+    assert torch.equal(Y1.view(bits), Y2.view(bits))
+    Anp, Wnp = oracle_inputs(A, W)
+    ref = oracle.forward(Anp, Wnp, q)
+    assert np.array_equal(to_np(Wq), ref["Wq"]) and np.array_equal(to_np(sW), ref["sW"])
+    if out == torch.float32:
+        assert_y_close(to_np(Y2), ref["Y"], ref["denom"])
+
+
 # ----------------------------------------------------------------------------- full sizes
 def _sample_pairs(rng, M, N, row_ptr, count=3000):
     ms = list(rng.integers(0, M, count))
