@@ -30,6 +30,7 @@ from workloads import CONFIGS, make_layer  # noqa: E402
 METRIC = "FP4 quantized-linear TFLOPS & % dense FP4 MFMA peak; quantizer HBM GB/s"
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak (10.1 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak (5.0 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fp4_gemm_llama7b_gate_up.json")
 GEMM_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "gemm.hip")
 
@@ -184,6 +185,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--emu", action="store_true",
+                    help="also time the FP4-on-FP8 emulation of the product (E4M3 expansion + FP8 MFMA) against "
+                         "the native FP4 product on the same codes, both without the dA term")
     ap.add_argument("--wq", default="per-step", choices=["per-step", "cached", "overlap"],
                     help="W quantization: inside every forward (the pages' scheme, default); once before the "
                          "timed steps (fixed inference weights); or on a second stream, each layer's under the "
@@ -348,6 +352,27 @@ def main():
         "wall_s_timed": round(wall, 3),
         "device": torch.cuda.get_device_properties(0).gcnArchName,
     }
+    if args.emu:
+        emu_ms = nat_ms = 0.0
+        for A, W, L, Ad, Wd, ws, Y in runs:
+            it = fp4.forward_intermediates(ws, L.M, L.K, L.N, A.dtype, L.q)
+            common = (fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K)
+            ews = torch.empty(fp4.lib().fp4_gemm_fp8emu_workspace_bytes(L.M, L.N, L.K), dtype=torch.uint8, device=dev)
+            emu = lambda: fp4.lib().fp4_gemm_fp8emu(  # noqa: E731
+                *common, fp4._ptr(Y), fp4._dt(Y), None, fp4._ptr(ews), ews.numel(), fp4._stream(Ad))
+            nat = lambda: fp4.lib().fp4_gemm(  # noqa: E731
+                *common, None, None, None, 0, None, fp4._dt(Wd), fp4._ptr(Y), fp4._dt(Y), None, None, 0,
+                fp4._stream(Ad))
+            emu_ms += time_on_stream(emu, args.steps, 2)
+            nat_ms += time_on_stream(nat, args.steps, 2)
+            del ews
+        out["fp8_emulation"] = {
+            "what": "E2M1 codes expanded to E4M3 bytes, product on the FP8 MFMA (the pages' execution mode); "
+                    "native = the FP4 MFMA on the same codes; both without the dA term",
+            "emulated_ms": round(emu_ms, 4), "native_ms": round(nat_ms, 4),
+            "emulated_TFLOP/s": round(flops / emu_ms / 1e9, 1), "native_TFLOP/s": round(flops / nat_ms / 1e9, 1),
+            "emulated_frac_of_fp8_peak": round(flops / emu_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "speedup_native": round(emu_ms / nat_ms, 3)}
     if not args.no_cpu_baseline:
         A, W, L = runs[0][0], runs[0][1], runs[0][2]
         out["cpu_baseline"] = cpu_baseline(A, W, L)

@@ -147,6 +147,20 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
                     int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *workspace,
                     size_t ws_bytes, void *stream);
 
+/* FP4-on-FP8 emulation of the product (the pages' own execution mode: the QbitAI report's
+ * format paragraph and the topaibox summary's simulation section hold FP4 values in FP8 and
+ * multiply them on FP8 matrix cores).  Aq and Wq (as for fp4_gemm) are expanded to E4M3
+ * bytes, which represent every E2M1 value exactly, into the workspace (M*K + N*K bytes,
+ * fp4_gemm_fp8emu_workspace_bytes), then multiplied on the E4M3 MFMA with fp32
+ * accumulation.  acc and Y are bit-identical to fp4_gemm without a compensation term; the
+ * matrix cores run at half the FP4 rate on twice the operand bytes.  Needs M*K and N*K
+ * below 2^31 besides fp4_gemm's limits.
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
+size_t fp4_gemm_fp8emu_workspace_bytes(int64_t M, int64_t N, int64_t K);
+fp4_status fp4_gemm_fp8emu(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW,
+                           int64_t M, int64_t N, int64_t K, void *Y, int32_t y_dtype,
+                           float *acc_out, void *workspace, size_t ws_bytes, void *stream);
+
 /* Byte offsets of the intermediates inside the fp4_linear_forward workspace, so a caller
  * can read T, the COO list, the codes and the scales after a forward. */
 struct fp4_ws_layout {

@@ -68,6 +68,9 @@ def load(path: str = LIB):
     sig = {
         "orc_e2m1_value": (C.c_double, [i32]),
         "orc_e2m1_encode": (i32, [C.c_float]),
+        "orc_e4m3_value": (C.c_double, [i32]),
+        "orc_e2m1_to_e4m3": (i32, [i32]),
+        "orc_expand_e4m3": (None, [vp, i64, vp]),
         "orc_encode_array": (None, [vp, i64, vp]),
         "orc_quant_rows": (None, [vp, i64, i64, vp, vp]),
         "orc_quant_cols": (None, [vp, i32, i64, i64, vp, vp]),
@@ -114,6 +117,22 @@ def e2m1_encode(y) -> np.ndarray:
     y = np.ascontiguousarray(np.asarray(y, dtype=np.float32)).reshape(-1)
     out = np.empty(y.size, dtype=np.uint8)
     load().orc_encode_array(_p(y), y.size, _p(out))
+    return out
+
+
+def e4m3_value(b: int) -> float:
+    return load().orc_e4m3_value(int(b))
+
+
+def e2m1_to_e4m3(code: int) -> int:
+    return load().orc_e2m1_to_e4m3(int(code))
+
+
+def expand_e4m3(packed: np.ndarray) -> np.ndarray:
+    """Packed E2M1 codes (R x C/2) -> E4M3 bytes (R x C), the FP4-on-FP8 operand form."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
+    load().orc_expand_e4m3(_p(packed), packed.size, _p(out))
     return out
 
 

@@ -18,6 +18,8 @@
  *              outlier clamping and compensation strategy.
  *   [Abstract] "Optimizing Large Language Model Training Using FP4 Quantization",
  *              paper-summary page (shd-paper.top), original English abstract.
+ *   [topaibox] German summary "Microsoft Research bringt den ersten FP4-Genauigkeits-
+ *              rahmen ...", section on FP4 simulation and training methods.
  * Readings taken where the pages are silent are listed next to the code that takes them.
  *
  * Parity pins: every function here is checked by the CPU test-suite against values the
@@ -52,6 +54,46 @@ static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 double orc_e2m1_value(int code) {
     double v = E2M1_MAG[code & 7];
     return (code & 8) ? -v : v;
+}
+
+/* ---------------------------------------------------------------------------------
+ * E4M3 (FP8 with 1 sign bit, 4 exponent bits of bias 7, 3 mantissa bits): the type the
+ * pages' framework holds FP4 values in to multiply them on FP8 tensor cores ([QbitAI],
+ * format paragraph; [topaibox], simulation section).  Exponent field 0 holds the
+ * subnormals m/8 * 2^-6; the pattern with every exponent and mantissa bit set is NaN
+ * (the format has no infinities).
+ * ------------------------------------------------------------------------------- */
+double orc_e4m3_value(int b) {
+    const int sign = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* The E4M3 byte holding the value of E2M1 code `code`, sign included (so +0 -> 0x00 and
+ * -0 -> 0x80), found by searching all 256 bytes; -1 if none (every E2M1 value is
+ * representable, so that is never the answer). */
+int orc_e2m1_to_e4m3(int code) {
+    const double v = orc_e2m1_value(code);
+    const int sign = (code >> 3) & 1;
+    for (int b = 0; b < 256; ++b) {
+        const double w = orc_e4m3_value(b);
+        if (!isnan(w) && w == v && ((b >> 7) & 1) == sign) return b;
+    }
+    return -1;
+}
+
+/* Expand packed E2M1 codes (two per byte, low nibble = even index) to one E4M3 byte per
+ * value, in index order: nbytes in, 2 * nbytes out. */
+void orc_expand_e4m3(const uint8_t *packed, int64_t nbytes, uint8_t *out) {
+    for (int64_t i = 0; i < nbytes; ++i) {
+        out[2 * i] = (uint8_t)orc_e2m1_to_e4m3(packed[i] & 15);
+        out[2 * i + 1] = (uint8_t)orc_e2m1_to_e4m3(packed[i] >> 4);
+    }
 }
 
 /* Round y to the nearest E2M1 value by looking it up in the table ([QbitAI], forward

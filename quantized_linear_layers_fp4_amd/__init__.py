@@ -27,7 +27,7 @@ FP4_PER_ROW, FP4_PER_COL = 0, 1
 EXPORTS = (
     "fp4_quantize", "fp4_outlier_capacity", "fp4_outlier_workspace_bytes", "fp4_outlier_clamp",
     "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_forward_layout", "fp4_forward_workspace_bytes", "fp4_linear_forward",
-    "fp4_linear_forward_wq",
+    "fp4_linear_forward_wq", "fp4_gemm_fp8emu_workspace_bytes", "fp4_gemm_fp8emu",
     "fp4_status_string",
 )
 
@@ -64,6 +64,8 @@ def lib():
         "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, dbl]),
         "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_linear_forward_wq": (i32, [vp, vp, vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
+        "fp4_gemm_fp8emu_workspace_bytes": (sz, [i64, i64, i64]),
+        "fp4_gemm_fp8emu": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]),
         "fp4_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -171,6 +173,23 @@ def gemm(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor,
     _check(lib().fp4_gemm(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, _ptr(row_ptr), _ptr(coo_col),
                           _ptr(coo_val), cap, _ptr(W), wdt, _ptr(Y), _out_dtype_code(out_dtype), _ptr(acc), _ptr(ws),
                           ws.numel() if ws is not None else 0, _stream(Aq)))
+    return (Y, acc) if acc_out else Y
+
+
+def gemm_fp8emu(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, K: int,
+                out_dtype: torch.dtype = torch.bfloat16, acc_out: bool = False, ws: torch.Tensor | None = None):
+    """The product on E4M3 matrix cores after an exact E2M1 -> E4M3 expansion (no dA term)."""
+    _need_cuda(Aq, sA, Wq, sW, ws)
+    M, N = Aq.shape[0], Wq.shape[0]
+    Y = torch.empty((M, N), dtype=out_dtype, device=Aq.device)
+    acc = torch.empty((M, N), dtype=torch.float32, device=Aq.device) if acc_out else None
+    if ws is None:
+        nbytes = lib().fp4_gemm_fp8emu_workspace_bytes(M, N, K)
+        if nbytes == 0:
+            raise Fp4Error("shape out of range for the FP8 emulation")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=Aq.device)
+    _check(lib().fp4_gemm_fp8emu(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, _ptr(Y), _out_dtype_code(out_dtype),
+                                 _ptr(acc), _ptr(ws), ws.numel(), _stream(Aq)))
     return (Y, acc) if acc_out else Y
 
 

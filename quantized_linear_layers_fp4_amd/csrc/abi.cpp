@@ -296,6 +296,38 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
     return hip_status(e);
 }
 
+static bool emu_ok(int64_t M, int64_t N, int64_t K) {
+    // E4M3 operands take K bytes per row; their buffer offsets stay below 2^31
+    return gemm_ok(M, N, K) && M * K <= INT32_MAX && N * K <= INT32_MAX;
+}
+
+size_t fp4_gemm_fp8emu_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!emu_ok(M, N, K)) return 0;
+    return align_up((size_t)M * (size_t)K) + align_up((size_t)N * (size_t)K);
+}
+
+fp4_status fp4_gemm_fp8emu(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
+                           int64_t N, int64_t K, void *Y, int32_t y_dtype, float *acc_out, void *workspace,
+                           size_t ws_bytes, void *stream) {
+    if (!Aq || !sA || !Wq || !sW || !Y || !workspace) return FP4_ERR_NULL;
+    if (!dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
+    if (!emu_ok(M, N, K)) return FP4_ERR_SHAPE;
+    if (ws_bytes < fp4_gemm_fp8emu_workspace_bytes(M, N, K)) return FP4_ERR_WORKSPACE;
+    if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(Y) || !aligned16(workspace) ||
+        (acc_out && !aligned16(acc_out)))
+        return FP4_ERR_ALIGN;
+    int cus;
+    fp4_status st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t *A8 = static_cast<uint8_t *>(workspace);
+    uint8_t *W8 = A8 + align_up((size_t)M * (size_t)K);
+    hipError_t e = launch_e2m1_to_e4m3(Aq, M * (K / 2), A8, s);
+    if (e == hipSuccess) e = launch_e2m1_to_e4m3(Wq, N * (K / 2), W8, s);
+    if (e == hipSuccess) e = launch_gemm(A8, sA, W8, sW, M, N, K, Y, dt_of(y_dtype), acc_out, s, true);
+    return hip_status(e);
+}
+
 fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q,
                               struct fp4_ws_layout *out) {
     if (!out) return FP4_ERR_NULL;

@@ -25,8 +25,12 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
                              uint8_t *codes, bool keys_zeroed, hipStream_t s);
 
 // FP4 GEMM + dequantization: Y = fl(fl(acc * sA) * sW) in y_dt.  acc_out: NULL or fp32[M*N].
+// f8: Aq (M x K) and Wq (N x K) hold E4M3 bytes, one K value each (the emulation path).
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s);
+                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8 = false);
+// E2M1 codes (two per byte, low nibble first) -> E4M3 bytes holding the same values, n_bytes
+// input bytes -> 2 * n_bytes output bytes.
+hipError_t launch_e2m1_to_e4m3(const uint8_t *codes, int64_t n_bytes, uint8_t *out, hipStream_t s);
 // Y = Y_main + dA . W, accumulated in fp32 in ascending k from Y_main, rounded once to y_dt.
 // Y_main and Y may be the same fp32 buffer.  capacity: what the dA list was sized for (picks
 // the kernel shape only; 0 if unknown).

@@ -97,6 +97,39 @@ __device__ __forceinline__ void frag_load(const uint8_t *buf, int wm, int wn, in
         b[j] = *reinterpret_cast<const u32x4 *>(buf + OPA + slot16(wn * 64 + j * 32 + (lane & 31), chunk) * 16);
 }
 
+// FP8 operands (the emulation path): lane l reads row l%32 and the two 16-byte chunks
+// 2*(l/32), 2*(l/32)+1 (32 consecutive K values, one per byte) of the stage's one K-step.
+__device__ __forceinline__ void frag_load8(const uint8_t *buf, int wm, int wn, int lane, u32x4 (&a)[4][2],
+                                           u32x4 (&b)[2][2]) {
+    const int chunk = 2 * (lane >> 5);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i][h] = *reinterpret_cast<const u32x4 *>(buf + slot16(wm * 128 + i * 32 + (lane & 31), chunk + h) * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            b[j][h] =
+                *reinterpret_cast<const u32x4 *>(buf + OPA + slot16(wn * 64 + j * 32 + (lane & 31), chunk + h) * 16);
+    }
+}
+
+// The same tile product on E4M3 operands (format code 0): 32 bytes per lane and MFMA.
+__device__ __forceinline__ void mfma_block8(v16f (&acc)[4][2], const u32x4 (&a)[4][2], const u32x4 (&b)[2][2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const v8i av = v8i{(int)a[i][0].x, (int)a[i][0].y, (int)a[i][0].z, (int)a[i][0].w,
+                           (int)a[i][1].x, (int)a[i][1].y, (int)a[i][1].z, (int)a[i][1].w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const v8i bv = v8i{(int)b[j][0].x, (int)b[j][0].y, (int)b[j][0].z, (int)b[j][0].w,
+                               (int)b[j][1].x, (int)b[j][1].y, (int)b[j][1].z, (int)b[j][1].w};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, UNIT_SCALE, 0,
+                                                                        UNIT_SCALE);
+        }
+    }
+}
+
 __device__ __forceinline__ void mfma_block(v16f (&acc)[4][2], const u32x4 (&a)[4], const u32x4 (&b)[2]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -122,7 +155,8 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int YDT, bool ACCOUT, bool KFULL>
+// F8: the operands are E4M3 bytes (one K value per byte) instead of packed E2M1 codes.
+template <int YDT, bool ACCOUT, bool KFULL, bool F8>
 __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sb0[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb1[STB];
@@ -146,7 +180,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     const int m0 = (first_m + in_group % gm) * BM;
     const int n0 = (in_group / gm) * BN;
 
-    const int KB = K / 2;
+    const int KB = F8 ? K : K / 2;  // operand bytes per row
     const int kstages = (KB + BKB - 1) / BKB;
     const __amdgpu_buffer_rsrc_t rsA =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.Aq), 0, M * KB, BUF_FLAGS);
@@ -192,6 +226,19 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     // kt+2, reads the K-step-1 fragments under the first eight MFMAs, runs the second
     // eight, and waits for its own loads of stage kt+1 before the barrier that ends it.
     auto step = [&](int kt, const uint8_t *cur, uint8_t *ahead) {
+        if constexpr (F8) {  // one K-step of 64 values per stage
+            u32x4 a8[4][2], b8[2][2];
+            __builtin_amdgcn_sched_barrier(0);
+            frag_load8(cur, wm, wn, lane, a8, b8);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_dma<KFULL>(rsA, rsB, ahead, wave, offA, offB, kt + 2, KB, lane_chunk16);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_block8(acc, a8, b8);
+            __builtin_amdgcn_sched_barrier(0);
+            WAIT_VMCNT(6);
+            lds_barrier();
+            return;
+        }
         u32x4 a0[4], b0[2], a1[4], b1[2];
         __builtin_amdgcn_sched_barrier(0);
         frag_load(cur, wm, wn, lane, 0, a0, b0);
@@ -327,7 +374,7 @@ static int raster_group_for(int tilesM) {
 }
 
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s) {
+                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8) {
     TileArgs p;
     p.Aq = Aq;
     p.Wq = Wq;
@@ -343,19 +390,28 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
     p.raster_group = raster_group_for(p.tilesM);
     const int64_t tiles = (int64_t)p.tilesM * p.tilesN;
     const int blocks = (int)((tiles + 7) / 8 * 8);
-#define G(YD, AO)                                                                                  \
-    do {                                                                                           \
-        if (K % 128 == 0) hipLaunchKernelGGL((k_fp4_gemm<YD, AO, true>), dim3(blocks), dim3(NT), 0, s, p); \
-        else hipLaunchKernelGGL((k_fp4_gemm<YD, AO, false>), dim3(blocks), dim3(NT), 0, s, p);             \
+    const bool kfull = f8 ? (K % 64 == 0) : (K % 128 == 0);  // every stage whole
+#define G3(YD, AO, KF, F) hipLaunchKernelGGL((k_fp4_gemm<YD, AO, KF, F>), dim3(blocks), dim3(NT), 0, s, p)
+#define G2(YD, AO, F)                        \
+    do {                                     \
+        if (kfull) G3(YD, AO, true, F);      \
+        else G3(YD, AO, false, F);           \
+    } while (0)
+#define G1(YD, AO)                  \
+    do {                            \
+        if (f8) G2(YD, AO, true);   \
+        else G2(YD, AO, false);     \
     } while (0)
     if (y_dt == DT_BF16) {
-        if (acc_out) G(DT_BF16, true);
-        else G(DT_BF16, false);
+        if (acc_out) G1(DT_BF16, true);
+        else G1(DT_BF16, false);
     } else {
-        if (acc_out) G(DT_F32, true);
-        else G(DT_F32, false);
+        if (acc_out) G1(DT_F32, true);
+        else G1(DT_F32, false);
     }
-#undef G
+#undef G1
+#undef G2
+#undef G3
     return hipGetLastError();
 }
 

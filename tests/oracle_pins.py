@@ -25,6 +25,8 @@ from __future__ import annotations
 
 from fractions import Fraction
 
+import math
+
 import numpy as np
 import torch
 
@@ -411,6 +413,41 @@ def pin_bf16_rounding():
     y = np.random.default_rng(5).standard_normal(10000).astype(np.float32)
     assert np.array_equal(oracle.to_bf16(y),
                           torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+# ----------------------------------------------------------------------------- FP4 held in FP8
+# E4M3 values at fixed bit patterns, from the format's definition (bias 7, subnormals at
+# exponent field 0, the all-ones pattern NaN, largest finite 448).
+E4M3_KNOWN = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0, 0x3C: 1.5,
+              0x40: 2.0, 0x44: 3.0, 0x48: 4.0, 0x4C: 6.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+
+
+def pin_e4m3_known_values():
+    for b, v in E4M3_KNOWN.items():
+        assert oracle.e4m3_value(b) == v, hex(b)
+    assert math.copysign(1.0, oracle.e4m3_value(0x80)) == -1.0 and oracle.e4m3_value(0x80) == 0.0
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+
+
+def pin_e4m3_monotone_and_symmetric():
+    pos = [oracle.e4m3_value(b) for b in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))
+    assert all(oracle.e4m3_value(0x80 | b) == -pos[b] for b in range(0x7F))
+
+
+def pin_e2m1_held_in_e4m3():
+    # every E2M1 value, sign included, has an exact E4M3 byte
+    for c in range(16):
+        b = oracle.e2m1_to_e4m3(c)
+        assert 0 <= b < 256, c
+        assert oracle.e4m3_value(b) == e2m1_closed_form(c), c
+        assert (b >> 7) == (c >> 3), c  # -0 stays -0
+
+
+def pin_expand_e4m3_order():
+    # low nibble first: byte 0x71 holds 0.5 (code 1) then 6 (code 7)
+    got = oracle.expand_e4m3(np.array([[0x71, 0x8F]], dtype=np.uint8))
+    assert got.tolist() == [[0x30, 0x4C, 0xCC, 0x80]]
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -18,7 +18,7 @@ FAKE = C.c_void_p(0x100000)  # aligned, never dereferenced: validation fails fir
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(fp4_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fp4_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_exports():

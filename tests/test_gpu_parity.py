@@ -195,6 +195,41 @@ def test_gemm_accumulator_exact(M, N, K):
     assert np.array_equal(to_np(Y), ref_y)  # no compensation: the dequantized product is bit-exact
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 264, 320), (513, 776, 1056), (64, 8, 32), (257, 136, 96)])
+def test_gemm_fp8_emulation(M, N, K):
+    """FP4 codes expanded to E4M3 and multiplied on the FP8 matrix cores: the accumulator
+    is the oracle's exact sum and Y is bit-identical to the native FP4 product (fp32 and
+    bf16 outputs).  K = 96 and 1056 leave a partial last stage."""
+    _say(f"gemm fp8 emulation {M}x{N}x{K}")
+    rng = np.random.default_rng(M * N + K + 1)
+    Aq, Wq = _random_codes(rng, M, K), _random_codes(rng, N, K)
+    sA = rng.lognormal(-2, 1, M).astype(np.float32)
+    sW = rng.lognormal(-4, 1, N).astype(np.float32)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    Y8, acc8 = fp4.gemm_fp8emu(t(Aq), t(sA), t(Wq), t(sW), K, out_dtype=torch.float32, acc_out=True)
+    Y4 = fp4.gemm(t(Aq), t(sA), t(Wq), t(sW), K, out_dtype=torch.float32)
+    Yb8 = fp4.gemm_fp8emu(t(Aq), t(sA), t(Wq), t(sW), K, out_dtype=torch.bfloat16)
+    Yb4 = fp4.gemm(t(Aq), t(sA), t(Wq), t(sW), K, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(acc8), oracle.accumulate(Aq, Wq, K))
+    assert torch.equal(Y8.view(torch.int32), Y4.view(torch.int32))
+    assert torch.equal(Yb8.view(torch.int16), Yb4.view(torch.int16))
+
+
+def test_gemm_fp8_emulation_full_size():
+    """The same identity on the gate+up shape's own codes (M=16384, K=4096, N=22016)."""
+    _say("gemm fp8 emulation llama7b_gate_up")
+    A, W, L = make_layer(3, 0)
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    ws = fp4.workspace(Ad, L.N, L.q)
+    fp4.linear_forward(Ad, Wd, L.q, ws=ws)
+    it = fp4.forward_intermediates(ws, L.M, L.K, L.N, A.dtype, L.q)
+    Y8 = fp4.gemm_fp8emu(it["Aq"], it["sA"], it["Wq"], it["sW"], L.K, out_dtype=torch.bfloat16)
+    Y4 = fp4.gemm(it["Aq"], it["sA"], it["Wq"], it["sW"], L.K, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(Y8.view(torch.int16), Y4.view(torch.int16))
+
+
 def test_gemm_accumulator_extremes():
     # every product +-36 over the longest K: |acc| = 36 * 65536, still exact in fp32
     M, N, K = 40, 24, 65536

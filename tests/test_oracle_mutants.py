@@ -34,6 +34,10 @@ MUTANTS = {
     "epilogue_drops_row_scale": ("float t = acc * sa;", "float t = acc;"),
     "compensation_transposed_w": ("(int64_t)coo_col[e] * N + n", "(int64_t)n * N + coo_col[e]"),
     "compensation_dropped": ("d += t;", "d += 0.0 * t;"),
+    "e4m3_bias_8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3_subnormal_scale": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
+    "expand_nibbles_swapped": ("out[2 * i] = (uint8_t)orc_e2m1_to_e4m3(packed[i] & 15);",
+                               "out[2 * i] = (uint8_t)orc_e2m1_to_e4m3(packed[i] >> 4);"),
     "col_scale_per_tensor": ("for (int64_t n = 0; n < N; ++n) vector_scale(amax[n], &r[n], &scales[n]);",
                              "for (int64_t n = 1; n < N; ++n) if (amax[n] > amax[0]) amax[0] = amax[n];\n"
                              "    for (int64_t n = 0; n < N; ++n) vector_scale(amax[0], &r[n], &scales[n]);"),
