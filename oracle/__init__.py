@@ -71,6 +71,10 @@ def load(path: str = LIB):
         "orc_e4m3_value": (C.c_double, [i32]),
         "orc_e2m1_to_e4m3": (i32, [i32]),
         "orc_expand_e4m3": (None, [vp, i64, vp]),
+        "orc_e4m3_encode": (i32, [C.c_float]),
+        "orc_e4m3_encode_array": (None, [vp, i64, vp]),
+        "orc_fp8_quantize": (None, [vp, i32, i64, vp, vp]),
+        "orc_fp8_dequantize": (None, [vp, i64, C.c_float, vp]),
         "orc_encode_array": (None, [vp, i64, vp]),
         "orc_quant_rows": (None, [vp, i64, i64, vp, vp]),
         "orc_quant_cols": (None, [vp, i32, i64, i64, vp, vp]),
@@ -133,6 +137,29 @@ def expand_e4m3(packed: np.ndarray) -> np.ndarray:
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
     load().orc_expand_e4m3(_p(packed), packed.size, _p(out))
+    return out
+
+
+def e4m3_encode(y) -> np.ndarray:
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float32)).reshape(-1)
+    out = np.empty(y.size, dtype=np.uint8)
+    load().orc_e4m3_encode_array(_p(y), y.size, _p(out))
+    return out
+
+
+def fp8_quantize(X: np.ndarray) -> tuple[np.ndarray, float]:
+    """FP8 (E4M3) gradient codec, per-tensor scale: (codes u8[n], s)."""
+    X = np.ascontiguousarray(X).reshape(-1)
+    codes = np.empty(X.size, dtype=np.uint8)
+    s = np.zeros(1, dtype=np.float32)
+    load().orc_fp8_quantize(_p(X), _dtype_code(X), X.size, _p(codes), _p(s))
+    return codes, float(s[0])
+
+
+def fp8_dequantize(codes: np.ndarray, s: float) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+    out = np.empty(codes.size, dtype=np.float32)
+    load().orc_fp8_dequantize(_p(codes), codes.size, float(np.float32(s)), _p(out))
     return out
 
 

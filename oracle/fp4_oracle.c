@@ -96,6 +96,57 @@ void orc_expand_e4m3(const uint8_t *packed, int64_t nbytes, uint8_t *out) {
     }
 }
 
+/* ---------------------------------------------------------------------------------
+ * FP8 gradient codec: the quantize/dequantize half of the pages' FP8 gradient
+ * communication ([QbitAI] and [Abstract]: gradients are exchanged in FP8; the pages give
+ * no scaling rule).
+ * Readings, chosen to mirror the FP4 path: per-tensor absmax scaling, multiplier
+ * r = fl(448 / amax) and dequantization scale s = fl(amax / 448) in fp32 (448 = the
+ * largest finite E4M3 value), amax < 2^-120 gives r = s = 0; y = fl(g * r) is rounded to
+ * the nearest E4M3 value with ties to the even mantissa, |y| > 448 saturates to 448 (no
+ * NaN is ever produced), and the sign is copied (-0 -> 0x80).  Dequantization is
+ * fl(value(code) * s).
+ * ------------------------------------------------------------------------------- */
+int orc_e4m3_encode(float y) {
+    double u = fabs((double)y);
+    if (u > 448.0) u = 448.0;
+    int best = 0;
+    double best_d = u;  /* distance to code 0 */
+    for (int b = 1; b < 0x7F; ++b) {  /* the finite positive codes, ascending in value */
+        const double d = fabs(u - orc_e4m3_value(b));
+        if (d < best_d || (d == best_d && (b & 1) == 0)) {
+            best = b;
+            best_d = d;
+        }
+    }
+    return (signbit(y) ? 0x80 : 0) | best;
+}
+
+void orc_e4m3_encode_array(const float *y, int64_t n, uint8_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_e4m3_encode(y[i]);
+}
+
+/* codes[i] = E4M3(fl(x[i] * r)) for n elements of X (fp32 or bf16); *scale = s. */
+void orc_fp8_quantize(const void *X, int dtype, int64_t n, uint8_t *codes, float *scale) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        const float v = fabsf(load_elem(X, dtype, i));
+        if (v > amax) amax = v;
+    }
+    float r = 0.0f, s = 0.0f;
+    if ((double)amax >= 7.52316384526264e-37) { /* 2^-120 */
+        r = 448.0f / amax;
+        s = amax / 448.0f;
+    }
+    for (int64_t i = 0; i < n; ++i) codes[i] = (uint8_t)orc_e4m3_encode(load_elem(X, dtype, i) * r);
+    *scale = s;
+}
+
+/* out[i] = fl(value(codes[i]) * s) in fp32. */
+void orc_fp8_dequantize(const uint8_t *codes, int64_t n, float s, float *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = (float)orc_e4m3_value(codes[i]) * s;
+}
+
 /* Round y to the nearest E2M1 value by looking it up in the table ([QbitAI], forward
  * quantization paragraph: nearest FP4 value by table lookup).
  * Reading: at equal distance the entry with mantissa bit 0 (even index) wins, which is

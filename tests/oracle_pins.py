@@ -450,4 +450,57 @@ def pin_expand_e4m3_order():
     assert got.tolist() == [[0x30, 0x4C, 0xCC, 0x80]]
 
 
+# ----------------------------------------------------------------------------- FP8 gradient codec
+def _e4m3_sweep_points(rng):
+    vals = np.array([oracle.e4m3_value(b) for b in range(0x7F)], dtype=np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids]).astype(np.float32)
+    up = np.nextafter(pts, np.float32(np.inf))
+    dn = np.nextafter(pts, np.float32(0))
+    rnd = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 200000)).astype(np.float32)
+    x = np.concatenate([pts, up, dn, rnd, np.float32(448.0)[None]])
+    x = x[(x >= 0) & (x <= 448)]
+    return np.concatenate([x, -x])
+
+
+def pin_e4m3_encoder_vs_library():
+    # torch's float8_e4m3fn cast is round-to-nearest-even on the same grid (it produces NaN
+    # instead of saturating above 448, so the sweep stays within range)
+    x = _e4m3_sweep_points(np.random.default_rng(71))
+    got = oracle.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def pin_e4m3_round_trip_and_saturation():
+    for b in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        assert oracle.e4m3_encode([oracle.e4m3_value(b)])[0] == b, hex(b)
+    assert oracle.e4m3_encode([449.0, 1e30, -464.0, -1e30]).tolist() == [0x7E, 0x7E, 0xFE, 0xFE]
+
+
+def pin_fp8_quantize_scale_and_error():
+    rng = np.random.default_rng(72)
+    g = (rng.standard_t(3, 50000) * 1e-3).astype(np.float32)
+    codes, s = oracle.fp8_quantize(g)
+    amax = np.float32(np.abs(g).max())
+    assert s == np.float32(amax / np.float32(448.0))
+    assert (codes & 0x7F).max() == 0x7E  # the largest magnitude maps onto 448
+    back = oracle.fp8_dequantize(codes, s)
+    # each value within half an E4M3 spacing (relative 2^-4, absolute 2^-10 below 2^-6) of g*r
+    r = np.float32(448.0) / amax
+    y = np.abs(g.astype(np.float64) * r)
+    half = np.maximum(2.0 ** -10, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 4))
+    assert np.all(np.abs(back.astype(np.float64) - g.astype(np.float64)) <= (half + 1e-6 * y) * s * 1.0001)
+
+
+def pin_fp8_zero_and_bf16():
+    codes, s = oracle.fp8_quantize(np.array([0.0, -0.0, 0.0], dtype=np.float32))
+    assert s == 0.0 and codes.tolist() == [0x00, 0x80, 0x00]
+    # bf16 input (as its bit patterns): amax 448 gives r = s = 1, so the codes are the
+    # values' own E4M3 bytes
+    x = torch.tensor([1.0, -3.5, 448.0, 2.0 ** -9], dtype=torch.bfloat16)
+    codes, s = oracle.fp8_quantize(x.view(torch.int16).numpy().view(np.uint16))
+    assert s == 1.0 and codes.tolist() == [0x38, 0xC6, 0x7E, 0x01]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -38,6 +38,11 @@ MUTANTS = {
     "e4m3_subnormal_scale": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
     "expand_nibbles_swapped": ("out[2 * i] = (uint8_t)orc_e2m1_to_e4m3(packed[i] & 15);",
                                "out[2 * i] = (uint8_t)orc_e2m1_to_e4m3(packed[i] >> 4);"),
+    "e4m3_tie_to_odd": ("if (d < best_d || (d == best_d && (b & 1) == 0)) {",
+                        "if (d < best_d || (d == best_d && (b & 1) == 1)) {"),
+    "e4m3_drops_largest_code": ("for (int b = 1; b < 0x7F; ++b) {  /* the finite positive codes",
+                                "for (int b = 1; b < 0x7E; ++b) {  /* the finite positive codes"),
+    "fp8_scale_inverted": ("s = amax / 448.0f;", "s = 448.0f / amax;"),
     "col_scale_per_tensor": ("for (int64_t n = 0; n < N; ++n) vector_scale(amax[n], &r[n], &scales[n]);",
                              "for (int64_t n = 1; n < N; ++n) if (amax[n] > amax[0]) amax[0] = amax[n];\n"
                              "    for (int64_t n = 0; n < N; ++n) vector_scale(amax[0], &r[n], &scales[n]);"),
