@@ -178,6 +178,32 @@ def run_copy(steps: int):
     print(json.dumps({"copy_bytes": 1 << 30, "ms_per_copy": ms, "GB/s_read+write": 2 * (1 << 30) / ms / 1e6}))
 
 
+def run_fp8codec(steps: int, warmup: int):
+    """FP8 (E4M3) gradient codec on a gradient the size of the 7B gate+up weight (4096 x 22016
+    bf16, seeded Student-t(3) x 1e-4): quantize (amax pass + encode pass; X read twice) and
+    dequantize to bf16.  HBM-bound: algorithmic bytes / time against 8 TB/s."""
+    n = 4096 * 22016
+    rng = np.random.default_rng(20250128)
+    g = torch.from_numpy((rng.standard_t(3, n) * 1e-4).astype(np.float32)).to(torch.bfloat16).to("cuda")
+    codes = torch.empty(n, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(fp4.lib().fp4_fp8_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    y = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    st = fp4._stream(g)
+    q = lambda: fp4.lib().fp4_fp8_quantize(fp4._ptr(g), fp4.FP4_BF16, n, fp4._ptr(codes), fp4._ptr(scale),  # noqa
+                                           fp4._ptr(ws), ws.numel(), st)
+    d = lambda: fp4.lib().fp4_fp8_dequantize(fp4._ptr(codes), n, fp4._ptr(scale), fp4._ptr(y), fp4.FP4_BF16, st)  # noqa
+    ms_q = time_on_stream(q, steps, warmup)
+    ms_d = time_on_stream(d, steps, warmup)
+    bq, bd = 2 * n * 2 + n, n + n * 2
+    print(json.dumps({
+        "metric": "FP8 gradient codec GB/s", "workload": "gradient of llama7b gate+up weight, 4096x22016 bf16",
+        "quantize": {"ms": round(ms_q, 4), "algorithmic_bytes": bq, "GB/s": round(bq / ms_q / 1e6, 1),
+                     "frac_of_hbm_peak": round(bq / ms_q / 1e6 / PEAK_HBM_GBS, 4)},
+        "dequantize": {"ms": round(ms_d, 4), "algorithmic_bytes": bd, "GB/s": round(bd / ms_d / 1e6, 1),
+                       "frac_of_hbm_peak": round(bd / ms_d / 1e6 / PEAK_HBM_GBS, 4)}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,7 +218,7 @@ def main():
                     help="W quantization: inside every forward (the pages' scheme, default); once before the "
                          "timed steps (fixed inference weights); or on a second stream, each layer's under the "
                          "previous layer's forward")
-    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic"])
+    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic", "fp8codec"])
     ap.add_argument("--traffic-dirs", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="--mode traffic: rocprofv3 --pmc output directories of FETCH_SIZE and WRITE_SIZE for "
                          "the full bench and for --mode copy")
@@ -207,6 +233,9 @@ def main():
     torch.cuda.set_device(0)
     if args.mode == "copy":
         run_copy(args.steps)
+        return
+    if args.mode == "fp8codec":
+        run_fp8codec(args.steps, args.warmup)
         return
 
     layers = [make_layer(args.config, li) for li in range(len(CONFIGS[args.config]))]

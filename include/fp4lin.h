@@ -147,6 +147,24 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
                     int32_t w_dtype, void *Y, int32_t y_dtype, float *acc_out, void *workspace,
                     size_t ws_bytes, void *stream);
 
+/* FP8 (E4M3) gradient codec: the single-GPU quantize/dequantize half of the FP8 gradient
+ * communication that the QbitAI report and the paper abstract pair with FP4 training (the
+ * pages give no scaling rule).  Readings: one per-tensor scale from amax = max |x|,
+ * multiplier r = fl(448 / amax), dequantization scale s = fl(amax / 448) (both 0 when
+ * amax < 2^-120); code = E4M3(fl(x * r)), nearest with ties to the even mantissa,
+ * saturating at 448 (never NaN), sign kept; dequantization fl(value(code) * s).
+ *   fp4_fp8_quantize:   X n elements of x_dtype (in); codes u8[n] (out); scale device
+ *                       fp32[1] (out, s); workspace >= fp4_fp8_workspace_bytes() bytes.
+ *   fp4_fp8_dequantize: codes u8[n] and scale fp32[1] (in); Y n elements of y_dtype
+ *                       (out; bf16 = round-to-nearest-even of the fp32 value).
+ * 1 <= n <= 2^40; X, codes, Y and workspace 16-byte aligned.
+ * Return FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
+size_t fp4_fp8_workspace_bytes(void);
+fp4_status fp4_fp8_quantize(const void *X, int32_t x_dtype, int64_t n, uint8_t *codes, float *scale,
+                            void *workspace, size_t ws_bytes, void *stream);
+fp4_status fp4_fp8_dequantize(const uint8_t *codes, int64_t n, const float *scale, void *Y,
+                              int32_t y_dtype, void *stream);
+
 /* FP4-on-FP8 emulation of the product (the pages' own execution mode: the QbitAI report's
  * format paragraph and the topaibox summary's simulation section hold FP4 values in FP8 and
  * multiply them on FP8 matrix cores).  Aq and Wq (as for fp4_gemm) are expanded to E4M3

@@ -28,6 +28,7 @@ EXPORTS = (
     "fp4_quantize", "fp4_outlier_capacity", "fp4_outlier_workspace_bytes", "fp4_outlier_clamp",
     "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_forward_layout", "fp4_forward_workspace_bytes", "fp4_linear_forward",
     "fp4_linear_forward_wq", "fp4_gemm_fp8emu_workspace_bytes", "fp4_gemm_fp8emu",
+    "fp4_fp8_workspace_bytes", "fp4_fp8_quantize", "fp4_fp8_dequantize",
     "fp4_status_string",
 )
 
@@ -65,6 +66,9 @@ def lib():
         "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_linear_forward_wq": (i32, [vp, vp, vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_gemm_fp8emu_workspace_bytes": (sz, [i64, i64, i64]),
+        "fp4_fp8_workspace_bytes": (sz, []),
+        "fp4_fp8_quantize": (i32, [vp, i32, i64, vp, vp, vp, sz, vp]),
+        "fp4_fp8_dequantize": (i32, [vp, i64, vp, vp, i32, vp]),
         "fp4_gemm_fp8emu": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]),
         "fp4_status_string": (C.c_char_p, [i32]),
     }
@@ -191,6 +195,25 @@ def gemm_fp8emu(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.
     _check(lib().fp4_gemm_fp8emu(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, _ptr(Y), _out_dtype_code(out_dtype),
                                  _ptr(acc), _ptr(ws), ws.numel(), _stream(Aq)))
     return (Y, acc) if acc_out else Y
+
+
+def fp8_quantize(X: torch.Tensor):
+    """FP8 (E4M3) gradient codec: (codes u8[n], scale fp32[1]) with one per-tensor scale."""
+    _need_cuda(X)
+    n = X.numel()
+    codes = torch.empty(n, dtype=torch.uint8, device=X.device)
+    scale = torch.empty(1, dtype=torch.float32, device=X.device)
+    ws = torch.empty(lib().fp4_fp8_workspace_bytes(), dtype=torch.uint8, device=X.device)
+    _check(lib().fp4_fp8_quantize(_ptr(X), _dt(X), n, _ptr(codes), _ptr(scale), _ptr(ws), ws.numel(), _stream(X)))
+    return codes, scale
+
+
+def fp8_dequantize(codes: torch.Tensor, scale: torch.Tensor, out_dtype: torch.dtype = torch.float32):
+    _need_cuda(codes, scale)
+    Y = torch.empty(codes.numel(), dtype=out_dtype, device=codes.device)
+    _check(lib().fp4_fp8_dequantize(_ptr(codes), codes.numel(), _ptr(scale), _ptr(Y), _out_dtype_code(out_dtype),
+                                    _stream(codes)))
+    return Y
 
 
 def forward_layout(M: int, K: int, N: int, dtype: torch.dtype, q: float) -> WsLayout:

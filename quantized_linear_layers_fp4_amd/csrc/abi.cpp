@@ -12,6 +12,9 @@
 
 using namespace fp4;
 
+// Element limit of the FP8 codec (its chunk indices stay far from int64 overflow).
+constexpr int64_t FP8_MAX_N = (int64_t)1 << 40;
+
 namespace {
 
 constexpr int64_t K_MAX = 65536;
@@ -294,6 +297,35 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
         e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype),
                         capacity > 0 ? capacity : 0, s);
     return hip_status(e);
+}
+
+size_t fp4_fp8_workspace_bytes(void) { return ALIGN; }
+
+fp4_status fp4_fp8_quantize(const void *X, int32_t x_dtype, int64_t n, uint8_t *codes, float *scale, void *workspace,
+                            size_t ws_bytes, void *stream) {
+    if (!X || !codes || !scale || !workspace) return FP4_ERR_NULL;
+    if (!dtype_ok(x_dtype)) return FP4_ERR_DTYPE;
+    if (n < 1 || n > FP8_MAX_N) return FP4_ERR_SHAPE;
+    if (ws_bytes < fp4_fp8_workspace_bytes()) return FP4_ERR_WORKSPACE;
+    if (!aligned16(X) || !aligned16(codes) || !aligned16(workspace)) return FP4_ERR_ALIGN;
+    int cus;
+    fp4_status st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    return hip_status(launch_fp8_quantize(X, dt_of(x_dtype), n, static_cast<uint32_t *>(workspace), codes, scale, cus,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+fp4_status fp4_fp8_dequantize(const uint8_t *codes, int64_t n, const float *scale, void *Y, int32_t y_dtype,
+                              void *stream) {
+    if (!codes || !scale || !Y) return FP4_ERR_NULL;
+    if (!dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
+    if (n < 1 || n > FP8_MAX_N) return FP4_ERR_SHAPE;
+    if (!aligned16(codes) || !aligned16(Y)) return FP4_ERR_ALIGN;
+    int cus;
+    fp4_status st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    return hip_status(launch_fp8_dequantize(codes, n, scale, Y, dt_of(y_dtype), cus,
+                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
 static bool emu_ok(int64_t M, int64_t N, int64_t K) {

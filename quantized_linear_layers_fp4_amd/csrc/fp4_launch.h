@@ -28,6 +28,11 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
 // f8: Aq (M x K) and Wq (N x K) hold E4M3 bytes, one K value each (the emulation path).
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
                        int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8 = false);
+// FP8 (E4M3) gradient codec, one per-tensor scale.  key: device u32 scratch (zeroed here).
+hipError_t launch_fp8_quantize(const void *X, int dt, int64_t n, uint32_t *key, uint8_t *codes, float *scale,
+                               int num_cus, hipStream_t s);
+hipError_t launch_fp8_dequantize(const uint8_t *codes, int64_t n, const float *scale, void *Y, int y_dt, int num_cus,
+                                 hipStream_t s);
 // E2M1 codes (two per byte, low nibble first) -> E4M3 bytes holding the same values, n_bytes
 // input bytes -> 2 * n_bytes output bytes.
 hipError_t launch_e2m1_to_e4m3(const uint8_t *codes, int64_t n_bytes, uint8_t *out, hipStream_t s);

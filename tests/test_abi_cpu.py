@@ -107,6 +107,26 @@ def test_linear_forward_wq_rejects():
     assert call(wsb=lay.total - 1) == EWS
 
 
+def test_fp8_codec_rejects():
+    L = fp4.lib()
+    wsb = L.fp4_fp8_workspace_bytes()
+    assert wsb >= 4
+    q = lambda **kw: L.fp4_fp8_quantize(kw.get("X", FAKE), kw.get("dt", 1), kw.get("n", 100), FAKE, FAKE,  # noqa
+                                        kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert q(X=None) == ENULL
+    assert q(dt=2) == EDTYPE
+    assert q(n=0) == ESHAPE
+    assert q(n=(1 << 40) + 1) == ESHAPE
+    assert q(wsb=wsb - 1) == EWS
+    assert q(X=C.c_void_p(0x100004)) == EALIGN
+    d = lambda **kw: L.fp4_fp8_dequantize(FAKE, kw.get("n", 100), FAKE, kw.get("Y", FAKE),  # noqa
+                                          kw.get("dt", 0), None)
+    assert d(Y=None) == ENULL
+    assert d(dt=9) == EDTYPE
+    assert d(n=-1) == ESHAPE
+    assert d(Y=C.c_void_p(0x100002)) == EALIGN
+
+
 def test_quantize_rejects():
     L = fp4.lib()
     c = C.c_void_p

@@ -361,6 +361,71 @@ def test_forward_with_cached_weights(dtype, M, K, N, q, out):
         assert_y_close(to_np(Y2), ref["Y"], ref["denom"])
 
 
+# ----------------------------------------------------------------------------- FP8 gradient codec
+def test_fp8_encoder_sweep():
+    """With amax = 448 the multiplier is exactly 1, so the codes are the encoder itself on
+    every E4M3 value, every midpoint, their fp32 neighbours and random points."""
+    _say("fp8 encoder sweep")
+    rng = np.random.default_rng(81)
+    vals = np.array([oracle.e4m3_value(b) for b in range(0x7F)], dtype=np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([vals.astype(np.float32), mids])
+    pts = np.concatenate([pts, np.nextafter(pts, np.float32(np.inf)), np.nextafter(pts, np.float32(0)),
+                          np.exp(rng.uniform(np.log(2.0 ** -14), np.log(448.0), 300000)).astype(np.float32)])
+    pts = np.clip(pts, 0, 448).astype(np.float32)
+    x = np.concatenate([pts, -pts, np.float32([448.0, -0.0, 0.0])]).astype(np.float32)
+    codes, scale = fp4.fp8_quantize(torch.from_numpy(x).to(DEV))
+    assert to_np(scale)[0] == 1.0
+    assert np.array_equal(to_np(codes), oracle.e4m3_encode(x))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("n,kind", [(1, "normal"), (7, "normal"), (8, "t"), (1000, "t"), ((1 << 20) + 3, "t"),
+                                    (4096, "zeros"), (65536, "tiny")])
+def test_fp8_codec(dtype, n, kind):
+    """Codes, the per-tensor scale and both dequantized outputs bit-exact against the oracle."""
+    _say(f"fp8 codec {dtype} n={n} {kind}")
+    rng = np.random.default_rng(n + len(kind))
+    if kind == "normal":
+        x = rng.standard_normal(n).astype(np.float32)
+    elif kind == "t":
+        x = (rng.standard_t(3, n) * 1e-3).astype(np.float32)
+    elif kind == "zeros":
+        x = np.zeros(n, dtype=np.float32)
+        x[::3] = -0.0
+    else:
+        x = (rng.standard_normal(n) * 1e-38).astype(np.float32)  # amax below 2^-120: scale 0
+    t = torch.from_numpy(x)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    xin = t.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else x
+    codes, scale = fp4.fp8_quantize(t.to(DEV))
+    ref_codes, ref_s = oracle.fp8_quantize(xin)
+    assert to_np(scale)[0] == np.float32(ref_s)
+    assert np.array_equal(to_np(codes), ref_codes)
+    ref_y = oracle.fp8_dequantize(ref_codes, ref_s)
+    y32 = fp4.fp8_dequantize(codes, scale, torch.float32)
+    y16 = fp4.fp8_dequantize(codes, scale, torch.bfloat16)
+    assert np.array_equal(to_np(y32).view(np.uint32), ref_y.view(np.uint32))
+    assert np.array_equal(to_np(y16.view(torch.int16)).view(np.uint16), oracle.to_bf16(ref_y))
+
+
+def test_fp8_codec_full_size():
+    """A gradient the size of the 7B gate+up weight (4096 x 22016 bf16): the scale exactly,
+    the codes at sampled positions, and decode(encode) within half an E4M3 spacing."""
+    _say("fp8 codec 4096x22016")
+    rng = np.random.default_rng(82)
+    g = torch.from_numpy((rng.standard_t(3, 4096 * 22016) * 1e-4).astype(np.float32)).to(torch.bfloat16)
+    codes, scale = fp4.fp8_quantize(g.to(DEV))
+    gf = g.float().numpy()
+    amax = np.float32(np.abs(gf).max())
+    assert to_np(scale)[0] == np.float32(amax / np.float32(448.0))
+    r = np.float32(448.0) / amax
+    idx = np.concatenate([rng.integers(0, gf.size, 200000), np.argsort(np.abs(gf))[-64:], [0, gf.size - 1]])
+    ref = oracle.e4m3_encode((gf[idx] * r).astype(np.float32))
+    assert np.array_equal(to_np(codes)[idx], ref)
+
+
 # ----------------------------------------------------------------------------- full sizes
 def _sample_pairs(rng, M, N, row_ptr, count=3000):
     ms = list(rng.integers(0, M, count))
