@@ -87,6 +87,11 @@ def load(path: str = LIB):
         "orc_output_pairs": (None, [vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, vp, i32, vp, vp]),
         "orc_to_bf16": (None, [vp, i64, vp]),
         "orc_forward": (i64, [vp, vp, i32, i64, i64, i64, dbl, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "orc_transpose_codes": (None, [vp, i64, i64, vp]),
+        "orc_scaled_quant_rows": (None, [vp, i32, i64, i64, vp, vp, vp]),
+        "orc_scaled_quant_cols": (None, [vp, i32, i64, i64, vp, vp, vp]),
+        "orc_scale_pairs": (None, [vp, vp, vp, i64, vp]),
+        "orc_backward": (None, [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -315,3 +320,80 @@ def forward_sampled(A: np.ndarray, W: np.ndarray, q: float, ms, ns) -> dict:
     Y, denom = output_pairs(acc, sA, sW, ms, ns, cl["row_ptr"], cl["coo_col"], cl["coo_val"], W)
     return dict(T=T, Aq=Aq, sA=sA, Wq=Wq, sW=sW, acc=acc, Y=Y, denom=denom, ms=np.asarray(ms),
                 ns=np.asarray(ns), **cl)
+
+
+# ----------------------------------------------------------------------------- backward
+def transpose_codes(codes: np.ndarray, R: int, Cc: int) -> np.ndarray:
+    """R x Cc codes packed R x Cc/2 -> the transposed codes packed Cc x R/2."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty((Cc, R // 2), dtype=np.uint8)
+    load().orc_transpose_codes(_p(codes), R, Cc, _p(out))
+    return out
+
+
+def scaled_quant_rows(X: np.ndarray, col_mult: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Token-wise quantization of fl(X * col_mult[None, :])."""
+    X = np.ascontiguousarray(X)
+    R, Cc = X.shape
+    mult = np.ascontiguousarray(col_mult, dtype=np.float32)
+    codes = np.empty((R, Cc // 2), dtype=np.uint8)
+    scales = np.empty(R, dtype=np.float32)
+    load().orc_scaled_quant_rows(_p(X), _dtype_code(X), R, Cc, _p(mult), _p(codes), _p(scales))
+    return codes, scales
+
+
+def scaled_quant_cols(X: np.ndarray, row_mult: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Channel-wise quantization of fl(row_mult[:, None] * X); codes are C x R/2."""
+    X = np.ascontiguousarray(X)
+    R, Cc = X.shape
+    mult = np.ascontiguousarray(row_mult, dtype=np.float32)
+    codes = np.empty((Cc, R // 2), dtype=np.uint8)
+    scales = np.empty(Cc, dtype=np.float32)
+    load().orc_scaled_quant_cols(_p(X), _dtype_code(X), R, Cc, _p(mult), _p(codes), _p(scales))
+    return codes, scales
+
+
+def scale_pairs(acc: np.ndarray, s: np.ndarray, idx) -> np.ndarray:
+    """fl(acc[i] * s[idx[i]]): a backward output from its exact accumulator."""
+    acc = np.ascontiguousarray(acc, dtype=np.float32)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    out = np.empty(acc.size, dtype=np.float32)
+    load().orc_scale_pairs(_p(acc), _p(s), _p(idx), acc.size, _p(out))
+    return out
+
+
+def backward(dY: np.ndarray, Aq: np.ndarray, sA: np.ndarray, Wq: np.ndarray, sW: np.ndarray, K: int) -> dict:
+    """Straight-through backward of the quantized product on small inputs."""
+    dY = np.ascontiguousarray(dY)
+    M, N = dY.shape
+    Gq = np.empty((M, N // 2), dtype=np.uint8)
+    sG = np.empty(M, dtype=np.float32)
+    Hq = np.empty((N, M // 2), dtype=np.uint8)
+    sH = np.empty(N, dtype=np.float32)
+    WqT = np.empty((K, N // 2), dtype=np.uint8)
+    AqT = np.empty((K, M // 2), dtype=np.uint8)
+    dA = np.empty((M, K), dtype=np.float32)
+    dW = np.empty((K, N), dtype=np.float32)
+    load().orc_backward(_p(dY), _dtype_code(dY), M, K, N, _p(np.ascontiguousarray(Aq)),
+                        _p(np.ascontiguousarray(sA, dtype=np.float32)), _p(np.ascontiguousarray(Wq)),
+                        _p(np.ascontiguousarray(sW, dtype=np.float32)), _p(Gq), _p(sG), _p(Hq), _p(sH),
+                        _p(WqT), _p(AqT), _p(dA), _p(dW))
+    return dict(Gq=Gq, sG=sG, Hq=Hq, sH=sH, WqT=WqT, AqT=AqT, dA=dA, dW=dW)
+
+
+def backward_sampled(dY: np.ndarray, Aq, sA, Wq, sW, K: int, mk, kn) -> dict:
+    """Full-size intermediates of the backward, and dA at the (m, k) pairs mk and dW at
+    the (k, n) pairs kn only."""
+    dY = np.ascontiguousarray(dY)
+    M, N = dY.shape
+    Gq, sG = scaled_quant_rows(dY, sW)
+    Hq, sH = scaled_quant_cols(dY, sA)
+    WqT = transpose_codes(Wq, N, K)
+    AqT = transpose_codes(Aq, M, K)
+    ms, ks = np.asarray(mk[0], dtype=np.int64), np.asarray(mk[1], dtype=np.int64)
+    ks2, ns2 = np.asarray(kn[0], dtype=np.int64), np.asarray(kn[1], dtype=np.int64)
+    accA = accumulate_pairs(Gq, WqT, N, ms, ks)
+    accW = accumulate_pairs(AqT, Hq, M, ks2, ns2)
+    return dict(Gq=Gq, sG=sG, Hq=Hq, sH=sH, WqT=WqT, AqT=AqT, accA=accA, accW=accW,
+                dA=scale_pairs(accA, sG, ms), dW=scale_pairs(accW, sH, ns2))

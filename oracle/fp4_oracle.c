@@ -438,3 +438,88 @@ int64_t orc_forward(const void *A, const void *W, int dtype, int64_t M, int64_t 
     orc_output(acc, sA, sW, M, N, row_ptr, coo_col, coo_val, W, dtype, Y, denom);
     return nnz;
 }
+
+/* ---------------------------------------------------------------------------------
+ * Backward of the layer with a straight-through gradient.
+ *
+ * The pages: in the backward pass the derivative of the hard quantizer is zero almost
+ * everywhere, and the authors replace it with the derivative of a smooth fit of the
+ * quantizer (their differentiable gradient estimator) ([QbitAI], backward paragraph;
+ * [Abstract]).  The pages do not give that function, so the correction is left out and
+ * the quantizer's derivative is taken as one (straight-through): the gradients of
+ * Y = deq(Aq) . deq(Wq) are
+ *      dA = dY . deq(Wq)^T          dW = deq(Aq)^T . dY
+ * with deq(Aq)[m][k] = value(Aq[m][k]) * sA[m] and deq(Wq)[k][n] = value(Wq[n][k]) * sW[n],
+ * the operands the forward multiplied.
+ *
+ * Readings, so both products run on FP4 operands like the forward's:
+ *   - the scale that lies along the contraction (sW[n] for dA, sA[m] for dW) is folded
+ *     into dY in fp32: G[m][n] = fl(dY[m][n] * sW[n]), H[m][n] = fl(sA[m] * dY[m][n]);
+ *   - G is quantized per row (token-wise, along n) and H per column (channel-wise, along
+ *     m) with the forward's rule (scale, rounding, saturation, zero vectors): the
+ *     quantization axes of the backward are the transposes of the forward's;
+ *   - the forward's codes are reused unchanged, re-laid out so that the new contraction
+ *     index is contiguous: WqT is K x N/2 and AqT is K x M/2;
+ *   - acc is exact as in the forward (contraction length <= 65536) and each output is
+ *     one rounding: dA[m][k] = fl(acc_A[m][k] * sG[m]), dW[k][n] = fl(acc_W[k][n] * sH[n]).
+ * The clamp and the compensation of the forward contribute no term (the gradient is
+ * taken through the quantized product only).
+ * ------------------------------------------------------------------------------- */
+
+/* R x C codes (R x C/2 bytes, element (r, c) in byte (r, c/2)) -> the same codes
+ * transposed: C x R/2 bytes, element (r, c) in byte (c, r/2); low nibble = even index. */
+void orc_transpose_codes(const uint8_t *in, int64_t R, int64_t C, uint8_t *out) {
+    for (int64_t i = 0; i < C * (R / 2); ++i) out[i] = 0;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c) {
+            const int code = (in[r * (C / 2) + c / 2] >> (4 * (c & 1))) & 15;
+            out[c * (R / 2) + r / 2] |= (uint8_t)(code << (4 * (r & 1)));
+        }
+}
+
+/* Token-wise quantization of G = fl(X[i][j] * col_mult[j]) (R x C, X fp32 or bf16). */
+void orc_scaled_quant_rows(const void *X, int dtype, int64_t R, int64_t C, const float *col_mult,
+                           uint8_t *codes, float *scales) {
+    float *G = (float *)malloc((size_t)(R * C) * sizeof(float));
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < C; ++j) G[i * C + j] = load_elem(X, dtype, i * C + j) * col_mult[j];
+    orc_quant_rows(G, R, C, codes, scales);
+    free(G);
+}
+
+/* Channel-wise quantization of H = fl(row_mult[i] * X[i][j]) (R x C): codes C x R/2. */
+void orc_scaled_quant_cols(const void *X, int dtype, int64_t R, int64_t C, const float *row_mult,
+                           uint8_t *codes, float *scales) {
+    float *H = (float *)malloc((size_t)(R * C) * sizeof(float));
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < C; ++j) H[i * C + j] = row_mult[i] * load_elem(X, dtype, i * C + j);
+    orc_quant_cols(H, ORC_F32, R, C, codes, scales);
+    free(H);
+}
+
+/* out[i] = fl(acc[i] * s[idx[i]]): the one rounding of a backward output. */
+static float scale_one(float acc, float s) { return acc * s; }
+
+void orc_scale_pairs(const float *acc, const float *s, const int64_t *idx, int64_t count, float *out) {
+    for (int64_t i = 0; i < count; ++i) out[i] = scale_one(acc[i], s[idx[i]]);
+}
+
+/* The whole backward, in the order above.  dY is M x N (fp32 or bf16); Aq, sA, Wq, sW as
+ * the forward produced them.  Outputs: Gq M x N/2, sG[M], Hq N x M/2, sH[N], WqT K x N/2,
+ * AqT K x M/2, dA M x K and dW K x N (fp32). */
+void orc_backward(const void *dY, int dtype, int64_t M, int64_t K, int64_t N, const uint8_t *Aq,
+                  const float *sA, const uint8_t *Wq, const float *sW, uint8_t *Gq, float *sG,
+                  uint8_t *Hq, float *sH, uint8_t *WqT, uint8_t *AqT, float *dA, float *dW) {
+    /* dA = dY . deq(Wq)^T: contraction over n */
+    orc_scaled_quant_rows(dY, dtype, M, N, sW, Gq, sG);
+    orc_transpose_codes(Wq, N, K, WqT);
+    orc_accumulate(Gq, WqT, M, K, N, dA);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) dA[m * K + k] = scale_one(dA[m * K + k], sG[m]);
+    /* dW = deq(Aq)^T . dY: contraction over m */
+    orc_scaled_quant_cols(dY, dtype, M, N, sA, Hq, sH);
+    orc_transpose_codes(Aq, M, K, AqT);
+    orc_accumulate(AqT, Hq, K, N, M, dW);
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) dW[k * N + n] = scale_one(dW[k * N + n], sH[n]);
+}

@@ -503,4 +503,148 @@ def pin_fp8_zero_and_bf16():
     assert s == 1.0 and codes.tolist() == [0x38, 0xC6, 0x7E, 0x01]
 
 
+
+# ------------------------------------------------------------------------- backward pins
+# Straight-through backward of the quantized product (QbitAI report, backward paragraph:
+# the quantizer's own derivative is replaced; here by one): dA = dY . deq(Wq)^T and
+# dW = deq(Aq)^T . dY, with the contraction-axis scale folded into dY before dY is
+# quantized (per row for dA, per column for dW).
+def _unpacked(codes: np.ndarray, cols: int) -> np.ndarray:
+    return oracle.unpack_codes(codes, cols)
+
+
+def pin_transpose_codes():
+    rng = np.random.default_rng(61)
+    for (R, Cn) in [(2, 2), (6, 10), (64, 96), (34, 130)]:
+        c = rng.integers(0, 16, (R, Cn)).astype(np.uint8)
+        packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+        t = oracle.transpose_codes(packed, R, Cn)
+        assert t.shape == (Cn, R // 2)
+        assert np.array_equal(_unpacked(t, R), c.T)          # numpy's transpose of the codes
+        assert np.array_equal(oracle.transpose_codes(t, Cn, R), packed)  # an involution
+
+
+def pin_scaled_quant_axes():
+    rng = np.random.default_rng(62)
+    X = (rng.standard_normal((24, 64)) * rng.lognormal(0, 1, (24, 1))).astype(np.float32)
+    X[4] = 0.0
+    # power-of-two multipliers: the scaled matrix is exact, and must quantize like it
+    cm = np.exp2(rng.integers(-6, 6, 64)).astype(np.float32)
+    codes, scales = oracle.scaled_quant_rows(X, cm)
+    _check_quantized_rows(X * cm[None, :], codes, scales)
+    rm = np.exp2(rng.integers(-6, 6, 24)).astype(np.float32)
+    codes, scales = oracle.scaled_quant_cols(X, rm)
+    assert codes.shape == (64, 12)
+    _check_quantized_rows(np.ascontiguousarray((rm[:, None] * X).T), codes, scales)
+    # general multipliers: the scaled matrix is the fp32 product (numpy's IEEE multiply)
+    cm = rng.uniform(0.01, 3.0, 64).astype(np.float32)
+    codes, scales = oracle.scaled_quant_rows(X, cm)
+    _check_quantized_rows(X * cm[None, :], codes, scales)
+    rm = rng.uniform(0.01, 3.0, 24).astype(np.float32)
+    codes, scales = oracle.scaled_quant_cols(X, rm)
+    _check_quantized_rows(np.ascontiguousarray((rm[:, None] * X).T), codes, scales)
+    # bf16 input bits give the same codes as their fp32 values
+    xb = torch.from_numpy(X).to(torch.bfloat16)
+    bits = xb.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.scaled_quant_rows(bits, cm)[0], oracle.scaled_quant_rows(xb.float().numpy(), cm)[0])
+
+
+def _lossless(rng, shape, axis: int, exps: np.ndarray) -> np.ndarray:
+    """E2M1 values times 2^exps along `axis`, with every slice along the other axis
+    reaching magnitude 6 * 2^e (so per-slice absmax quantization is lossless)."""
+    c = rng.integers(0, 16, shape).astype(np.uint8)
+    if axis == 0:   # one exponent per row, each row holds a +-6
+        c[np.arange(shape[0]), rng.integers(0, shape[1], shape[0])] = 7
+        return decode(c) * np.exp2(exps)[:, None]
+    c[rng.integers(0, shape[0], shape[1]), np.arange(shape[1])] = 15
+    return decode(c) * np.exp2(exps)[None, :]
+
+
+def pin_backward_lossless_dA():
+    # W and G = dY * sW quantize losslessly -> dA == dY @ W^T exactly (float64 matmul)
+    rng = np.random.default_rng(63)
+    M, K, N = 10, 64, 96
+    e = rng.integers(-4, 5, N)
+    f = rng.integers(-4, 5, M)
+    W = _lossless(rng, (K, N), 1, e).astype(np.float32)
+    u = _lossless(rng, (M, N), 0, np.zeros(M))
+    dY = (u * np.exp2(f[:, None] - e[None, :])).astype(np.float32)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    Aq, sA = oracle.quant_rows(A)
+    Wq, sW = oracle.quant_cols(W)
+    assert np.array_equal(sW, np.exp2(e).astype(np.float32))
+    ref = dY.astype(np.float64) @ W.astype(np.float64).T
+    for d in (dY, torch.from_numpy(dY).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)):
+        out = oracle.backward(d, Aq, sA, Wq, sW, K)
+        assert np.array_equal(out["sG"], np.exp2(f).astype(np.float32))
+        assert np.array_equal(out["dA"].astype(np.float64), ref)
+
+
+def pin_backward_lossless_dW():
+    # A and H = sA * dY quantize losslessly -> dW == A^T @ dY exactly
+    rng = np.random.default_rng(64)
+    M, K, N = 64, 32, 24
+    g = rng.integers(-4, 5, M)
+    h = rng.integers(-4, 5, N)
+    A = _lossless(rng, (M, K), 0, g).astype(np.float32)
+    u = _lossless(rng, (M, N), 1, np.zeros(N))
+    dY = (u * np.exp2(h[None, :] - g[:, None])).astype(np.float32)
+    W = rng.standard_normal((K, N)).astype(np.float32)
+    Aq, sA = oracle.quant_rows(A)
+    Wq, sW = oracle.quant_cols(W)
+    assert np.array_equal(sA, np.exp2(g).astype(np.float32))
+    out = oracle.backward(dY, Aq, sA, Wq, sW, K)
+    assert np.array_equal(out["sH"], np.exp2(h).astype(np.float32))
+    assert np.array_equal(out["dW"].astype(np.float64), A.astype(np.float64).T @ dY.astype(np.float64))
+
+
+def pin_backward_decoded_operands():
+    # general inputs: each output is the float64 product of the decoded, scaled operands
+    # (exact there: every partial sum is a short dyadic) rounded once to fp32
+    rng = np.random.default_rng(65)
+    M, K, N = 32, 64, 96
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    dY = (rng.standard_normal((M, N)) * 1e-3).astype(np.float32)
+    Aq, sA = oracle.quant_rows(A)
+    Wq, sW = oracle.quant_cols(W)
+    out = oracle.backward(dY, Aq, sA, Wq, sW, K)
+    g = decode(_unpacked(out["Gq"], N))
+    wv = decode(_unpacked(Wq, K))          # N x K
+    dA = (g @ wv) * out["sG"].astype(np.float64)[:, None]
+    assert np.array_equal(out["dA"], dA.astype(np.float32))
+    av = decode(_unpacked(Aq, K))          # M x K
+    hv = decode(_unpacked(out["Hq"], M))   # N x M
+    dW = (av.T @ hv.T) * out["sH"].astype(np.float64)[None, :]
+    assert np.array_equal(out["dW"], dW.astype(np.float32))
+    # and the straight-through products they approximate, to FP4 accuracy
+    ref = dY.astype(np.float64) @ (wv.T * sW.astype(np.float64)[None, :]).T
+    assert np.linalg.norm(out["dA"] - ref) <= 0.25 * np.linalg.norm(ref)
+
+
+def pin_backward_sampled():
+    # the sampled form (used at full size) on lossless inputs: dA at (m, k) pairs equals
+    # the float64 dY @ W^T there, and dW at (k, n) pairs equals A^T @ dY
+    rng = np.random.default_rng(66)
+    M, K, N = 32, 64, 96
+    e, f = rng.integers(-4, 5, N), rng.integers(-4, 5, M)
+    W = _lossless(rng, (K, N), 1, e).astype(np.float32)
+    dY = (_lossless(rng, (M, N), 0, np.zeros(M)) * np.exp2(f[:, None] - e[None, :])).astype(np.float32)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    Aq, sA = oracle.quant_rows(A)
+    Wq, sW = oracle.quant_cols(W)
+    mk = (rng.integers(0, M, 40), rng.integers(0, K, 40))
+    kn = (rng.integers(0, K, 40), rng.integers(0, N, 40))
+    out = oracle.backward_sampled(dY, Aq, sA, Wq, sW, K, mk, kn)
+    ref = dY.astype(np.float64) @ W.astype(np.float64).T
+    assert np.array_equal(out["dA"].astype(np.float64), ref[mk])
+    g = rng.integers(-4, 5, M)
+    h = rng.integers(-4, 5, N)
+    A = _lossless(rng, (M, K), 0, g).astype(np.float32)
+    dY = (_lossless(rng, (M, N), 1, np.zeros(N)) * np.exp2(h[None, :] - g[:, None])).astype(np.float32)
+    Aq, sA = oracle.quant_rows(A)
+    out = oracle.backward_sampled(dY, Aq, sA, Wq, sW, K, mk, kn)
+    ref = A.astype(np.float64).T @ dY.astype(np.float64)
+    assert np.array_equal(out["dW"].astype(np.float64), ref[kn])
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -46,6 +46,17 @@ MUTANTS = {
     "col_scale_per_tensor": ("for (int64_t n = 0; n < N; ++n) vector_scale(amax[n], &r[n], &scales[n]);",
                              "for (int64_t n = 1; n < N; ++n) if (amax[n] > amax[0]) amax[0] = amax[n];\n"
                              "    for (int64_t n = 0; n < N; ++n) vector_scale(amax[0], &r[n], &scales[n]);"),
+    "transpose_nibble_parity": ("out[c * (R / 2) + r / 2] |= (uint8_t)(code << (4 * (r & 1)));",
+                                "out[c * (R / 2) + r / 2] |= (uint8_t)(code << (4 * (c & 1)));"),
+    "bwd_row_mult_dropped": ("G[i * C + j] = load_elem(X, dtype, i * C + j) * col_mult[j];",
+                             "G[i * C + j] = load_elem(X, dtype, i * C + j);"),
+    "bwd_col_mult_dropped": ("H[i * C + j] = row_mult[i] * load_elem(X, dtype, i * C + j);",
+                             "H[i * C + j] = load_elem(X, dtype, i * C + j);"),
+    "bwd_dA_scale_of_row0": ("dA[m * K + k] = scale_one(dA[m * K + k], sG[m]);",
+                             "dA[m * K + k] = scale_one(dA[m * K + k], sG[0]);"),
+    "bwd_dW_scale_of_col0": ("dW[k * N + n] = scale_one(dW[k * N + n], sH[n]);",
+                             "dW[k * N + n] = scale_one(dW[k * N + n], sH[0]);"),
+    "bwd_scale_pairs_index": ("out[i] = scale_one(acc[i], s[idx[i]]);", "out[i] = scale_one(acc[i], s[i % 1]);"),
 }
 
 
