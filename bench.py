@@ -11,6 +11,7 @@ clamp quantile 0.999).  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes as C
 import hashlib
 import json
 import os
@@ -204,6 +205,63 @@ def run_fp8codec(steps: int, warmup: int):
                        "frac_of_hbm_peak": round(bd / ms_d / 1e6 / PEAK_HBM_GBS, 4)}}))
 
 
+def bwd_quantizer_bytes(M, K, N, bi) -> int:
+    """Algorithmic HBM bytes of the backward's operand preparation: dY read once for the
+    per-row quantization of G = dY * sW and twice for the per-column quantization of
+    H = sA * dY (a column's maximum must be known before any of its codes), codes and
+    scales written; the forward's codes read and written transposed."""
+    g = M * N * bi + M * N // 2 + 4 * N + 4 * M
+    h = 2 * M * N * bi + M * N // 2 + 4 * M + 4 * N
+    return g + h + K * N + M * K
+
+
+def run_backward(args):
+    """Straight-through backward of one layer: dA = dY . deq(Wq)^T and dW = deq(Aq)^T . dY,
+    both on the FP4 GEMM (fp4_linear_backward), on the forward's codes of the same seeded
+    workload and a seeded dY."""
+    from workloads import make_grad
+    A, W, L = make_layer(args.config, 0)
+    dev = torch.device("cuda:0")
+    Ad, Wd, dYd = A.to(dev), W.to(dev), make_grad(args.config, 0).to(dev)
+    M, K, N = L.M, L.K, L.N
+    ws_f = fp4.workspace(Ad, N, L.q)
+    fp4.linear_forward(Ad, Wd, L.q, ws=ws_f)
+    it = fp4.forward_intermediates(ws_f, M, K, N, A.dtype, L.q)
+    lay = fp4.backward_layout(M, K, N)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device=dev)
+    odt = dYd.dtype
+    dA = torch.empty((M, K), dtype=odt, device=dev)
+    dW = torch.empty((K, N), dtype=odt, device=dev)
+    st = fp4._stream(dYd)
+    step = lambda: fp4.linear_backward(dYd, it["Aq"], it["sA"], it["Wq"], it["sW"], K, ws=ws, dA=dA, dW=dW)  # noqa
+    ms_step = time_on_stream(step, args.steps, args.warmup)
+    P = lambda off: C.c_void_p(ws.data_ptr() + off)  # noqa: E731
+    ga = lambda: fp4.lib().fp4_gemm(P(lay.Gq), P(lay.sG), P(lay.WqT), P(lay.ones), M, K, N, None, None, None, 0,  # noqa
+                                    None, fp4.FP4_BF16, fp4._ptr(dA), fp4._dt(dA), None, None, 0, st)
+    gw = lambda: fp4.lib().fp4_gemm(P(lay.AqT), P(lay.ones), P(lay.Hq), P(lay.sH), K, N, M, None, None, None, 0,  # noqa
+                                    None, fp4.FP4_BF16, fp4._ptr(dW), fp4._dt(dW), None, None, 0, st)
+    ms_a = time_on_stream(ga, args.steps, 2)
+    ms_w = time_on_stream(gw, args.steps, 2)
+    flops = 2 * L.flops
+    q_ms = max(ms_step - ms_a - ms_w, 1e-9)
+    qb = bwd_quantizer_bytes(M, K, N, b_in(A.dtype))
+    g_tf = flops / (ms_a + ms_w) / 1e9
+    print(json.dumps({
+        "metric": "FP4 quantized-linear backward TFLOPS (dA and dW, straight-through)",
+        "value": round(flops / ms_step / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "dtype": "fp4e2m1 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": L.name + "_backward", "M": M, "K": K, "N": N, "in_dtype": L.dtype,
+                   "out_dtype": L.dtype, "grad_std": 1e-3},
+        "roofline": {"bound": "mfma", "kernel": "k_fp4_gemm", "achieved": round(g_tf, 1), "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(g_tf / PEAK_FP4_TFLOPS, 4),
+                     "ms_dA": round(ms_a, 4), "ms_dW": round(ms_w, 4)},
+        "operand_prep": {"bound": "hbm", "ms": round(q_ms, 4), "algorithmic_bytes": qb,
+                         "achieved": round(qb / q_ms / 1e6, 1), "unit": "GB/s",
+                         "frac": round(qb / q_ms / 1e6 / PEAK_HBM_GBS, 4)},
+        "device": torch.cuda.get_device_properties(0).gcnArchName}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,7 +276,8 @@ def main():
                     help="W quantization: inside every forward (the pages' scheme, default); once before the "
                          "timed steps (fixed inference weights); or on a second stream, each layer's under the "
                          "previous layer's forward")
-    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic", "fp8codec"])
+    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic", "fp8codec",
+                                                          "backward"])
     ap.add_argument("--traffic-dirs", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="--mode traffic: rocprofv3 --pmc output directories of FETCH_SIZE and WRITE_SIZE for "
                          "the full bench and for --mode copy")
@@ -236,6 +295,9 @@ def main():
         return
     if args.mode == "fp8codec":
         run_fp8codec(args.steps, args.warmup)
+        return
+    if args.mode == "backward":
+        run_backward(args)
         return
 
     layers = [make_layer(args.config, li) for li in range(len(CONFIGS[args.config]))]

@@ -222,6 +222,48 @@ fp4_status fp4_linear_forward_wq(const void *A, const void *W, const uint8_t *Wq
                                  void *Y, int32_t y_dtype, void *workspace, size_t ws_bytes,
                                  void *stream);
 
+/* Straight-through backward of the quantized product (QbitAI report, backward paragraph:
+ * the hard quantizer is kept in the forward and its derivative is replaced in the
+ * backward; the pages' smooth substitute is not given, so the derivative is taken as one).
+ * With deq(Aq)[m][k] = value(Aq[m][k]) * sA[m] and deq(Wq)[k][n] = value(Wq[n][k]) * sW[n]
+ * (the operands the forward multiplied):
+ *      dA = dY . deq(Wq)^T  (M x K)        dW = deq(Aq)^T . dY  (K x N)
+ * Both run on the FP4 GEMM, with the quantization axes transposed against the forward's:
+ *   - G = fl32(dY[m][n] * sW[n]) is quantized per row (Gq M x N/2, sG fp32[M]) and the
+ *     forward's Wq is transposed to WqT (K x N/2); dA[m][k] = fl32(acc * sG[m]) with acc the
+ *     exact sum over n of value(Gq[m][n]) * value(WqT[k][n]);
+ *   - H = fl32(sA[m] * dY[m][n]) is quantized per column (Hq N x M/2, sH fp32[N]) and Aq is
+ *     transposed to AqT (K x M/2); dW[k][n] = fl32(acc * sH[n]) with acc the exact sum over
+ *     m of value(AqT[k][m]) * value(Hq[n][m]).
+ * Quantization follows the forward's rule (fl32(6/amax) multiplier, nearest E2M1 with ties
+ * to even, saturation, zero vectors).  The clamp and the compensation of the forward add no
+ * term.  Arguments:
+ *   dY  M x N of dy_dtype (the gradient of Y)
+ *   Aq, sA, Wq, sW: the forward's codes and scales (fp4_forward_layout regions of the
+ *       forward workspace, or fp4_quantize's outputs); Aq/sA are needed only for dW and
+ *       Wq/sW only for dA
+ *   dA  NULL (not wanted) or M x K of da_dtype (out); needs N % 32 == 0, N <= 65536
+ *   dW  NULL (not wanted) or K x N of dw_dtype (out); needs M % 32 == 0, M <= 65536
+ *   workspace: at least fp4_backward_workspace_bytes(M, K, N) bytes; after the call it
+ *       holds the intermediates at the fp4_backward_layout offsets (Gq, sG, WqT when dA
+ *       was asked for; Hq, sH, AqT when dW was).
+ * Kernels, in stream order: fill, [row quantization of G, transpose of Wq, GEMM],
+ * [column quantization of H, transpose of Aq, GEMM].
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
+struct fp4_bwd_layout {
+    size_t total;        /* bytes needed */
+    size_t Gq, sG;       /* M x N/2 codes, fp32[M] */
+    size_t Hq, sH;       /* N x M/2 codes, fp32[N] */
+    size_t WqT, AqT;     /* K x N/2 and K x M/2 codes */
+    size_t ones;         /* fp32[K], internal */
+};
+fp4_status fp4_backward_layout(int64_t M, int64_t K, int64_t N, struct fp4_bwd_layout *out);
+size_t fp4_backward_workspace_bytes(int64_t M, int64_t K, int64_t N);
+fp4_status fp4_linear_backward(const void *dY, int32_t dy_dtype, int64_t M, int64_t K, int64_t N,
+                               const uint8_t *Aq, const float *sA, const uint8_t *Wq,
+                               const float *sW, void *dA, int32_t da_dtype, void *dW,
+                               int32_t dw_dtype, void *workspace, size_t ws_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *fp4_status_string(fp4_status s);
 

@@ -29,6 +29,7 @@ EXPORTS = (
     "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_forward_layout", "fp4_forward_workspace_bytes", "fp4_linear_forward",
     "fp4_linear_forward_wq", "fp4_gemm_fp8emu_workspace_bytes", "fp4_gemm_fp8emu",
     "fp4_fp8_workspace_bytes", "fp4_fp8_quantize", "fp4_fp8_dequantize",
+    "fp4_backward_layout", "fp4_backward_workspace_bytes", "fp4_linear_backward",
     "fp4_status_string",
 )
 
@@ -36,6 +37,10 @@ EXPORTS = (
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("total", "T", "nnz", "row_ptr", "coo_row", "coo_col", "coo_val",
                                           "Aq", "sA", "Wq", "sW", "ymain", "scratch")] + [("capacity", C.c_int64)]
+
+
+class BwdLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("total", "Gq", "sG", "Hq", "sH", "WqT", "AqT", "ones")]
 
 
 class Fp4Error(RuntimeError):
@@ -70,6 +75,9 @@ def lib():
         "fp4_fp8_quantize": (i32, [vp, i32, i64, vp, vp, vp, sz, vp]),
         "fp4_fp8_dequantize": (i32, [vp, i64, vp, vp, i32, vp]),
         "fp4_gemm_fp8emu": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]),
+        "fp4_backward_layout": (i32, [i64, i64, i64, C.POINTER(BwdLayout)]),
+        "fp4_backward_workspace_bytes": (sz, [i64, i64, i64]),
+        "fp4_linear_backward": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp]),
         "fp4_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -293,3 +301,46 @@ def forward_intermediates(ws: torch.Tensor, M: int, K: int, N: int, dtype: torch
         Aq=view(lay.Aq, M * (K // 2), torch.uint8, (M, K // 2)), sA=view(lay.sA, M, torch.float32),
         Wq=view(lay.Wq, N * (K // 2), torch.uint8, (N, K // 2)), sW=view(lay.sW, N, torch.float32),
         capacity=int(lay.capacity))
+
+
+# --------------------------------------------------------------------------- backward
+def backward_layout(M: int, K: int, N: int) -> BwdLayout:
+    lay = BwdLayout()
+    _check(lib().fp4_backward_layout(M, K, N, C.byref(lay)))
+    return lay
+
+
+def linear_backward(dY: torch.Tensor, Aq: torch.Tensor | None, sA: torch.Tensor | None, Wq: torch.Tensor | None,
+                    sW: torch.Tensor | None, K: int, want_dA: bool = True, want_dW: bool = True,
+                    out_dtype: torch.dtype | None = None, ws: torch.Tensor | None = None,
+                    dA: torch.Tensor | None = None, dW: torch.Tensor | None = None):
+    """Straight-through backward of the quantized product: (dA, dW), each None when not
+    wanted.  Aq/sA/Wq/sW are the forward's codes and scales (forward_intermediates)."""
+    _need_cuda(dY, Aq, sA, Wq, sW, ws, dA, dW)
+    M, N = dY.shape
+    out_dtype = out_dtype or dY.dtype
+    if ws is None:
+        ws = torch.empty(backward_layout(M, K, N).total, dtype=torch.uint8, device=dY.device)
+    if want_dA and dA is None:
+        dA = torch.empty((M, K), dtype=out_dtype, device=dY.device)
+    if want_dW and dW is None:
+        dW = torch.empty((K, N), dtype=out_dtype, device=dY.device)
+    dA = dA if want_dA else None
+    dW = dW if want_dW else None
+    _check(lib().fp4_linear_backward(_ptr(dY), _dt(dY), M, K, N, _ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), _ptr(dA),
+                                     _dt(dA) if dA is not None else FP4_F32, _ptr(dW),
+                                     _dt(dW) if dW is not None else FP4_F32, _ptr(ws), ws.numel(), _stream(dY)))
+    return dA, dW
+
+
+def backward_intermediates(ws: torch.Tensor, M: int, K: int, N: int) -> dict:
+    """Views of Gq, sG, Hq, sH, WqT and AqT inside a backward workspace."""
+    lay = backward_layout(M, K, N)
+
+    def view(off, nbytes, dt, shape):
+        return ws[off:off + nbytes].view(dt).view(shape)
+
+    return dict(Gq=view(lay.Gq, M * (N // 2), torch.uint8, (M, N // 2)), sG=view(lay.sG, 4 * M, torch.float32, (M,)),
+                Hq=view(lay.Hq, N * (M // 2), torch.uint8, (N, M // 2)), sH=view(lay.sH, 4 * N, torch.float32, (N,)),
+                WqT=view(lay.WqT, K * (N // 2), torch.uint8, (K, N // 2)),
+                AqT=view(lay.AqT, K * (M // 2), torch.uint8, (K, M // 2)))

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libfp4lin.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "quant.hip", "gemm.hip", "comp.hip", "emu.hip", "fp8codec.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "gemm.hip", "comp.hip", "emu.hip", "fp8codec.hip", "bwd.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -406,4 +406,79 @@ fp4_status fp4_linear_forward_wq(const void *A, const void *W, const uint8_t *Wq
     return forward_impl(A, W, Wq, sW, in_dtype, M, K, N, q, Y, y_dtype, workspace, ws_bytes, stream);
 }
 
+// ----------------------------------------------------------------------------- backward
+// Shapes of the straight-through backward: the forward's (Aq, Wq), and each requested
+// product's contraction (n for dA, m for dW) within the GEMM's K limits.
+static fp4_status bwd_shape(int64_t M, int64_t K, int64_t N, bool want_dA, bool want_dW) {
+    if (!gemm_ok(M, N, K)) return FP4_ERR_SHAPE;
+    if (want_dA && !(k_ok(N) && mk_ok(M, N) && mk_ok(K, N))) return FP4_ERR_SHAPE;
+    if (want_dW && !(k_ok(M) && mk_ok(N, M) && mk_ok(K, M))) return FP4_ERR_SHAPE;
+    return FP4_OK;
+}
+
+fp4_status fp4_backward_layout(int64_t M, int64_t K, int64_t N, struct fp4_bwd_layout *out) {
+    if (!out) return FP4_ERR_NULL;
+    std::memset(out, 0, sizeof(*out));
+    if (!gemm_ok(M, N, K)) return FP4_ERR_SHAPE;  // the forward's shapes; each product checks its own
+    size_t off = 0;
+    out->Gq = off; off += align_up((size_t)M * (size_t)(N / 2));
+    out->sG = off; off += align_up((size_t)M * 4);
+    out->Hq = off; off += align_up((size_t)N * (size_t)(M / 2));
+    out->sH = off; off += align_up((size_t)N * 4);
+    out->WqT = off; off += align_up((size_t)K * (size_t)(N / 2));
+    out->AqT = off; off += align_up((size_t)K * (size_t)(M / 2));
+    out->ones = off; off += align_up((size_t)K * 4);
+    out->total = off;
+    return FP4_OK;
+}
+
+size_t fp4_backward_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    fp4_bwd_layout l;
+    return fp4_backward_layout(M, K, N, &l) == FP4_OK ? l.total : 0;
+}
+
+fp4_status fp4_linear_backward(const void *dY, int32_t dy_dtype, int64_t M, int64_t K, int64_t N, const uint8_t *Aq,
+                               const float *sA, const uint8_t *Wq, const float *sW, void *dA, int32_t da_dtype,
+                               void *dW, int32_t dw_dtype, void *workspace, size_t ws_bytes, void *stream) {
+    const bool want_dA = dA != nullptr, want_dW = dW != nullptr;
+    if (!dY || !workspace || (!want_dA && !want_dW)) return FP4_ERR_NULL;
+    if (want_dA && (!Wq || !sW)) return FP4_ERR_NULL;
+    if (want_dW && (!Aq || !sA)) return FP4_ERR_NULL;
+    if (!dtype_ok(dy_dtype) || (want_dA && !dtype_ok(da_dtype)) || (want_dW && !dtype_ok(dw_dtype)))
+        return FP4_ERR_DTYPE;
+    fp4_status st = bwd_shape(M, K, N, want_dA, want_dW);
+    if (st != FP4_OK) return st;
+    fp4_bwd_layout l;
+    fp4_backward_layout(M, K, N, &l);
+    if (ws_bytes < l.total) return FP4_ERR_WORKSPACE;
+    if (!aligned16(dY) || !aligned16(workspace) || (want_dA && (!aligned16(Wq) || !aligned16(sW) || !aligned16(dA))) ||
+        (want_dW && (!aligned16(Aq) || !aligned16(sA) || !aligned16(dW))))
+        return FP4_ERR_ALIGN;
+    int cus;
+    st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    float *ones = reinterpret_cast<float *>(ws + l.ones);
+    const int dt = dt_of(dy_dtype);
+    hipError_t e = launch_fill_f32(ones, K, 1.0f, s);
+    if (want_dA && e == hipSuccess) {
+        // dA = deq(Q_rows(dY * sW)) . value(Wq)^T: GEMM with M rows, K columns, contraction N
+        uint8_t *Gq = ws + l.Gq, *WqT = ws + l.WqT;
+        float *sG = reinterpret_cast<float *>(ws + l.sG);
+        e = launch_scaled_quant_rows(dY, dt, M, N, sW, Gq, sG, s);
+        if (e == hipSuccess) e = launch_codes_transpose(Wq, N, K, WqT, s);
+        if (e == hipSuccess) e = launch_gemm(Gq, sG, WqT, ones, M, K, N, dA, dt_of(da_dtype), nullptr, s);
+    }
+    if (want_dW && e == hipSuccess) {
+        // dW = value(Aq)^T . deq(Q_cols(sA * dY)): GEMM with K rows, N columns, contraction M
+        uint8_t *Hq = ws + l.Hq, *AqT = ws + l.AqT;
+        float *sH = reinterpret_cast<float *>(ws + l.sH);
+        e = launch_quant_cols(dY, dt, M, N, sH, Hq, false, s, sA);
+        if (e == hipSuccess) e = launch_codes_transpose(Aq, M, K, AqT, s);
+        if (e == hipSuccess) e = launch_gemm(AqT, ones, Hq, sH, K, N, M, dW, dt_of(dw_dtype), nullptr, s);
+    }
+    return hip_status(e);
+}
+
 }  // extern "C"

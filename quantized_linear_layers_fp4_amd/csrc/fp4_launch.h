@@ -21,8 +21,15 @@ hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64
                       const State *st, int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val,
                       hipStream_t s);
 // keys_zeroed: the column-maximum keys (in the scales buffer) were zeroed by an earlier launch.
+// row_mult: NULL, or fp32[K]: quantize fl(row_mult[k] * W[k][n]) instead of W.
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
-                             uint8_t *codes, bool keys_zeroed, hipStream_t s);
+                             uint8_t *codes, bool keys_zeroed, hipStream_t s, const float *row_mult = nullptr);
+// Backward operands: R x C codes (R x C/2 bytes) -> their transpose (C x R/2 bytes), R and C
+// multiples of 32; token-wise quantization of fl(X[r][c] * mult[c]) (C <= 65536); fill.
+hipError_t launch_codes_transpose(const uint8_t *in, int64_t R, int64_t C, uint8_t *out, hipStream_t s);
+hipError_t launch_scaled_quant_rows(const void *X, int dt, int64_t R, int64_t C, const float *mult, uint8_t *codes,
+                                    float *scales, hipStream_t s);
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
 
 // FP4 GEMM + dequantization: Y = fl(fl(acc * sA) * sW) in y_dt.  acc_out: NULL or fp32[M*N].
 // f8: Aq (M x K) and Wq (N x K) hold E4M3 bytes, one K value each (the emulation path).

@@ -405,11 +405,29 @@ __global__ __launch_bounds__(256) void k_coo_scatter(Staging stg, const State *_
 }
 
 // ----------------------------------------------------------------------------- columns (W)
+// Row k of the matrix as quantized: the input itself, or (RM) fl(row_mult[k] * x), the
+// form the backward quantizes per column.
+template <int DT, bool RM>
+__device__ __forceinline__ void load8_rm(const void *__restrict__ W, const float *__restrict__ row_mult, int64_t k,
+                                         int64_t N, int64_t col, float v[8], uint32_t key[8]) {
+    uint32_t sg[8];
+    load8<DT>(W, k * N + col, v, key, sg);
+    if constexpr (RM) {
+        const float m = row_mult[k];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[e] = m * v[e];
+            key[e] = __float_as_uint(v[e]) & 0x7FFFFFFFu;
+        }
+    }
+}
+
 // Column maxima of K x N W (keys), merged with atomicMax into colmax_key (zeroed before).
 // Block: 256 threads = 4 waves over the same 512 columns (8 per lane), rows split by wave.
-template <int DT>
+template <int DT, bool RM>
 __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int64_t K, int64_t N,
-                                                int rows_per_block, uint32_t *__restrict__ colmax_key) {
+                                                int rows_per_block, const float *__restrict__ row_mult,
+                                                uint32_t *__restrict__ colmax_key) {
     __shared__ uint32_t red[4][512];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
@@ -420,9 +438,9 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
         int64_t r = r0 + wave;
         for (; r + 12 < r1; r += 16) {
             float v[4][8];
-            uint32_t key[4][8], sg[4][8];
+            uint32_t key[4][8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) load8<DT>(W, (r + 4 * u) * N + col, v[u], key[u], sg[u]);
+            for (int u = 0; u < 4; ++u) load8_rm<DT, RM>(W, row_mult, r + 4 * u, N, col, v[u], key[u]);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -430,8 +448,8 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
         }
         for (; r < r1; r += 4) {
             float v[8];
-            uint32_t key[8], sg[8];
-            load8<DT>(W, r * N + col, v, key, sg);
+            uint32_t key[8];
+            load8_rm<DT, RM>(W, row_mult, r, N, col, v, key);
 #pragma unroll
             for (int e = 0; e < 8; ++e) mx[e] = max(mx[e], key[e]);
         }
@@ -450,8 +468,9 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
 // transposed: Wq[n][k/2].  Loads: 8 threads per row (16 bytes = 8 columns each), two rows
 // (k, k+1) per thread per pass so each output byte (pair of k) is formed in registers; the
 // transpose goes through a 64 x 128-byte LDS tile.
-template <int DT>
+template <int DT, bool RM>
 __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, int64_t K, int64_t N,
+                                                    const float *__restrict__ row_mult,
                                                     const uint32_t *__restrict__ colmax_key,
                                                     uint8_t *__restrict__ codes) {
     __shared__ float rs[64];
@@ -476,9 +495,9 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
         uint32_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (col < N && k < K) {  // K % 32 == 0: both rows of a pair are in range together
             float v0[8], v1[8];
-            uint32_t key0[8], key1[8], sg0[8], sg1[8];
-            load8<DT>(W, k * N + col, v0, key0, sg0);
-            load8<DT>(W, (k + 1) * N + col, v1, key1, sg1);
+            uint32_t key0[8], key1[8];
+            load8_rm<DT, RM>(W, row_mult, k, N, col, v0, key0);
+            load8_rm<DT, RM>(W, row_mult, k + 1, N, col, v1, key1);
 #pragma unroll
             for (int e = 0; e < 8; ++e) b[e] = e2m1_pack2<0>(0u, v0[e] * r8[e], v1[e] * r8[e]) & 0xFFu;
         }
@@ -587,7 +606,7 @@ hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64
 }
 
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
-                             uint8_t *codes, bool keys_zeroed, hipStream_t s) {
+                             uint8_t *codes, bool keys_zeroed, hipStream_t s, const float *row_mult) {
     uint32_t *keys = reinterpret_cast<uint32_t *>(scales_as_keys);
     if (!keys_zeroed) {
         hipError_t e = launch_zero(keys, N, nullptr, 0, s);
@@ -596,13 +615,19 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
     const int rows_per_block = 256;
     dim3 g1((unsigned)((N + 511) / 512), (unsigned)((K + rows_per_block - 1) / rows_per_block));
     dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
+#define QC(DT, RM)                                                                                         \
+    do {                                                                                                   \
+        hipLaunchKernelGGL((k_colmax<DT, RM>), g1, dim3(256), 0, s, W, K, N, rows_per_block, row_mult, keys); \
+        hipLaunchKernelGGL((k_quant_cols<DT, RM>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);     \
+    } while (0)
     if (dt == DT_BF16) {
-        hipLaunchKernelGGL(k_colmax<DT_BF16>, g1, dim3(256), 0, s, W, K, N, rows_per_block, keys);
-        hipLaunchKernelGGL(k_quant_cols<DT_BF16>, g2, dim3(256), 0, s, W, K, N, keys, codes);
+        if (row_mult) QC(DT_BF16, true);
+        else QC(DT_BF16, false);
     } else {
-        hipLaunchKernelGGL(k_colmax<DT_F32>, g1, dim3(256), 0, s, W, K, N, rows_per_block, keys);
-        hipLaunchKernelGGL(k_quant_cols<DT_F32>, g2, dim3(256), 0, s, W, K, N, keys, codes);
+        if (row_mult) QC(DT_F32, true);
+        else QC(DT_F32, false);
     }
+#undef QC
     hipLaunchKernelGGL(k_col_scales, dim3(blocks_for(N, 256, 1 << 20)), dim3(256), 0, s, keys, N);
     return hipGetLastError();
 }

@@ -183,3 +183,52 @@ def test_gemm_workspace_bytes():
     assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 1) == 0   # fp32 Y is updated in place
     assert L.fp4_gemm_workspace_bytes(0, 264, fp4.FP4_BF16, 1) == 0
     assert L.fp4_gemm_workspace_bytes(300, 100, fp4.FP4_BF16, 1) == 0
+
+
+def test_backward_layout_is_disjoint_and_aligned():
+    L = fp4.lib()
+    lay = fp4.BwdLayout()
+    M, K, N = 96, 160, 224
+    assert L.fp4_backward_layout(M, K, N, C.byref(lay)) == OK
+    parts = sorted([(lay.Gq, M * N // 2), (lay.sG, M * 4), (lay.Hq, N * M // 2), (lay.sH, N * 4),
+                    (lay.WqT, K * N // 2), (lay.AqT, K * M // 2), (lay.ones, K * 4)])
+    for (a, na), (b, _) in zip(parts, parts[1:]):
+        assert a % 256 == 0 and a + na <= b
+    assert parts[-1][0] + parts[-1][1] <= lay.total
+    assert L.fp4_backward_workspace_bytes(M, K, N) == lay.total
+    assert L.fp4_backward_workspace_bytes(M, 100, N) == 0     # K % 32
+    assert L.fp4_backward_layout(M, K, N, None) == ENULL
+
+
+def test_linear_backward_rejects():
+    """Checks of the backward: pointers per requested product, dtypes, each product's
+    contraction (n for dA, m for dW), workspace and alignment, all before any HIP call."""
+    L = fp4.lib()
+    M, K, N = 64, 128, 96
+    wsb = L.fp4_backward_workspace_bytes(M, K, N)
+    assert wsb > 0
+
+    def call(**kw):
+        return L.fp4_linear_backward(kw.get("dY", FAKE), kw.get("dt", 1), kw.get("M", M), kw.get("K", K),
+                                     kw.get("N", N), kw.get("Aq", FAKE), kw.get("sA", FAKE), kw.get("Wq", FAKE),
+                                     kw.get("sW", FAKE), kw.get("dA", FAKE), kw.get("dadt", 1), kw.get("dW", FAKE),
+                                     kw.get("dwdt", 0), kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert call(dY=None) == ENULL
+    assert call(dA=None, dW=None) == ENULL          # nothing asked for
+    assert call(Wq=None) == ENULL                   # dA needs Wq and sW
+    assert call(sW=None) == ENULL
+    assert call(Aq=None) == ENULL                   # dW needs Aq and sA
+    assert call(sA=None) == ENULL
+    assert call(dA=None, Wq=None, sW=None, wsb=1 << 40) != ENULL  # dW alone does not
+    assert call(dt=2) == EDTYPE
+    assert call(dadt=3) == EDTYPE
+    assert call(dwdt=-1) == EDTYPE
+    assert call(N=104) == ESHAPE                    # dA contracts over n: N % 32
+    assert call(N=104, dA=None, wsb=1 << 40) not in (ESHAPE, ENULL)  # dW alone: N % 8 suffices
+    assert call(M=48) == ESHAPE                     # dW contracts over m: M % 32
+    assert call(M=48, dW=None, wsb=1 << 40) not in (ESHAPE, ENULL)   # dA alone: any M
+    assert call(M=65536 + 32, dA=None) == ESHAPE    # contraction above 65536
+    assert call(K=100) == ESHAPE
+    assert call(wsb=wsb - 1) == EWS
+    assert call(dA=C.c_void_p(0x100004)) == EALIGN
+    assert call(sA=C.c_void_p(0x100004)) == EALIGN

@@ -15,7 +15,7 @@ import torch
 import oracle
 import quantized_linear_layers_fp4_amd as fp4
 from parity_util import (assert_bf16_close, assert_y_close, bf16_to_f64, oracle_inputs, to_np)
-from workloads import CONFIGS, as_numpy_bits, make_custom, make_layer
+from workloads import CONFIGS, as_numpy_bits, make_custom, make_custom_grad, make_layer
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -491,3 +491,121 @@ def test_forward_full_size(cfg, li):
     if L.out_dtype == "bf16":
         assert_bf16_close(to_np(Y.view(-1)[idx]), r_y, denom)
     _say(f"  sampled acc bit-exact, Y max rel err {err:.3e}")
+
+
+# ----------------------------------------------------------------------------- backward
+def _fwd_codes_gpu(Ad, Wd, q):
+    M, K = Ad.shape
+    N = Wd.shape[1]
+    ws = fp4.workspace(Ad, N, q)
+    fp4.linear_forward(Ad, Wd, q, out_dtype=torch.float32, ws=ws)
+    return fp4.forward_intermediates(ws, M, K, N, Ad.dtype, q)
+
+
+def _check_backward_small(A, W, dY, q, out_dtype, want_dA=True, want_dW=True):
+    M, K = A.shape
+    N = W.shape[1]
+    Ad, Wd, dYd = A.to(DEV), W.to(DEV), dY.to(DEV)
+    inter = _fwd_codes_gpu(Ad, Wd, q)
+    Anp, Wnp = oracle_inputs(A, W)
+    dYnp = as_numpy_bits(dY)
+    ref_f = oracle.forward(Anp, Wnp, q)
+    for k in ("Aq", "sA", "Wq", "sW"):  # the backward's inputs agree before it starts
+        assert np.array_equal(to_np(inter[k]), ref_f[k]), k
+    ws = torch.empty(fp4.backward_layout(M, K, N).total, dtype=torch.uint8, device=DEV)
+    dA, dW = fp4.linear_backward(dYd, inter["Aq"], inter["sA"], inter["Wq"], inter["sW"], K, want_dA=want_dA,
+                                 want_dW=want_dW, out_dtype=out_dtype, ws=ws)
+    torch.cuda.synchronize()
+    bi = fp4.backward_intermediates(ws, M, K, N)
+    ref = oracle.backward(dYnp, ref_f["Aq"], ref_f["sA"], ref_f["Wq"], ref_f["sW"], K)
+    if want_dA:
+        for k in ("Gq", "sG", "WqT"):
+            assert np.array_equal(to_np(bi[k]), ref[k]), k
+        exp = ref["dA"] if out_dtype == torch.float32 else oracle.to_bf16(ref["dA"])
+        assert np.array_equal(to_np(dA), exp), "dA"
+    else:
+        assert dA is None
+    if want_dW:
+        for k in ("Hq", "sH", "AqT"):
+            assert np.array_equal(to_np(bi[k]), ref[k]), k
+        exp = ref["dW"] if out_dtype == torch.float32 else oracle.to_bf16(ref["dW"])
+        assert np.array_equal(to_np(dW), exp), "dW"
+    else:
+        assert dW is None
+
+
+# (dtype, M, K, N, out): M and N multiples of 32 (the two contractions); several GEMM
+# tiles with ragged tails in every output dimension
+BWD_CASES = [("bf16", 96, 64, 160, "fp32"), ("fp32", 288, 320, 544, "fp32"), ("bf16", 544, 1056, 800, "bf16"),
+             ("bf16", 32, 32, 32, "fp32"), ("fp32", 320, 96, 4128, "bf16")]
+
+
+@pytest.mark.parametrize("dtype,M,K,N,out", BWD_CASES)
+def test_backward_small(dtype, M, K, N, out):
+    _say(f"backward {dtype} M={M} K={K} N={N} -> {out}")
+    A, W = make_custom(M, K, N, dtype=dtype, seed=M + N)
+    dY = make_custom_grad(M, N, dtype=dtype, seed=K)
+    _check_backward_small(A, W, dY, 0.99, _dt(out))
+
+
+def test_backward_one_product():
+    # dA alone allows any M; dW alone allows N % 8 == 0
+    _say("backward dA only (M=300), dW only (N=264)")
+    A, W = make_custom(300, 128, 256, dtype="bf16", seed=5)
+    _check_backward_small(A, W, make_custom_grad(300, 256, dtype="bf16", seed=5), 0.99, torch.float32,
+                          want_dW=False)
+    A, W = make_custom(256, 128, 264, dtype="bf16", seed=6)
+    _check_backward_small(A, W, make_custom_grad(256, 264, dtype="bf16", seed=6), 0.99, torch.float32,
+                          want_dA=False)
+
+
+def test_backward_zero_gradient_rows_and_columns():
+    _say("backward with zero rows and columns of dY")
+    A, W = make_custom(128, 64, 96, dtype="bf16", seed=7)
+    dY = make_custom_grad(128, 96, dtype="bf16", seed=7)
+    dY[5] = 0.0
+    dY[:, 17] = 0.0
+    _check_backward_small(A, W, dY, 0.99, torch.float32)
+    _check_backward_small(A, W, torch.zeros_like(dY), 0.99, torch.float32)
+
+
+BWD_FULL = [(2, 0), (3, 0)]
+
+
+@pytest.mark.parametrize("cfg,li", BWD_FULL, ids=[f"cfg{c}-{CONFIGS[c][li].name}" for c, li in BWD_FULL])
+def test_backward_full_size(cfg, li):
+    """The backward at the workload sizes, as the benchmark runs it: every intermediate
+    compared in full, dA and dW at sampled outputs."""
+    from workloads import make_grad
+    L = CONFIGS[cfg][li]
+    M, K, N = L.M, L.K, L.N
+    _say(f"backward full size {L.name} M={M} K={K} N={N}")
+    A, W, _ = make_layer(cfg, li)
+    dY = make_grad(cfg, li)
+    Ad, Wd, dYd = A.to(DEV), W.to(DEV), dY.to(DEV)
+    inter = _fwd_codes_gpu(Ad, Wd, L.q)
+    ws = torch.empty(fp4.backward_layout(M, K, N).total, dtype=torch.uint8, device=DEV)
+    dA, dW = fp4.linear_backward(dYd, inter["Aq"], inter["sA"], inter["Wq"], inter["sW"], K,
+                                 out_dtype=torch.float32, ws=ws)
+    torch.cuda.synchronize()
+    Anp, Wnp = oracle_inputs(A, W)
+    T = oracle.abs_quantile(Anp, L.q)
+    cl = oracle.clamp_coo(Anp, T, want_clamped=True, cap=oracle.capacity(M, K, L.q))
+    Aq, sA = oracle.quant_rows(cl.pop("A_clamped"))
+    Wq, sW = oracle.quant_cols(Wnp)
+    for k, v in (("Aq", Aq), ("sA", sA), ("Wq", Wq), ("sW", sW)):
+        assert np.array_equal(to_np(inter[k]), v), k
+    rng = np.random.default_rng(100 + cfg)
+    count = 2000
+    mk = (np.concatenate([rng.integers(0, M, count), [0, M - 1]]), np.concatenate([rng.integers(0, K, count), [0, K - 1]]))
+    kn = (np.concatenate([rng.integers(0, K, count), [0, K - 1]]), np.concatenate([rng.integers(0, N, count), [0, N - 1]]))
+    ref = oracle.backward_sampled(as_numpy_bits(dY), Aq, sA, Wq, sW, K, mk, kn)
+    bi = fp4.backward_intermediates(ws, M, K, N)
+    for k in ("Gq", "sG", "Hq", "sH", "WqT", "AqT"):
+        assert np.array_equal(to_np(bi[k]), ref[k]), k
+    _say("  backward intermediates bit-exact")
+    gA = dA.view(-1)[torch.from_numpy(mk[0] * K + mk[1]).to(DEV)].cpu().numpy()
+    gW = dW.view(-1)[torch.from_numpy(kn[0] * N + kn[1]).to(DEV)].cpu().numpy()
+    assert np.array_equal(gA, ref["dA"])
+    assert np.array_equal(gW, ref["dW"])
+    _say("  sampled dA and dW bit-exact")

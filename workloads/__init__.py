@@ -12,7 +12,8 @@ per configuration below.
 
 Recipe (all draws host-side, numpy PCG64 seeded by [20250128, cfg, layer, stream]):
   stream 0 = base values of A, stream 1 = A structure (outlier positions,
-  channels, per-row RMS), stream 2 = W.  Values are drawn in float32; every
+  channels, per-row RMS), stream 2 = W, stream 3 = the output gradient dY of the
+  backward (N(0, 1e-3), the magnitude of a loss-scaled activation gradient).  Values are drawn in float32; every
   scaling is applied in float32; bf16 tensors are the round-to-nearest-even
   cast of the float32 draw (torch CPU cast).
 """
@@ -120,6 +121,21 @@ def make_layer(cfg: int, li: int = 0) -> tuple[torch.Tensor, torch.Tensor, Layer
     A = _draw_A(L, cfg, li)
     W = _normal(_rng(cfg, li, 2), (L.K, L.N), std=L.w_std)
     return _to_dtype(A, L.dtype), _to_dtype(W, L.dtype), L
+
+
+GRAD_STD = 1e-3
+
+
+def make_grad(cfg: int, li: int = 0) -> torch.Tensor:
+    """dY (M x N) for the backward of the layer, as a CPU tensor of the layer's dtype."""
+    L = CONFIGS[cfg][li]
+    return _to_dtype(_normal(_rng(cfg, li, 3), (L.M, L.N), std=GRAD_STD), L.dtype)
+
+
+def make_custom_grad(M: int, N: int, dtype: str = "bf16", seed: int = 0) -> torch.Tensor:
+    """Small seeded dY for parity tests of arbitrary shapes."""
+    rng = np.random.Generator(np.random.PCG64([SEED_ROOT, 2000 + seed, M, N]))
+    return _to_dtype(rng.standard_normal((M, N), dtype=np.float32) * np.float32(GRAD_STD), dtype)
 
 
 def make_custom(M: int, K: int, N: int, dtype: str = "bf16", seed: int = 0,
