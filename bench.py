@@ -32,7 +32,7 @@ METRIC = "FP4 quantized-linear TFLOPS & % dense FP4 MFMA peak; quantizer HBM GB/
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak (10.1 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak (5.0 PFLOP/s)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fp4_gemm_llama7b_gate_up.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_llama7b_gate_up.json")
 GEMM_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "gemm.hip")
 
 
@@ -73,6 +73,21 @@ def time_on_stream(fn, steps: int, warmup: int, rounds: int = 3) -> float:
         torch.cuda.synchronize()
         out.append(e0.elapsed_time(e1) / steps)
     return sorted(out)[len(out) // 2]
+
+
+def gemm_kernel(M: int, N: int, K: int) -> str:
+    """Name of the GEMM kernel the library launches for this shape (its selection rule: the
+    persistent 256 x 256 kernel when K % 512 == 0 and there are at least four such tiles per
+    CU, else the 256 x 128 kernel)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wide = (K % 512 == 0 and ((M + 255) // 256) * ((N + 255) // 256) >= 4 * cus
+            and os.environ.get("FP4_GEMM_WIDE", "1") != "0")
+    return "k_fp4_gemm_wide" if wide else "k_fp4_gemm"
+
+
+def _kernel_is(name: str):
+    """Predicate on rocprofv3 kernel names: the templated kernel `name`, no other."""
+    return lambda n: n.replace("void ", "").startswith(f"fp4::{name}<")
 
 
 def gemm_src_sha() -> str:
@@ -147,16 +162,22 @@ def _counter_per_dispatch(d: str, counter: str, kernel_pred) -> float:
 
 
 def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write: str):
-    """HBM bytes per k_fp4_gemm launch (and per k_comp_apply launch) on the 7B gate+up shape:
+    """HBM bytes per GEMM launch (and per k_comp_apply launch) on the 7B gate+up shape:
     FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the bytes a plain 1 GiB copy moves
     per unit of the same counter.  Written with the hash of the GEMM source it was measured on."""
-    is_gemm = lambda n: "k_fp4_gemm" in n  # noqa: E731
-    is_comp = lambda n: "k_comp_apply" in n  # noqa: E731
+    # the GEMM kernel the library picked for this shape: the one present in the counters
+    kname = "k_fp4_gemm_wide"
+    try:
+        _counter_per_dispatch(gemm_fetch, "FETCH_SIZE", _kernel_is(kname))
+    except SystemExit:
+        kname = "k_fp4_gemm"
+    is_gemm = _kernel_is(kname)
+    is_comp = _kernel_is("k_comp_apply")
     is_copy = lambda n: "copyBuffer" in n  # noqa: E731
     c_f = _counter_per_dispatch(copy_fetch, "FETCH_SIZE", is_copy)
     c_w = _counter_per_dispatch(copy_write, "WRITE_SIZE", is_copy)
     f_fetch, f_write = (1 << 30) / c_f, (1 << 30) / c_w
-    rec = {"gemm_src_sha": gemm_src_sha(), "workload": "llama7b_gate_up",
+    rec = {"gemm_src_sha": gemm_src_sha(), "workload": "llama7b_gate_up", "gemm_kernel": kname,
            "copy_fetch_size": c_f, "copy_write_size": c_w,
            "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write}
     for name, pred in (("gemm", is_gemm), ("comp", is_comp)):
@@ -253,7 +274,8 @@ def run_backward(args):
         "dtype": "fp4e2m1 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": L.name + "_backward", "M": M, "K": K, "N": N, "in_dtype": L.dtype,
                    "out_dtype": L.dtype, "grad_std": 1e-3},
-        "roofline": {"bound": "mfma", "kernel": "k_fp4_gemm", "achieved": round(g_tf, 1), "peak": PEAK_FP4_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": {"dA": gemm_kernel(M, K, N), "dW": gemm_kernel(K, N, M)},
+                     "achieved": round(g_tf, 1), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g_tf / PEAK_FP4_TFLOPS, 4),
                      "ms_dA": round(ms_a, 4), "ms_dW": round(ms_w, 4)},
         "operand_prep": {"bound": "hbm", "ms": round(q_ms, 4), "algorithmic_bytes": qb,
@@ -429,7 +451,7 @@ def main():
                    "out_dtype": first.out_dtype, "q": first.q, "layers": len(runs), "w_quant": args.wq,
                    "parallelism": "none (1 GPU)"},
         "forward_frac_of_fp4_peak": round(fwd_tflops / PEAK_FP4_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "k_fp4_gemm", "achieved": round(gemm_tflops, 1),
+        "roofline": {"bound": "mfma", "kernel": gemm_kernel(first.M, first.N, first.K), "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(gemm_ms, 4)},
         "compensation": {"bound": "hbm", "kernel": "k_comp_apply", "achieved": round(cbytes / comp_ms / 1e6, 1),

@@ -18,6 +18,10 @@
 // Epilogue: Y = fl(fl(acc * sA) * sW); each wave reorders its result tiles through a
 // private patch of LDS so that the stores are 16 bytes per lane along rows.  The sparse compensation
 // dA . W is a separate kernel (comp.hip) that runs on the fp32 result.
+//
+// Large products (K a multiple of 512 and at least four 256 x 256 tiles per CU) run on a
+// second, persistent kernel with 256 x 256 tiles (see "wide tiles" below); both compute the
+// same exact accumulator and epilogue, so their outputs are identical.
 #include "fp4_common.h"
 #include "fp4_launch.h"
 
@@ -59,17 +63,18 @@ struct Book {
     float sW[BN];
 };
 
-// One stage of DMA for this wave: 4 loads of A (rows 64w..64w+63) and 2 of B (rows
-// 32w..32w+31).  Lane i of a load fills slot 64*blk + i: row 16*blk + i/4, at the swizzled
+// One stage of DMA for this wave: 4 loads of A (rows 64w..64w+63) and NB of B (rows
+// 16*NB*w ..).  Lane i of a load fills slot 64*blk + i: row 16*blk + i/4, at the swizzled
 // position i%4.  KFULL (K a multiple of 128: every stage is whole): the stage's K offset
 // goes in the scalar offset and rows past the matrix read zeros through their offset
 // alone; the look-ahead stages past the end reload the last stage (never consumed), so
 // every address stays inside its row.  Otherwise each lane also checks its chunk against
-// K, so a partial last stage and the stages past the end read zeros.
-template <bool KFULL>
+// K, so a partial last stage and the stages past the end read zeros.  opa: bytes of the
+// A tile in the stage buffer.
+template <bool KFULL, int NB>
 __device__ __forceinline__ void stage_dma(__amdgpu_buffer_rsrc_t rsA, __amdgpu_buffer_rsrc_t rsB, uint8_t *buf,
-                                          int wave, const int (&offA)[4], const int (&offB)[2], int kt, int KB,
-                                          int lane_chunk16) {
+                                          int wave, const int (&offA)[4], const int (&offB)[NB], int kt, int KB,
+                                          int lane_chunk16, int opa = OPA) {
     const bool kin = KFULL || kt * BKB + lane_chunk16 < KB;
     const int soff = KFULL ? min(kt, KB / BKB - 1) * BKB : 0;
 #pragma unroll
@@ -78,23 +83,26 @@ __device__ __forceinline__ void stage_dma(__amdgpu_buffer_rsrc_t rsA, __amdgpu_b
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, LDS_PTR(buf + (wave * 4 + j) * 1024), 16, oa, soff, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NB; ++j) {
         const int ob = KFULL ? offB[j] : ((kin && offB[j] != OOB) ? offB[j] + kt * BKB : OOB);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, LDS_PTR(buf + OPA + (wave * 2 + j) * 1024), 16, ob, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, LDS_PTR(buf + opa + (wave * NB + j) * 1024), 16, ob, soff, 0,
+                                                 0);
     }
 }
 
 // Fragments of K-step s (0 or 1) of a stage: lane l reads row l%32 of each 32-row tile and
-// the 16-byte chunk 2s + l/32 (32 codes).
+// the 16-byte chunk 2s + l/32 (32 codes).  The wave's tiles: 4 of A from row 128*wm and NJ
+// of B from row 32*NJ*wn.
+template <int NJ>
 __device__ __forceinline__ void frag_load(const uint8_t *buf, int wm, int wn, int lane, int s, u32x4 (&a)[4],
-                                          u32x4 (&b)[2]) {
+                                          u32x4 (&b)[NJ], int opa = OPA) {
     const int chunk = 2 * s + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         a[i] = *reinterpret_cast<const u32x4 *>(buf + slot16(wm * 128 + i * 32 + (lane & 31), chunk) * 16);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const u32x4 *>(buf + OPA + slot16(wn * 64 + j * 32 + (lane & 31), chunk) * 16);
+    for (int j = 0; j < NJ; ++j)
+        b[j] = *reinterpret_cast<const u32x4 *>(buf + opa + slot16(wn * 32 * NJ + j * 32 + (lane & 31), chunk) * 16);
 }
 
 // FP8 operands (the emulation path): lane l reads row l%32 and the two 16-byte chunks
@@ -130,12 +138,13 @@ __device__ __forceinline__ void mfma_block8(v16f (&acc)[4][2], const u32x4 (&a)[
     }
 }
 
-__device__ __forceinline__ void mfma_block(v16f (&acc)[4][2], const u32x4 (&a)[4], const u32x4 (&b)[2]) {
+template <int NJ>
+__device__ __forceinline__ void mfma_block(v16f (&acc)[4][NJ], const u32x4 (&a)[4], const u32x4 (&b)[NJ]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const v8i av = v8i{(int)a[i].x, (int)a[i].y, (int)a[i].z, (int)a[i].w, 0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const v8i bv = v8i{(int)b[j].x, (int)b[j].y, (int)b[j].z, (int)b[j].w, 0, 0, 0, 0};
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 0, UNIT_SCALE, 0,
                                                                         UNIT_SCALE);
@@ -362,6 +371,255 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     }
 }
 
+// ----------------------------------------------------------------------------- wide tiles
+// For large products: a 256 x 256 tile per workgroup, 4 waves of 128 x 128 (4 x 4 MFMA tiles:
+// 8 fragment reads per 16 MFMAs instead of 6 per 8, and a third less operand traffic per
+// output than 256 x 128), one workgroup per CU (the accumulators fill the 256 AGPRs), four
+// LDS stage buffers (three stages of look-ahead) and a barrier between the two K-steps of a
+// stage.  Persistent: the workgroup walks its XCD's tiles, and the DMA of the next tile's
+// first four stages is issued during the current tile's last four steps, so they land while
+// the epilogue runs.  Needs K % 512 == 0 (whole groups of four 128-code stages).
+constexpr int WBN = 256;
+constexpr int WSTB = (BM + WBN) * BKB;  // 32 KiB per stage buffer
+
+struct WBook {
+    float sA[BM];
+    float sW[WBN];
+};
+
+// 16 MFMAs with 8 fragment reads spread among them
+#define INTERLEAVE16()                                         \
+    do {                                                       \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q) {        \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
+        }                                                      \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     \
+    } while (0)
+
+template <int YDT, bool ACCOUT>
+__global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t sb0[WSTB];
+    __shared__ __attribute__((aligned(16))) uint8_t sb1[WSTB];
+    __shared__ __attribute__((aligned(16))) uint8_t sb2[WSTB];
+    __shared__ __attribute__((aligned(16))) uint8_t sb3[WSTB];
+    __shared__ __attribute__((aligned(16))) float patch[NW][1024];
+    __shared__ __attribute__((aligned(16))) WBook bk[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const int tiles = p.tilesM * p.tilesN;
+    const int per_xcd_wg = gridDim.x / 8;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int tpx = (tiles + 7) / 8;
+    const int hi = min((xcd + 1) * tpx, tiles);
+    int logical = xcd * tpx + slot;
+    if (logical >= hi) return;
+
+    auto origin = [&](int lg, int &m0, int &n0) {
+        const int group = lg / (p.raster_group * p.tilesN);
+        const int first_m = group * p.raster_group;
+        const int gm = min(p.raster_group, p.tilesM - first_m);
+        const int in_group = lg - group * p.raster_group * p.tilesN;
+        m0 = (first_m + in_group % gm) * BM;
+        n0 = (in_group / gm) * WBN;
+    };
+    const int KB = K / 2;
+    const int kstages = KB / BKB;  // a multiple of 4
+    const __amdgpu_buffer_rsrc_t rsA =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.Aq), 0, M * KB, BUF_FLAGS);
+    const __amdgpu_buffer_rsrc_t rsB =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.Wq), 0, N * KB, BUF_FLAGS);
+    const int lane_chunk16 = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+    auto offsets = [&](int m0, int n0, int (&oa)[4], int (&ob)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = (wave * 4 + j) * 16 + (lane >> 2);
+            oa[j] = (m0 + r < M) ? (m0 + r) * KB + lane_chunk16 : OOB;
+            ob[j] = (n0 + r < N) ? (n0 + r) * KB + lane_chunk16 : OOB;
+        }
+    };
+    int m0, n0, offA[4], offB[4];
+    origin(logical, m0, n0);
+    offsets(m0, n0, offA, offB);
+
+    v16f acc[4][4];
+    u32x4 a0[4], b0[4], a1[4], b1[4];
+
+    // prologue of the first tile
+    stage_dma<true, 4>(rsA, rsB, sb0, wave, offA, offB, 0, KB, lane_chunk16);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const float bA = (m0 + tid < M) ? p.sA[m0 + tid] : 0.0f;
+        const float bW = (n0 + tid < N) ? p.sW[n0 + tid] : 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+        stage_dma<true, 4>(rsA, rsB, sb1, wave, offA, offB, 1, KB, lane_chunk16);
+        stage_dma<true, 4>(rsA, rsB, sb2, wave, offA, offB, 2, KB, lane_chunk16);
+        stage_dma<true, 4>(rsA, rsB, sb3, wave, offA, offB, 3, KB, lane_chunk16);
+        __builtin_amdgcn_sched_barrier(0);
+        WAIT_VMCNT(24);
+        bk[0].sA[tid] = bA;
+        bk[0].sW[tid] = bW;
+    }
+    lds_barrier();
+    frag_load(sb0, wm, wn, lane, 0, a0, b0);
+
+    auto step = [&](uint8_t *cur, const uint8_t *nxt, const int (&oa)[4], const int (&ob)[4], int dma_stage,
+                    bool load_next) {
+        __builtin_amdgcn_sched_barrier(0);
+        frag_load(cur, wm, wn, lane, 1, a1, b1);
+        mfma_block(acc, a0, b0);
+        INTERLEAVE16();
+        __builtin_amdgcn_sched_barrier(0);
+        WAIT_VMCNT(16);
+        lds_barrier();
+        stage_dma<true, 4>(rsA, rsB, cur, wave, oa, ob, dma_stage, KB, lane_chunk16);
+        __builtin_amdgcn_sched_barrier(0);
+        if (load_next) {
+            frag_load(nxt, wm, wn, lane, 0, a0, b0);
+            mfma_block(acc, a1, b1);
+            INTERLEAVE16();
+        } else {
+            mfma_block(acc, a1, b1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    for (int tt = 0;; ++tt) {
+        const int nlog = logical + per_xcd_wg;
+        const bool has_next = nlog < hi;
+        int nm0 = m0, nn0 = n0, noffA[4], noffB[4];
+        if (has_next) origin(nlog, nm0, nn0);
+        offsets(nm0, nn0, noffA, noffB);
+        // without a next tile the last four loads re-read this tile's last stage (in bounds,
+        // never consumed)
+        const int nbase = has_next ? 0 : kstages - 1;
+        const int nstep = has_next ? 1 : 0;
+
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        int kt = 0;
+        for (; kt + 4 < kstages; kt += 4) {
+            step(sb0, sb1, offA, offB, kt + 4, true);
+            step(sb1, sb2, offA, offB, kt + 5, true);
+            step(sb2, sb3, offA, offB, kt + 6, true);
+            step(sb3, sb0, offA, offB, kt + 7, true);
+        }
+        step(sb0, sb1, noffA, noffB, nbase, true);
+        step(sb1, sb2, noffA, noffB, nbase + nstep, true);
+        step(sb2, sb3, noffA, noffB, nbase + 2 * nstep, true);
+        step(sb3, sb0, noffA, noffB, nbase + 3 * nstep, false);
+
+        // pin the accumulators here: keeps the last step's MFMAs (and their fragments) out of
+        // the epilogue's blocks
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+        // next tile's scales, fetched under this epilogue
+        const float nbA = (has_next && nm0 + tid < M) ? p.sA[nm0 + tid] : 0.0f;
+        const float nbW = (has_next && nn0 + tid < N) ? p.sW[nn0 + tid] : 0.0f;
+
+        const WBook &b = bk[tt & 1];
+        float *E = patch[wave];
+        float sw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sw[j] = b.sW[wn * 128 + j * 32 + (lane & 31)];
+        const bool full = (m0 + BM <= M) && (n0 + WBN <= N);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float sa[16];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 v = *reinterpret_cast<const float4 *>(&b.sA[wm * 128 + i * 32 + 8 * r4 + 4 * (lane >> 5)]);
+                sa[4 * r4] = v.x;
+                sa[4 * r4 + 1] = v.y;
+                sa[4 * r4 + 2] = v.z;
+                sa[4 * r4 + 3] = v.w;
+            }
+            const int row0 = m0 + wm * 128 + i * 32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int col0 = n0 + wn * 128 + j * 32;
+                if constexpr (ACCOUT) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int grow = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        if (full || (grow < M && col0 + (lane & 31) < N))
+                            p.acc_out[(size_t)grow * N + col0 + (lane & 31)] = acc[i][j][r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    E[lr * 32 + (lane & 31)] = (acc[i][j][r] * sa[r]) * sw[j];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                f4 e[4];
+                if constexpr (YDT == DT_BF16) {
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        e[2 * k] = *reinterpret_cast<const f4 *>(&E[8 * (k * 64 + lane)]);
+                        e[2 * k + 1] = *reinterpret_cast<const f4 *>(&E[8 * (k * 64 + lane) + 4]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const int c = k * 64 + lane, lr = c >> 2, cc = (c & 3) * 8;
+                        const f4 e0 = e[2 * k], e1 = e[2 * k + 1];
+                        const int grow = row0 + lr, gcol = col0 + cc;
+                        if (full || (grow < M && gcol < N)) {
+                            v4i o;
+                            o[0] = (int)(f32_to_bf16_bits(e0[0]) | (f32_to_bf16_bits(e0[1]) << 16));
+                            o[1] = (int)(f32_to_bf16_bits(e0[2]) | (f32_to_bf16_bits(e0[3]) << 16));
+                            o[2] = (int)(f32_to_bf16_bits(e1[0]) | (f32_to_bf16_bits(e1[1]) << 16));
+                            o[3] = (int)(f32_to_bf16_bits(e1[2]) | (f32_to_bf16_bits(e1[3]) << 16));
+                            __builtin_nontemporal_store(
+                                o, reinterpret_cast<v4i *>(reinterpret_cast<uint16_t *>(p.Y) + (size_t)grow * N + gcol));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) e[k] = *reinterpret_cast<const f4 *>(&E[4 * (k * 64 + lane)]);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int c = k * 64 + lane, lr = c >> 3, cc = (c & 7) * 4;
+                        const int grow = row0 + lr, gcol = col0 + cc;
+                        if (full || (grow < M && gcol < N))
+                            __builtin_nontemporal_store(
+                                e[k], reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.Y) + (size_t)grow * N + gcol));
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+        bk[(tt + 1) & 1].sA[tid] = nbA;
+        bk[(tt + 1) & 1].sW[tid] = nbW;
+        if (!has_next) break;
+        // the next tile's stage 0 landed before the last step's barrier
+        frag_load(sb0, wm, wn, lane, 0, a0, b0);
+        logical = nlog;
+        m0 = nm0;
+        n0 = nn0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            offA[j] = noffA[j];
+            offB[j] = noffB[j];
+        }
+    }
+    WAIT_VMCNT(0);
+}
+
 // Tile-rows per column sweep within an XCD.  FP4_GEMM_RASTER overrides (tuning aid).
 static int raster_group_for(int tilesM) {
     static int env = -2;
@@ -371,6 +629,29 @@ static int raster_group_for(int tilesM) {
     }
     const int g = env > 0 ? env : 4;
     return g < tilesM ? g : tilesM;
+}
+
+// CUs of the current device (the persistent grid's size), looked up once per device.
+static int num_cus() {
+    static int cache[64];
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 0;
+    int n = __atomic_load_n(&cache[d], __ATOMIC_RELAXED);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) return 0;
+        __atomic_store_n(&cache[d], n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+
+// FP4_GEMM_WIDE=0 keeps every product on the 256 x 128 kernel (a tuning aid).
+static bool wide_gemm_enabled() {
+    static int env = -2;
+    if (env == -2) {
+        const char *e = getenv("FP4_GEMM_WIDE");
+        env = e ? atoi(e) : 1;
+    }
+    return env != 0;
 }
 
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
@@ -388,6 +669,24 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
     p.tilesM = (int)((M + BM - 1) / BM);
     p.tilesN = (int)((N + BN - 1) / BN);
     p.raster_group = raster_group_for(p.tilesM);
+    // wide persistent tiles when there are enough of them to keep every CU busy for a few
+    // rounds (few large tiles would leave the per-tile prologue and epilogue exposed)
+    if (!f8 && K % 512 == 0 && wide_gemm_enabled()) {
+        const int cus = num_cus();
+        const int64_t wtiles = ((M + BM - 1) / BM) * ((N + WBN - 1) / WBN);
+        if (cus >= 8 && wtiles >= 4 * (int64_t)cus) {
+            p.tilesN = (int)((N + WBN - 1) / WBN);
+            const int blocks = cus / 8 * 8;
+            if (y_dt == DT_BF16) {
+                if (acc_out) hipLaunchKernelGGL((k_fp4_gemm_wide<DT_BF16, true>), dim3(blocks), dim3(NT), 0, s, p);
+                else hipLaunchKernelGGL((k_fp4_gemm_wide<DT_BF16, false>), dim3(blocks), dim3(NT), 0, s, p);
+            } else {
+                if (acc_out) hipLaunchKernelGGL((k_fp4_gemm_wide<DT_F32, true>), dim3(blocks), dim3(NT), 0, s, p);
+                else hipLaunchKernelGGL((k_fp4_gemm_wide<DT_F32, false>), dim3(blocks), dim3(NT), 0, s, p);
+            }
+            return hipGetLastError();
+        }
+    }
     const int64_t tiles = (int64_t)p.tilesM * p.tilesN;
     const int blocks = (int)((tiles + 7) / 8 * 8);
     const bool kfull = f8 ? (K % 64 == 0) : (K % 128 == 0);  // every stage whole

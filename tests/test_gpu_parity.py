@@ -195,6 +195,29 @@ def test_gemm_accumulator_exact(M, N, K):
     assert np.array_equal(to_np(Y), ref_y)  # no compensation: the dequantized product is bit-exact
 
 
+# More output tiles than the chip has CUs, ragged in both dimensions, K a multiple of 512: the
+# product then walks several tiles per workgroup.  Checked at sampled outputs plus whole
+# edge rows and columns.
+@pytest.mark.parametrize("M,N,K,out", [(4200, 4136, 1024, "fp32"), (4352, 4360, 512, "bf16"), (1030, 9000, 2048, "fp32")])
+def test_gemm_many_tiles(M, N, K, out):
+    _say(f"gemm many tiles {M}x{N}x{K} -> {out}")
+    rng = np.random.default_rng(M + N + K)
+    Aq, Wq = _random_codes(rng, M, K), _random_codes(rng, N, K)
+    sA = rng.lognormal(-2, 1, M).astype(np.float32)
+    sW = rng.lognormal(-4, 1, N).astype(np.float32)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    Y, acc = fp4.gemm(t(Aq), t(sA), t(Wq), t(sW), K, out_dtype=_dt(out), acc_out=True)
+    ms = np.concatenate([rng.integers(0, M, 20000), np.full(N, M - 1), np.arange(M), np.zeros(N, dtype=np.int64)])
+    ns = np.concatenate([rng.integers(0, N, 20000), np.arange(N), np.full(M, N - 1), np.arange(N)])
+    idx = torch.from_numpy(ms * N + ns).to(DEV)
+    g_acc = acc.view(-1)[idx].cpu().numpy()
+    r_acc = oracle.accumulate_pairs(Aq, Wq, K, ms, ns)
+    assert np.array_equal(g_acc, r_acc)
+    r_y, _ = oracle.output_pairs(r_acc, sA, sW, ms, ns, None, None, None, np.zeros((1, N), dtype=np.float32))
+    g_y = to_np(Y.view(-1)[idx])
+    assert np.array_equal(g_y, r_y if out == "fp32" else oracle.to_bf16(r_y))
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 264, 320), (513, 776, 1056), (64, 8, 32), (257, 136, 96)])
 def test_gemm_fp8_emulation(M, N, K):
     """FP4 codes expanded to E4M3 and multiplied on the FP8 matrix cores: the accumulator
