@@ -475,14 +475,26 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         WAIT_VMCNT(16);
         lds_barrier();
+        // the refill's eight loads and the next fragments' eight reads go between the
+        // K-step-1 MFMAs, so the matrix core restarts right after the barrier
         stage_dma<true, 4>(rsA, rsB, cur, wave, oa, ob, dma_stage, KB, lane_chunk16);
-        __builtin_amdgcn_sched_barrier(0);
         if (load_next) {
             frag_load(nxt, wm, wn, lane, 0, a0, b0);
             mfma_block(acc, a1, b1);
-            INTERLEAVE16();
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load to LDS
+            }
         } else {
             mfma_block(acc, a1, b1);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -532,6 +544,18 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) sw[j] = b.sW[wn * 128 + j * 32 + (lane & 31)];
         const bool full = (m0 + BM <= M) && (n0 + WBN <= N);
+        // Row-major read-back of a 32 x 32 patch, the same lanes for every tile: chunk
+        // c = 64k + lane holds row c/8, columns 4(c%8).. (fp32) or row c/4, columns 8(c%4).. (bf16).
+        constexpr int NK = YDT == DT_BF16 ? 2 : 4;
+        int lrow[NK], lcol[NK];
+        uint32_t loff[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            const int c = k * 64 + lane;
+            lrow[k] = YDT == DT_BF16 ? c >> 2 : c >> 3;
+            lcol[k] = YDT == DT_BF16 ? (c & 3) * 8 : (c & 7) * 4;
+            loff[k] = (uint32_t)lrow[k] * (uint32_t)N + (uint32_t)lcol[k];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sa[16];
@@ -556,14 +580,14 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                             p.acc_out[(size_t)grow * N + col0 + (lane & 31)] = acc[i][j][r];
                     }
                 }
+                // The patch is private to the wave and a wave's LDS accesses execute in
+                // order, so the read-back sees these writes and the next tile's writes
+                // cannot overtake it: no barrier.
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                     E[lr * 32 + (lane & 31)] = (acc[i][j][r] * sa[r]) * sw[j];
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 f4 e[4];
                 if constexpr (YDT == DT_BF16) {
 #pragma unroll
@@ -571,36 +595,45 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                         e[2 * k] = *reinterpret_cast<const f4 *>(&E[8 * (k * 64 + lane)]);
                         e[2 * k + 1] = *reinterpret_cast<const f4 *>(&E[8 * (k * 64 + lane) + 4]);
                     }
+                    v4i o[2];
 #pragma unroll
                     for (int k = 0; k < 2; ++k) {
-                        const int c = k * 64 + lane, lr = c >> 2, cc = (c & 3) * 8;
                         const f4 e0 = e[2 * k], e1 = e[2 * k + 1];
-                        const int grow = row0 + lr, gcol = col0 + cc;
-                        if (full || (grow < M && gcol < N)) {
-                            v4i o;
-                            o[0] = (int)(f32_to_bf16_bits(e0[0]) | (f32_to_bf16_bits(e0[1]) << 16));
-                            o[1] = (int)(f32_to_bf16_bits(e0[2]) | (f32_to_bf16_bits(e0[3]) << 16));
-                            o[2] = (int)(f32_to_bf16_bits(e1[0]) | (f32_to_bf16_bits(e1[1]) << 16));
-                            o[3] = (int)(f32_to_bf16_bits(e1[2]) | (f32_to_bf16_bits(e1[3]) << 16));
-                            __builtin_nontemporal_store(
-                                o, reinterpret_cast<v4i *>(reinterpret_cast<uint16_t *>(p.Y) + (size_t)grow * N + gcol));
+                        o[k][0] = (int)(f32_to_bf16_bits(e0[0]) | (f32_to_bf16_bits(e0[1]) << 16));
+                        o[k][1] = (int)(f32_to_bf16_bits(e0[2]) | (f32_to_bf16_bits(e0[3]) << 16));
+                        o[k][2] = (int)(f32_to_bf16_bits(e1[0]) | (f32_to_bf16_bits(e1[1]) << 16));
+                        o[k][3] = (int)(f32_to_bf16_bits(e1[2]) | (f32_to_bf16_bits(e1[3]) << 16));
+                    }
+                    uint16_t *Yb = reinterpret_cast<uint16_t *>(p.Y);
+                    if (full) {
+                        uint16_t *base = Yb + (size_t)row0 * N + col0;
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) __builtin_nontemporal_store(o[k], reinterpret_cast<v4i *>(base + loff[k]));
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const int grow = row0 + lrow[k], gcol = col0 + lcol[k];
+                            if (grow < M && gcol < N)
+                                __builtin_nontemporal_store(o[k], reinterpret_cast<v4i *>(Yb + (size_t)grow * N + gcol));
                         }
                     }
                 } else {
 #pragma unroll
                     for (int k = 0; k < 4; ++k) e[k] = *reinterpret_cast<const f4 *>(&E[4 * (k * 64 + lane)]);
+                    float *Yf = reinterpret_cast<float *>(p.Y);
+                    if (full) {
+                        float *base = Yf + (size_t)row0 * N + col0;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int c = k * 64 + lane, lr = c >> 3, cc = (c & 7) * 4;
-                        const int grow = row0 + lr, gcol = col0 + cc;
-                        if (full || (grow < M && gcol < N))
-                            __builtin_nontemporal_store(
-                                e[k], reinterpret_cast<f4 *>(reinterpret_cast<float *>(p.Y) + (size_t)grow * N + gcol));
+                        for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(e[k], reinterpret_cast<f4 *>(base + loff[k]));
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int grow = row0 + lrow[k], gcol = col0 + lcol[k];
+                            if (grow < M && gcol < N)
+                                __builtin_nontemporal_store(e[k], reinterpret_cast<f4 *>(Yf + (size_t)grow * N + gcol));
+                        }
                     }
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         }
         bk[(tt + 1) & 1].sA[tid] = nbA;
