@@ -227,13 +227,13 @@ def run_fp8codec(steps: int, warmup: int):
 
 
 def bwd_quantizer_bytes(M, K, N, bi) -> int:
-    """Algorithmic HBM bytes of the backward's operand preparation: dY read once for the
-    per-row quantization of G = dY * sW and twice for the per-column quantization of
-    H = sA * dY (a column's maximum must be known before any of its codes), codes and
-    scales written; the forward's codes read and written transposed."""
-    g = M * N * bi + M * N // 2 + 4 * N + 4 * M
-    h = 2 * M * N * bi + M * N // 2 + 4 * M + 4 * N
-    return g + h + K * N + M * K
+    """Algorithmic HBM bytes of the backward's operand preparation: dY read twice (a column's
+    maximum of H = sA * dY must be known before any of its codes; the first read also gives
+    G = dY * sW its row maxima and codes), the codes and scales of G and H written, and the
+    forward's codes read and written transposed."""
+    reads = 2 * M * N * bi + 4 * N + 4 * M
+    writes = M * N // 2 + 4 * M + M * N // 2 + 4 * N
+    return reads + writes + K * N + M * K
 
 
 def run_backward(args):

@@ -248,7 +248,8 @@ fp4_status fp4_linear_forward_wq(const void *A, const void *W, const uint8_t *Wq
  *       holds the intermediates at the fp4_backward_layout offsets (Gq, sG, WqT when dA
  *       was asked for; Hq, sH, AqT when dW was).
  * Kernels, in stream order: fill, [row quantization of G, transpose of Wq, GEMM],
- * [column quantization of H, transpose of Aq, GEMM].
+ * [column quantization of H, transpose of Aq, GEMM]; for both products of a bf16 dY with
+ * N <= 24576 the row quantization of G also collects H's column maxima (dY read once less).
  * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
 struct fp4_bwd_layout {
     size_t total;        /* bytes needed */
@@ -256,6 +257,7 @@ struct fp4_bwd_layout {
     size_t Hq, sH;       /* N x M/2 codes, fp32[N] */
     size_t WqT, AqT;     /* K x N/2 and K x M/2 codes */
     size_t ones;         /* fp32[K], internal */
+    size_t part;         /* 512 x N column-maximum keys, internal */
 };
 fp4_status fp4_backward_layout(int64_t M, int64_t K, int64_t N, struct fp4_bwd_layout *out);
 size_t fp4_backward_workspace_bytes(int64_t M, int64_t K, int64_t N);

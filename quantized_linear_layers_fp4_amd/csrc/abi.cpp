@@ -3,6 +3,7 @@
 // before the first HIP call; the library never allocates or synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -407,6 +408,8 @@ fp4_status fp4_linear_forward_wq(const void *A, const void *W, const uint8_t *Wq
 }
 
 // ----------------------------------------------------------------------------- backward
+// Workgroups of the fused pass over a bf16 dY (each leaves one row of column-maximum keys).
+constexpr int BWD_PART_ROWS = 512;
 // Shapes of the straight-through backward: the forward's (Aq, Wq), and each requested
 // product's contraction (n for dA, m for dW) within the GEMM's K limits.
 static fp4_status bwd_shape(int64_t M, int64_t K, int64_t N, bool want_dA, bool want_dW) {
@@ -428,6 +431,7 @@ fp4_status fp4_backward_layout(int64_t M, int64_t K, int64_t N, struct fp4_bwd_l
     out->WqT = off; off += align_up((size_t)K * (size_t)(N / 2));
     out->AqT = off; off += align_up((size_t)K * (size_t)(M / 2));
     out->ones = off; off += align_up((size_t)K * 4);
+    out->part = off; off += align_up((size_t)BWD_PART_ROWS * (size_t)N * 4);
     out->total = off;
     return FP4_OK;
 }
@@ -462,19 +466,27 @@ fp4_status fp4_linear_backward(const void *dY, int32_t dy_dtype, int64_t M, int6
     float *ones = reinterpret_cast<float *>(ws + l.ones);
     const int dt = dt_of(dy_dtype);
     hipError_t e = launch_fill_f32(ones, K, 1.0f, s);
+    uint8_t *Gq = ws + l.Gq, *WqT = ws + l.WqT, *Hq = ws + l.Hq, *AqT = ws + l.AqT;
+    float *sG = reinterpret_cast<float *>(ws + l.sG), *sH = reinterpret_cast<float *>(ws + l.sH);
+    // Both products of a bf16 dY with rows up to 24576: one pass reads dY for G's codes and for
+    // H's column maxima together, so dY is read twice in all instead of three times.
+    const bool fused = want_dA && want_dW && dt == DT_BF16 && fused_rows_cpt(N) <= 3;
+    if (fused) {
+        const int G = (int)std::min<int64_t>(M, std::min(BWD_PART_ROWS, cus));  // one 1024-thread workgroup per CU
+        if (e == hipSuccess)
+            e = launch_bwd_rows_fused(dY, M, N, sW, sA, Gq, sG, reinterpret_cast<uint32_t *>(ws + l.part), G,
+                                      reinterpret_cast<uint32_t *>(sH), s);
+    }
     if (want_dA && e == hipSuccess) {
         // dA = deq(Q_rows(dY * sW)) . value(Wq)^T: GEMM with M rows, K columns, contraction N
-        uint8_t *Gq = ws + l.Gq, *WqT = ws + l.WqT;
-        float *sG = reinterpret_cast<float *>(ws + l.sG);
-        e = launch_scaled_quant_rows(dY, dt, M, N, sW, Gq, sG, s);
+        if (!fused) e = launch_scaled_quant_rows(dY, dt, M, N, sW, Gq, sG, s);
         if (e == hipSuccess) e = launch_codes_transpose(Wq, N, K, WqT, s);
         if (e == hipSuccess) e = launch_gemm(Gq, sG, WqT, ones, M, K, N, dA, dt_of(da_dtype), nullptr, s);
     }
     if (want_dW && e == hipSuccess) {
         // dW = value(Aq)^T . deq(Q_cols(sA * dY)): GEMM with K rows, N columns, contraction M
-        uint8_t *Hq = ws + l.Hq, *AqT = ws + l.AqT;
-        float *sH = reinterpret_cast<float *>(ws + l.sH);
-        e = launch_quant_cols(dY, dt, M, N, sH, Hq, false, s, sA);
+        if (fused) e = launch_quant_cols_keyed(dY, dt, M, N, sH, Hq, sA, s);
+        else e = launch_quant_cols(dY, dt, M, N, sH, Hq, false, s, sA);
         if (e == hipSuccess) e = launch_codes_transpose(Aq, M, K, AqT, s);
         if (e == hipSuccess) e = launch_gemm(AqT, ones, Hq, sH, K, N, M, dW, dt_of(dw_dtype), nullptr, s);
     }

@@ -136,6 +136,124 @@ __global__ __launch_bounds__(256) void k_scaled_rows(const void *__restrict__ X,
     }
 }
 
+// Both per-row reads of a bf16 dY in one pass: the token-wise quantization of
+// G = fl(dY[m][n] * sW[n]) as above, and for the channel-wise quantization of
+// H = fl(sA[m] * dY[m][n]) the maximum over the workgroup's rows of |H| for each column,
+// kept by the thread that owns the column (chunk i*1024 + tid) and written once per workgroup
+// as a row of keys into part[blockIdx.x][N].  Workgroup g takes rows g, g + G, g + 2G, ...
+// 1024 threads per row keep the per-thread state (the row's CPT chunks and their 8*CPT
+// column maxima) small enough for two workgroups per CU.
+template <int CPT>
+__global__ __launch_bounds__(1024) void k_bwd_rows_fused(const void *__restrict__ X, int64_t M, int64_t C,
+                                                         const float *__restrict__ mult,
+                                                         const float *__restrict__ row_mult,
+                                                         uint8_t *__restrict__ codes, float *__restrict__ scales,
+                                                         uint32_t *__restrict__ part) {
+    __shared__ uint32_t red[2][16];
+    const int tid = threadIdx.x;
+    const int64_t nchunk = C / 8;
+    // the thread's columns are the same in every row: their multipliers stay in registers
+    float m[CPT][8];
+    uint32_t cmax[CPT][8];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int64_t c = i * 1024 + tid;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            m[i][e] = c < nchunk ? mult[c * 8 + e] : 0.0f;
+            cmax[i][e] = 0u;
+        }
+    }
+    int par = 0;
+    // the next row's loads are issued before this row is processed
+    uint4 raw[CPT][2], nxt[CPT][2];
+    float rm_nxt = 0.0f;
+    auto load_row = [&](int64_t row, uint4 (&dst)[CPT][2]) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            if (i * 1024 + tid < nchunk) load_raw8<DT_BF16>(X, row * C + (int64_t)(i * 1024 + tid) * 8, dst[i]);
+    };
+    if (blockIdx.x < M) {
+        load_row(blockIdx.x, nxt);
+        rm_nxt = row_mult[blockIdx.x];
+    }
+    for (int64_t row = blockIdx.x; row < M; row += gridDim.x, par ^= 1) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            raw[i][0] = nxt[i][0];
+            raw[i][1] = nxt[i][1];
+        }
+        const float rm = rm_nxt;
+        if (row + gridDim.x < M) {
+            load_row(row + gridDim.x, nxt);
+            rm_nxt = row_mult[row + gridDim.x];
+        }
+        float g[CPT][8];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = i * 1024 + tid;
+            if (c < nchunk) {
+                const uint32_t w[4] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = bf16_to_f32((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+                    g[i][e] = v * m[i][e];
+                    mx = max(mx, __float_as_uint(g[i][e]) & 0x7FFFFFFFu);
+                    cmax[i][e] = max(cmax[i][e], __float_as_uint(rm * v) & 0x7FFFFFFFu);
+                }
+            }
+        }
+        // one slot set per row parity: a wave may start the next row's reduction while a
+        // slower wave still reads this one's
+        mx = wave_max_u32(mx);
+        if ((tid & 63) == 0) red[par][tid >> 6] = mx;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < 16; ++w) mx = max(mx, red[par][w]);
+        float r, s;
+        vector_scale(__uint_as_float(mx), r, s);
+        if (tid == 0) scales[row] = s;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t c = i * 1024 + tid;
+            if (c < nchunk) {
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = g[i][e] * r;
+                *reinterpret_cast<uint32_t *>(codes + row * (C / 2) + c * 4) = e2m1_pack8(y);
+            }
+        }
+    }
+    uint32_t *out = part + (int64_t)blockIdx.x * C;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int64_t c = i * 1024 + tid;
+        if (c < nchunk) {
+            uint4 *o = reinterpret_cast<uint4 *>(out + c * 8);
+            o[0] = make_uint4(cmax[i][0], cmax[i][1], cmax[i][2], cmax[i][3]);
+            o[1] = make_uint4(cmax[i][4], cmax[i][5], cmax[i][6], cmax[i][7]);
+        }
+    }
+}
+
+// keys[n] = max over the G partial rows of part[g][n]; eight rows' loads in flight per thread.
+__global__ __launch_bounds__(256) void k_colmax_reduce(const uint32_t *__restrict__ part, int G, int64_t C,
+                                                       uint32_t *__restrict__ keys) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= C) return;
+    uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int g = 0;
+    for (; g + 8 <= G; g += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m[u] = max(m[u], part[(int64_t)(g + u) * C + n]);
+    }
+    for (; g < G; ++g) m[0] = max(m[0], part[(int64_t)g * C + n]);
+#pragma unroll
+    for (int u = 1; u < 8; ++u) m[0] = max(m[0], m[u]);
+    keys[n] = m[0];
+}
+
 __global__ void k_fill_f32(float *__restrict__ p, int64_t n, float v) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = v;
@@ -164,6 +282,22 @@ hipError_t launch_scaled_quant_rows(const void *X, int dt, int64_t R, int64_t C,
     else if (per <= 24) SR(24);
     else SR(32);
 #undef SR
+    return hipGetLastError();
+}
+
+int fused_rows_cpt(int64_t C) { return (int)((C / 8 + 1023) / 1024); }
+
+hipError_t launch_bwd_rows_fused(const void *X, int64_t M, int64_t C, const float *mult, const float *row_mult,
+                                 uint8_t *codes, float *scales, uint32_t *part, int G, uint32_t *keys,
+                                 hipStream_t s) {
+    const int per = fused_rows_cpt(C);
+#define FR(CPT) hipLaunchKernelGGL((k_bwd_rows_fused<CPT>), dim3((unsigned)G), dim3(1024), 0, s, X, M, C, mult, \
+                                   row_mult, codes, scales, part)
+    if (per <= 1) FR(1);
+    else if (per <= 2) FR(2);
+    else FR(3);
+#undef FR
+    hipLaunchKernelGGL(k_colmax_reduce, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, s, part, G, C, keys);
     return hipGetLastError();
 }
 

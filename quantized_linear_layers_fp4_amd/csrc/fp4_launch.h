@@ -30,6 +30,17 @@ hipError_t launch_codes_transpose(const uint8_t *in, int64_t R, int64_t C, uint8
 hipError_t launch_scaled_quant_rows(const void *X, int dt, int64_t R, int64_t C, const float *mult, uint8_t *codes,
                                     float *scales, hipStream_t s);
 hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
+// One read of a bf16 X (M x C, C <= 24576): token-wise codes/scales of fl(X * mult[col]) and
+// the column-maximum keys of |fl(row_mult[row] * X)| (per-workgroup partials in part, G x C
+// keys, then reduced into keys[C]).  G workgroups, G <= M.
+int fused_rows_cpt(int64_t C);
+hipError_t launch_bwd_rows_fused(const void *X, int64_t M, int64_t C, const float *mult, const float *row_mult,
+                                 uint8_t *codes, float *scales, uint32_t *part, int G, uint32_t *keys,
+                                 hipStream_t s);
+// The channel-wise quantization of fl(row_mult[k] * W[k][n]) with the column-maximum keys
+// already in scales_as_keys (turned into scales at the end).
+hipError_t launch_quant_cols_keyed(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
+                                   uint8_t *codes, const float *row_mult, hipStream_t s);
 
 // FP4 GEMM + dequantization: Y = fl(fl(acc * sA) * sW) in y_dt.  acc_out: NULL or fp32[M*N].
 // f8: Aq (M x K) and Wq (N x K) hold E4M3 bytes, one K value each (the emulation path).

@@ -632,4 +632,19 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
     return hipGetLastError();
 }
 
+hipError_t launch_quant_cols_keyed(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
+                                   uint8_t *codes, const float *row_mult, hipStream_t s) {
+    uint32_t *keys = reinterpret_cast<uint32_t *>(scales_as_keys);
+    dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
+    if (dt == DT_BF16) {
+        if (row_mult) hipLaunchKernelGGL((k_quant_cols<DT_BF16, true>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+        else hipLaunchKernelGGL((k_quant_cols<DT_BF16, false>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+    } else {
+        if (row_mult) hipLaunchKernelGGL((k_quant_cols<DT_F32, true>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+        else hipLaunchKernelGGL((k_quant_cols<DT_F32, false>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+    }
+    hipLaunchKernelGGL(k_col_scales, dim3(blocks_for(N, 256, 1 << 20)), dim3(256), 0, s, keys, N);
+    return hipGetLastError();
+}
+
 }  // namespace fp4

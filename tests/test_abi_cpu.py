@@ -191,7 +191,7 @@ def test_backward_layout_is_disjoint_and_aligned():
     M, K, N = 96, 160, 224
     assert L.fp4_backward_layout(M, K, N, C.byref(lay)) == OK
     parts = sorted([(lay.Gq, M * N // 2), (lay.sG, M * 4), (lay.Hq, N * M // 2), (lay.sH, N * 4),
-                    (lay.WqT, K * N // 2), (lay.AqT, K * M // 2), (lay.ones, K * 4)])
+                    (lay.WqT, K * N // 2), (lay.AqT, K * M // 2), (lay.ones, K * 4), (lay.part, 512 * N * 4)])
     for (a, na), (b, _) in zip(parts, parts[1:]):
         assert a % 256 == 0 and a + na <= b
     assert parts[-1][0] + parts[-1][1] <= lay.total

@@ -558,9 +558,12 @@ def _check_backward_small(A, W, dY, q, out_dtype, want_dA=True, want_dW=True):
 
 
 # (dtype, M, K, N, out): M and N multiples of 32 (the two contractions); several GEMM
-# tiles with ragged tails in every output dimension
+# tiles with ragged tails in every output dimension; bf16 dY with N up to 24576 takes the fused
+# row pass (1, 2 or 3 chunks of 8 per thread of a 1024-thread row), wider rows and fp32 dY the
+# separate passes
 BWD_CASES = [("bf16", 96, 64, 160, "fp32"), ("fp32", 288, 320, 544, "fp32"), ("bf16", 544, 1056, 800, "bf16"),
-             ("bf16", 32, 32, 32, "fp32"), ("fp32", 320, 96, 4128, "bf16")]
+             ("bf16", 32, 32, 32, "fp32"), ("fp32", 320, 96, 4128, "bf16"), ("bf16", 64, 64, 16416, "fp32"),
+             ("bf16", 96, 32, 24608, "bf16"), ("bf16", 576, 96, 8224, "fp32")]
 
 
 @pytest.mark.parametrize("dtype,M,K,N,out", BWD_CASES)
