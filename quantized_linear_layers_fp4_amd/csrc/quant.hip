@@ -9,6 +9,8 @@
 #include "fp4_common.h"
 #include "fp4_launch.h"
 
+#include <cstdlib>
+
 namespace fp4 {
 
 // ----------------------------------------------------------------------------- zero fill
@@ -464,33 +466,38 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
     }
 }
 
-// Quantize a 256 (k) x 64 (n) tile of W with the finished column maxima and write it
-// transposed: Wq[n][k/2].  Loads: 8 threads per row (16 bytes = 8 columns each), two rows
+// Quantize a 256 (k) x TN (n) tile of W with the finished column maxima and write it
+// transposed: Wq[n][k/2].  Loads: TN/8 threads per row (16 bytes = 8 columns each), two rows
 // (k, k+1) per thread per pass so each output byte (pair of k) is formed in registers; the
-// transpose goes through a 64 x 128-byte LDS tile.
-template <int DT, bool RM>
+// transpose goes through a TN x 128-byte LDS tile, written out as 128-byte rows of Wq.
+template <int DT, bool RM, int TN>
 __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, int64_t K, int64_t N,
                                                     const float *__restrict__ row_mult,
                                                     const uint32_t *__restrict__ colmax_key,
                                                     uint8_t *__restrict__ codes) {
-    __shared__ float rs[64];
-    __shared__ uint8_t tile[64][128 + 4];
+    constexpr int TPR = TN / 8;         // threads per row
+    constexpr int RPP = 256 / TPR;      // row pairs per pass
+    constexpr int PASSES = 128 / RPP;   // 128 row pairs = 256 rows per tile
+    constexpr int TPN = 256 / TN;       // threads per output row
+    constexpr int BPT = 128 / TPN;      // output bytes per thread
+    __shared__ float rs[TN];
+    __shared__ uint8_t tile[TN][128 + 4];
     const int tid = threadIdx.x;
-    const int64_t n0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 256;
-    if (tid < 64) {
+    const int64_t n0 = (int64_t)blockIdx.x * TN, k0 = (int64_t)blockIdx.y * 256;
+    if (tid < TN) {
         float r = 0.0f, s;
         if (n0 + tid < N) vector_scale(__uint_as_float(colmax_key[n0 + tid]), r, s);
         rs[tid] = r;
     }
     __syncthreads();
-    const int c8 = tid & 7;           // columns n0 + 8*c8 .. +7
+    const int c8 = tid % TPR;         // columns n0 + 8*c8 .. +7
     const int64_t col = n0 + c8 * 8;
     float r8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) r8[e] = rs[c8 * 8 + e];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int j = (tid >> 3) + 32 * p;  // row pair: rows 2j, 2j+1 of the tile
+    for (int p = 0; p < PASSES; ++p) {
+        const int j = tid / TPR + RPP * p;  // row pair: rows 2j, 2j+1 of the tile
         const int64_t k = k0 + 2 * j;
         uint32_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (col < N && k < K) {  // K % 32 == 0: both rows of a pair are in range together
@@ -505,24 +512,49 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
         for (int e = 0; e < 8; ++e) tile[c8 * 8 + e][j] = (uint8_t)b[e];
     }
     __syncthreads();
-    // write out: n = tid / 4, 32 bytes (64 k) per thread
-    const int nl = tid >> 2, part = tid & 3;
+    // write out: n = tid / TPN, BPT bytes (2*BPT values of k) per thread
+    const int nl = tid / TPN, part = tid % TPN;
     const int64_t n = n0 + nl;
-    const int64_t kb = k0 / 2 + part * 32;  // byte offset within the row of Wq
+    const int64_t kb = k0 / 2 + part * BPT;  // byte offset within the row of Wq
     if (n < N) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < BPT / 16; ++h) {
             if (kb + h * 16 < K / 2) {
                 uint32_t w[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int o = part * 32 + h * 16 + i * 4;
+                    const int o = part * BPT + h * 16 + i * 4;
                     w[i] = (uint32_t)tile[nl][o] | ((uint32_t)tile[nl][o + 1] << 8) |
                            ((uint32_t)tile[nl][o + 2] << 16) | ((uint32_t)tile[nl][o + 3] << 24);
                 }
                 *reinterpret_cast<uint4 *>(codes + n * (K / 2) + kb + h * 16) = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
+    }
+}
+
+// Column width of the transposing tile: 128 (256-byte row segments of the input; 3 % faster
+// than 64 on the 16384 x 22016 gradient, equal on the 4096 x 22016 weight).  FP4_QCOLS_TN=64|128
+// overrides (a tuning aid).
+static int qcols_tn() {
+    static int tn = 0;
+    if (!tn) {
+        const char *e = getenv("FP4_QCOLS_TN");
+        const int v = e ? atoi(e) : 0;
+        tn = (v == 64 || v == 128) ? v : 128;
+    }
+    return tn;
+}
+
+template <int DT, bool RM>
+static void launch_qcols_tile(const void *W, int64_t K, int64_t N, const float *row_mult, const uint32_t *keys,
+                              uint8_t *codes, hipStream_t s) {
+    if (qcols_tn() == 128) {
+        dim3 g((unsigned)((N + 127) / 128), (unsigned)((K + 255) / 256));
+        hipLaunchKernelGGL((k_quant_cols<DT, RM, 128>), g, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+    } else {
+        dim3 g((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
+        hipLaunchKernelGGL((k_quant_cols<DT, RM, 64>), g, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
     }
 }
 
@@ -614,11 +646,10 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
     }
     const int rows_per_block = 256;
     dim3 g1((unsigned)((N + 511) / 512), (unsigned)((K + rows_per_block - 1) / rows_per_block));
-    dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
 #define QC(DT, RM)                                                                                         \
     do {                                                                                                   \
         hipLaunchKernelGGL((k_colmax<DT, RM>), g1, dim3(256), 0, s, W, K, N, rows_per_block, row_mult, keys); \
-        hipLaunchKernelGGL((k_quant_cols<DT, RM>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);     \
+        launch_qcols_tile<DT, RM>(W, K, N, row_mult, keys, codes, s);                                       \
     } while (0)
     if (dt == DT_BF16) {
         if (row_mult) QC(DT_BF16, true);
@@ -635,13 +666,12 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
 hipError_t launch_quant_cols_keyed(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
                                    uint8_t *codes, const float *row_mult, hipStream_t s) {
     uint32_t *keys = reinterpret_cast<uint32_t *>(scales_as_keys);
-    dim3 g2((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
     if (dt == DT_BF16) {
-        if (row_mult) hipLaunchKernelGGL((k_quant_cols<DT_BF16, true>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
-        else hipLaunchKernelGGL((k_quant_cols<DT_BF16, false>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+        if (row_mult) launch_qcols_tile<DT_BF16, true>(W, K, N, row_mult, keys, codes, s);
+        else launch_qcols_tile<DT_BF16, false>(W, K, N, row_mult, keys, codes, s);
     } else {
-        if (row_mult) hipLaunchKernelGGL((k_quant_cols<DT_F32, true>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
-        else hipLaunchKernelGGL((k_quant_cols<DT_F32, false>), g2, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+        if (row_mult) launch_qcols_tile<DT_F32, true>(W, K, N, row_mult, keys, codes, s);
+        else launch_qcols_tile<DT_F32, false>(W, K, N, row_mult, keys, codes, s);
     }
     hipLaunchKernelGGL(k_col_scales, dim3(blocks_for(N, 256, 1 << 20)), dim3(256), 0, s, keys, N);
     return hipGetLastError();
