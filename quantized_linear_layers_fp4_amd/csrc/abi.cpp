@@ -75,15 +75,17 @@ fp4_status device_check(int *cus) {
 
 // Scratch of one outlier pass.  [state, hist, hist_lo) is zero-filled per call.
 struct OutlierWs {
-    size_t state, hist, hist_lo, zero_end, rowmax, row_cnt, slots, over, total;
+    size_t state, hist, hist_lo, zero_end, rowmax, row_cnt, slots, total;
     int32_t S;  // staging slots per row
 };
 
-// Slots per row: twice the mean outlier count per row that the capacity bound allows,
-// plus a margin, at most K.  Rows with more outliers spill into the overflow list.
+// Slots per row: twice the mean outlier count per row that the capacity bound allows plus
+// a margin, at least 128 (rows vary widely: with log-normal row scales a few rows hold a
+// hundred times the mean), at most K.  Rows with more outliers are read again by the COO pass.
 int32_t slots_per_row(int64_t M, int64_t K, int64_t cap) {
-    int64_t mean = (cap + M - 1) / M;
+    const int64_t mean = (cap + M - 1) / M;
     int64_t S = 2 * mean + 8;
+    if (S < 128) S = 128;
     return (int32_t)(S < K ? S : K);
 }
 
@@ -104,8 +106,6 @@ OutlierWs outlier_ws(int64_t M, int64_t K, int32_t dtype, int64_t cap) {
     off += align_up((size_t)M * 4);
     w.slots = off;
     off += align_up((size_t)M * (size_t)w.S * sizeof(SlotEntry));
-    w.over = off;
-    off += align_up((size_t)(cap > 0 ? cap : 1) * sizeof(OverEntry));
     w.total = off;
     return w;
 }
@@ -125,9 +125,7 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     int32_t *row_cnt = reinterpret_cast<int32_t *>(ws + w.row_cnt);
     Staging stg;
     stg.slots = reinterpret_cast<SlotEntry *>(ws + w.slots);
-    stg.over = reinterpret_cast<OverEntry *>(ws + w.over);
     stg.S = w.S;
-    stg.over_cap = cap > 0 ? cap : 1;
     const int dt = dt_of(dtype);
     const int64_t n = M * K;
     const uint64_t k = (uint64_t)std::floor(q * (double)(n - 1));
@@ -139,7 +137,8 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     if (e == hipSuccess)
         e = launch_quant_rows(A, dt, M, K, codes ? rowmax : nullptr, T, Aq, sA, row_cnt, stg, st,
                               /*emit=*/true, /*write_codes=*/codes, s);
-    if (e == hipSuccess) e = launch_coo(row_cnt, M, row_ptr, nnz, stg, st, cap, coo_row, coo_col, coo_val, s);
+    if (e == hipSuccess)
+        e = launch_coo(row_cnt, M, row_ptr, nnz, stg, cap, coo_row, coo_col, coo_val, A, dt, K, T, s);
     return hip_status(e);
 }
 
@@ -229,7 +228,7 @@ fp4_status fp4_quantize(const void *X, int32_t x_dtype, int64_t R, int64_t C, in
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (axis == FP4_PER_ROW)
         return hip_status(launch_quant_rows(X, dt_of(x_dtype), R, C, nullptr, clamp_T, codes, scales, nullptr,
-                                            Staging{nullptr, nullptr, 0, 0}, nullptr, false, true, s));
+                                            Staging{nullptr, 0}, nullptr, false, true, s));
     return hip_status(launch_quant_cols(X, dt_of(x_dtype), R, C, scales, codes, false, s));
 }
 

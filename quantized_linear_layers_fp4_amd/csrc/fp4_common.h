@@ -23,32 +23,25 @@ constexpr int HIST_LO_BINS = 65536;  // level-2 histogram for fp32 keys: key & 0
 struct State {
     uint64_t k_rem;        // rank left inside the level-1 bin (fp32 inputs)
     uint64_t nnz_hist;     // #{|a| > T} counted from the histograms
-    unsigned long long over_count;  // outliers staged past their row's slots
     uint32_t T_key;        // key of T
     float T;               // T itself
     uint32_t hi_bin;       // selected level-1 bin
     uint32_t hi_count;     // population of that bin
 };
-static_assert(sizeof(State) == 40, "State layout");
+static_assert(sizeof(State) == 32, "State layout");
 
 // Outlier staging.  Row m owns S slots; the outlier of rank j (ascending column) in row m
-// goes to slot m*S + j, and ranks >= S go to the shared overflow list (rare: S is twice the
-// mean count per row plus a margin).  No global atomic is touched unless a row overflows.
+// goes to slot m*S + j when j < S.  A row with more outliers (rare: S is at least 128 and twice
+// the mean count per row plus a margin) is read again when the COO list is assembled, and its
+// outliers of rank >= S are written straight to their final positions there.  No atomic is
+// involved.
 struct SlotEntry {
     int32_t col;
     float val;   // delta = a - copysign(T, a)
 };
-struct OverEntry {
-    int32_t row;
-    int32_t rank;
-    int32_t col;
-    float val;
-};
 struct Staging {
     SlotEntry *slots;
-    OverEntry *over;
     int32_t S;
-    int64_t over_cap;
 };
 
 // Per-vector scales: r = fl(6 / amax) multiplies, s = fl(amax / 6) dequantizes; a vector

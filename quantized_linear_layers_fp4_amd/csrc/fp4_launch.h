@@ -17,9 +17,11 @@ hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint
 hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const uint32_t *rowmax_key,
                              const float *T_src, uint8_t *codes, float *scales, int32_t *row_cnt,
                              const Staging &stg, State *st, bool emit, bool write_codes, hipStream_t s);
+// Exclusive scan of the row counts into row_ptr / nnz, then the staged entries (and, for rows
+// that outgrew their slots, a second read of those rows of A) into the (row, col)-sorted list.
 hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
-                      const State *st, int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val,
-                      hipStream_t s);
+                      int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val, const void *A, int dt,
+                      int64_t K, const float *T_src, hipStream_t s);
 // keys_zeroed: the column-maximum keys (in the scales buffer) were zeroed by an earlier launch.
 // row_mult: NULL, or fp32[K]: quantize fl(row_mult[k] * W[k][n]) instead of W.
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,

@@ -263,31 +263,29 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, 
                 if (valid) *reinterpret_cast<uint32_t *>(codes + row * (C / 2) + c * 4) = e2m1_pack8(y);
             }
             if constexpr (EMIT) {
-                const uint32_t cnt = __popc(omask);
-                if (__ballot(cnt != 0)) {
-                    const uint32_t incl = wave_incl_scan(cnt, lane);
-                    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-                    uint32_t rank = running + incl - cnt;
+                if (__ballot(omask != 0)) {
+                    // rank of this lane's first outlier = outliers in the lower lanes: one
+                    // ballot per element position, counted below the lane with mbcnt (no
+                    // cross-lane shuffles, whose LDS round trips made this path slow)
+                    uint32_t before = 0, total = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint64_t b = __ballot((omask >> e) & 1u);
+                        before += __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                        total += (uint32_t)__popcll(b);
+                    }
+                    uint32_t rank = running + before;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         if (omask & (1u << e)) {
                             const int32_t col = (int32_t)(c * 8 + e);
                             const float val = v[e] - __uint_as_float(sg[e] | tkey);
-                            if (rank < (uint32_t)stg.S) {
+                            if (rank < (uint32_t)stg.S) {  // ranks past S: see k_coo_scatter
                                 SlotEntry se;
                                 se.col = col;
                                 se.val = val;
                                 stg.slots[row * stg.S + rank] = se;
-                            } else {
-                                const unsigned long long i = atomicAdd(&st->over_count, 1ull);
-                                if (i < (unsigned long long)stg.over_cap) {
-                                    OverEntry oe;
-                                    oe.row = (int32_t)row;
-                                    oe.rank = (int32_t)rank;
-                                    oe.col = col;
-                                    oe.val = val;
-                                    stg.over[i] = oe;
-                                }
                             }
                             ++rank;
                         }
@@ -367,41 +365,94 @@ __global__ __launch_bounds__(1024) void k_coo_scan(const int32_t *__restrict__ r
     }
 }
 
-// Move each staged entry to row_ptr[row] + rank: one wave per row for the slots; the
-// last OVER_BLOCKS workgroups move the overflow list.
-constexpr int OVER_BLOCKS = 16;
-__global__ __launch_bounds__(256) void k_coo_scatter(Staging stg, const State *__restrict__ st,
-                                                     const int32_t *__restrict__ row_cnt,
+// Move each staged entry to row_ptr[row] + rank, one wave per row (ranks below S).
+__global__ __launch_bounds__(256) void k_coo_scatter(Staging stg, const int32_t *__restrict__ row_cnt,
                                                      const int32_t *__restrict__ row_ptr, int64_t M, int64_t cap,
                                                      int32_t *__restrict__ coo_row, int32_t *__restrict__ coo_col,
                                                      float *__restrict__ coo_val) {
-    const int64_t row_blocks = (M + 3) / 4;
-    if ((int64_t)blockIdx.x < row_blocks) {
-        const int lane = threadIdx.x & 63;
-        const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-        if (row >= M) return;
-        const int32_t n = min(row_cnt[row], stg.S);
-        const int64_t base = row_ptr[row];
-        for (int32_t j = lane; j < n; j += 64) {
-            const SlotEntry se = stg.slots[row * stg.S + j];
-            const int64_t pos = base + j;
-            if (pos < cap) {
-                if (coo_row) coo_row[pos] = (int32_t)row;
-                coo_col[pos] = se.col;
-                coo_val[pos] = se.val;
-            }
-        }
-        return;
-    }
-    const int64_t n = min((int64_t)st->over_count, stg.over_cap);
-    const int64_t stride = (int64_t)OVER_BLOCKS * blockDim.x;
-    for (int64_t i = (blockIdx.x - row_blocks) * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
-        const OverEntry oe = stg.over[i];
-        const int64_t pos = (int64_t)row_ptr[oe.row] + oe.rank;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const int32_t n = min(row_cnt[row], stg.S);
+    const int64_t base = row_ptr[row];
+    for (int32_t j = lane; j < n; j += 64) {
+        const SlotEntry se = stg.slots[row * stg.S + j];
+        const int64_t pos = base + j;
         if (pos < cap) {
-            if (coo_row) coo_row[pos] = oe.row;
-            coo_col[pos] = oe.col;
-            coo_val[pos] = oe.val;
+            if (coo_row) coo_row[pos] = (int32_t)row;
+            coo_col[pos] = se.col;
+            coo_val[pos] = se.val;
+        }
+    }
+}
+
+// Rows with more outliers than staging slots (rare: S is at least 128 and twice the mean count
+// plus a margin).  A workgroup checks 64 rows' counts at once and deals the rows past S to its
+// four waves; for each such row a wave reads the row of A again, ranks its outliers as the
+// quantize pass did (ascending column) and writes those of rank >= S straight to
+// row_ptr[row] + rank.  A kernel of its own: with this code in the quantize kernel (as an
+// atomic overflow list) that kernel took twice as long, and in the scatter kernel every row
+// waited for the few rescans.
+template <int DT>
+__global__ __launch_bounds__(256) void k_coo_overflow(int32_t S, const int32_t *__restrict__ row_cnt,
+                                                      const int32_t *__restrict__ row_ptr, int64_t M, int64_t cap,
+                                                      const void *__restrict__ A, int64_t K,
+                                                      const float *__restrict__ T_src, int32_t *__restrict__ coo_row,
+                                                      int32_t *__restrict__ coo_col, float *__restrict__ coo_val) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * 64;  // the workgroup's 64 rows, shared by its 4 waves
+    const int32_t cnt = (r0 + lane < M) ? row_cnt[r0 + lane] : 0;
+    uint64_t todo = __ballot(cnt > S);
+    if (!todo) return;
+    const uint32_t tkey = key_of_f32(__float_as_uint(*T_src));
+    const int64_t nchunk = K / 8;
+    for (int i = 0; todo; ++i) {
+        const int bit = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        if ((i & 3) != wave) continue;  // the group's overflowing rows are dealt to the 4 waves
+        const int64_t row = r0 + bit;
+        const int64_t base = row_ptr[row];
+        uint32_t run = 0;
+        // U chunks of 8 per lane are loaded together: one memory round trip per 512*U elements
+        constexpr int U = 8;
+        for (int64_t cg = 0; cg < nchunk; cg += 64 * U) {
+          float vv[U][8];
+          uint32_t kk[U][8], ss[U][8];
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+              if (cg + u * 64 + lane < nchunk) load8<DT>(A, row * K + (cg + u * 64 + lane) * 8, vv[u], kk[u], ss[u]);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int64_t c = cg + u * 64 + lane;
+            const float *v = vv[u];
+            const uint32_t *sg = ss[u];
+            uint32_t omask = 0;
+            if (c < nchunk) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) omask |= (uint32_t)(kk[u][e] > tkey) << e;
+            }
+            uint32_t before = 0, total = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint64_t b = __ballot((omask >> e) & 1u);
+                before += __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                total += (uint32_t)__popcll(b);
+            }
+            uint32_t rank = run + before;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (omask & (1u << e)) {
+                    const int64_t pos = base + rank;
+                    if (rank >= (uint32_t)S && pos < cap) {
+                        if (coo_row) coo_row[pos] = (int32_t)row;
+                        coo_col[pos] = (int32_t)(c * 8 + e);
+                        coo_val[pos] = v[e] - __uint_as_float(sg[e] | tkey);
+                    }
+                    ++rank;
+                }
+            }
+            run += total;
+          }
         }
     }
 }
@@ -628,12 +679,18 @@ hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const 
 }
 
 hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
-                      const State *st, int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val,
-                      hipStream_t s) {
+                      int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val, const void *A, int dt,
+                      int64_t K, const float *T_src, hipStream_t s) {
     hipLaunchKernelGGL(k_coo_scan, dim3(1), dim3(1024), 0, s, row_cnt, M, row_ptr, nnz_out);
-    const int blocks = (int)((M + 3) / 4) + OVER_BLOCKS;
-    hipLaunchKernelGGL(k_coo_scatter, dim3(blocks), dim3(256), 0, s, stg, st, row_cnt, row_ptr, M, cap, coo_row,
-                       coo_col, coo_val);
+    hipLaunchKernelGGL(k_coo_scatter, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, stg, row_cnt, row_ptr, M, cap,
+                       coo_row, coo_col, coo_val);
+    const dim3 go((unsigned)((M + 63) / 64));  // 64 rows per workgroup
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(k_coo_overflow<DT_BF16>, go, dim3(256), 0, s, stg.S, row_cnt, row_ptr, M, cap, A, K, T_src,
+                           coo_row, coo_col, coo_val);
+    else
+        hipLaunchKernelGGL(k_coo_overflow<DT_F32>, go, dim3(256), 0, s, stg.S, row_cnt, row_ptr, M, cap, A, K, T_src,
+                           coo_row, coo_col, coo_val);
     return hipGetLastError();
 }
 

@@ -152,18 +152,21 @@ def test_outlier_clamp(dtype, M, K, q, kind):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_outlier_clamp_row_overflow(dtype):
-    # nearly every outlier in one row: the row's staging slots overflow into the shared list
-    M, K, q = 256, 512, 0.999
-    _say(f"outlier overflow {dtype}")
+@pytest.mark.parametrize("rows", [(3,), (1, 2, 30, 31, 64, 100, 101, 200, 254, 255)], ids=["one_row", "ten_rows"])
+def test_outlier_clamp_row_overflow(dtype, rows):
+    # nearly every outlier in a few rows: those rows outgrow their staging slots and are read
+    # again when the COO list is assembled
+    M, K, q = 256, 1024, 0.995
+    _say(f"outlier overflow {dtype} rows={rows}")
     A, W = make_custom(M, K, 64, dtype=dtype, seed=77, kind="plain")
-    A[3] *= 100
+    for r in rows:
+        A[r] *= 100
     A[200, 7] = 1000.0
     out = fp4.outlier_clamp(A.to(DEV), q)
     Anp = as_numpy_bits(A)
     T = oracle.abs_quantile(Anp, q)
     ref = oracle.clamp_coo(Anp, T, want_clamped=False)
-    assert ref["row_ptr"][4] - ref["row_ptr"][3] > 50  # far beyond the per-row slots
+    assert max(ref["row_ptr"][r + 1] - ref["row_ptr"][r] for r in rows) > 64  # beyond the per-row slots
     assert float(out["T"].item()) == T
     assert np.array_equal(to_np(out["row_ptr"]), ref["row_ptr"])
     assert np.array_equal(to_np(out["coo_col"]), ref["coo_col"])
