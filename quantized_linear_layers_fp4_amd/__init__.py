@@ -40,7 +40,7 @@ class WsLayout(C.Structure):
 
 
 class BwdLayout(C.Structure):
-    _fields_ = [(n, C.c_size_t) for n in ("total", "Gq", "sG", "Hq", "sH", "WqT", "AqT", "ones")]
+    _fields_ = [(n, C.c_size_t) for n in ("total", "Gq", "sG", "Hq", "sH", "WqT", "AqT", "ones", "part")]
 
 
 class Fp4Error(RuntimeError):
