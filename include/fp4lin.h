@@ -75,6 +75,13 @@ enum {
     FP4_ERR_ALIGN = 9      /* a pointer is not 16-byte aligned */
 };
 enum { FP4_F32 = 0, FP4_BF16 = 1 };          /* element types of A, W, X, Y */
+/* Output type of fp4_gemm only (no compensation term): the exact accumulator in two bytes.
+ * Element (m, n) is the int16 4*acc (acc is a multiple of 1/4), except in the 256 x 128
+ * output blocks that hold some |acc| > 8191.75: there every element is -32768 and the
+ * workspace holds fl(fl(acc*sA)*sW) as fp32 at element (m, n) (those blocks are recomputed
+ * by a second launch).  This is how the GEMM hands its result to the compensation pass
+ * inside fp4_gemm and fp4_linear_forward. */
+enum { FP4_Q16 = 2 };
 enum { FP4_PER_ROW = 0, FP4_PER_COL = 1 };   /* token-wise (A) / channel-wise (W) */
 
 /* Limits shared by all calls: 32 <= K <= 65536 and K % 32 == 0 (contraction length:
@@ -120,8 +127,12 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
                              int64_t capacity, int32_t *row_ptr, int64_t *nnz, void *workspace,
                              size_t ws_bytes, void *stream);
 
-/* Host-only: workspace bytes fp4_gemm needs: M * N * 4 (an fp32 copy of Y_main) when it
- * adds the compensation term into a bf16 Y, else 0 (also 0 for invalid arguments). */
+/* Host-only: workspace bytes fp4_gemm needs: with the compensation term about M * N * 4 for
+ * a bf16 Y (the fp32 escapes of the two-byte hand-over; the accumulators go through Y
+ * itself) and about M * N * 2 for an fp32 Y (the accumulators; the escapes go through Y);
+ * for y_dtype FP4_Q16 (no compensation term) about M * N * 4 (the escapes); each plus 4 bytes
+ * per 256 x 128 output block (flags of the escape pass); else 0 (also 0 for invalid
+ * arguments). */
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t with_comp);
 
 /* The FP4 GEMM with dequantization, plus the sparse compensation term (QbitAI report,
@@ -134,11 +145,13 @@ size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t w
  *            compensation term; W (K x N, w_dtype) is then unused and may be NULL.
  *   capacity the number of entries the dA lists were sized for (fp4_outlier_capacity),
  *            or 0 if unknown; it only picks the shape of the compensation kernel.
- *   Y        M x N of y_dtype (out)
+ *   Y        M x N of y_dtype (out); FP4_Q16 (int16 elements) only without dA
  *   acc_out  NULL, or device fp32[M*N] receiving the raw accumulator acc (a check aid).
  *   workspace, ws_bytes: device scratch of at least fp4_gemm_workspace_bytes() bytes
- *            (may be NULL when that is 0).  Y_main is written there in fp32 and the
- *            compensation pass reads it back; with an fp32 Y it works in place in Y.
+ *            (may be NULL when that is 0).  With dA the GEMM hands its accumulator to the
+ *            compensation pass as FP4_Q16 elements (in Y for a bf16 Y, in the workspace for
+ *            an fp32 Y) with the escapes in the other buffer; the pass rebuilds
+ *            Y_main = fl(fl(acc*sA)*sW) bit for bit from them.
  * Two kernels run on the stream: the GEMM, then (with dA) the compensation pass.
  * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW,
@@ -188,7 +201,9 @@ struct fp4_ws_layout {
     size_t row_ptr;               /* int32[M+1] */
     size_t coo_row, coo_col, coo_val; /* capacity entries each */
     size_t Aq, sA, Wq, sW;        /* codes and scales */
-    size_t ymain;                 /* fp32[M*N]: Y_main before the compensation pass */
+    size_t handoff;               /* the GEMM's hand-over to the compensation pass (fp32
+                                     escapes for a bf16 Y, int16 accumulators for an fp32
+                                     Y; see FP4_Q16) and the escape pass's flags */
     size_t scratch;               /* internal */
     int64_t capacity;             /* fp4_outlier_capacity(M, K, q) */
 };

@@ -22,6 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4lin.so")
 
 FP4_F32, FP4_BF16 = 0, 1
+FP4_Q16 = 2  # fp4_gemm output only: int16 4*acc with fp32 escapes in the workspace
 FP4_PER_ROW, FP4_PER_COL = 0, 1
 
 EXPORTS = (
@@ -36,7 +37,7 @@ EXPORTS = (
 
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("total", "T", "nnz", "row_ptr", "coo_row", "coo_col", "coo_val",
-                                          "Aq", "sA", "Wq", "sW", "ymain", "scratch")] + [("capacity", C.c_int64)]
+                                          "Aq", "sA", "Wq", "sW", "handoff", "scratch")] + [("capacity", C.c_int64)]
 
 
 class BwdLayout(C.Structure):
@@ -186,6 +187,22 @@ def gemm(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor,
                           _ptr(coo_val), cap, _ptr(W), wdt, _ptr(Y), _out_dtype_code(out_dtype), _ptr(acc), _ptr(ws),
                           ws.numel() if ws is not None else 0, _stream(Aq)))
     return (Y, acc) if acc_out else Y
+
+
+def gemm_q16(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, K: int,
+             acc_out: bool = False):
+    """The exact accumulator in two bytes (FP4_Q16): (Yq int16 M x N, esc fp32 M x N), where
+    Yq = 4*acc when |acc| <= 8191.75, else -32768 with esc = fl(fl(acc*sA)*sW) there."""
+    _need_cuda(Aq, sA, Wq, sW)
+    M, N = Aq.shape[0], Wq.shape[0]
+    Yq = torch.empty((M, N), dtype=torch.int16, device=Aq.device)
+    acc = torch.empty((M, N), dtype=torch.float32, device=Aq.device) if acc_out else None
+    nbytes = lib().fp4_gemm_workspace_bytes(M, N, FP4_Q16, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=Aq.device)
+    _check(lib().fp4_gemm(_ptr(Aq), _ptr(sA), _ptr(Wq), _ptr(sW), M, N, K, None, None, None, 0, None, FP4_BF16,
+                          _ptr(Yq), FP4_Q16, _ptr(acc), _ptr(ws), nbytes, _stream(Aq)))
+    esc = ws[:M * N * 4].view(torch.float32).view(M, N)  # the escape values come first in the workspace
+    return (Yq, esc, acc) if acc_out else (Yq, esc)
 
 
 def gemm_fp8emu(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, K: int,

@@ -36,6 +36,34 @@ bool gemm_ok(int64_t M, int64_t N, int64_t K) { return mk_ok(M, K) && n_ok(N) &&
 bool wcomp_ok(int64_t N, int64_t K, int32_t w_dtype) {
     return K * N * (w_dtype == FP4_BF16 ? 2 : 4) <= (int64_t)0x7FFFFFFF;
 }
+// Where the GEMM's two-byte accumulators, their fp32 escapes and the escape pass's tile
+// flags go on the way to a compensated Y (or to an FP4_Q16 output): a bf16 Y (and an
+// FP4_Q16 output) holds the accumulators itself and the workspace the escapes (M*N*4 bytes);
+// an fp32 Y holds the escapes and the workspace the accumulators (M*N*2 bytes).  The flags
+// follow in the workspace.
+size_t q16_main_bytes(int64_t M, int64_t N, int32_t y_dtype) {
+    return align_up((size_t)M * (size_t)N * (y_dtype == FP4_F32 ? 2 : 4));
+}
+size_t q16_ws_bytes(int64_t M, int64_t N, int32_t y_dtype) {
+    return q16_main_bytes(M, N, y_dtype) + align_up(gemm_flag_bytes(M, N));
+}
+struct Q16Bufs {
+    int16_t *yq;
+    float *esc;
+    uint8_t *flags;
+};
+Q16Bufs q16_buffers(void *Y, int32_t y_dtype, uint8_t *ws, int64_t M, int64_t N) {
+    Q16Bufs b;
+    if (y_dtype == FP4_F32) {
+        b.yq = reinterpret_cast<int16_t *>(ws);
+        b.esc = static_cast<float *>(Y);
+    } else {
+        b.yq = static_cast<int16_t *>(Y);
+        b.esc = reinterpret_cast<float *>(ws);
+    }
+    b.flags = ws + q16_main_bytes(M, N, y_dtype);
+    return b;
+}
 
 // The COO list of dA is indexed with int32 (row_ptr), and the kernels address it with
 // 32-bit byte offsets: the capacity bound must stay below 2^29 entries.
@@ -182,11 +210,12 @@ fp4_status forward_impl(const void *A, const void *W, const uint8_t *Wq_in, cons
     hipError_t e = hipSuccess;
     if (!wq_given)
         e = launch_quant_cols(W, dt_of(in_dtype), K, N, reinterpret_cast<float *>(sW_keys), ws + l.Wq, true, s);
-    // Y_main in fp32 (straight into Y when Y is fp32), then Y = Y_main + dA . W
-    float *ymain = y_dtype == FP4_F32 ? static_cast<float *>(Y) : reinterpret_cast<float *>(ws + l.ymain);
-    if (e == hipSuccess) e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, nullptr, s);
+    // The accumulator as int16 4*acc (into a bf16 Y itself, else into the workspace) with
+    // fp32 escapes (into the workspace, else into the fp32 Y), then Y = Y_main + dA . W
+    const Q16Bufs b = q16_buffers(Y, y_dtype, ws + l.handoff, M, N);
+    if (e == hipSuccess) e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, nullptr, s, false, b.esc, b.flags);
     if (e == hipSuccess)
-        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype),
+        e = launch_comp(b.yq, b.esc, sA, sW, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype),
                         l.capacity, s);
     return hip_status(e);
 }
@@ -265,8 +294,10 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
 }
 
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t with_comp) {
-    if (M < 1 || !n_ok(N) || !dtype_ok(y_dtype)) return 0;
-    return (with_comp && y_dtype == FP4_BF16) ? (size_t)M * (size_t)N * 4 : 0;
+    if (M < 1 || !n_ok(N)) return 0;
+    if (y_dtype == FP4_Q16) return with_comp ? 0 : q16_ws_bytes(M, N, y_dtype);
+    if (!dtype_ok(y_dtype) || !with_comp) return 0;
+    return q16_ws_bytes(M, N, y_dtype);
 }
 
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
@@ -278,23 +309,28 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
     if (ncomp != 0 && ncomp != 3) return FP4_ERR_NULL;
     const bool comp = ncomp == 3;
     if (comp && !W) return FP4_ERR_NULL;
-    if (!dtype_ok(y_dtype) || (comp && !dtype_ok(w_dtype))) return FP4_ERR_DTYPE;
+    const bool q16 = y_dtype == FP4_Q16;
+    if (!(dtype_ok(y_dtype) || q16) || (comp && (q16 || !dtype_ok(w_dtype)))) return FP4_ERR_DTYPE;
     if (!gemm_ok(M, N, K) || (comp && !wcomp_ok(N, K, w_dtype))) return FP4_ERR_SHAPE;
-    const bool staged = comp && y_dtype == FP4_BF16;  // Y_main goes through the workspace
-    if (staged && !workspace) return FP4_ERR_NULL;
-    if (staged && ws_bytes < (size_t)M * (size_t)N * 4) return FP4_ERR_WORKSPACE;
+    const size_t need = fp4_gemm_workspace_bytes(M, N, y_dtype, comp);
+    if (need && !workspace) return FP4_ERR_NULL;
+    if (ws_bytes < need) return FP4_ERR_WORKSPACE;
     if (!aligned16(Aq) || !aligned16(Wq) || !aligned16(Y) || (comp && !aligned16(W)) ||
-        (acc_out && !aligned16(acc_out)) || (staged && !aligned16(workspace)))
+        (acc_out && !aligned16(acc_out)) || (need && !aligned16(workspace)))
         return FP4_ERR_ALIGN;
     int cus;
     fp4_status st = device_check(&cus);
     if (st != FP4_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (q16) {
+        const Q16Bufs b = q16_buffers(Y, y_dtype, static_cast<uint8_t *>(workspace), M, N);
+        return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, acc_out, s, false, b.esc, b.flags));
+    }
     if (!comp) return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, Y, dt_of(y_dtype), acc_out, s));
-    float *ymain = staged ? static_cast<float *>(workspace) : static_cast<float *>(Y);
-    hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, ymain, DT_F32, acc_out, s);
+    const Q16Bufs b = q16_buffers(Y, y_dtype, static_cast<uint8_t *>(workspace), M, N);
+    hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, acc_out, s, false, b.esc, b.flags);
     if (e == hipSuccess)
-        e = launch_comp(ymain, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype),
+        e = launch_comp(b.yq, b.esc, sA, sW, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype),
                         capacity > 0 ? capacity : 0, s);
     return hip_status(e);
 }
@@ -381,7 +417,7 @@ fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype,
     out->sA = off; off += align_up((size_t)M * 4);
     out->Wq = off; off += align_up((size_t)N * (size_t)(K / 2));
     out->sW = off; off += align_up((size_t)N * 4);
-    out->ymain = off; off += align_up((size_t)M * (size_t)N * 4);
+    out->handoff = off; off += q16_ws_bytes(M, N, FP4_BF16);  // the larger of the two hand-overs
     out->scratch = off; off += outlier_ws(M, K, in_dtype, cap).total;
     out->total = off;
     out->capacity = cap;

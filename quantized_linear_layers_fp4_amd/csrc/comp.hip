@@ -1,22 +1,25 @@
 // gfx950 kernel of the sparse compensation term dA . W of the FP4 linear forward (outlier
 // paragraph of the QbitAI report on "Optimizing Large Language Model Training Using FP4
 // Quantization": the entries clamped away from A are kept as a sparse matrix and their
-// product with the weights is added back).  It runs after the FP4 GEMM has written the
-// dequantized product Y_main in fp32, and writes Y = Y_main + dA . W in the output type,
-// rounded once.
+// product with the weights is added back).  It runs after the FP4 GEMM, which hands over
+// its exact accumulator as two-byte integers 4*acc (fp32 escapes for |acc| > 8191.75); the
+// pass rebuilds the dequantized product Y_main = fl(fl(acc*sA)*sW) bit for bit and writes
+// Y = Y_main + dA . W in the output type, rounded once.  The two-byte hand-over halves the
+// bytes that a fp32 Y_main would cost on both sides of the pass.
 //
 // One wave per (row, chunk of 64*CC columns) task; lane l owns the CC columns CC*l .. of
-// the chunk.  The wave first issues its Y_main loads and the row's two CSR offsets
-// together, then takes the row's dA entries (ascending column k) 64 at a time, one
-// (k, delta) pair per lane, and walks them in groups of eight: the eight W row segments are
-// loaded together and added to the running sums in ascending k (one fp32 fma each).
+// the chunk.  The wave first issues its accumulator and column-scale loads and the row's
+// two CSR offsets together, then takes the row's dA entries (ascending column k) 64 at a
+// time, one (k, delta) pair per lane, and walks them in groups of eight: the eight W row
+// segments are loaded together and added to the running sums in ascending k (one fp32 fma
+// each).
 //
 // Task order: the tasks are dealt out to the eight XCDs in contiguous ranges (consecutive
 // workgroup ids go to different XCDs), chunk-major within a range, so each XCD streams all
 // rows over one chunk at a time and the W rows that chunk gathers stay in that XCD's L2.
-// Y_main and Y are streamed with non-temporal hints so they do not evict those rows.
-// Two widths: CC = 8 (512-column chunks, more Y_main bytes in flight per wave) when the
-// rows hold few entries and the pass streams Y_main; CC = 4 (256-column chunks, half the
+// The accumulators and Y are streamed with non-temporal hints so they do not evict those rows.
+// Two widths: CC = 8 (512-column chunks, more bytes in flight per wave) when the
+// rows hold few entries and the pass streams; CC = 4 (256-column chunks, half the
 // W strip per chunk) when many entries per row make it bound by its gathers.
 #include "fp4_common.h"
 #include "fp4_launch.h"
@@ -54,10 +57,14 @@ __device__ __forceinline__ float seg_elem(const v4i (&raw)[2], int c) {
     }
 }
 
-// INPLACE: Y is the fp32 Y_main buffer itself; a row without entries is then left alone.
-template <int YDT, int WDT, bool INPLACE, int CC>
-__global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y, int M, int N, int K,
-                                                    int chunks, int per_xcd,
+// Y_main of the lane's CC columns, rebuilt from the GEMM's DT_Q16 output: acc = q / 4 exactly,
+// Y_main = fl(fl(acc * sA) * sW) as the GEMM's own epilogue rounds it; escaped elements
+// take their fp32 value from esc.  Yq may be Y itself (bf16 Y) and esc may be Y itself
+// (fp32 Y): every lane reads exactly the bytes it later writes, and no other lane touches them.
+template <int YDT, int WDT, int CC>
+__global__ __launch_bounds__(256) void k_comp_apply(const int16_t *Yq, const float *esc,
+                                                    const float *__restrict__ sA, const float *__restrict__ sW,
+                                                    void *Y, int M, int N, int K, int chunks, int per_xcd,
                                                     const int32_t *__restrict__ row_ptr,
                                                     const int32_t *__restrict__ coo_col,
                                                     const float *__restrict__ coo_val, const void *__restrict__ W) {
@@ -71,27 +78,40 @@ __global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y,
     const bool active = col < N;  // N % 8 == 0: a lane's columns are in range together
     const size_t yoff = (size_t)row * N + col;
 
-    // The row's CSR offsets (lane l loads row_ptr[row + (l & 1)]) and the lane's Y_main
-    // segment, issued together and unconditionally; Y_main goes through a descriptor over
-    // the row, so a lane past N reads zeros.
+    // The row's CSR offsets (lane l loads row_ptr[row + (l & 1)]), the lane's accumulator
+    // codes and column scales, issued together; the codes and scales go through
+    // descriptors, so a lane past N reads zeros.
     const int32_t rp = row_ptr[row + (lane & 1)];
-    const __amdgpu_buffer_rsrc_t rsY =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(Ymain) + (size_t)row * N, 0, N * 4, 0x00020000);
-    v4i yv[CC / 4];
-    auto load_y = [&]() {
+    const __amdgpu_buffer_rsrc_t rsQ =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t *>(Yq) + (size_t)row * N, 0, N * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(sW), 0, N * 4, 0x00020000);
+    v4i qv = v4i{0, 0, 0, 0};
+    if constexpr (CC == 8) {
+        qv = __builtin_amdgcn_raw_buffer_load_b128(rsQ, col * 2, 0, 2);
+    } else {
+        const v2i q2 = __builtin_amdgcn_raw_buffer_load_b64(rsQ, col * 2, 0, 2);
+        qv = v4i{q2.x, q2.y, 0, 0};
+    }
+    v4i swv[CC / 4];
 #pragma unroll
-        for (int h = 0; h < CC / 4; ++h) yv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsY, col * 4 + 16 * h, 0, 2);
-    };
-    if constexpr (!INPLACE) load_y();
+    for (int h = 0; h < CC / 4; ++h) swv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16 * h, 0, 0);
+    const float sa = sA[row];
     const int32_t e0 = __builtin_amdgcn_readlane(rp, 0);
     const int32_t e1 = __builtin_amdgcn_readlane(rp, 1);
-    if constexpr (INPLACE) {
-        if (e0 == e1) return;
-        load_y();
-    }
     float y[CC];
+    bool escaped = false;
 #pragma unroll
-    for (int c = 0; c < CC; ++c) y[c] = __int_as_float(yv[c >> 2][c & 3]);
+    for (int c = 0; c < CC; ++c) {
+        const int q = (int)(int16_t)(((uint32_t)qv[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
+        escaped |= q == Q16_ESC;
+        y[c] = ((float)q * 0.25f * sa) * __int_as_float(swv[c >> 2][c & 3]);
+    }
+    if (__builtin_amdgcn_ballot_w64(escaped)) {  // |acc| > Q16_MAX_ACC somewhere in the wave
+#pragma unroll
+        for (int c = 0; c < CC; ++c)
+            if (active && (int)(int16_t)(((uint32_t)qv[c >> 1] >> (16 * (c & 1))) & 0xFFFFu) == Q16_ESC)
+                y[c] = esc[yoff + c];
+    }
 
     // W through a buffer descriptor.  Offsets are unsigned 32-bit: K*N*ESZ < 2^31, so the
     // largest (a lane past N on the last row of W) stays below 2^32 and reads zeros; such a
@@ -146,39 +166,37 @@ __global__ __launch_bounds__(256) void k_comp_apply(const float *Ymain, void *Y,
 }
 
 template <int CC>
-static hipError_t launch_comp_w(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K,
-                                const int32_t *row_ptr, const int32_t *coo_col, const float *coo_val, const void *W,
-                                int w_dt, hipStream_t s) {
+static hipError_t launch_comp_w(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y,
+                                int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
+                                const int32_t *coo_col, const float *coo_val, const void *W, int w_dt,
+                                hipStream_t s) {
     const int chunks = (int)((N + 64 * CC - 1) / (64 * CC));
     const int64_t tasks = (int64_t)chunks * M;
     const int64_t blocks = (tasks + 3) / 4;
     const int per_xcd = (int)((blocks + 7) / 8);
     const dim3 grid((unsigned)per_xcd * 8u), block(256);
-    const bool inplace = static_cast<const void *>(Ymain) == Y;
-#define C(YD, WD, IP)                                                                                        \
-    hipLaunchKernelGGL((k_comp_apply<YD, WD, IP, CC>), grid, block, 0, s, Ymain, Y, (int)M, (int)N, (int)K, \
+#define C(YD, WD)                                                                                               \
+    hipLaunchKernelGGL((k_comp_apply<YD, WD, CC>), grid, block, 0, s, Yq, esc, sA, sW, Y, (int)M, (int)N, (int)K, \
                        chunks, per_xcd, row_ptr, coo_col, coo_val, W)
     if (y_dt == DT_BF16) {
-        if (w_dt == DT_BF16) C(DT_BF16, DT_BF16, false);
-        else C(DT_BF16, DT_F32, false);
-    } else if (inplace) {
-        if (w_dt == DT_BF16) C(DT_F32, DT_BF16, true);
-        else C(DT_F32, DT_F32, true);
+        if (w_dt == DT_BF16) C(DT_BF16, DT_BF16);
+        else C(DT_BF16, DT_F32);
     } else {
-        if (w_dt == DT_BF16) C(DT_F32, DT_BF16, false);
-        else C(DT_F32, DT_F32, false);
+        if (w_dt == DT_BF16) C(DT_F32, DT_BF16);
+        else C(DT_F32, DT_F32);
     }
 #undef C
     return hipGetLastError();
 }
 
-hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
-                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, int64_t capacity,
-                       hipStream_t s) {
+hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y, int y_dt,
+                       int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
+                       const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s) {
     // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
     // gathers and the narrower chunks keep more of each W strip in L2
-    if (capacity > 64 * M) return launch_comp_w<4>(Ymain, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
-    return launch_comp_w<8>(Ymain, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
+    if (capacity > 64 * M)
+        return launch_comp_w<4>(Yq, esc, sA, sW, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
+    return launch_comp_w<8>(Yq, esc, sA, sW, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
 }
 
 }  // namespace fp4

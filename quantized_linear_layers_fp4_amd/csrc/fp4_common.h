@@ -7,7 +7,17 @@
 
 namespace fp4 {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q16 = 2 };
+
+// DT_Q16: the GEMM's accumulator handed to the compensation pass in two bytes.  The FP4
+// products are multiples of 1/4 and their fp32 sum is exact, so 4*acc is an integer; when
+// |4*acc| <= 32767 it is stored as int16, otherwise the element holds Q16_ESC and the
+// dequantized value fl(fl(acc*sA)*sW) goes, in fp32, to the same position of an escape
+// buffer.  Either way the pass recovers Y_main bit for bit.
+constexpr int Q16_ESC = -32768;
+constexpr float Q16_MAX_ACC = 8191.75f;  // largest |acc| stored inline
+// fl(acc * 4 + 1.5 * 2^23) is exact for |4*acc| < 2^22 and its low 16 bits are 4*acc as int16
+constexpr float Q16_MAGIC = 12582912.0f;
 
 // |x| as an unsigned key: the fp32 bit pattern of |x|.  For non-negative finite floats
 // the unsigned order of the bit patterns is the numeric order, so every comparison of

@@ -44,10 +44,17 @@ hipError_t launch_bwd_rows_fused(const void *X, int64_t M, int64_t C, const floa
 hipError_t launch_quant_cols_keyed(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
                                    uint8_t *codes, const float *row_mult, hipStream_t s);
 
-// FP4 GEMM + dequantization: Y = fl(fl(acc * sA) * sW) in y_dt.  acc_out: NULL or fp32[M*N].
+// FP4 GEMM + dequantization: Y = fl(fl(acc * sA) * sW) in y_dt.  With y_dt == DT_Q16, Y
+// receives the accumulator as int16 4*acc, and a second launch (the escape pass) recomputes
+// in fp32 the tiles that hold some |acc| > Q16_MAX_ACC: their fl(fl(acc*sA)*sW) goes to esc
+// (fp32[M*N]) and their int16 elements become Q16_ESC.  flags: gemm_flag_bytes(M, N) bytes
+// of device scratch (written by the first launch, read by the second).
+// acc_out: NULL or fp32[M*N].
 // f8: Aq (M x K) and Wq (N x K) hold E4M3 bytes, one K value each (the emulation path).
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8 = false);
+                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8 = false,
+                       float *esc = nullptr, uint8_t *flags = nullptr);
+size_t gemm_flag_bytes(int64_t M, int64_t N);
 // FP8 (E4M3) gradient codec, one per-tensor scale.  key: device u32 scratch (zeroed here).
 hipError_t launch_fp8_quantize(const void *X, int dt, int64_t n, uint32_t *key, uint8_t *codes, float *scale,
                                int num_cus, hipStream_t s);
@@ -57,10 +64,11 @@ hipError_t launch_fp8_dequantize(const uint8_t *codes, int64_t n, const float *s
 // input bytes -> 2 * n_bytes output bytes.
 hipError_t launch_e2m1_to_e4m3(const uint8_t *codes, int64_t n_bytes, uint8_t *out, hipStream_t s);
 // Y = Y_main + dA . W, accumulated in fp32 in ascending k from Y_main, rounded once to y_dt.
-// Y_main and Y may be the same fp32 buffer.  capacity: what the dA list was sized for (picks
-// the kernel shape only; 0 if unknown).
-hipError_t launch_comp(const float *Ymain, void *Y, int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
-                       const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, int64_t capacity,
-                       hipStream_t s);
+// Y_main comes from the GEMM's DT_Q16 output (Yq, esc) and the scales sA, sW.  Yq may be a
+// bf16 Y itself, esc may be an fp32 Y itself.  capacity: what the dA list was sized for
+// (picks the kernel shape only; 0 if unknown).
+hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y, int y_dt,
+                       int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
+                       const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s);
 
 }  // namespace fp4

@@ -54,6 +54,8 @@ struct TileArgs {
     int M, N, K;
     void *Y;
     float *acc_out;
+    int16_t *yq;     // FB: the DT_Q16 output whose escaped blocks are marked
+    uint8_t *flags;  // DT_Q16 / FB: per tile and wave, 1 when the wave's block holds |acc| > Q16_MAX_ACC
     int tilesM, tilesN, raster_group;
 };
 
@@ -164,8 +166,64 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// DT_Q16 epilogue of two side-by-side 32 x 32 result tiles x0, x1 (MFMA layout; rows
+// row0.., columns col0.. and col0+32..): the low 16 bits of fl(4*acc + 1.5*2^23), which are
+// 4*acc as int16 whenever |acc| <= Q16_MAX_ACC, go into a private 32 x 64 patch of LDS, are
+// read back row-major and stored 16 bytes per lane, so each row segment is 128 bytes.
+// esc: set when some lane of the wave holds |acc| > Q16_MAX_ACC in these tiles.  Read-back chunk c = 64k + lane holds
+// row c/8 = 8k + lane/8, columns 8(c%8)..; loff0: its row-major offset (elements) for k = 0.
+// The patch is private to the wave and a wave's LDS accesses execute in order, so the
+// read-back sees the writes and the next call's writes cannot overtake it.
+__device__ __forceinline__ void epi_q16_pair(const v16f &x0, const v16f &x1, bool &esc, int16_t *P, int lane,
+                                             int row0, int col0, int M, int N, bool full, int16_t *Yq,
+                                             uint32_t loff0) {
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        P[lr * 64 + (lane & 31)] = (int16_t)__float_as_uint(__builtin_fmaf(x0[r], 4.0f, Q16_MAGIC));
+        P[lr * 64 + 32 + (lane & 31)] = (int16_t)__float_as_uint(__builtin_fmaf(x1[r], 4.0f, Q16_MAGIC));
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(x0[r]), __builtin_fabsf(x1[r])));
+    }
+    esc |= __builtin_amdgcn_ballot_w64(m > Q16_MAX_ACC) != 0;  // wave-uniform
+    v4i e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e[k] = *reinterpret_cast<const v4i *>(&P[8 * (k * 64 + lane)]);
+    if (full) {
+        int16_t *base = Yq + (size_t)row0 * N + col0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(base + loff0 + (uint32_t)(8 * k) * (uint32_t)N));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = k * 64 + lane, grow = row0 + (c >> 3), gcol = col0 + (c & 7) * 8;
+            if (grow < M && gcol < N)
+                __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(Yq + (size_t)grow * N + gcol));
+        }
+    }
+}
+
+// The escape pass of a DT_Q16 product (FB kernels): after a tile's fp32 epilogue has
+// written fl(fl(acc*sA)*sW) to the escape buffer, every int16 element of the wave's
+// 128 x 32*NJ result block (rows rbase.., columns cbase..) becomes Q16_ESC, 16 bytes per
+// lane along rows.
+template <int NJ>
+__device__ __forceinline__ void q16_fill_esc(int16_t *Yq, int lane, int rbase, int cbase, int M, int N, bool full) {
+    constexpr int CPR = 4 * NJ;  // 16-byte chunks per row
+    const int pat = (int)(((uint32_t)(uint16_t)Q16_ESC << 16) | (uint16_t)Q16_ESC);
+#pragma unroll
+    for (int k = 0; k < 2 * CPR; ++k) {  // 128 rows x CPR chunks, 64 per instruction
+        const int c = k * 64 + lane, grow = rbase + c / CPR, gcol = cbase + (c % CPR) * 8;
+        if (full || (grow < M && gcol < N))
+            __builtin_nontemporal_store(v4i{pat, pat, pat, pat}, reinterpret_cast<v4i *>(Yq + (size_t)grow * N + gcol));
+    }
+}
+
 // F8: the operands are E4M3 bytes (one K value per byte) instead of packed E2M1 codes.
-template <int YDT, bool ACCOUT, bool KFULL, bool F8>
+// FB: the escape pass of a DT_Q16 product (YDT = DT_F32 into the escape buffer): only the
+// tiles whose flags the DT_Q16 launch set are computed.
+template <int YDT, bool ACCOUT, bool KFULL, bool F8, bool FB>
 __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sb0[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb1[STB];
@@ -182,6 +240,9 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     const int per_xcd = gridDim.x / 8;
     const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= p.tilesM * p.tilesN) return;
+    if constexpr (FB) {
+        if (!reinterpret_cast<const uint32_t *>(p.flags)[logical]) return;
+    }
     const int group = logical / (p.raster_group * p.tilesN);
     const int first_m = group * p.raster_group;
     const int gm = min(p.raster_group, p.tilesM - first_m);
@@ -294,6 +355,8 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) sw[j] = bk.sW[wn * 64 + j * 32 + (lane & 31)];
     const bool full = (m0 + BM <= M) && (n0 + BN <= N);
+    const uint32_t qoff = (uint32_t)(lane >> 3) * (uint32_t)N + (uint32_t)((lane & 7) * 8);  // DT_Q16 read-back
+    bool qesc = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float sa[16];
@@ -306,6 +369,21 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
             sa[4 * r4 + 3] = v.w;
         }
         const int row0 = m0 + wm * 128 + i * 32;  // first row of this 32-row tile
+        if constexpr (YDT == DT_Q16) {
+            if constexpr (ACCOUT) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int grow = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const int gcol = n0 + wn * 64 + j * 32 + (lane & 31);
+                        if (full || (grow < M && gcol < N)) p.acc_out[(size_t)grow * N + gcol] = acc[i][j][r];
+                    }
+            }
+            epi_q16_pair(acc[i][0], acc[i][1], qesc, reinterpret_cast<int16_t *>(E), lane, row0, n0 + wn * 64, M, N,
+                         full, static_cast<int16_t *>(p.Y), qoff);
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col0 = n0 + wn * 64 + j * 32;
@@ -369,6 +447,10 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
+    if constexpr (YDT == DT_Q16) {
+        if (lane == 0) p.flags[logical * 4 + wave] = qesc ? 1 : 0;
+    }
+    if constexpr (FB) q16_fill_esc<2>(p.yq, lane, m0 + wm * 128, n0 + wn * 64, M, N, full);
 }
 
 // ----------------------------------------------------------------------------- wide tiles
@@ -397,7 +479,8 @@ struct WBook {
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     \
     } while (0)
 
-template <int YDT, bool ACCOUT>
+// FB as in k_fp4_gemm: the escape pass, on the flagged tiles of the workgroup's walk only.
+template <int YDT, bool ACCOUT, bool FB>
 __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sb0[WSTB];
     __shared__ __attribute__((aligned(16))) uint8_t sb1[WSTB];
@@ -415,7 +498,15 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int tpx = (tiles + 7) / 8;
     const int hi = min((xcd + 1) * tpx, tiles);
-    int logical = xcd * tpx + slot;
+    // FB: the next tile of the walk at or after lg that the DT_Q16 launch flagged
+    auto flagged = [&](int lg) {
+        if constexpr (FB) {
+            const uint32_t *f = reinterpret_cast<const uint32_t *>(p.flags);
+            while (lg < hi && !f[lg]) lg += per_xcd_wg;
+        }
+        return lg;
+    };
+    int logical = flagged(xcd * tpx + slot);
     if (logical >= hi) return;
 
     auto origin = [&](int lg, int &m0, int &n0) {
@@ -500,7 +591,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     };
 
     for (int tt = 0;; ++tt) {
-        const int nlog = logical + per_xcd_wg;
+        const int nlog = flagged(logical + per_xcd_wg);
         const bool has_next = nlog < hi;
         int nm0 = m0, nn0 = n0, noffA[4], noffB[4];
         if (has_next) origin(nlog, nm0, nn0);
@@ -546,16 +637,17 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
         const bool full = (m0 + BM <= M) && (n0 + WBN <= N);
         // Row-major read-back of a 32 x 32 patch, the same lanes for every tile: chunk
         // c = 64k + lane holds row c/8, columns 4(c%8).. (fp32) or row c/4, columns 8(c%4).. (bf16).
-        constexpr int NK = YDT == DT_BF16 ? 2 : 4;
+        constexpr int NK = YDT == DT_F32 ? 4 : (YDT == DT_BF16 ? 2 : 1);
         int lrow[NK], lcol[NK];
         uint32_t loff[NK];
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
             const int c = k * 64 + lane;
             lrow[k] = YDT == DT_BF16 ? c >> 2 : c >> 3;
-            lcol[k] = YDT == DT_BF16 ? (c & 3) * 8 : (c & 7) * 4;
+            lcol[k] = YDT == DT_BF16 ? (c & 3) * 8 : (c & 7) * (YDT == DT_Q16 ? 8 : 4);
             loff[k] = (uint32_t)lrow[k] * (uint32_t)N + (uint32_t)lcol[k];
         }
+        bool qesc = false;  // DT_Q16: some |acc| of the wave's block is past the int16 range
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sa[16];
@@ -568,6 +660,25 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                 sa[4 * r4 + 3] = v.w;
             }
             const int row0 = m0 + wm * 128 + i * 32;
+            if constexpr (YDT == DT_Q16) {
+#pragma unroll
+                for (int jp = 0; jp < 2; ++jp) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (ACCOUT) {
+#pragma unroll
+                        for (int j = 2 * jp; j < 2 * jp + 2; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int grow = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                                const int gcol = n0 + wn * 128 + j * 32 + (lane & 31);
+                                if (full || (grow < M && gcol < N)) p.acc_out[(size_t)grow * N + gcol] = acc[i][j][r];
+                            }
+                    }
+                    epi_q16_pair(acc[i][2 * jp], acc[i][2 * jp + 1], qesc, reinterpret_cast<int16_t *>(E), lane, row0,
+                                 n0 + wn * 128 + 64 * jp, M, N, full, static_cast<int16_t *>(p.Y), loff[0]);
+                }
+                continue;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -636,6 +747,10 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                 }
             }
         }
+        if constexpr (YDT == DT_Q16) {
+            if (lane == 0) p.flags[logical * 4 + wave] = qesc ? 1 : 0;
+        }
+        if constexpr (FB) q16_fill_esc<4>(p.yq, lane, m0 + wm * 128, n0 + wn * 128, M, N, full);
         bk[(tt + 1) & 1].sA[tid] = nbA;
         bk[(tt + 1) & 1].sW[tid] = nbW;
         if (!has_next) break;
@@ -687,8 +802,82 @@ static bool wide_gemm_enabled() {
     return env != 0;
 }
 
+size_t gemm_flag_bytes(int64_t M, int64_t N) {
+    // one byte per wave and tile of the 256 x 128 kernel, which has the most tiles
+    return (size_t)4 * (size_t)((M + BM - 1) / BM) * (size_t)((N + BN - 1) / BN);
+}
+
+// One launch of the product.  FB: the escape pass of a DT_Q16 product (fp32 into Y = the
+// escape buffer, flagged tiles only).
+static hipError_t launch_gemm_one(const TileArgs &p0, int y_dt, bool acc, bool f8, bool fb, hipStream_t s) {
+    TileArgs p = p0;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    // wide persistent tiles when there are enough of them to keep every CU busy for a few
+    // rounds (few large tiles would leave the per-tile prologue and epilogue exposed)
+    if (!f8 && K % 512 == 0 && wide_gemm_enabled()) {
+        const int cus = num_cus();
+        const int64_t wtiles = ((M + BM - 1) / BM) * ((N + WBN - 1) / WBN);
+        if (cus >= 8 && wtiles >= 4 * (int64_t)cus) {
+            p.tilesN = (int)((N + WBN - 1) / WBN);
+            const int blocks = cus / 8 * 8;
+#define W3(YD, AO, FBK) hipLaunchKernelGGL((k_fp4_gemm_wide<YD, AO, FBK>), dim3(blocks), dim3(NT), 0, s, p)
+            if (fb) W3(DT_F32, false, true);
+            else if (y_dt == DT_Q16) {
+                if (acc) W3(DT_Q16, true, false);
+                else W3(DT_Q16, false, false);
+            } else if (y_dt == DT_BF16) {
+                if (acc) W3(DT_BF16, true, false);
+                else W3(DT_BF16, false, false);
+            } else {
+                if (acc) W3(DT_F32, true, false);
+                else W3(DT_F32, false, false);
+            }
+#undef W3
+            return hipGetLastError();
+        }
+    }
+    const int64_t tiles = (int64_t)p.tilesM * p.tilesN;
+    const int blocks = (int)((tiles + 7) / 8 * 8);
+    const bool kfull = f8 ? (K % 64 == 0) : (K % 128 == 0);  // every stage whole
+#define G3(YD, AO, KF, F, FBK) hipLaunchKernelGGL((k_fp4_gemm<YD, AO, KF, F, FBK>), dim3(blocks), dim3(NT), 0, s, p)
+#define G2(YD, AO, F)                               \
+    do {                                            \
+        if (kfull) G3(YD, AO, true, F, false);      \
+        else G3(YD, AO, false, F, false);           \
+    } while (0)
+#define G1(YD, AO)                  \
+    do {                            \
+        if (f8) G2(YD, AO, true);   \
+        else G2(YD, AO, false);     \
+    } while (0)
+    if (fb) {  // never F8
+        if (kfull) G3(DT_F32, false, true, false, true);
+        else G3(DT_F32, false, false, false, true);
+    } else if (y_dt == DT_Q16) {  // never F8
+        if (kfull) {
+            if (acc) G3(DT_Q16, true, true, false, false);
+            else G3(DT_Q16, false, true, false, false);
+        } else {
+            if (acc) G3(DT_Q16, true, false, false, false);
+            else G3(DT_Q16, false, false, false, false);
+        }
+    } else if (y_dt == DT_BF16) {
+        if (acc) G1(DT_BF16, true);
+        else G1(DT_BF16, false);
+    } else {
+        if (acc) G1(DT_F32, true);
+        else G1(DT_F32, false);
+    }
+#undef G1
+#undef G2
+#undef G3
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8) {
+                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8, float *esc,
+                       uint8_t *flags) {
+    if (y_dt == DT_Q16 && (f8 || !esc || !flags)) return hipErrorInvalidValue;
     TileArgs p;
     p.Aq = Aq;
     p.Wq = Wq;
@@ -699,52 +888,18 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
     p.K = (int)K;
     p.Y = Y;
     p.acc_out = acc_out;
+    p.yq = nullptr;
+    p.flags = flags;
     p.tilesM = (int)((M + BM - 1) / BM);
     p.tilesN = (int)((N + BN - 1) / BN);
     p.raster_group = raster_group_for(p.tilesM);
-    // wide persistent tiles when there are enough of them to keep every CU busy for a few
-    // rounds (few large tiles would leave the per-tile prologue and epilogue exposed)
-    if (!f8 && K % 512 == 0 && wide_gemm_enabled()) {
-        const int cus = num_cus();
-        const int64_t wtiles = ((M + BM - 1) / BM) * ((N + WBN - 1) / WBN);
-        if (cus >= 8 && wtiles >= 4 * (int64_t)cus) {
-            p.tilesN = (int)((N + WBN - 1) / WBN);
-            const int blocks = cus / 8 * 8;
-            if (y_dt == DT_BF16) {
-                if (acc_out) hipLaunchKernelGGL((k_fp4_gemm_wide<DT_BF16, true>), dim3(blocks), dim3(NT), 0, s, p);
-                else hipLaunchKernelGGL((k_fp4_gemm_wide<DT_BF16, false>), dim3(blocks), dim3(NT), 0, s, p);
-            } else {
-                if (acc_out) hipLaunchKernelGGL((k_fp4_gemm_wide<DT_F32, true>), dim3(blocks), dim3(NT), 0, s, p);
-                else hipLaunchKernelGGL((k_fp4_gemm_wide<DT_F32, false>), dim3(blocks), dim3(NT), 0, s, p);
-            }
-            return hipGetLastError();
-        }
-    }
-    const int64_t tiles = (int64_t)p.tilesM * p.tilesN;
-    const int blocks = (int)((tiles + 7) / 8 * 8);
-    const bool kfull = f8 ? (K % 64 == 0) : (K % 128 == 0);  // every stage whole
-#define G3(YD, AO, KF, F) hipLaunchKernelGGL((k_fp4_gemm<YD, AO, KF, F>), dim3(blocks), dim3(NT), 0, s, p)
-#define G2(YD, AO, F)                        \
-    do {                                     \
-        if (kfull) G3(YD, AO, true, F);      \
-        else G3(YD, AO, false, F);           \
-    } while (0)
-#define G1(YD, AO)                  \
-    do {                            \
-        if (f8) G2(YD, AO, true);   \
-        else G2(YD, AO, false);     \
-    } while (0)
-    if (y_dt == DT_BF16) {
-        if (acc_out) G1(DT_BF16, true);
-        else G1(DT_BF16, false);
-    } else {
-        if (acc_out) G1(DT_F32, true);
-        else G1(DT_F32, false);
-    }
-#undef G1
-#undef G2
-#undef G3
-    return hipGetLastError();
+    hipError_t e = launch_gemm_one(p, y_dt, acc_out != nullptr, f8, false, s);
+    if (e != hipSuccess || y_dt != DT_Q16) return e;
+    // the escape pass: the tiles whose accumulators left the int16 range, again in fp32
+    p.Y = esc;
+    p.yq = static_cast<int16_t *>(Y);
+    p.acc_out = nullptr;
+    return launch_gemm_one(p, DT_F32, false, false, true, s);
 }
 
 }  // namespace fp4

@@ -56,7 +56,7 @@ def test_forward_layout_is_disjoint_and_aligned():
     cap = lay.capacity
     parts = [(lay.T, 4), (lay.nnz, 8), (lay.row_ptr, 301 * 4), (lay.coo_row, cap * 4), (lay.coo_col, cap * 4),
              (lay.coo_val, cap * 4), (lay.Aq, 300 * 256), (lay.sA, 300 * 4), (lay.Wq, 264 * 256),
-             (lay.sW, 264 * 4), (lay.ymain, 300 * 264 * 4), (lay.scratch, 1)]
+             (lay.sW, 264 * 4), (lay.handoff, 300 * 264 * 4), (lay.scratch, 1)]
     parts.sort()
     for (a, na), (b, _) in zip(parts, parts[1:]):
         assert a % 256 == 0 and a + na <= b
@@ -165,9 +165,16 @@ def test_gemm_rejects():
     assert g(rp=FAKE) == ENULL            # partial compensation arguments
     assert g(rp=FAKE, cc=FAKE) == ENULL
     assert g(rp=FAKE, cc=FAKE, cv=FAKE) == ENULL  # compensation without W
-    assert g(**comp) == ENULL             # bf16 Y with compensation needs the fp32 workspace
-    assert g(**comp, ws=FAKE, wsb=64 * 64 * 4 - 1) == EWS
-    assert g(**comp, ws=C.c_void_p(0x100008), wsb=64 * 64 * 4) == EALIGN
+    assert g(**comp) == ENULL             # bf16 Y with compensation needs the escape workspace
+    need = {d: L.fp4_gemm_workspace_bytes(64, 64, d, int(d != 2)) for d in (0, 1, 2)}
+    assert need[1] > 64 * 64 * 4 and need[0] > 64 * 64 * 2 and need[2] > 64 * 64 * 4
+    assert g(**comp, ws=FAKE, wsb=need[1] - 1) == EWS
+    assert g(**comp, ws=C.c_void_p(0x100008), wsb=need[1]) == EALIGN
+    assert g(**comp, ydt=0) == ENULL      # so does an fp32 Y (the int16 accumulators)
+    assert g(**comp, ydt=0, ws=FAKE, wsb=need[0] - 1) == EWS
+    assert g(ydt=2) == ENULL              # the two-byte accumulator output needs its escape buffer
+    assert g(ydt=2, ws=FAKE, wsb=need[2] - 1) == EWS
+    assert g(**comp, ydt=2, ws=FAKE, wsb=1 << 40) == EDTYPE  # and takes no dA term
     assert g(ydt=5) == EDTYPE
     assert g(K=96 + 16) == ESHAPE
     assert g(N=0) == ESHAPE
@@ -178,9 +185,14 @@ def test_gemm_rejects():
 
 def test_gemm_workspace_bytes():
     L = fp4.lib()
-    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 1) == 300 * 264 * 4
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    flags = up(4 * 2 * 3)  # a byte per wave of each 256 x 128 tile: 2 x 3 tiles
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 1) == up(300 * 264 * 4) + flags  # fp32 escapes
     assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 0) == 0
-    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 1) == 0   # fp32 Y is updated in place
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 1) == up(300 * 264 * 2) + flags   # int16 accumulators
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 0) == 0
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_Q16, 0) == up(300 * 264 * 4) + flags   # fp32 escapes
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_Q16, 1) == 0   # no dA term on the raw hand-over
     assert L.fp4_gemm_workspace_bytes(0, 264, fp4.FP4_BF16, 1) == 0
     assert L.fp4_gemm_workspace_bytes(300, 100, fp4.FP4_BF16, 1) == 0
 

@@ -294,6 +294,93 @@ def test_gemm_with_compensation(M, N, K, wdt, wide):
     assert np.array_equal(to_np(Y16), to_np(Y32.to(torch.bfloat16)))
 
 
+def _escape_codes(rng, M, N, K, rows, cols):
+    """Random codes, except rows of Aq and of Wq (output channels) holding +6 everywhere:
+    their products reach acc = 36 K, past the two-byte hand-over's range once K > 227."""
+    Aq, Wq = _random_codes(rng, M, K), _random_codes(rng, N, K)
+    Aq[list(rows)] = 0x77
+    Wq[list(cols)] = 0x77
+    return Aq, Wq
+
+
+def _check_q16(Yq, esc, acc, sA, sW, block=(256, 128)):
+    """The FP4_Q16 contract element by element: the int16 4*acc, or -32768 with esc holding
+    fl(fl(acc*sA)*sW) in fp32; every |acc| > 8191.75 is escaped, and escapes stay inside the
+    output tiles (256 x 128 or 256 x 256) that hold such an accumulator.  Returns the number of
+    escaped elements."""
+    yq = Yq.cpu().numpy().astype(np.int64)
+    a = acc.cpu().numpy()
+    escaped = yq == -32768
+    big = np.abs(a) > 8191.75
+    assert np.all(escaped[big])
+    assert np.array_equal(yq[~escaped], (a[~escaped] * 4).astype(np.int64))
+    if escaped.any():
+        e = esc.cpu().numpy()
+        ymain = (a[escaped] * sA[np.nonzero(escaped)[0]]).astype(np.float32) * sW[np.nonzero(escaped)[1]]
+        assert np.array_equal(e[escaped], ymain.astype(np.float32))
+        M, N = a.shape
+        bm, bn = block
+        hot = np.zeros(((M + bm - 1) // bm, (N + bn - 1) // bn), dtype=bool)
+        r, c = np.nonzero(big)
+        hot[r // bm, c // bn] = True
+        r, c = np.nonzero(escaped)
+        assert np.all(hot[r // bm, c // bn])
+    return int(escaped.sum())
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 512), (513, 776, 1056), (64, 8, 256), (257, 136, 96)])
+def test_gemm_q16_handover(M, N, K):
+    """The GEMM's two-byte accumulator output (the hand-over to the compensation pass) on the
+    256 x 128 kernel: exact 4*acc, escapes where |acc| > 8191.75 (rows and channels of +6
+    codes; none for K = 96, where 36 K < 8192), fp32 values there."""
+    _say(f"gemm q16 {M}x{N}x{K}")
+    rng = np.random.default_rng(M + 3 * N + K)
+    rows, cols = {0, M // 2, M - 1}, {0, N // 2, N - 1}
+    Aq, Wq = _escape_codes(rng, M, N, K, rows, cols)
+    sA = rng.lognormal(-2, 1, M).astype(np.float32)
+    sW = rng.lognormal(-4, 1, N).astype(np.float32)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    Yq, esc, acc = fp4.gemm_q16(t(Aq), t(sA), t(Wq), t(sW), K, acc_out=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(acc), oracle.accumulate(Aq, Wq, K))
+    n_esc = _check_q16(Yq, esc, acc, sA, sW)
+    assert (n_esc > 0) == (36 * K > 8191.75)
+
+
+def test_gemm_q16_handover_wide():
+    """The same contract on the persistent 256 x 256 kernel (8192 x 8192 x 512: 1024 tiles),
+    its escape pass recomputing only the flagged tiles."""
+    M, N, K = 8192, 8192, 512
+    _say(f"gemm q16 wide {M}x{N}x{K}")
+    rng = np.random.default_rng(77)
+    rows, cols = {0, 4000, M - 1}, {5, 4100, N - 1}
+    Aq, Wq = _escape_codes(rng, M, N, K, rows, cols)
+    sA = rng.lognormal(-2, 1, M).astype(np.float32)
+    sW = rng.lognormal(-4, 1, N).astype(np.float32)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    Yq, esc, acc = fp4.gemm_q16(t(Aq), t(sA), t(Wq), t(sW), K, acc_out=True)
+    torch.cuda.synchronize()
+    ms = np.concatenate([rng.integers(0, M, 20000), np.repeat(sorted(rows), N)])
+    ns = np.concatenate([rng.integers(0, N, 20000), np.tile(np.arange(N), len(rows))])
+    g = acc.view(-1)[torch.from_numpy(ms * N + ns).to(DEV)].cpu().numpy()
+    assert np.array_equal(g, oracle.accumulate_pairs(Aq, Wq, K, ms, ns))
+    n_esc = _check_q16(Yq, esc, acc, sA, sW, block=(256, 256))
+    assert n_esc > 0
+
+
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "fp32"), ("fp32", "fp32")])
+def test_forward_with_escaped_accumulators(dtype, out):
+    """Rows of A and columns of W that quantize to +6 everywhere give acc = 36 K = 18432:
+    the GEMM hands those tiles over in fp32 (the workspace for a bf16 Y, Y itself for an fp32
+    Y) and the compensation pass must still produce the oracle's Y."""
+    _say(f"forward escapes {dtype} out={out}")
+    A, W = make_custom(300, 512, 264, dtype=dtype, seed=21)
+    A[5:8] = 1.0
+    W[:, 10:13] = 0.02
+    W[:, 200] = -0.02
+    _check_forward_small(A, W, 0.99, _dt(out))
+
+
 # ----------------------------------------------------------------------------- forward
 def _check_forward_small(A, W, q, out_dtype):
     M, K = A.shape
