@@ -213,7 +213,8 @@ fp4_status forward_impl(const void *A, const void *W, const uint8_t *Wq_in, cons
     // The accumulator as int16 4*acc (into a bf16 Y itself, else into the workspace) with
     // fp32 escapes (into the workspace, else into the fp32 Y), then Y = Y_main + dA . W
     const Q16Bufs b = q16_buffers(Y, y_dtype, ws + l.handoff, M, N);
-    if (e == hipSuccess) e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, nullptr, s, false, b.esc, b.flags);
+    if (e == hipSuccess)
+        e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, nullptr, s, false, b.esc, b.flags);
     if (e == hipSuccess)
         e = launch_comp(b.yq, b.esc, sA, sW, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype),
                         l.capacity, s);

@@ -1,26 +1,23 @@
-// gfx950 kernel of the sparse compensation term dA . W of the FP4 linear forward (outlier
+// gfx950 kernels of the sparse compensation term dA . W of the FP4 linear forward (outlier
 // paragraph of the QbitAI report on "Optimizing Large Language Model Training Using FP4
 // Quantization": the entries clamped away from A are kept as a sparse matrix and their
-// product with the weights is added back).  It runs after the FP4 GEMM, which hands over
+// product with the weights is added back).  They run after the FP4 GEMM, which hands over
 // its exact accumulator as two-byte integers 4*acc (fp32 escapes for |acc| > 8191.75); the
 // pass rebuilds the dequantized product Y_main = fl(fl(acc*sA)*sW) bit for bit and writes
-// Y = Y_main + dA . W in the output type, rounded once.  The two-byte hand-over halves the
-// bytes that a fp32 Y_main would cost on both sides of the pass.
+// Y = Y_main + dA . W in the output type, rounded once, the entries added in ascending k with
+// one fp32 fma each.  The two-byte hand-over halves the bytes that an fp32 Y_main would cost
+// on both sides of the pass.
 //
 // One wave per (row, chunk of 64*CC columns) task; lane l owns the CC columns CC*l .. of
-// the chunk.  The wave first issues its accumulator and column-scale loads and the row's
-// two CSR offsets together, then takes the row's dA entries (ascending column k) 64 at a
-// time, one (k, delta) pair per lane, and walks them in groups of eight: the eight W row
-// segments are loaded together and added to the running sums in ascending k (one fp32 fma
-// each).
-//
-// Task order: the tasks are dealt out to the eight XCDs in contiguous ranges (consecutive
-// workgroup ids go to different XCDs), chunk-major within a range, so each XCD streams all
-// rows over one chunk at a time and the W rows that chunk gathers stay in that XCD's L2.
-// The accumulators and Y are streamed with non-temporal hints so they do not evict those rows.
-// Two widths: CC = 8 (512-column chunks, more bytes in flight per wave) when the
-// rows hold few entries and the pass streams; CC = 4 (256-column chunks, half the
-// W strip per chunk) when many entries per row make it bound by its gathers.
+// the chunk.  The wave first issues its accumulator and column-scale loads and the row's two
+// CSR offsets together, then takes the row's dA entries 64 at a time, one (k, delta) pair per
+// lane, and walks them in groups of eight W row segments loaded together.  Tasks are dealt
+// out to the eight XCDs in contiguous ranges (consecutive workgroup ids go to different
+// XCDs), chunk-major within a range, so each XCD streams all rows over one chunk at a time
+// and the W rows that chunk gathers stay in its L2.  CC = 8 (512-column chunks) up to 64
+// entries per row on average, CC = 4 (256-column chunks, half the W strip per chunk) beyond,
+// where the gathers bound it.
+// The accumulators and Y are streamed with non-temporal hints so they do not evict W.
 #include "fp4_common.h"
 #include "fp4_launch.h"
 
@@ -57,34 +54,72 @@ __device__ __forceinline__ float seg_elem(const v4i (&raw)[2], int c) {
     }
 }
 
-// Y_main of the lane's CC columns, rebuilt from the GEMM's DT_Q16 output: acc = q / 4 exactly,
-// Y_main = fl(fl(acc * sA) * sW) as the GEMM's own epilogue rounds it; escaped elements
-// take their fp32 value from esc.  Yq may be Y itself (bf16 Y) and esc may be Y itself
-// (fp32 Y): every lane reads exactly the bytes it later writes, and no other lane touches them.
+// Decodes the lane's CC int16 accumulator codes q (packed in qv) into Y_main: acc = q / 4
+// exactly, Y_main = fl(fl(acc * sA) * sW) as the GEMM's own epilogue rounds it; escaped
+// elements take their fp32 value from er (the row's escape values).  Yq may be Y itself
+// (bf16 Y) and esc may be Y itself (fp32 Y): every lane reads exactly the bytes it later
+// writes, and no other lane touches them.
+template <int CC>
+__device__ __forceinline__ void decode_ymain(const v4i &qv, const v4i (&swv)[2], float sa, bool active,
+                                             const float *er, int col, float (&y)[CC]) {
+    bool escaped = false;
+#pragma unroll
+    for (int i = 0; i < CC; ++i) {
+        const int q = (int)(int16_t)(((uint32_t)qv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        escaped |= q == Q16_ESC;
+        y[i] = ((float)q * 0.25f * sa) * __int_as_float(swv[i >> 2][i & 3]);
+    }
+    if (__builtin_amdgcn_ballot_w64(escaped)) {  // |acc| > Q16_MAX_ACC somewhere in the wave
+#pragma unroll
+        for (int i = 0; i < CC; ++i)
+            if (active && (int)(int16_t)(((uint32_t)qv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) == Q16_ESC)
+                y[i] = er[col + i];
+    }
+}
+
+// Y[row][col .. col+CC) in the output type (16 or 8 bytes per lane, non-temporal).
+template <int YDT, int CC>
+__device__ __forceinline__ void store_y(void *Y, size_t off, const float (&y)[CC]) {
+    if constexpr (YDT == DT_BF16) {
+        uint32_t o[CC / 2];
+#pragma unroll
+        for (int i = 0; i < CC / 2; ++i) o[i] = f32_to_bf16_bits(y[2 * i]) | (f32_to_bf16_bits(y[2 * i + 1]) << 16);
+        uint16_t *yp = reinterpret_cast<uint16_t *>(Y) + off;
+        if constexpr (CC == 8)
+            __builtin_nontemporal_store(v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]}, reinterpret_cast<v4i *>(yp));
+        else
+            __builtin_nontemporal_store(v2i{(int)o[0], (int)o[1]}, reinterpret_cast<v2i *>(yp));
+    } else {
+        f4 *yp = reinterpret_cast<f4 *>(reinterpret_cast<float *>(Y) + off);
+#pragma unroll
+        for (int h = 0; h < CC / 4; ++h) __builtin_nontemporal_store(f4{y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]}, yp + h);
+    }
+}
+
+struct CompArgs {
+    const int16_t *Yq;
+    const float *esc;
+    const float *sA, *sW;
+    void *Y;
+    int M, N, K;
+    const int32_t *row_ptr, *coo_col;
+    const float *coo_val;
+    const void *W;
+};
+
+// One (row, chunk) task: lane l owns the CC columns chunk*64*CC + CC*l ...
 template <int YDT, int WDT, int CC>
-__global__ __launch_bounds__(256) void k_comp_apply(const int16_t *Yq, const float *esc,
-                                                    const float *__restrict__ sA, const float *__restrict__ sW,
-                                                    void *Y, int M, int N, int K, int chunks, int per_xcd,
-                                                    const int32_t *__restrict__ row_ptr,
-                                                    const int32_t *__restrict__ coo_col,
-                                                    const float *__restrict__ coo_val, const void *__restrict__ W) {
-    const int lane = threadIdx.x & 63;
-    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    const int64_t task = (int64_t)logical * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (task >= (int64_t)chunks * M) return;  // whole wave
-    const int chunk = (int)(task / M);
-    const int row = (int)(task - (int64_t)chunk * M);
+__device__ __forceinline__ void comp_task(const CompArgs &a, int row, int chunk, int lane) {
+    const int N = a.N;
     const int col = chunk * (64 * CC) + lane * CC;
     const bool active = col < N;  // N % 8 == 0: a lane's columns are in range together
-    const size_t yoff = (size_t)row * N + col;
-
     // The row's CSR offsets (lane l loads row_ptr[row + (l & 1)]), the lane's accumulator
     // codes and column scales, issued together; the codes and scales go through
     // descriptors, so a lane past N reads zeros.
-    const int32_t rp = row_ptr[row + (lane & 1)];
+    const int32_t rp = a.row_ptr[row + (lane & 1)];
     const __amdgpu_buffer_rsrc_t rsQ =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t *>(Yq) + (size_t)row * N, 0, N * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(sW), 0, N * 4, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t *>(a.Yq) + (size_t)row * N, 0, N * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.sW), 0, N * 4, 0x00020000);
     v4i qv = v4i{0, 0, 0, 0};
     if constexpr (CC == 8) {
         qv = __builtin_amdgcn_raw_buffer_load_b128(rsQ, col * 2, 0, 2);
@@ -92,41 +127,29 @@ __global__ __launch_bounds__(256) void k_comp_apply(const int16_t *Yq, const flo
         const v2i q2 = __builtin_amdgcn_raw_buffer_load_b64(rsQ, col * 2, 0, 2);
         qv = v4i{q2.x, q2.y, 0, 0};
     }
-    v4i swv[CC / 4];
+    v4i swv[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
 #pragma unroll
     for (int h = 0; h < CC / 4; ++h) swv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16 * h, 0, 0);
-    const float sa = sA[row];
+    const float sa = a.sA[row];
     const int32_t e0 = __builtin_amdgcn_readlane(rp, 0);
     const int32_t e1 = __builtin_amdgcn_readlane(rp, 1);
     float y[CC];
-    bool escaped = false;
-#pragma unroll
-    for (int c = 0; c < CC; ++c) {
-        const int q = (int)(int16_t)(((uint32_t)qv[c >> 1] >> (16 * (c & 1))) & 0xFFFFu);
-        escaped |= q == Q16_ESC;
-        y[c] = ((float)q * 0.25f * sa) * __int_as_float(swv[c >> 2][c & 3]);
-    }
-    if (__builtin_amdgcn_ballot_w64(escaped)) {  // |acc| > Q16_MAX_ACC somewhere in the wave
-#pragma unroll
-        for (int c = 0; c < CC; ++c)
-            if (active && (int)(int16_t)(((uint32_t)qv[c >> 1] >> (16 * (c & 1))) & 0xFFFFu) == Q16_ESC)
-                y[c] = esc[yoff + c];
-    }
+    decode_ymain<CC>(qv, swv, sa, active, a.esc + (size_t)row * N, col, y);
 
     // W through a buffer descriptor.  Offsets are unsigned 32-bit: K*N*ESZ < 2^31, so the
     // largest (a lane past N on the last row of W) stays below 2^32 and reads zeros; such a
     // lane is never stored.
     constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
     const __amdgpu_buffer_rsrc_t rsW =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(W), 0, (int)((int64_t)K * N * ESZ), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.W), 0, (int)((int64_t)a.K * N * ESZ), 0x00020000);
     const uint32_t row_bytes = (uint32_t)N * ESZ;
     const uint32_t lane_off = (uint32_t)col * ESZ;
     for (int32_t e = e0; e < e1; e += 64) {
         int32_t kk = 0;
         float dd = 0.0f;
         if (e + lane < e1) {
-            kk = coo_col[e + lane];
-            dd = coo_val[e + lane];
+            kk = a.coo_col[e + lane];
+            dd = a.coo_val[e + lane];
         }
         const int nb = min(64, e1 - e);  // wave-uniform
         for (int s = 0; s < nb; s += CB) {
@@ -147,37 +170,28 @@ __global__ __launch_bounds__(256) void k_comp_apply(const int16_t *Yq, const flo
             }
         }
     }
-    if (!active) return;
-    if constexpr (YDT == DT_BF16) {
-        uint32_t o[CC / 2];
-#pragma unroll
-        for (int i = 0; i < CC / 2; ++i) o[i] = f32_to_bf16_bits(y[2 * i]) | (f32_to_bf16_bits(y[2 * i + 1]) << 16);
-        uint16_t *yp = reinterpret_cast<uint16_t *>(Y) + yoff;
-        if constexpr (CC == 8)
-            __builtin_nontemporal_store(v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]}, reinterpret_cast<v4i *>(yp));
-        else
-            __builtin_nontemporal_store(v2i{(int)o[0], (int)o[1]}, reinterpret_cast<v2i *>(yp));
-    } else {
-        f4 *yp = reinterpret_cast<f4 *>(reinterpret_cast<float *>(Y) + yoff);
-#pragma unroll
-        for (int h = 0; h < CC / 4; ++h)
-            __builtin_nontemporal_store(f4{y[4 * h], y[4 * h + 1], y[4 * h + 2], y[4 * h + 3]}, yp + h);
-    }
+    if (active) store_y<YDT, CC>(a.Y, (size_t)row * N + col, y);
+}
+
+template <int YDT, int WDT, int CC>
+__global__ __launch_bounds__(256) void k_comp_apply(CompArgs a, int chunks, int per_xcd) {
+    const int lane = threadIdx.x & 63;
+    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    const int64_t task = (int64_t)logical * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (task >= (int64_t)chunks * a.M) return;  // whole wave
+    const int chunk = (int)(task / a.M);
+    const int row = (int)(task - (int64_t)chunk * a.M);
+    comp_task<YDT, WDT, CC>(a, row, chunk, lane);
 }
 
 template <int CC>
-static hipError_t launch_comp_w(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y,
-                                int y_dt, int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
-                                const int32_t *coo_col, const float *coo_val, const void *W, int w_dt,
-                                hipStream_t s) {
-    const int chunks = (int)((N + 64 * CC - 1) / (64 * CC));
-    const int64_t tasks = (int64_t)chunks * M;
+static hipError_t launch_comp_tasks(const CompArgs &a, int y_dt, int w_dt, hipStream_t s) {
+    const int chunks = (int)((a.N + 64 * CC - 1) / (64 * CC));
+    const int64_t tasks = (int64_t)chunks * a.M;
     const int64_t blocks = (tasks + 3) / 4;
     const int per_xcd = (int)((blocks + 7) / 8);
     const dim3 grid((unsigned)per_xcd * 8u), block(256);
-#define C(YD, WD)                                                                                               \
-    hipLaunchKernelGGL((k_comp_apply<YD, WD, CC>), grid, block, 0, s, Yq, esc, sA, sW, Y, (int)M, (int)N, (int)K, \
-                       chunks, per_xcd, row_ptr, coo_col, coo_val, W)
+#define C(YD, WD) hipLaunchKernelGGL((k_comp_apply<YD, WD, CC>), grid, block, 0, s, a, chunks, per_xcd)
     if (y_dt == DT_BF16) {
         if (w_dt == DT_BF16) C(DT_BF16, DT_BF16);
         else C(DT_BF16, DT_F32);
@@ -192,11 +206,11 @@ static hipError_t launch_comp_w(const int16_t *Yq, const float *esc, const float
 hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y, int y_dt,
                        int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s) {
+    const CompArgs a{Yq, esc, sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
     // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
     // gathers and the narrower chunks keep more of each W strip in L2
-    if (capacity > 64 * M)
-        return launch_comp_w<4>(Yq, esc, sA, sW, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
-    return launch_comp_w<8>(Yq, esc, sA, sW, Y, y_dt, M, N, K, row_ptr, coo_col, coo_val, W, w_dt, s);
+    if (capacity > 64 * M) return launch_comp_tasks<4>(a, y_dt, w_dt, s);
+    return launch_comp_tasks<8>(a, y_dt, w_dt, s);
 }
 
 }  // namespace fp4

@@ -498,11 +498,17 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int tpx = (tiles + 7) / 8;
     const int hi = min((xcd + 1) * tpx, tiles);
-    // FB: the next tile of the walk at or after lg that the DT_Q16 launch flagged
+    // FB: the next tile of the walk at or after lg that the DT_Q16 launch flagged (64 of the
+    // walk's flags per round trip, one per lane)
     auto flagged = [&](int lg) {
         if constexpr (FB) {
             const uint32_t *f = reinterpret_cast<const uint32_t *>(p.flags);
-            while (lg < hi && !f[lg]) lg += per_xcd_wg;
+            while (lg < hi) {
+                const int mine = lg + lane * per_xcd_wg;
+                const uint64_t b = __builtin_amdgcn_ballot_w64(mine < hi && f[mine] != 0);
+                if (b) return lg + (int)__builtin_ctzll(b) * per_xcd_wg;
+                lg += 64 * per_xcd_wg;
+            }
         }
         return lg;
     };

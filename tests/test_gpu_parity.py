@@ -272,13 +272,14 @@ def test_gemm_accumulator_extremes():
     assert to_np(acc)[0, 1] == 36.0 * K and to_np(acc)[1, 1] == -36.0 * K
 
 
-@pytest.mark.parametrize("wide", [True, False], ids=["chunk512", "chunk256"])
+@pytest.mark.parametrize("shape", ["chunk512", "chunk256"])
 @pytest.mark.parametrize("M,N,K,wdt", [(300, 264, 512, "bf16"), (513, 520, 1056, "fp32"), (64, 8, 96, "bf16"),
                                        (70, 776, 128, "fp32")])
-def test_gemm_with_compensation(M, N, K, wdt, wide):
+def test_gemm_with_compensation(M, N, K, wdt, shape):
     """Both shapes of the compensation kernel (the capacity hint picks one: more than 64
     entries per row selects the 256-column chunks)."""
-    _say(f"gemm comp {M}x{N}x{K} {wdt} {'wide' if wide else 'narrow'}")
+    _say(f"gemm comp {M}x{N}x{K} {wdt} {shape}")
+    wide = shape != "chunk256"
     A, W = make_custom(M, K, N, dtype=wdt, seed=11)
     Anp, Wnp = oracle_inputs(A, W)
     q = 0.98
@@ -286,7 +287,7 @@ def test_gemm_with_compensation(M, N, K, wdt, wide):
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     args = (t(ref["Aq"]), t(ref["sA"]), t(ref["Wq"]), t(ref["sW"]), K)
     kw = dict(row_ptr=t(ref["row_ptr"]), coo_col=t(ref["coo_col"]), coo_val=t(ref["coo_val"]), W=W.to(DEV),
-              capacity=0 if wide else 65 * M)
+              capacity={"chunk512": 0, "chunk256": 65 * M}[shape])
     Y32 = fp4.gemm(*args, **kw, out_dtype=torch.float32)
     Y16 = fp4.gemm(*args, **kw, out_dtype=torch.bfloat16)
     assert_y_close(to_np(Y32), ref["Y"], ref["denom"])
@@ -366,6 +367,23 @@ def test_gemm_q16_handover_wide():
     assert np.array_equal(g, oracle.accumulate_pairs(Aq, Wq, K, ms, ns))
     n_esc = _check_q16(Yq, esc, acc, sA, sW, block=(256, 256))
     assert n_esc > 0
+
+
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("fp32", "fp32")])
+def test_forward_rows_of_every_length(dtype, out):
+    """A high clamp quantile with rows of 0, 1-8, 9-16 and up to 64+ entries (one, two and
+    several groups of eight W segments, and more than 64 entries: two windows of (k, delta)
+    pairs), including the first and last rows."""
+    _say(f"forward row lengths {dtype} out={out}")
+    M, K, N = 300, 1024, 776
+    A, W = make_custom(M, K, N, dtype=dtype, seed=31, outlier_frac=0.0)
+    rng = np.random.default_rng(5)
+    for r, n in ((0, 40), (3, 17), (50, 12), (51, 9), (100, 70), (200, 3), (M - 1, 30)):
+        cols = rng.choice(K, n, replace=False)
+        A[r, cols] = torch.from_numpy((rng.choice([-1.0, 1.0], n) * rng.uniform(60, 90, n)).astype(np.float32)).to(A.dtype)
+    q = 0.999  # about 300 entries: the 175 planted ones and the largest normal values
+    assert fp4.outlier_capacity(M, K, q) <= 8 * M
+    _check_forward_small(A, W, q, _dt(out))
 
 
 @pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "fp32"), ("fp32", "fp32")])
