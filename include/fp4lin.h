@@ -76,10 +76,10 @@ enum {
 };
 enum { FP4_F32 = 0, FP4_BF16 = 1 };          /* element types of A, W, X, Y */
 /* Output type of fp4_gemm only (no compensation term): the exact accumulator in two bytes.
- * Element (m, n) is the int16 4*acc (acc is a multiple of 1/4), except in the 256 x 128
- * output blocks that hold some |acc| > 8191.75: there every element is -32768 and the
- * workspace holds fl(fl(acc*sA)*sW) as fp32 at element (m, n) (those blocks are recomputed
- * by a second launch).  This is how the GEMM hands its result to the compensation pass
+ * Element (m, n) is the int16 4*acc (acc is a multiple of 1/4), except in the output tiles
+ * (256 x 128 or 256 x 256, as the library tiles the shape) that hold some |acc| > 8191.75:
+ * there every element is -32768 and the workspace holds fl(fl(acc*sA)*sW) as fp32 at
+ * element (m, n) (those tiles are recomputed by a second launch).  This is how the GEMM hands its result to the compensation pass
  * inside fp4_gemm and fp4_linear_forward. */
 enum { FP4_Q16 = 2 };
 enum { FP4_PER_ROW = 0, FP4_PER_COL = 1 };   /* token-wise (A) / channel-wise (W) */
