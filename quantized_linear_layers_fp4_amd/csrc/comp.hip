@@ -14,9 +14,10 @@
 // lane, and walks them in groups of eight W row segments loaded together.  Tasks are dealt
 // out to the eight XCDs in contiguous ranges (consecutive workgroup ids go to different
 // XCDs), chunk-major within a range, so each XCD streams all rows over one chunk at a time
-// and the W rows that chunk gathers stay in its L2.  CC = 8 (512-column chunks) up to 64
-// entries per row on average, CC = 4 (256-column chunks, half the W strip per chunk) beyond,
-// where the gathers bound it.
+// and the W rows that chunk gathers stay in its L2.  Up to 64 entries per row on average
+// (the list's capacity over M) the tasks are (row, 512-column chunk); beyond that the gathers
+// bound the pass and the tasks are (8 rows, 64-column chunk) blocks (k_comp_block64), whose
+// W strip fits in L2.
 // The accumulators and Y are streamed with non-temporal hints so they do not evict W.
 #include "fp4_common.h"
 #include "fp4_launch.h"
@@ -184,6 +185,107 @@ __global__ __launch_bounds__(256) void k_comp_apply(CompArgs a, int chunks, int 
     comp_task<YDT, WDT, CC>(a, row, chunk, lane);
 }
 
+// Many entries per row: one wave per (block of 8 rows, chunk of 64 columns) task, lane
+// 8r + g on row r of the block and columns 8g .. 8g+7 of the chunk.  The waves an XCD runs
+// at once then gather from a W strip 64 columns wide (K x 128 bytes of bf16, 1.8 MB for
+// K = 13824), which stays in its 4 MB L2, while every load instruction still moves 16 bytes
+// per lane.  Each row's entries go in groups of eight: lane 8r + g loads the row's entry g
+// of the group, the group's k reach the row's lanes by lane permutes, and the next group's
+// entries are requested with the current group's W segments.  Every load of the entry loop
+// is issued unconditionally (absent ones at an offset past their buffer: zeros, no access),
+// so the compiler can count what is in flight.
+template <int YDT, int WDT>
+__global__ __launch_bounds__(256) void k_comp_block64(CompArgs a, int nrb, int per_xcd) {
+    constexpr int CC = 8;
+    const int lane = threadIdx.x & 63;
+    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    const int64_t task = (int64_t)logical * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int M = a.M, N = a.N;
+    const int chunks = (N + 63) / 64;
+    if (task >= (int64_t)chunks * nrb) return;  // whole wave
+    const int chunk = (int)(task / nrb);
+    const int r0 = (int)(task - (int64_t)chunk * nrb) * 8;
+    const int r = lane >> 3, g = lane & 7;
+    const int row = r0 + r;
+    const int col = chunk * 64 + g * CC;
+    const bool active = row < M && col < N;  // N % 8 == 0: a lane's columns are in range together
+    const int rowc = min(row, M - 1);
+
+    const int32_t rp = a.row_ptr[min(r0 + (lane & 15), M)];
+    const int32_t e0 = __shfl(rp, r), e1 = row < M ? __shfl(rp, r + 1) : e0;
+    const int32_t n = e1 - e0;
+    int32_t nmax = n;
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) nmax = max(nmax, __shfl_xor(nmax, o));
+
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.sW), 0, N * 4, 0x00020000);
+    const v4i qv = active ? *reinterpret_cast<const v4i *>(a.Yq + (size_t)rowc * N + col) : v4i{0, 0, 0, 0};
+    v4i swv[2];
+    swv[0] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4, 0, 0);
+    swv[1] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16, 0, 0);
+    const float sa = a.sA[rowc];
+    float y[CC];
+    decode_ymain<CC>(qv, swv, sa, active, a.esc + (size_t)rowc * N, col, y);
+
+    constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t rsW =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.W), 0, (int)((int64_t)a.K * N * ESZ), 0x00020000);
+    // the lists through descriptors without a bound of their own (the row offsets bound every
+    // real access, as in the chunk tasks); an absent entry's offset is 2^31, past the range
+    const __amdgpu_buffer_rsrc_t rsK =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(a.coo_col), 0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsD =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.coo_val), 0, 0x7FFFFFFF, 0x00020000);
+    const uint32_t row_bytes = (uint32_t)N * ESZ;
+    const uint32_t lane_off = (uint32_t)col * ESZ;
+    // entry g of the group starting at e (past the row: an offset past the lists)
+    auto load_ent = [&](int e, int32_t &kk, int32_t &dd) {
+        const uint32_t off = e + g < n ? (uint32_t)(e0 + e + g) * 4u : 0x80000000u;  // nnz*4 < 2^31
+        kk = __builtin_amdgcn_raw_buffer_load_b32(rsK, (int)off, 0, 0);
+        dd = __builtin_amdgcn_raw_buffer_load_b32(rsD, (int)off, 0, 0);
+    };
+    int32_t kk, dd;
+    load_ent(0, kk, dd);
+    for (int e = 0; e < nmax; e += 8) {
+        v4i w[8][2];
+        float d[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t k = (uint32_t)__shfl(kk, (lane & ~7) + u);
+            d[u] = __int_as_float(__shfl(dd, (lane & ~7) + u));
+            const uint32_t off = (e + u < n && active) ? k * row_bytes + lane_off : 0x80000000u;  // K*N*ESZ < 2^31
+            load_seg<WDT, CC>(rsW, off, true, w[u]);
+        }
+        load_ent(e + 8, kk, dd);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (e + u < n) {  // per row; ascending k
+#pragma unroll
+                for (int c = 0; c < CC; ++c) y[c] = __builtin_fmaf(d[u], seg_elem<WDT>(w[u], c), y[c]);
+            }
+        }
+    }
+    if (active) store_y<YDT, CC>(a.Y, (size_t)row * N + col, y);
+}
+
+static hipError_t launch_comp_block64(const CompArgs &a, int y_dt, int w_dt, hipStream_t s) {
+    const int nrb = (a.M + 7) / 8;
+    const int chunks = (a.N + 63) / 64;
+    const int64_t blocks = ((int64_t)nrb * chunks + 3) / 4;
+    const int per_xcd = (int)((blocks + 7) / 8);
+    const dim3 grid((unsigned)per_xcd * 8u), block(256);
+#define C(YD, WD) hipLaunchKernelGGL((k_comp_block64<YD, WD>), grid, block, 0, s, a, nrb, per_xcd)
+    if (y_dt == DT_BF16) {
+        if (w_dt == DT_BF16) C(DT_BF16, DT_BF16);
+        else C(DT_BF16, DT_F32);
+    } else {
+        if (w_dt == DT_BF16) C(DT_F32, DT_BF16);
+        else C(DT_F32, DT_F32);
+    }
+#undef C
+    return hipGetLastError();
+}
+
 template <int CC>
 static hipError_t launch_comp_tasks(const CompArgs &a, int y_dt, int w_dt, hipStream_t s) {
     const int chunks = (int)((a.N + 64 * CC - 1) / (64 * CC));
@@ -209,7 +311,7 @@ hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, con
     const CompArgs a{Yq, esc, sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
     // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
     // gathers and the narrower chunks keep more of each W strip in L2
-    if (capacity > 64 * M) return launch_comp_tasks<4>(a, y_dt, w_dt, s);
+    if (capacity > 64 * M) return launch_comp_block64(a, y_dt, w_dt, s);
     return launch_comp_tasks<8>(a, y_dt, w_dt, s);
 }
 

@@ -272,14 +272,14 @@ def test_gemm_accumulator_extremes():
     assert to_np(acc)[0, 1] == 36.0 * K and to_np(acc)[1, 1] == -36.0 * K
 
 
-@pytest.mark.parametrize("shape", ["chunk512", "chunk256"])
+@pytest.mark.parametrize("shape", ["chunk512", "block64"])
 @pytest.mark.parametrize("M,N,K,wdt", [(300, 264, 512, "bf16"), (513, 520, 1056, "fp32"), (64, 8, 96, "bf16"),
                                        (70, 776, 128, "fp32")])
 def test_gemm_with_compensation(M, N, K, wdt, shape):
     """Both shapes of the compensation kernel (the capacity hint picks one: more than 64
-    entries per row selects the 256-column chunks)."""
+    entries per row selects the 8-row x 64-column blocks)."""
     _say(f"gemm comp {M}x{N}x{K} {wdt} {shape}")
-    wide = shape != "chunk256"
+    wide = shape != "block64"
     A, W = make_custom(M, K, N, dtype=wdt, seed=11)
     Anp, Wnp = oracle_inputs(A, W)
     q = 0.98
@@ -287,7 +287,7 @@ def test_gemm_with_compensation(M, N, K, wdt, shape):
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     args = (t(ref["Aq"]), t(ref["sA"]), t(ref["Wq"]), t(ref["sW"]), K)
     kw = dict(row_ptr=t(ref["row_ptr"]), coo_col=t(ref["coo_col"]), coo_val=t(ref["coo_val"]), W=W.to(DEV),
-              capacity={"chunk512": 0, "chunk256": 65 * M}[shape])
+              capacity={"chunk512": 0, "block64": 65 * M}[shape])
     Y32 = fp4.gemm(*args, **kw, out_dtype=torch.float32)
     Y16 = fp4.gemm(*args, **kw, out_dtype=torch.bfloat16)
     assert_y_close(to_np(Y32), ref["Y"], ref["denom"])
@@ -471,7 +471,7 @@ def test_forward_is_deterministic():
 @pytest.mark.parametrize("dtype,M,K,N,q,out", [
     ("bf16", 300, 512, 264, 0.99, torch.bfloat16),
     ("fp32", 130, 256, 72, 0.95, torch.float32),
-    ("bf16", 1024, 2048, 1032, 0.9, torch.float32),   # many entries per row: separate 256-column pass
+    ("bf16", 1024, 2048, 1032, 0.9, torch.float32),   # many entries per row: the 8-row x 64-column blocks
 ])
 def test_forward_with_cached_weights(dtype, M, K, N, q, out):
     """W quantized once (fp4_quantize per column) and reused: the forward on those codes is
