@@ -16,8 +16,10 @@
 // first stage.
 //
 // Epilogue: Y = fl(fl(acc * sA) * sW); each wave reorders its result tiles through a
-// private patch of LDS so that the stores are 16 bytes per lane along rows.  The sparse compensation
-// dA . W is a separate kernel (comp.hip) that runs on the fp32 result.
+// private patch of LDS so that the stores are 16 bytes per lane along rows.  In front of the
+// sparse compensation dA . W (a separate kernel, comp.hip) the output is instead the exact
+// accumulator as the int16 4*acc (DT_Q16), with a second, flagged launch (FB) that recomputes
+// in fp32 the tiles where it does not fit; the compensation pass rebuilds Y_main from it.
 //
 // Large products (K a multiple of 512 and at least four 256 x 256 tiles per CU) run on a
 // second, persistent kernel with 256 x 256 tiles (see "wide tiles" below); both compute the
@@ -170,8 +172,10 @@ __device__ __forceinline__ void lds_barrier() {
 // row0.., columns col0.. and col0+32..): the low 16 bits of fl(4*acc + 1.5*2^23), which are
 // 4*acc as int16 whenever |acc| <= Q16_MAX_ACC, go into a private 32 x 64 patch of LDS, are
 // read back row-major and stored 16 bytes per lane, so each row segment is 128 bytes.
-// esc: set when some lane of the wave holds |acc| > Q16_MAX_ACC in these tiles.  Read-back chunk c = 64k + lane holds
-// row c/8 = 8k + lane/8, columns 8(c%8)..; loff0: its row-major offset (elements) for k = 0.
+// esc: set when some lane of the wave holds |acc| > Q16_MAX_ACC in these tiles (one ballot
+// per pair: a running maximum over the whole tile pushed the wide kernel into spills).
+// Read-back chunk c = 64k + lane holds row c/8 = 8k + lane/8, columns 8(c%8)..; loff0: its
+// row-major offset (elements) for k = 0.
 // The patch is private to the wave and a wave's LDS accesses execute in order, so the
 // read-back sees the writes and the next call's writes cannot overtake it.
 __device__ __forceinline__ void epi_q16_pair(const v16f &x0, const v16f &x1, bool &esc, int16_t *P, int lane,
