@@ -310,7 +310,7 @@ hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, con
                        const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s) {
     const CompArgs a{Yq, esc, sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
     // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
-    // gathers and the narrower chunks keep more of each W strip in L2
+    // gathers, and the 8-row x 64-column blocks keep each XCD's W strip in its L2
     if (capacity > 64 * M) return launch_comp_block64(a, y_dt, w_dt, s);
     return launch_comp_tasks<8>(a, y_dt, w_dt, s);
 }
