@@ -624,6 +624,55 @@ def test_forward_full_size(cfg, li):
     _say(f"  sampled acc bit-exact, Y max rel err {err:.3e}")
 
 
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_forward_escapes_wide(out):
+    """The forward on the persistent 256 x 256 GEMM (8192 x 512 x 8192: 1024 tiles) with
+    accumulators past the two-byte range (rows of A and channels of W quantizing to +-6
+    everywhere: acc = +-36 K): its escape pass recomputes those tiles in fp32 and the
+    compensation pass takes them from there (the workspace for a bf16 Y, Y for an fp32 Y).
+    Intermediates in full; the accumulator and Y at sampled outputs, all of them in the
+    escaped tiles' rows."""
+    M, K, N = 8192, 512, 8192
+    _say(f"forward escapes wide {M}x{K}x{N} out={out}")
+    A, W = make_custom(M, K, N, dtype="bf16", seed=41)
+    rows, cols = (0, 4000, M - 1), (5, 4100, N - 1)
+    for r in rows:
+        A[r] = 1.0
+    for c in cols:
+        W[:, c] = 0.02 if c != 4100 else -0.02
+    q = 0.99
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    ws = fp4.workspace(Ad, N, q)
+    Y = fp4.linear_forward(Ad, Wd, q, out_dtype=_dt(out), ws=ws)
+    inter = fp4.forward_intermediates(ws, M, K, N, A.dtype, q)
+    Anp, Wnp = oracle_inputs(A, W)
+    T = oracle.abs_quantile(Anp, q)
+    assert float(inter["T"].item()) == T
+    cl = oracle.clamp_coo(Anp, T, want_clamped=True, cap=oracle.capacity(M, K, q))
+    nnz = cl["nnz"]
+    assert int(inter["nnz"].item()) == nnz
+    assert np.array_equal(to_np(inter["row_ptr"]), cl["row_ptr"])
+    assert np.array_equal(to_np(inter["coo_col"][:nnz]), cl["coo_col"])
+    assert np.array_equal(to_np(inter["coo_val"][:nnz]), cl["coo_val"])
+    Aq, sA = oracle.quant_rows(cl.pop("A_clamped"))
+    Wq, sW = oracle.quant_cols(Wnp)
+    assert np.array_equal(to_np(inter["Aq"]), Aq) and np.array_equal(to_np(inter["sA"]), sA)
+    assert np.array_equal(to_np(inter["Wq"]), Wq) and np.array_equal(to_np(inter["sW"]), sW)
+    rng = np.random.default_rng(43)
+    ms, ns = _sample_pairs(rng, M, N, cl["row_ptr"])
+    ms = np.concatenate([ms, np.repeat(rows, 600), np.repeat(rows, len(cols))])
+    ns = np.concatenate([ns, rng.integers(0, N, 600 * len(rows)), np.tile(cols, len(rows))])
+    r_acc = oracle.accumulate_pairs(Aq, Wq, K, ms, ns)
+    assert np.abs(r_acc).max() > 8191.75  # the sample holds escaped accumulators
+    r_y, denom = oracle.output_pairs(r_acc, sA, sW, ms, ns, cl["row_ptr"], cl["coo_col"], cl["coo_val"], Wnp)
+    g_y = to_np(Y.view(-1)[torch.from_numpy(ms * N + ns).to(DEV)])
+    if out == "fp32":
+        err = assert_y_close(g_y, r_y, denom)
+        _say(f"  Y max rel err {err:.3e}")
+    else:
+        assert_bf16_close(g_y, r_y, denom)
+
+
 # ----------------------------------------------------------------------------- backward
 def _fwd_codes_gpu(Ad, Wd, q):
     M, K = Ad.shape
