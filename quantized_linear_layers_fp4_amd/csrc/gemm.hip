@@ -142,7 +142,9 @@ __device__ __forceinline__ void mfma_block8(v16f (&acc)[4][2], const u32x4 (&a)[
     }
 }
 
-template <int NJ>
+// SW: the operands swapped, so tile (i, j) holds the transpose (lane l: row l%32 of the
+// product, columns 8(r/4) + 4(l/32) + r%4 in register r: four consecutive columns per quad).
+template <int NJ, bool SW = false>
 __device__ __forceinline__ void mfma_block(v16f (&acc)[4][NJ], const u32x4 (&a)[4], const u32x4 (&b)[NJ]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -150,8 +152,12 @@ __device__ __forceinline__ void mfma_block(v16f (&acc)[4][NJ], const u32x4 (&a)[
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const v8i bv = v8i{(int)b[j].x, (int)b[j].y, (int)b[j].z, (int)b[j].w, 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 0, UNIT_SCALE, 0,
-                                                                        UNIT_SCALE);
+            if constexpr (SW)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 4, 4, 0, UNIT_SCALE, 0,
+                                                                            UNIT_SCALE);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 0, UNIT_SCALE, 0,
+                                                                            UNIT_SCALE);
         }
     }
 }
@@ -222,6 +228,55 @@ __device__ __forceinline__ void q16_fill_esc(int16_t *Yq, int lane, int rbase, i
         const int c = k * 64 + lane, grow = rbase + c / CPR, gcol = cbase + (c % CPR) * 8;
         if (full || (grow < M && gcol < N))
             __builtin_nontemporal_store(v4i{pat, pat, pat, pat}, reinterpret_cast<v4i *>(Yq + (size_t)grow * N + gcol));
+    }
+}
+
+// The DT_Q16 epilogue for tiles computed with swapped MFMA operands (mfma_block<.., true>):
+// lane l holds row l%32 and, per quad a, the four consecutive columns 8a + 4(l/32) ...  Each
+// quad goes to the patch as one 8-byte write (two int16 per dword), rows 68 int16 apart so
+// the 32 rows' writes fall on distinct banks; the read-back takes each 16-byte row chunk as
+// two 8-byte reads.  Otherwise as epi_q16_pair.
+__device__ __forceinline__ void epi_q16_pair_t(const v16f &x0, const v16f &x1, bool &esc, int16_t *P, int lane,
+                                               int row0, int col0, int M, int N, bool full, int16_t *Yq,
+                                               uint32_t loff0) {
+    constexpr int PS = 68;  // patch row stride, int16
+    const int lr = lane & 31, h = lane >> 5;
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const v16f &x = t ? x1 : x0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            uint32_t q[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[e] = __float_as_uint(__builtin_fmaf(x[4 * a + e], 4.0f, Q16_MAGIC));
+            const uint32_t w0 = (q[0] & 0xFFFFu) | (q[1] << 16), w1 = (q[2] & 0xFFFFu) | (q[3] << 16);
+            *reinterpret_cast<uint2 *>(&P[lr * PS + 32 * t + 8 * a + 4 * h]) = make_uint2(w0, w1);
+            asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a]), "v"(x[4 * a + 1]), "v"(m));
+            asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a + 2]), "v"(x[4 * a + 3]), "v"(m));
+        }
+    }
+    esc |= __builtin_amdgcn_ballot_w64(m > Q16_MAX_ACC) != 0;  // wave-uniform
+    v4i e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = k * 64 + lane;
+        const uint2 u0 = *reinterpret_cast<const uint2 *>(&P[(c >> 3) * PS + (c & 7) * 8]);
+        const uint2 u1 = *reinterpret_cast<const uint2 *>(&P[(c >> 3) * PS + (c & 7) * 8 + 4]);
+        e[k] = v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
+    }
+    if (full) {
+        int16_t *base = Yq + (size_t)row0 * N + col0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(base + loff0 + (uint32_t)(8 * k) * (uint32_t)N));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = k * 64 + lane, grow = row0 + (c >> 3), gcol = col0 + (c & 7) * 8;
+            if (grow < M && gcol < N)
+                __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(Yq + (size_t)grow * N + gcol));
+        }
     }
 }
 
@@ -491,7 +546,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sb1[WSTB];
     __shared__ __attribute__((aligned(16))) uint8_t sb2[WSTB];
     __shared__ __attribute__((aligned(16))) uint8_t sb3[WSTB];
-    __shared__ __attribute__((aligned(16))) float patch[NW][1024];
+    __shared__ __attribute__((aligned(16))) float patch[NW][1088];  // 32 x 68 int16 for the transposed pair
     __shared__ __attribute__((aligned(16))) WBook bk[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -572,7 +627,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                     bool load_next) {
         __builtin_amdgcn_sched_barrier(0);
         frag_load(cur, wm, wn, lane, 1, a1, b1);
-        mfma_block(acc, a0, b0);
+        mfma_block<4, YDT == DT_Q16>(acc, a0, b0);
         INTERLEAVE16();
         __builtin_amdgcn_sched_barrier(0);
         WAIT_VMCNT(16);
@@ -582,7 +637,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
         stage_dma<true, 4>(rsA, rsB, cur, wave, oa, ob, dma_stage, KB, lane_chunk16);
         if (load_next) {
             frag_load(nxt, wm, wn, lane, 0, a0, b0);
-            mfma_block(acc, a1, b1);
+            mfma_block<4, YDT == DT_Q16>(acc, a1, b1);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -591,7 +646,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load to LDS
             }
         } else {
-            mfma_block(acc, a1, b1);
+            mfma_block<4, YDT == DT_Q16>(acc, a1, b1);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -675,17 +730,17 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
                     __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (ACCOUT) {
+                    if constexpr (ACCOUT) {  // the swapped layout: row lane%32, columns 8(r/4) + 4(lane/32) + r%4
 #pragma unroll
                         for (int j = 2 * jp; j < 2 * jp + 2; ++j)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
-                                const int grow = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                                const int gcol = n0 + wn * 128 + j * 32 + (lane & 31);
+                                const int grow = row0 + (lane & 31);
+                                const int gcol = n0 + wn * 128 + j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                                 if (full || (grow < M && gcol < N)) p.acc_out[(size_t)grow * N + gcol] = acc[i][j][r];
                             }
                     }
-                    epi_q16_pair(acc[i][2 * jp], acc[i][2 * jp + 1], qesc, reinterpret_cast<int16_t *>(E), lane, row0,
+                    epi_q16_pair_t(acc[i][2 * jp], acc[i][2 * jp + 1], qesc, reinterpret_cast<int16_t *>(E), lane, row0,
                                  n0 + wn * 128 + 64 * jp, M, N, full, static_cast<int16_t *>(p.Y), loff[0]);
                 }
                 continue;
