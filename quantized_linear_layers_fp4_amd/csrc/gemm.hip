@@ -231,15 +231,20 @@ __device__ __forceinline__ void q16_fill_esc(int16_t *Yq, int lane, int rbase, i
     }
 }
 
-// The DT_Q16 epilogue for tiles computed with swapped MFMA operands (mfma_block<.., true>):
-// lane l holds row l%32 and, per quad a, the four consecutive columns 8a + 4(l/32) ...  Each
-// quad goes to the patch as one 8-byte write (two int16 per dword), rows 68 int16 apart so
-// the 32 rows' writes fall on distinct banks; the read-back takes each 16-byte row chunk as
-// two 8-byte reads.  Otherwise as epi_q16_pair.
-__device__ __forceinline__ void epi_q16_pair_t(const v16f &x0, const v16f &x1, bool &esc, int16_t *P, int lane,
-                                               int row0, int col0, int M, int N, bool full, int16_t *Yq,
-                                               uint32_t loff0) {
-    constexpr int PS = 68;  // patch row stride, int16
+// The epilogue of two side-by-side tiles computed with swapped MFMA operands
+// (mfma_block<.., true>): lane l holds row l%32 and, per quad a, the four consecutive columns
+// 8a + 4(l/32) ...  DT_Q16: the two-byte accumulator as in epi_q16_pair; DT_BF16: the
+// bf16 (nearest-even) of fl(fl(acc * sA) * sW), sAw: the lane's row scale, sWp: the pair's 64
+// column scales (LDS).  Each quad goes to the patch as one 8-byte write (two 16-bit values
+// per dword), rows 68 values apart so the 32 rows' writes fall on distinct banks; the
+// read-back takes each 16-byte row chunk as two 8-byte reads and stores it, so each row
+// segment is 128 bytes.  The patch is private to the wave and a wave's LDS accesses execute
+// in order, so the read-back sees the writes and the next call's writes cannot overtake it.
+template <int YDT>
+__device__ __forceinline__ void epi_pair_t(const v16f &x0, const v16f &x1, bool &esc, float sa, const float *sWp,
+                                           uint16_t *P, int lane, int row0, int col0, int M, int N, bool full,
+                                           uint16_t *Yo, uint32_t loff0) {
+    constexpr int PS = 68;  // patch row stride, 16-bit values
     const int lr = lane & 31, h = lane >> 5;
     float m = 0.0f;
 #pragma unroll
@@ -248,15 +253,23 @@ __device__ __forceinline__ void epi_q16_pair_t(const v16f &x0, const v16f &x1, b
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             uint32_t q[4];
+            if constexpr (YDT == DT_Q16) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) q[e] = __float_as_uint(__builtin_fmaf(x[4 * a + e], 4.0f, Q16_MAGIC));
+                for (int e = 0; e < 4; ++e) q[e] = __float_as_uint(__builtin_fmaf(x[4 * a + e], 4.0f, Q16_MAGIC));
+                asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a]), "v"(x[4 * a + 1]), "v"(m));
+                asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a + 2]), "v"(x[4 * a + 3]), "v"(m));
+            } else {
+                const float4 sw = *reinterpret_cast<const float4 *>(&sWp[32 * t + 8 * a + 4 * h]);
+                q[0] = f32_to_bf16_bits((x[4 * a] * sa) * sw.x);
+                q[1] = f32_to_bf16_bits((x[4 * a + 1] * sa) * sw.y);
+                q[2] = f32_to_bf16_bits((x[4 * a + 2] * sa) * sw.z);
+                q[3] = f32_to_bf16_bits((x[4 * a + 3] * sa) * sw.w);
+            }
             const uint32_t w0 = (q[0] & 0xFFFFu) | (q[1] << 16), w1 = (q[2] & 0xFFFFu) | (q[3] << 16);
             *reinterpret_cast<uint2 *>(&P[lr * PS + 32 * t + 8 * a + 4 * h]) = make_uint2(w0, w1);
-            asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a]), "v"(x[4 * a + 1]), "v"(m));
-            asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a + 2]), "v"(x[4 * a + 3]), "v"(m));
         }
     }
-    esc |= __builtin_amdgcn_ballot_w64(m > Q16_MAX_ACC) != 0;  // wave-uniform
+    if constexpr (YDT == DT_Q16) esc |= __builtin_amdgcn_ballot_w64(m > Q16_MAX_ACC) != 0;  // wave-uniform
     v4i e[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -266,7 +279,7 @@ __device__ __forceinline__ void epi_q16_pair_t(const v16f &x0, const v16f &x1, b
         e[k] = v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
     }
     if (full) {
-        int16_t *base = Yq + (size_t)row0 * N + col0;
+        uint16_t *base = Yo + (size_t)row0 * N + col0;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(base + loff0 + (uint32_t)(8 * k) * (uint32_t)N));
@@ -275,7 +288,7 @@ __device__ __forceinline__ void epi_q16_pair_t(const v16f &x0, const v16f &x1, b
         for (int k = 0; k < 4; ++k) {
             const int c = k * 64 + lane, grow = row0 + (c >> 3), gcol = col0 + (c & 7) * 8;
             if (grow < M && gcol < N)
-                __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(Yq + (size_t)grow * N + gcol));
+                __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(Yo + (size_t)grow * N + gcol));
         }
     }
 }
@@ -627,7 +640,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                     bool load_next) {
         __builtin_amdgcn_sched_barrier(0);
         frag_load(cur, wm, wn, lane, 1, a1, b1);
-        mfma_block<4, YDT == DT_Q16>(acc, a0, b0);
+        mfma_block<4, YDT != DT_F32>(acc, a0, b0);
         INTERLEAVE16();
         __builtin_amdgcn_sched_barrier(0);
         WAIT_VMCNT(16);
@@ -637,7 +650,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
         stage_dma<true, 4>(rsA, rsB, cur, wave, oa, ob, dma_stage, KB, lane_chunk16);
         if (load_next) {
             frag_load(nxt, wm, wn, lane, 0, a0, b0);
-            mfma_block<4, YDT == DT_Q16>(acc, a1, b1);
+            mfma_block<4, YDT != DT_F32>(acc, a1, b1);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -646,7 +659,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load to LDS
             }
         } else {
-            mfma_block<4, YDT == DT_Q16>(acc, a1, b1);
+            mfma_block<4, YDT != DT_F32>(acc, a1, b1);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -703,14 +716,14 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
         const bool full = (m0 + BM <= M) && (n0 + WBN <= N);
         // Row-major read-back of a 32 x 32 patch, the same lanes for every tile: chunk
         // c = 64k + lane holds row c/8, columns 4(c%8).. (fp32) or row c/4, columns 8(c%4).. (bf16).
-        constexpr int NK = YDT == DT_F32 ? 4 : (YDT == DT_BF16 ? 2 : 1);
+        constexpr int NK = YDT == DT_F32 ? 4 : 1;
         int lrow[NK], lcol[NK];
         uint32_t loff[NK];
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
             const int c = k * 64 + lane;
-            lrow[k] = YDT == DT_BF16 ? c >> 2 : c >> 3;
-            lcol[k] = YDT == DT_BF16 ? (c & 3) * 8 : (c & 7) * (YDT == DT_Q16 ? 8 : 4);
+            lrow[k] = c >> 3;
+            lcol[k] = (c & 7) * (YDT == DT_F32 ? 4 : 8);
             loff[k] = (uint32_t)lrow[k] * (uint32_t)N + (uint32_t)lcol[k];
         }
         bool qesc = false;  // DT_Q16: some |acc| of the wave's block is past the int16 range
@@ -726,7 +739,8 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                 sa[4 * r4 + 3] = v.w;
             }
             const int row0 = m0 + wm * 128 + i * 32;
-            if constexpr (YDT == DT_Q16) {
+            if constexpr (YDT != DT_F32) {  // the transposed product: pairs of tiles
+                const float sar = b.sA[wm * 128 + i * 32 + (lane & 31)];
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -740,8 +754,9 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                                 if (full || (grow < M && gcol < N)) p.acc_out[(size_t)grow * N + gcol] = acc[i][j][r];
                             }
                     }
-                    epi_q16_pair_t(acc[i][2 * jp], acc[i][2 * jp + 1], qesc, reinterpret_cast<int16_t *>(E), lane, row0,
-                                 n0 + wn * 128 + 64 * jp, M, N, full, static_cast<int16_t *>(p.Y), loff[0]);
+                    epi_pair_t<YDT>(acc[i][2 * jp], acc[i][2 * jp + 1], qesc, sar, &b.sW[wn * 128 + 64 * jp],
+                                    reinterpret_cast<uint16_t *>(E), lane, row0, n0 + wn * 128 + 64 * jp, M, N, full,
+                                    static_cast<uint16_t *>(p.Y), loff[0]);
                 }
                 continue;
             }

@@ -199,9 +199,11 @@ def test_gemm_accumulator_exact(M, N, K):
 
 
 # More output tiles than the chip has CUs, ragged in both dimensions, K a multiple of 512: the
-# product then walks several tiles per workgroup.  Checked at sampled outputs plus whole
+# product then walks several tiles per workgroup (the last two shapes have over 1024 tiles of
+# 256 x 256, so they run on the persistent kernel).  Checked at sampled outputs plus whole
 # edge rows and columns.
-@pytest.mark.parametrize("M,N,K,out", [(4200, 4136, 1024, "fp32"), (4352, 4360, 512, "bf16"), (1030, 9000, 2048, "fp32")])
+@pytest.mark.parametrize("M,N,K,out", [(4200, 4136, 1024, "fp32"), (4352, 4360, 512, "bf16"), (1030, 9000, 2048, "fp32"),
+                                       (8192, 8200, 512, "bf16"), (8200, 8192, 1024, "fp32")])
 def test_gemm_many_tiles(M, N, K, out):
     _say(f"gemm many tiles {M}x{N}x{K} -> {out}")
     rng = np.random.default_rng(M + N + K)
