@@ -174,47 +174,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// DT_Q16 epilogue of two side-by-side 32 x 32 result tiles x0, x1 (MFMA layout; rows
-// row0.., columns col0.. and col0+32..): the low 16 bits of fl(4*acc + 1.5*2^23), which are
-// 4*acc as int16 whenever |acc| <= Q16_MAX_ACC, go into a private 32 x 64 patch of LDS, are
-// read back row-major and stored 16 bytes per lane, so each row segment is 128 bytes.
-// esc: set when some lane of the wave holds |acc| > Q16_MAX_ACC in these tiles (one ballot
-// per pair: a running maximum over the whole tile pushed the wide kernel into spills).
-// Read-back chunk c = 64k + lane holds row c/8 = 8k + lane/8, columns 8(c%8)..; loff0: its
-// row-major offset (elements) for k = 0.
-// The patch is private to the wave and a wave's LDS accesses execute in order, so the
-// read-back sees the writes and the next call's writes cannot overtake it.
-__device__ __forceinline__ void epi_q16_pair(const v16f &x0, const v16f &x1, bool &esc, int16_t *P, int lane,
-                                             int row0, int col0, int M, int N, bool full, int16_t *Yq,
-                                             uint32_t loff0) {
-    float m = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        P[lr * 64 + (lane & 31)] = (int16_t)__float_as_uint(__builtin_fmaf(x0[r], 4.0f, Q16_MAGIC));
-        P[lr * 64 + 32 + (lane & 31)] = (int16_t)__float_as_uint(__builtin_fmaf(x1[r], 4.0f, Q16_MAGIC));
-        // one v_max3 per two accumulators (the compiler's own max chain took three times as many)
-        asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x0[r]), "v"(x1[r]), "v"(m));
-    }
-    esc |= __builtin_amdgcn_ballot_w64(m > Q16_MAX_ACC) != 0;  // wave-uniform
-    v4i e[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) e[k] = *reinterpret_cast<const v4i *>(&P[8 * (k * 64 + lane)]);
-    if (full) {
-        int16_t *base = Yq + (size_t)row0 * N + col0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(base + loff0 + (uint32_t)(8 * k) * (uint32_t)N));
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int c = k * 64 + lane, grow = row0 + (c >> 3), gcol = col0 + (c & 7) * 8;
-            if (grow < M && gcol < N)
-                __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(Yq + (size_t)grow * N + gcol));
-        }
-    }
-}
-
 // The escape pass of a DT_Q16 product (FB kernels): after a tile's fp32 epilogue has
 // written fl(fl(acc*sA)*sW) to the escape buffer, every int16 element of the wave's
 // 128 x 32*NJ result block (rows rbase.., columns cbase..) becomes Q16_ESC, 16 bytes per
@@ -231,11 +190,16 @@ __device__ __forceinline__ void q16_fill_esc(int16_t *Yq, int lane, int rbase, i
     }
 }
 
-// The epilogue of two side-by-side tiles computed with swapped MFMA operands
-// (mfma_block<.., true>): lane l holds row l%32 and, per quad a, the four consecutive columns
-// 8a + 4(l/32) ...  DT_Q16: the two-byte accumulator as in epi_q16_pair; DT_BF16: the
-// bf16 (nearest-even) of fl(fl(acc * sA) * sW), sAw: the lane's row scale, sWp: the pair's 64
-// column scales (LDS).  Each quad goes to the patch as one 8-byte write (two 16-bit values
+// The epilogue of two side-by-side 32 x 32 tiles (rows row0.., columns col0.. and col0+32..)
+// computed with swapped MFMA operands (mfma_block<.., true>): lane l holds row l%32 and, per
+// quad a, the four consecutive columns 8a + 4(l/32) ...
+// DT_Q16: the low 16 bits of fl(4*acc + 1.5*2^23), which are 4*acc as int16 whenever
+// |acc| <= Q16_MAX_ACC; esc is set when some lane of the wave holds a larger |acc| (one ballot
+// per pair: a running maximum over the whole tile pushed the wide kernel into spills).
+// DT_BF16: the bf16 (nearest-even) of fl(fl(acc * sA) * sW); sa: the lane's row scale, sWp:
+// the pair's 64 column scales (LDS).
+// Read-back chunk c = 64k + lane holds row c/8 = 8k + lane/8, columns 8(c%8)..; loff0: its
+// row-major offset (elements) for k = 0.  Each quad goes to the patch as one 8-byte write (two 16-bit values
 // per dword), rows 68 values apart so the 32 rows' writes fall on distinct banks; the
 // read-back takes each 16-byte row chunk as two 8-byte reads and stores it, so each row
 // segment is 128 bytes.  The patch is private to the wave and a wave's LDS accesses execute
@@ -298,6 +262,8 @@ __device__ __forceinline__ void epi_pair_t(const v16f &x0, const v16f &x1, bool 
 // tiles whose flags the DT_Q16 launch set are computed.
 template <int YDT, bool ACCOUT, bool KFULL, bool F8, bool FB>
 __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
+    // two-byte outputs run on the transposed product (swapped MFMA operands, see epi_pair_t)
+    constexpr bool TR = YDT != DT_F32 && !F8;
     __shared__ __attribute__((aligned(16))) uint8_t sb0[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb1[STB];
     __shared__ __attribute__((aligned(16))) uint8_t sb2[STB];
@@ -389,7 +355,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
         stage_dma<KFULL>(rsA, rsB, ahead, wave, offA, offB, kt + 2, KB, lane_chunk16);
         __builtin_amdgcn_sched_barrier(0);
         frag_load(cur, wm, wn, lane, 1, a1, b1);
-        mfma_block(acc, a0, b0);
+        mfma_block<2, TR>(acc, a0, b0);
 #pragma unroll
         for (int q = 0; q < 6; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -397,7 +363,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_block(acc, a1, b1);
+        mfma_block<2, TR>(acc, a1, b1);
         __builtin_amdgcn_sched_barrier(0);
         WAIT_VMCNT(6);
         lds_barrier();
@@ -423,12 +389,12 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     // MFMA 32x32 output layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, col l%32.
     const int last = (kstages + 2) % 3;
     uint8_t *stg = last == 0 ? sb0 : (last == 1 ? sb1 : sb2);
-    float *E = reinterpret_cast<float *>(stg + wave * 4096);
+    float *E = reinterpret_cast<float *>(stg + wave * 4352);  // 4 x 4352 bytes fit the 24 KiB stage buffer
     float sw[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) sw[j] = bk.sW[wn * 64 + j * 32 + (lane & 31)];
     const bool full = (m0 + BM <= M) && (n0 + BN <= N);
-    const uint32_t qoff = (uint32_t)(lane >> 3) * (uint32_t)N + (uint32_t)((lane & 7) * 8);  // DT_Q16 read-back
+    const uint32_t qoff = (uint32_t)(lane >> 3) * (uint32_t)N + (uint32_t)((lane & 7) * 8);  // epi_pair_t read-back
     bool qesc = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -442,19 +408,20 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
             sa[4 * r4 + 3] = v.w;
         }
         const int row0 = m0 + wm * 128 + i * 32;  // first row of this 32-row tile
-        if constexpr (YDT == DT_Q16) {
-            if constexpr (ACCOUT) {
+        if constexpr (TR) {  // the transposed product: both tiles of the row band as one pair
+            if constexpr (ACCOUT) {  // row lane%32, columns 8(r/4) + 4(lane/32) + r%4
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int grow = row0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        const int gcol = n0 + wn * 64 + j * 32 + (lane & 31);
+                        const int grow = row0 + (lane & 31);
+                        const int gcol = n0 + wn * 64 + j * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                         if (full || (grow < M && gcol < N)) p.acc_out[(size_t)grow * N + gcol] = acc[i][j][r];
                     }
             }
-            epi_q16_pair(acc[i][0], acc[i][1], qesc, reinterpret_cast<int16_t *>(E), lane, row0, n0 + wn * 64, M, N,
-                         full, static_cast<int16_t *>(p.Y), qoff);
+            epi_pair_t<YDT>(acc[i][0], acc[i][1], qesc, bk.sA[wm * 128 + i * 32 + (lane & 31)], &bk.sW[wn * 64],
+                            reinterpret_cast<uint16_t *>(E), lane, row0, n0 + wn * 64, M, N, full,
+                            static_cast<uint16_t *>(p.Y), qoff);
             continue;
         }
 #pragma unroll
