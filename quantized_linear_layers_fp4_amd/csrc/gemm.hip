@@ -257,6 +257,69 @@ __device__ __forceinline__ void epi_pair_t(const v16f &x0, const v16f &x1, bool 
     }
 }
 
+// The two halves of epi_pair_t, for an epilogue whose stores are deferred into the next
+// tile's main loop: pair_pack turns the pair into 16 packed words per lane (quad (t, a) in
+// words 2(4t + a), 2(4t + a) + 1), pair_store writes them through the patch.
+template <int YDT>
+__device__ __forceinline__ void pair_pack(const v16f &x0, const v16f &x1, float &m, float sa, const float *sWp,
+                                          int lane, uint32_t (&pk)[16]) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const v16f &x = t ? x1 : x0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            uint32_t q[4];
+            if constexpr (YDT == DT_Q16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[e] = __float_as_uint(__builtin_fmaf(x[4 * a + e], 4.0f, Q16_MAGIC));
+                asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a]), "v"(x[4 * a + 1]), "v"(m));
+                asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m) : "v"(x[4 * a + 2]), "v"(x[4 * a + 3]), "v"(m));
+            } else {
+                const float4 sw = *reinterpret_cast<const float4 *>(&sWp[32 * t + 8 * a + 4 * h]);
+                q[0] = f32_to_bf16_bits((x[4 * a] * sa) * sw.x);
+                q[1] = f32_to_bf16_bits((x[4 * a + 1] * sa) * sw.y);
+                q[2] = f32_to_bf16_bits((x[4 * a + 2] * sa) * sw.z);
+                q[3] = f32_to_bf16_bits((x[4 * a + 3] * sa) * sw.w);
+            }
+            pk[2 * (4 * t + a)] = (q[0] & 0xFFFFu) | (q[1] << 16);
+            pk[2 * (4 * t + a) + 1] = (q[2] & 0xFFFFu) | (q[3] << 16);
+        }
+    }
+}
+
+__device__ __forceinline__ void pair_store(const uint32_t (&pk)[16], uint16_t *P, int lane, int row0, int col0,
+                                           int M, int N, bool full, uint16_t *Yo, uint32_t loff0) {
+    constexpr int PS = 68;
+    const int lr = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            *reinterpret_cast<uint2 *>(&P[lr * PS + 32 * t + 8 * a + 4 * h]) =
+                make_uint2(pk[2 * (4 * t + a)], pk[2 * (4 * t + a) + 1]);
+    v4i e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = k * 64 + lane;
+        const uint2 u0 = *reinterpret_cast<const uint2 *>(&P[(c >> 3) * PS + (c & 7) * 8]);
+        const uint2 u1 = *reinterpret_cast<const uint2 *>(&P[(c >> 3) * PS + (c & 7) * 8 + 4]);
+        e[k] = v4i{(int)u0.x, (int)u0.y, (int)u1.x, (int)u1.y};
+    }
+    if (full) {
+        uint16_t *base = Yo + (size_t)row0 * N + col0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(base + loff0 + (uint32_t)(8 * k) * (uint32_t)N));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = k * 64 + lane, grow = row0 + (c >> 3), gcol = col0 + (c & 7) * 8;
+            if (grow < M && gcol < N)
+                __builtin_nontemporal_store(e[k], reinterpret_cast<v4i *>(Yo + (size_t)grow * N + gcol));
+        }
+    }
+}
 // F8: the operands are E4M3 bytes (one K value per byte) instead of packed E2M1 codes.
 // FB: the escape pass of a DT_Q16 product (YDT = DT_F32 into the escape buffer): only the
 // tiles whose flags the DT_Q16 launch set are computed.
@@ -636,6 +699,43 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    // DT_Q16 outputs: the last ND pairs of a tile are packed in registers and stored during the
+    // next tile's first steps, under its MFMAs (the bf16 epilogue stores at once: deferring it spills)
+    constexpr bool DEFER = YDT == DT_Q16;
+    constexpr int ND = 4;  // pairs deferred (the tile's last ND; the others are stored at once)
+    uint32_t pk[ND][16];
+    bool pend = false;
+    int pr0 = 0, pc0 = 0;
+    bool pfull = false;
+    uint32_t dloff = (uint32_t)(lane >> 3) * (uint32_t)N + (uint32_t)((lane & 7) * 8);
+    auto flush_pair = [&](const uint32_t (&q)[16], int pp) {
+        pair_store(q, reinterpret_cast<uint16_t *>(patch[wave]), lane, pr0 + ((pp + 8 - ND) >> 1) * 32, pc0 + (pp & 1) * 64, M, N,
+                   pfull, static_cast<uint16_t *>(p.Y), dloff);
+    };
+    auto step_d = [&](uint8_t *cur, const uint8_t *nxt, const int (&oa)[4], const int (&ob)[4], int dma_stage,
+                      const uint32_t (&qa)[16], int pa, const uint32_t (&qb)[16], int pb) {
+        __builtin_amdgcn_sched_barrier(0);
+        frag_load(cur, wm, wn, lane, 1, a1, b1);
+        mfma_block<4, YDT != DT_F32>(acc, a0, b0);
+        flush_pair(qa, pa);
+        INTERLEAVE16();
+        __builtin_amdgcn_sched_barrier(0);
+        WAIT_VMCNT(16);
+        lds_barrier();
+        stage_dma<true, 4>(rsA, rsB, cur, wave, oa, ob, dma_stage, KB, lane_chunk16);
+        frag_load(nxt, wm, wn, lane, 0, a0, b0);
+        mfma_block<4, YDT != DT_F32>(acc, a1, b1);
+        flush_pair(qb, pb);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     for (int tt = 0;; ++tt) {
         const int nlog = flagged(logical + per_xcd_wg);
         const bool has_next = nlog < hi;
@@ -654,6 +754,21 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         int kt = 0;
+        if constexpr (DEFER) {
+            if (pend) {
+                if (kstages >= 8) {  // the previous tile's stores under this tile's first four steps
+                    step_d(sb0, sb1, offA, offB, 4, pk[0], 0, pk[1], 1);
+                    step_d(sb1, sb2, offA, offB, 5, pk[2], 2, pk[3], 3);
+                    step(sb2, sb3, offA, offB, 6, true);
+                    step(sb3, sb0, offA, offB, 7, true);
+                    kt = 4;
+                } else {
+#pragma unroll
+                    for (int pp = 0; pp < ND; ++pp) flush_pair(pk[pp], pp);
+                }
+                pend = false;
+            }
+        }
         for (; kt + 4 < kstages; kt += 4) {
             step(sb0, sb1, offA, offB, kt + 4, true);
             step(sb1, sb2, offA, offB, kt + 5, true);
@@ -694,6 +809,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
             loff[k] = (uint32_t)lrow[k] * (uint32_t)N + (uint32_t)lcol[k];
         }
         bool qesc = false;  // DT_Q16: some |acc| of the wave's block is past the int16 range
+        float qmx = 0.0f;   // DT_Q16: the lane's largest |acc|
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sa[16];
@@ -710,7 +826,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                 const float sar = b.sA[wm * 128 + i * 32 + (lane & 31)];
 #pragma unroll
                 for (int jp = 0; jp < 2; ++jp) {
-                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (!DEFER) __builtin_amdgcn_sched_barrier(0);
                     if constexpr (ACCOUT) {  // the swapped layout: row lane%32, columns 8(r/4) + 4(lane/32) + r%4
 #pragma unroll
                         for (int j = 2 * jp; j < 2 * jp + 2; ++j)
@@ -721,9 +837,21 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                                 if (full || (grow < M && gcol < N)) p.acc_out[(size_t)grow * N + gcol] = acc[i][j][r];
                             }
                     }
-                    epi_pair_t<YDT>(acc[i][2 * jp], acc[i][2 * jp + 1], qesc, sar, &b.sW[wn * 128 + 64 * jp],
-                                    reinterpret_cast<uint16_t *>(E), lane, row0, n0 + wn * 128 + 64 * jp, M, N, full,
-                                    static_cast<uint16_t *>(p.Y), loff[0]);
+                    if constexpr (DEFER) {  // packed now; the tile's last ND pairs are stored later
+                        if (2 * i + jp >= 8 - ND) {
+                            pair_pack<YDT>(acc[i][2 * jp], acc[i][2 * jp + 1], qmx, sar, &b.sW[wn * 128 + 64 * jp], lane,
+                                           pk[2 * i + jp - (8 - ND)]);
+                        } else {
+                            uint32_t q[16];
+                            pair_pack<YDT>(acc[i][2 * jp], acc[i][2 * jp + 1], qmx, sar, &b.sW[wn * 128 + 64 * jp], lane, q);
+                            pair_store(q, reinterpret_cast<uint16_t *>(E), lane, row0, n0 + wn * 128 + 64 * jp, M, N, full,
+                                       static_cast<uint16_t *>(p.Y), loff[0]);
+                        }
+                    } else {
+                        epi_pair_t<YDT>(acc[i][2 * jp], acc[i][2 * jp + 1], qesc, sar, &b.sW[wn * 128 + 64 * jp],
+                                        reinterpret_cast<uint16_t *>(E), lane, row0, n0 + wn * 128 + 64 * jp, M, N, full,
+                                        static_cast<uint16_t *>(p.Y), loff[0]);
+                    }
                 }
                 continue;
             }
@@ -796,7 +924,19 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
             }
         }
         if constexpr (YDT == DT_Q16) {
+            qesc = __builtin_amdgcn_ballot_w64(qmx > Q16_MAX_ACC) != 0;
             if (lane == 0) p.flags[logical * 4 + wave] = qesc ? 1 : 0;
+        }
+        if constexpr (DEFER) {
+            pr0 = m0 + wm * 128;
+            pc0 = n0 + wn * 128;
+            pfull = full;
+            if (has_next) {
+                pend = true;
+            } else {
+#pragma unroll
+                for (int pp = 0; pp < ND; ++pp) flush_pair(pk[pp], pp);
+            }
         }
         if constexpr (FB) q16_fill_esc<4>(p.yq, lane, m0 + wm * 128, n0 + wn * 128, M, N, full);
         bk[(tt + 1) & 1].sA[tid] = nbA;
