@@ -1,6 +1,6 @@
 """Benchmark of the FP4 quantized linear forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama7b_gate_up]
 
 A step is one fp4_linear_forward (quantile + clamp + dA, token-wise quantization of A,
 channel-wise quantization of W, FP4 GEMM with dequantization, compensation pass) over one
@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import quantized_linear_layers_fp4_amd as fp4  # noqa: E402
-from workloads import CONFIGS, make_layer  # noqa: E402
+from workloads import WORKLOADS, make_layer  # noqa: E402
 
 METRIC = "FP4 quantized-linear TFLOPS & % dense FP4 MFMA peak; quantizer HBM GB/s"
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 matrix peak (10.1 PFLOP/s)
@@ -248,9 +248,9 @@ def run_backward(args):
     both on the FP4 GEMM (fp4_linear_backward), on the forward's codes of the same seeded
     workload and a seeded dY."""
     from workloads import make_grad
-    A, W, L = make_layer(args.config, 0)
+    A, W, L = make_layer(args.workload, 0)
     dev = torch.device("cuda:0")
-    Ad, Wd, dYd = A.to(dev), W.to(dev), make_grad(args.config, 0).to(dev)
+    Ad, Wd, dYd = A.to(dev), W.to(dev), make_grad(args.workload, 0).to(dev)
     M, K, N = L.M, L.K, L.N
     ws_f = fp4.workspace(Ad, N, L.q)
     fp4.linear_forward(Ad, Wd, L.q, ws=ws_f)
@@ -296,7 +296,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
+    ap.add_argument("--workload", default="llama7b_gate_up", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--emu", action="store_true",
                     help="also time the FP4-on-FP8 emulation of the product (E4M3 expansion + FP8 MFMA) against "
@@ -329,7 +329,7 @@ def main():
         run_backward(args)
         return
 
-    layers = [make_layer(args.config, li) for li in range(len(CONFIGS[args.config]))]
+    layers = [make_layer(args.workload, li) for li in range(len(WORKLOADS[args.workload].layers))]
     dev = torch.device("cuda:0")
     runs = []
     for A, W, L in layers:
@@ -441,8 +441,8 @@ def main():
     fwd_tflops = flops / ms_step / 1e9
     quant_gbs = qbytes / quant_ms / 1e6
     first = runs[0][2]
-    traffic = load_traffic(None) if (args.config == 3) else None
-    name = first.name if len(runs) == 1 else f"llama7b_layer_chain(x{len(runs)})"
+    traffic = load_traffic(None) if args.workload == "llama7b_gate_up" else None
+    name = first.name if len(runs) == 1 else f"{args.workload}(x{len(runs)} layers)"
     out = {
         "metric": METRIC,
         "value": round(fwd_tflops, 2),

@@ -15,7 +15,7 @@ import torch
 import oracle
 import quantized_linear_layers_fp4_amd as fp4
 from parity_util import (assert_bf16_close, assert_y_close, bf16_to_f64, oracle_inputs, to_np)
-from workloads import CONFIGS, as_numpy_bits, make_custom, make_custom_grad, make_layer
+from workloads import WORKLOADS, as_numpy_bits, make_custom, make_custom_grad, make_layer
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -247,7 +247,7 @@ def test_gemm_fp8_emulation(M, N, K):
 def test_gemm_fp8_emulation_full_size():
     """The same identity on the gate+up shape's own codes (M=16384, K=4096, N=22016)."""
     _say("gemm fp8 emulation llama7b_gate_up")
-    A, W, L = make_layer(3, 0)
+    A, W, L = make_layer("llama7b_gate_up", 0)
     Ad, Wd = A.to(DEV), W.to(DEV)
     ws = fp4.workspace(Ad, L.N, L.q)
     fp4.linear_forward(Ad, Wd, L.q, ws=ws)
@@ -429,11 +429,11 @@ def _check_forward_small(A, W, q, out_dtype):
     return None
 
 
-def test_forward_config1_tiny():
-    _say("forward config 1")
-    A, W, L = make_layer(1)
+def test_forward_tiny():
+    _say("forward tiny")
+    A, W, L = make_layer("tiny")
     err = _check_forward_small(A, W, L.q, torch.float32)
-    _say(f"config 1 max rel err {err:.3e}")
+    _say(f"tiny max rel err {err:.3e}")
 
 
 @pytest.mark.parametrize("dtype,M,K,N,q,out", [
@@ -574,16 +574,17 @@ def _sample_pairs(rng, M, N, row_ptr, count=3000):
     return np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
 
 
-FULL = [(c, li) for c in (2, 3, 4, 5) for li in range(len(CONFIGS[c]))]
+FULL = [(w, li) for w in ("llama1.3b_qkv", "llama7b_gate_up", "llama13b_down", "llama7b_block")
+        for li in range(len(WORKLOADS[w].layers))]
 
 
-@pytest.mark.parametrize("cfg,li", FULL, ids=[f"cfg{c}-{CONFIGS[c][li].name}" for c, li in FULL])
-def test_forward_full_size(cfg, li):
+@pytest.mark.parametrize("wl,li", FULL, ids=[f"{w}-{WORKLOADS[w].layers[li].name}" for w, li in FULL])
+def test_forward_full_size(wl, li):
     """The workload sizes, in the launch configuration the benchmark times: every
     intermediate compared in full, the accumulator and Y at sampled outputs."""
-    L = CONFIGS[cfg][li]
+    L = WORKLOADS[wl].layers[li]
     _say(f"full size {L.name} M={L.M} K={L.K} N={L.N} q={L.q}")
-    A, W, _ = make_layer(cfg, li)
+    A, W, _ = make_layer(wl, li)
     M, K, N = L.M, L.K, L.N
     Ad, Wd = A.to(DEV), W.to(DEV)
     ws = fp4.workspace(Ad, N, L.q)
@@ -612,7 +613,7 @@ def test_forward_full_size(cfg, li):
                         out_dtype=torch.float32, acc_out=True)
     if L.out_dtype == "bf16":
         assert torch.equal(Y.view(torch.int16), Y32.to(torch.bfloat16).view(torch.int16))
-    rng = np.random.default_rng(cfg * 10 + li)
+    rng = np.random.default_rng(WORKLOADS[wl].seed_id * 10 + li)
     ms, ns = _sample_pairs(rng, M, N, cl["row_ptr"])
     idx = torch.from_numpy(ms * N + ns).to(DEV)
     g_acc = acc.view(-1)[idx].cpu().numpy()
@@ -754,19 +755,19 @@ def test_backward_zero_gradient_rows_and_columns():
     _check_backward_small(A, W, torch.zeros_like(dY), 0.99, torch.float32)
 
 
-BWD_FULL = [(2, 0), (3, 0)]
+BWD_FULL = [("llama1.3b_qkv", 0), ("llama7b_gate_up", 0)]
 
 
-@pytest.mark.parametrize("cfg,li", BWD_FULL, ids=[f"cfg{c}-{CONFIGS[c][li].name}" for c, li in BWD_FULL])
-def test_backward_full_size(cfg, li):
+@pytest.mark.parametrize("wl,li", BWD_FULL, ids=[f"{w}-{WORKLOADS[w].layers[li].name}" for w, li in BWD_FULL])
+def test_backward_full_size(wl, li):
     """The backward at the workload sizes, as the benchmark runs it: every intermediate
     compared in full, dA and dW at sampled outputs."""
     from workloads import make_grad
-    L = CONFIGS[cfg][li]
+    L = WORKLOADS[wl].layers[li]
     M, K, N = L.M, L.K, L.N
     _say(f"backward full size {L.name} M={M} K={K} N={N}")
-    A, W, _ = make_layer(cfg, li)
-    dY = make_grad(cfg, li)
+    A, W, _ = make_layer(wl, li)
+    dY = make_grad(wl, li)
     Ad, Wd, dYd = A.to(DEV), W.to(DEV), dY.to(DEV)
     inter = _fwd_codes_gpu(Ad, Wd, L.q)
     ws = torch.empty(fp4.backward_layout(M, K, N).total, dtype=torch.uint8, device=DEV)
@@ -780,7 +781,7 @@ def test_backward_full_size(cfg, li):
     Wq, sW = oracle.quant_cols(Wnp)
     for k, v in (("Aq", Aq), ("sA", sA), ("Wq", Wq), ("sW", sW)):
         assert np.array_equal(to_np(inter[k]), v), k
-    rng = np.random.default_rng(100 + cfg)
+    rng = np.random.default_rng(100 + WORKLOADS[wl].seed_id)
     count = 2000
     mk = (np.concatenate([rng.integers(0, M, count), [0, M - 1]]), np.concatenate([rng.integers(0, K, count), [0, K - 1]]))
     kn = (np.concatenate([rng.integers(0, K, count), [0, K - 1]]), np.concatenate([rng.integers(0, N, count), [0, N - 1]]))

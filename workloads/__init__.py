@@ -10,7 +10,7 @@ FP4 Quantization", abstract and experiment summary): no dataset or trained
 weight is involved, the value distributions are the synthetic stand-ins stated
 per configuration below.
 
-Recipe (all draws host-side, numpy PCG64 seeded by [20250128, cfg, layer, stream]):
+Recipe (all draws host-side, numpy PCG64 seeded by [20250128, seed_id, layer, stream]):
   stream 0 = base values of A, stream 1 = A structure (outlier positions,
   channels, per-row RMS), stream 2 = W, stream 3 = the output gradient dY of the
   backward (N(0, 1e-3), the magnitude of a loss-scaled activation gradient).  Values are drawn in float32; every
@@ -47,23 +47,31 @@ class Layer:
         return 2 * self.M * self.N * self.K
 
 
-# name -> list of layers.  Config 5 is a chain of four independent layers.
-CONFIGS: dict[int, list[Layer]] = {
-    1: [Layer("tiny", 128, 256, 128, "fp32", "fp32", 0.99, "normal_sparse_outliers", 0.02, (0.005, 50.0))],
-    2: [Layer("llama1.3b_qkv", 8192, 2048, 6144, "bf16", "bf16", 0.99, "normal_channel_outliers", 0.02, (8, 30.0))],
-    3: [Layer("llama7b_gate_up", 16384, 4096, 22016, "bf16", "bf16", 0.999, "lognormal_rows_sparse_outliers", 0.015, (0.5, 0.001, 40.0))],
-    4: [Layer("llama13b_down", 16384, 13824, 5120, "bf16", "bf16", 0.99, "student_t", 0.01, (3.0,))],
-    5: [
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """A named set of layers; seed_id keys its random streams."""
+    seed_id: int
+    layers: tuple
+
+
+# name -> workload.  llama7b_block is a chain of four independent layers (one LLaMA-7B block's
+# projections at 8192 tokens).
+WORKLOADS: dict[str, Workload] = {
+    "tiny": Workload(1, (Layer("tiny", 128, 256, 128, "fp32", "fp32", 0.99, "normal_sparse_outliers", 0.02, (0.005, 50.0)),)),
+    "llama1.3b_qkv": Workload(2, (Layer("llama1.3b_qkv", 8192, 2048, 6144, "bf16", "bf16", 0.99, "normal_channel_outliers", 0.02, (8, 30.0)),)),
+    "llama7b_gate_up": Workload(3, (Layer("llama7b_gate_up", 16384, 4096, 22016, "bf16", "bf16", 0.999, "lognormal_rows_sparse_outliers", 0.015, (0.5, 0.001, 40.0)),)),
+    "llama13b_down": Workload(4, (Layer("llama13b_down", 16384, 13824, 5120, "bf16", "bf16", 0.99, "student_t", 0.01, (3.0,)),)),
+    "llama7b_block": Workload(5, (
         Layer("llama7b_qkv", 8192, 4096, 12288, "bf16", "bf16", 0.99, "normal_channel_outliers", 0.02, (6, 50.0)),
         Layer("llama7b_o", 8192, 4096, 4096, "bf16", "bf16", 0.99, "normal_channel_outliers", 0.02, (6, 50.0)),
         Layer("llama7b_gate_up", 8192, 4096, 22016, "bf16", "bf16", 0.99, "normal_channel_outliers", 0.02, (6, 50.0)),
         Layer("llama7b_down", 8192, 11008, 4096, "bf16", "bf16", 0.99, "normal_channel_outliers", 0.02, (6, 50.0)),
-    ],
+    )),
 }
 
 
-def _rng(cfg: int, layer: int, stream: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64([SEED_ROOT, cfg, layer, stream]))
+def _rng(seed_id: int, layer: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64([SEED_ROOT, seed_id, layer, stream]))
 
 
 def _normal(rng, shape, std=1.0, chunk_rows=2048) -> np.ndarray:
@@ -76,10 +84,10 @@ def _normal(rng, shape, std=1.0, chunk_rows=2048) -> np.ndarray:
     return out
 
 
-def _draw_A(L: Layer, cfg: int, li: int) -> np.ndarray:
+def _draw_A(L: Layer, seed_id: int, li: int) -> np.ndarray:
     M, K = L.M, L.K
-    base = _rng(cfg, li, 0)
-    struct = _rng(cfg, li, 1)
+    base = _rng(seed_id, li, 0)
+    struct = _rng(seed_id, li, 1)
     if L.a_kind == "normal_sparse_outliers":
         frac, mult = L.a_param
         A = _normal(base, (M, K))
@@ -115,21 +123,23 @@ def _to_dtype(x: np.ndarray, dtype: str) -> torch.Tensor:
     return t.to(torch.bfloat16) if dtype == "bf16" else t.clone()
 
 
-def make_layer(cfg: int, li: int = 0) -> tuple[torch.Tensor, torch.Tensor, Layer]:
+def make_layer(workload: str, li: int = 0) -> tuple[torch.Tensor, torch.Tensor, Layer]:
     """Return (A, W, layer) as CPU tensors of the layer's dtype."""
-    L = CONFIGS[cfg][li]
-    A = _draw_A(L, cfg, li)
-    W = _normal(_rng(cfg, li, 2), (L.K, L.N), std=L.w_std)
+    wl = WORKLOADS[workload]
+    L = wl.layers[li]
+    A = _draw_A(L, wl.seed_id, li)
+    W = _normal(_rng(wl.seed_id, li, 2), (L.K, L.N), std=L.w_std)
     return _to_dtype(A, L.dtype), _to_dtype(W, L.dtype), L
 
 
 GRAD_STD = 1e-3
 
 
-def make_grad(cfg: int, li: int = 0) -> torch.Tensor:
+def make_grad(workload: str, li: int = 0) -> torch.Tensor:
     """dY (M x N) for the backward of the layer, as a CPU tensor of the layer's dtype."""
-    L = CONFIGS[cfg][li]
-    return _to_dtype(_normal(_rng(cfg, li, 3), (L.M, L.N), std=GRAD_STD), L.dtype)
+    wl = WORKLOADS[workload]
+    L = wl.layers[li]
+    return _to_dtype(_normal(_rng(wl.seed_id, li, 3), (L.M, L.N), std=GRAD_STD), L.dtype)
 
 
 def make_custom_grad(M: int, N: int, dtype: str = "bf16", seed: int = 0) -> torch.Tensor:
