@@ -350,10 +350,12 @@ def test_gemm_q16_handover(M, N, K):
     assert (n_esc > 0) == (36 * K > 8191.75)
 
 
-def test_gemm_q16_handover_wide():
-    """The same contract on the persistent 256 x 256 kernel (8192 x 8192 x 512: 1024 tiles),
-    its escape pass recomputing only the flagged tiles."""
-    M, N, K = 8192, 8192, 512
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 512), (8200, 8192, 1024)])
+def test_gemm_q16_handover_wide(M, N, K):
+    """The same contract on the persistent 256 x 256 kernel (1024 or more tiles), its escape
+    pass recomputing only the flagged tiles.  K = 1024 (eight K-stages) is the first depth at
+    which a tile's last pairs are stored under the next tile's first steps; M = 8200 adds a
+    ragged row of tiles."""
     _say(f"gemm q16 wide {M}x{N}x{K}")
     rng = np.random.default_rng(77)
     rows, cols = {0, 4000, M - 1}, {5, 4100, N - 1}
@@ -627,15 +629,15 @@ def test_forward_full_size(wl, li):
     _say(f"  sampled acc bit-exact, Y max rel err {err:.3e}")
 
 
-@pytest.mark.parametrize("out", ["bf16", "fp32"])
-def test_forward_escapes_wide(out):
-    """The forward on the persistent 256 x 256 GEMM (8192 x 512 x 8192: 1024 tiles) with
+@pytest.mark.parametrize("out,M,K", [("bf16", 8192, 512), ("fp32", 8192, 512), ("bf16", 8200, 1024)])
+def test_forward_escapes_wide(out, M, K):
+    """The forward on the persistent 256 x 256 GEMM (M x K x 8192: 1024 tiles or more) with
     accumulators past the two-byte range (rows of A and channels of W quantizing to +-6
     everywhere: acc = +-36 K): its escape pass recomputes those tiles in fp32 and the
     compensation pass takes them from there (the workspace for a bf16 Y, Y for an fp32 Y).
     Intermediates in full; the accumulator and Y at sampled outputs, all of them in the
-    escaped tiles' rows."""
-    M, K, N = 8192, 512, 8192
+    escaped tiles' rows.  K = 1024 with M = 8200: deferred stores and a ragged row of tiles."""
+    N = 8192
     _say(f"forward escapes wide {M}x{K}x{N} out={out}")
     A, W = make_custom(M, K, N, dtype="bf16", seed=41)
     rows, cols = (0, 4000, M - 1), (5, 4100, N - 1)
