@@ -1,0 +1,74 @@
+"""The seeded input generator: its draws stay fixed, and each workload has the shape and
+the value structure its recipe states (no GPU, no oracle: the generator holds none of the
+method's arithmetic)."""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import WORKLOADS, make_grad, make_layer
+
+
+def _sha(t: torch.Tensor) -> str:
+    return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+
+
+def test_draws_are_fixed():
+    """A change to the recipe, a seed or the bf16 cast changes these digests; every GPU
+    parity case and bench figure is taken on these draws."""
+    A, W, L = make_layer("tiny")
+    assert (A.dtype, W.dtype) == (torch.float32, torch.float32)
+    assert _sha(A) == "c01256630798b1fc"
+    assert _sha(W) == "5890b07adbc01b03"
+    assert _sha(make_grad("tiny")) == "d670a6082b16d0d5"
+
+
+def test_draws_repeat():
+    A1, W1, _ = make_layer("tiny")
+    A2, W2, _ = make_layer("tiny")
+    assert torch.equal(A1, A2) and torch.equal(W1, W2)
+
+
+def test_table_shapes_fit_the_library_limits():
+    """K % 32 == 0, 32 <= K <= 65536, N % 8 == 0 and M*K < 2^32 for every layer."""
+    names = set()
+    for wl in WORKLOADS.values():
+        for L in wl.layers:
+            assert L.K % 32 == 0 and 32 <= L.K <= 65536
+            assert L.N % 8 == 0 and L.M * L.K < 2**32
+            assert 0.0 < L.q < 1.0
+        names.add(wl.seed_id)
+    assert len(names) == len(WORKLOADS)  # distinct random streams
+
+
+def test_sparse_outliers_structure():
+    """tiny: N(0, 1) with floor(0.005 M K) distinct entries scaled by 50."""
+    L = WORKLOADS["tiny"].layers[0]
+    A = workloads._draw_A(L, WORKLOADS["tiny"].seed_id, 0)
+    frac, mult = L.a_param
+    base = workloads._normal(workloads._rng(WORKLOADS["tiny"].seed_id, 0, 0), (L.M, L.K))
+    scaled = A != base
+    assert scaled.sum() == int(frac * L.M * L.K)
+    assert np.array_equal(A[scaled], base[scaled] * np.float32(mult))
+
+
+def test_channel_outliers_structure():
+    """llama1.3b_qkv: 8 columns of A scaled by 30, the rest N(0, 1)."""
+    L = WORKLOADS["llama1.3b_qkv"].layers[0]
+    A = workloads._draw_A(L, WORKLOADS["llama1.3b_qkv"].seed_id, 0)
+    n_ch, mult = L.a_param
+    std = A[:2048].std(axis=0)
+    hot = np.nonzero(std > 10.0)[0]
+    assert len(hot) == n_ch
+    assert np.allclose(std[hot], mult, rtol=0.1)
+    cold = np.delete(std, hot)
+    assert np.allclose(cold, 1.0, rtol=0.1)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_weights_std(name):
+    L = WORKLOADS[name].layers[0]
+    W = workloads._normal(workloads._rng(WORKLOADS[name].seed_id, 0, 2), (min(L.K, 512), L.N), std=L.w_std)
+    assert abs(float(W.std()) / L.w_std - 1.0) < 0.02
