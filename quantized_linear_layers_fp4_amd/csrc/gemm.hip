@@ -1000,12 +1000,12 @@ size_t gemm_flag_bytes(int64_t M, int64_t N) {
 static hipError_t launch_gemm_one(const TileArgs &p0, int y_dt, bool acc, bool f8, bool fb, hipStream_t s) {
     TileArgs p = p0;
     const int64_t M = p.M, N = p.N, K = p.K;
-    // wide persistent tiles when there are enough of them to keep every CU busy for a few
-    // rounds (few large tiles would leave the per-tile prologue and epilogue exposed)
+    // wide persistent tiles when there are at least two per CU (with fewer, the per-tile
+    // prologue and epilogue of the large tiles are left exposed)
     if (!f8 && K % 512 == 0 && wide_gemm_enabled()) {
         const int cus = num_cus();
         const int64_t wtiles = ((M + BM - 1) / BM) * ((N + WBN - 1) / WBN);
-        if (cus >= 8 && wtiles >= 4 * (int64_t)cus) {
+        if (cus >= 8 && wtiles >= 2 * (int64_t)cus) {
             p.tilesN = (int)((N + WBN - 1) / WBN);
             const int blocks = cus / 8 * 8;
 #define W3(YD, AO, FBK) hipLaunchKernelGGL((k_fp4_gemm_wide<YD, AO, FBK>), dim3(blocks), dim3(NT), 0, s, p)
