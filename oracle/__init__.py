@@ -307,21 +307,6 @@ def forward(A: np.ndarray, W: np.ndarray, q: float) -> dict:
                 denom=denom)
 
 
-def forward_sampled(A: np.ndarray, W: np.ndarray, q: float, ms, ns) -> dict:
-    """Full-size intermediates (T, COO, codes, scales) and acc / Y only at (ms, ns)."""
-    A, W = np.ascontiguousarray(A), np.ascontiguousarray(W)
-    M, K = A.shape
-    T = abs_quantile(A, q)
-    cl = clamp_coo(A, T, want_clamped=True, cap=capacity(M, K, q))
-    Aq, sA = quant_rows(cl["A_clamped"])
-    del cl["A_clamped"]
-    Wq, sW = quant_cols(W)
-    acc = accumulate_pairs(Aq, Wq, K, ms, ns)
-    Y, denom = output_pairs(acc, sA, sW, ms, ns, cl["row_ptr"], cl["coo_col"], cl["coo_val"], W)
-    return dict(T=T, Aq=Aq, sA=sA, Wq=Wq, sW=sW, acc=acc, Y=Y, denom=denom, ms=np.asarray(ms),
-                ns=np.asarray(ns), **cl)
-
-
 # ----------------------------------------------------------------------------- backward
 def transpose_codes(codes: np.ndarray, R: int, Cc: int) -> np.ndarray:
     """R x Cc codes packed R x Cc/2 -> the transposed codes packed Cc x R/2."""

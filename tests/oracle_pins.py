@@ -405,6 +405,70 @@ def pin_forward_bruteforce():
     assert np.array_equal(out["Y"], Y)
 
 
+def _output_case(w_bf16: bool):
+    """Inputs of the output stage built directly: accumulators that are multiples of 1/4,
+    distinct scales on every row and column, a (row, col)-sorted dA list with 1 to 6
+    entries per row, and more rows than columns (so a row index taken for a column index
+    stays in range); W in fp32 or as bf16 bit patterns (with its float32 values)."""
+    rng = np.random.default_rng(56 + int(w_bf16))
+    M, K, N = 13, 64, 6
+    acc = (rng.integers(-4000, 4000, (M, N)) / 4.0).astype(np.float32)
+    sA = (rng.uniform(0.5, 2.0, M) * np.exp2(rng.integers(-4, 4, M))).astype(np.float32)
+    sW = (rng.uniform(0.5, 2.0, N) * np.exp2(rng.integers(-9, -5, N))).astype(np.float32)
+    cnt = rng.integers(1, 7, M)
+    cols = [np.sort(rng.choice(K, c, replace=False)) for c in cnt]
+    row_ptr = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    coo_col = np.concatenate(cols).astype(np.int32)
+    coo_val = (rng.standard_normal(coo_col.size) * 30.0).astype(np.float32)
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    Wpass = W
+    if w_bf16:
+        Wb = torch.from_numpy(W).to(torch.bfloat16)
+        W = Wb.float().numpy()
+        Wpass = Wb.view(torch.int16).numpy().view(np.uint16)
+    assert len(np.unique(sA)) == M and len(np.unique(sW)) == N
+    return acc, sA, sW, row_ptr, coo_col, coo_val, W, Wpass
+
+
+def pin_output_pairs_exact():
+    # the sampled output (the Y checker of every full-size comparison) against its
+    # definition at (m, n) pairs: Y_main = fl(fl(acc * sA[m]) * sW[n]), then the exact
+    # rational sum over row m's dA entries of delta * W[k][n], rounded once to fp32
+    f32 = np.float32
+    for w_bf16 in (False, True):
+        acc, sA, sW, row_ptr, coo_col, coo_val, W, Wpass = _output_case(w_bf16)
+        M, N = acc.shape
+        rng = np.random.default_rng(57)
+        ms = np.concatenate([rng.integers(0, M, 60), [0, M - 1]])
+        ns = np.concatenate([rng.integers(0, N, 60), [N - 1, 0]])
+        Y, _ = oracle.output_pairs(acc[ms, ns], sA, sW, ms, ns, row_ptr, coo_col, coo_val, Wpass)
+        for i, (m, n) in enumerate(zip(ms, ns)):
+            ym = f32(f32(acc[m, n] * sA[m]) * sW[n])
+            comp = sum(Fraction(float(coo_val[e])) * Fraction(float(W[coo_col[e], n]))
+                       for e in range(row_ptr[m], row_ptr[m + 1]))
+            assert Y[i] == f32(float(Fraction(float(ym)) + comp)), (w_bf16, m, n)
+        # the whole-output form agrees at the same points
+        Yall, _ = oracle.output(acc, sA, sW, row_ptr, coo_col, coo_val, Wpass)
+        assert np.array_equal(Y, Yall[ms, ns])
+
+
+def pin_tolerance_denominator():
+    # the scale of the Y tolerance: |Y_main| + sum over the row's entries of |delta * W[k][n]|,
+    # recomputed in float64 from the dA list, for the whole output and for sampled pairs
+    for w_bf16 in (False, True):
+        acc, sA, sW, row_ptr, coo_col, coo_val, W, Wpass = _output_case(w_bf16)
+        M, N = acc.shape
+        ymain = ((acc * sA[:, None]).astype(np.float32) * sW[None, :]).astype(np.float32)
+        dense = np.zeros((M, W.shape[0]))
+        dense[np.repeat(np.arange(M), np.diff(row_ptr)), coo_col] = coo_val
+        ref = np.abs(ymain.astype(np.float64)) + np.abs(dense) @ np.abs(W.astype(np.float64))
+        _, d_all = oracle.output(acc, sA, sW, row_ptr, coo_col, coo_val, Wpass)
+        assert np.allclose(d_all, ref, rtol=1e-12, atol=0)
+        ms, ns = np.arange(M), np.arange(M)[::-1] % N
+        _, d = oracle.output_pairs(acc[ms, ns], sA, sW, ms, ns, row_ptr, coo_col, coo_val, Wpass)
+        assert np.allclose(d, ref[ms, ns], rtol=1e-12, atol=0)
+
+
 def pin_bf16_rounding():
     x = np.array([1.0, 1.00390625, 1.005859375, 1.0078125, -2.5, 3.0e-3, 65504.0], dtype=np.float32)
     got = oracle.to_bf16(x)

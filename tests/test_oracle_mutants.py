@@ -56,6 +56,12 @@ MUTANTS = {
                              "dA[m * K + k] = scale_one(dA[m * K + k], sG[0]);"),
     "bwd_dW_scale_of_col0": ("dW[k * N + n] = scale_one(dW[k * N + n], sH[n]);",
                              "dW[k * N + n] = scale_one(dW[k * N + n], sH[0]);"),
+    "output_pairs_scale_index": ("float ym = dequant_one(acc[i], sA[ms[i]], sW[ns[i]]);",
+                                 "float ym = dequant_one(acc[i], sA[ns[i]], sW[ns[i]]);"),
+    "output_pairs_entries_of_other_row": ("Y[i] = compensate_one(ym, ms[i], ns[i], N,",
+                                          "Y[i] = compensate_one(ym, ns[i], ns[i], N,"),
+    "denom_inflated": ("s += fabs(t);", "s += 2.0 * fabs(t);"),
+    "denom_without_ymain": ("double d = 0.0, s = fabs((double)ymain);", "double d = 0.0, s = 0.0;"),
     "bwd_scale_pairs_index": ("out[i] = scale_one(acc[i], s[idx[i]]);", "out[i] = scale_one(acc[i], s[i % 1]);"),
 }
 
