@@ -76,13 +76,9 @@ def time_on_stream(fn, steps: int, warmup: int, rounds: int = 3) -> float:
 
 
 def gemm_kernel(M: int, N: int, K: int) -> str:
-    """Name of the GEMM kernel the library launches for this shape (its selection rule: the
-    persistent 256 x 256 kernel when K % 512 == 0 and there are at least four such tiles per
-    CU, else the 256 x 128 kernel)."""
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    wide = (K % 512 == 0 and ((M + 255) // 256) * ((N + 255) // 256) >= 4 * cus
-            and os.environ.get("FP4_GEMM_WIDE", "1") != "0")
-    return "k_fp4_gemm_wide" if wide else "k_fp4_gemm"
+    """Name of the GEMM kernel the library launches for this shape on this device (the
+    library's own selection rule, exported through the C ABI)."""
+    return fp4.gemm_kernel_name(M, N, K, torch.cuda.get_device_properties(0).multi_processor_count)
 
 
 def _kernel_is(name: str):
@@ -463,7 +459,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": gemm_kernel(first.M, first.N, first.K), "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(gemm_ms, 4)},
-        "compensation": {"bound": "hbm", "kernel": "k_comp_apply", "achieved": round(cbytes / comp_ms / 1e6, 1),
+        "compensation": {"bound": "hbm", "kernel": fp4.comp_kernel_name(first.M, fp4.outlier_capacity(first.M, first.K, first.q)), "achieved": round(cbytes / comp_ms / 1e6, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(cbytes / comp_ms / 1e6 / PEAK_HBM_GBS, 4),
                          "ms": round(comp_ms, 4), "algorithmic_bytes": cbytes},
         "quantizer": {"bound": "hbm", "achieved": round(quant_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

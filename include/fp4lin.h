@@ -43,8 +43,9 @@
  * The library never allocates, frees or synchronizes, and never copies device data to
  * the host: each call only validates its arguments on the host and enqueues kernels on
  * the caller's HIP stream (hipStream_t passed as void*, NULL = default stream); results
- * are ready when that stream reaches them.  No mutable global state: calls on different
- * streams are independent as long as their buffers do not overlap.
+ * are ready when that stream reaches them.  The only global state is a per-device cache of
+ * the device's properties (gfx950 or not, compute-unit count), filled on first use under a
+ * lock: calls on different streams are independent as long as their buffers do not overlap.
  *
  * Errors: every argument check runs on the host before the first HIP call and returns a
  * status; nothing is enqueued then.  FP4_ERR_DEVICE: the current device is not gfx950.
@@ -280,6 +281,18 @@ fp4_status fp4_linear_backward(const void *dY, int32_t dy_dtype, int64_t M, int6
                                const uint8_t *Aq, const float *sA, const uint8_t *Wq,
                                const float *sW, void *dA, int32_t da_dtype, void *dW,
                                int32_t dw_dtype, void *workspace, size_t ws_bytes, void *stream);
+
+/* Host-only: the kernel selection, the same rule the launches use, so a caller (a profiler
+ * summary, a benchmark) can name what runs.  fp4_gemm_kernel_name: the FP4 GEMM kernel that
+ * fp4_gemm and fp4_linear_forward launch for an M x N x K product on a device with num_cus
+ * compute units ("k_fp4_gemm_wide": persistent 256 x 256 tiles, chosen when K % 512 == 0 and
+ * there are at least two such tiles per CU; else "k_fp4_gemm": 256 x 128 tiles).
+ * fp4_comp_kernel_name: the compensation kernel for M rows and a dA list of `capacity`
+ * entries (fp4_outlier_capacity; the forward uses that bound) ("k_comp_block64" above 64
+ * entries per row on average, else "k_comp_apply").  Both return a static string, or NULL
+ * for invalid arguments (num_cus < 1, sizes out of range). */
+const char *fp4_gemm_kernel_name(int64_t M, int64_t N, int64_t K, int32_t num_cus);
+const char *fp4_comp_kernel_name(int64_t M, int64_t capacity);
 
 /* Static description of a status code (never NULL). */
 const char *fp4_status_string(fp4_status s);

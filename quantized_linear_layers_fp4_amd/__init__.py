@@ -31,7 +31,7 @@ EXPORTS = (
     "fp4_linear_forward_wq", "fp4_gemm_fp8emu_workspace_bytes", "fp4_gemm_fp8emu",
     "fp4_fp8_workspace_bytes", "fp4_fp8_quantize", "fp4_fp8_dequantize",
     "fp4_backward_layout", "fp4_backward_workspace_bytes", "fp4_linear_backward",
-    "fp4_status_string",
+    "fp4_gemm_kernel_name", "fp4_comp_kernel_name", "fp4_status_string",
 )
 
 
@@ -79,6 +79,8 @@ def lib():
         "fp4_backward_layout": (i32, [i64, i64, i64, C.POINTER(BwdLayout)]),
         "fp4_backward_workspace_bytes": (sz, [i64, i64, i64]),
         "fp4_linear_backward": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp]),
+        "fp4_gemm_kernel_name": (C.c_char_p, [i64, i64, i64, i32]),
+        "fp4_comp_kernel_name": (C.c_char_p, [i64, i64]),
         "fp4_status_string": (C.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -133,6 +135,22 @@ def quantize(X: torch.Tensor, axis: int = FP4_PER_ROW, clamp_T: torch.Tensor | N
         scales = torch.empty(Cn, dtype=torch.float32, device=X.device)
     _check(lib().fp4_quantize(_ptr(X), _dt(X), R, Cn, axis, _ptr(clamp_T), _ptr(codes), _ptr(scales), _stream(X)))
     return codes, scales
+
+
+def gemm_kernel_name(M: int, N: int, K: int, num_cus: int) -> str:
+    """The FP4 GEMM kernel the library launches for an M x N x K product on num_cus CUs."""
+    r = lib().fp4_gemm_kernel_name(M, N, K, num_cus)
+    if r is None:
+        raise Fp4Error(f"no GEMM kernel for M={M} N={N} K={K} on {num_cus} CUs")
+    return r.decode()
+
+
+def comp_kernel_name(M: int, capacity: int) -> str:
+    """The compensation kernel the library launches for M rows and a dA list of `capacity`."""
+    r = lib().fp4_comp_kernel_name(M, capacity)
+    if r is None:
+        raise Fp4Error(f"no compensation kernel for M={M} capacity={capacity}")
+    return r.decode()
 
 
 def outlier_capacity(M: int, K: int, q: float) -> int:

@@ -336,6 +336,16 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
     return hip_status(e);
 }
 
+const char *fp4_gemm_kernel_name(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
+    if (num_cus < 1 || !gemm_ok(M, N, K)) return nullptr;
+    return gemm_kernel_choice(M, N, K, false, num_cus) == GEMM_WIDE ? "k_fp4_gemm_wide" : "k_fp4_gemm";
+}
+
+const char *fp4_comp_kernel_name(int64_t M, int64_t capacity) {
+    if (M < 1 || capacity < 0) return nullptr;
+    return comp_kernel_choice(M, capacity) == COMP_BLOCK64 ? "k_comp_block64" : "k_comp_apply";
+}
+
 size_t fp4_fp8_workspace_bytes(void) { return ALIGN; }
 
 fp4_status fp4_fp8_quantize(const void *X, int32_t x_dtype, int64_t n, uint8_t *codes, float *scale, void *workspace,

@@ -305,13 +305,15 @@ static hipError_t launch_comp_tasks(const CompArgs &a, int y_dt, int w_dt, hipSt
     return hipGetLastError();
 }
 
+int comp_kernel_choice(int64_t M, int64_t capacity) { return capacity > 64 * M ? COMP_BLOCK64 : COMP_CHUNK; }
+
 hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y, int y_dt,
                        int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s) {
     const CompArgs a{Yq, esc, sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
     // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
     // gathers, and the 8-row x 64-column blocks keep each XCD's W strip in its L2
-    if (capacity > 64 * M) return launch_comp_block64(a, y_dt, w_dt, s);
+    if (comp_kernel_choice(M, capacity) == COMP_BLOCK64) return launch_comp_block64(a, y_dt, w_dt, s);
     return launch_comp_tasks<8>(a, y_dt, w_dt, s);
 }
 

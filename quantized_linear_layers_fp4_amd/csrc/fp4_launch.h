@@ -55,6 +55,9 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
                        int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8 = false,
                        float *esc = nullptr, uint8_t *flags = nullptr);
 size_t gemm_flag_bytes(int64_t M, int64_t N);
+// The GEMM kernel launch_gemm picks for a shape on a device with `cus` compute units.
+enum : int { GEMM_TILED = 0, GEMM_WIDE = 1 };
+int gemm_kernel_choice(int64_t M, int64_t N, int64_t K, bool f8, int cus);
 // FP8 (E4M3) gradient codec, one per-tensor scale.  key: device u32 scratch (zeroed here).
 hipError_t launch_fp8_quantize(const void *X, int dt, int64_t n, uint32_t *key, uint8_t *codes, float *scale,
                                int num_cus, hipStream_t s);
@@ -67,6 +70,10 @@ hipError_t launch_e2m1_to_e4m3(const uint8_t *codes, int64_t n_bytes, uint8_t *o
 // Y_main comes from the GEMM's DT_Q16 output (Yq, esc) and the scales sA, sW.  Yq may be a
 // bf16 Y itself, esc may be an fp32 Y itself.  capacity: what the dA list was sized for
 // (picks the kernel shape only; 0 if unknown).
+// The compensation kernel launch_comp picks: chunk tasks up to 64 entries per row on average
+// (capacity / M), 8-row blocks beyond.
+enum : int { COMP_CHUNK = 0, COMP_BLOCK64 = 1 };
+int comp_kernel_choice(int64_t M, int64_t capacity);
 hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y, int y_dt,
                        int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s);

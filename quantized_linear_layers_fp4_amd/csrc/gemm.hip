@@ -21,13 +21,11 @@
 // accumulator as the int16 4*acc (DT_Q16), with a second, flagged launch (FB) that recomputes
 // in fp32 the tiles where it does not fit; the compensation pass rebuilds Y_main from it.
 //
-// Large products (K a multiple of 512 and at least four 256 x 256 tiles per CU) run on a
+// Large products (K a multiple of 512 and at least two 256 x 256 tiles per CU) run on a
 // second, persistent kernel with 256 x 256 tiles (see "wide tiles" below); both compute the
 // same exact accumulator and epilogue, so their outputs are identical.
 #include "fp4_common.h"
 #include "fp4_launch.h"
-
-#include <cstdlib>
 
 namespace fp4 {
 
@@ -956,14 +954,13 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     WAIT_VMCNT(0);
 }
 
-// Tile-rows per column sweep within an XCD.  FP4_GEMM_RASTER overrides (tuning aid).
+// Tile-rows per column sweep within an XCD (measured on five layer shapes: 2, 4 and 8 within
+// 3 % of each other, 4 best on most; 16 and more lose L2 reuse).  A compile-time tuning aid.
+#ifndef FP4_GEMM_RASTER_GROUP
+#define FP4_GEMM_RASTER_GROUP 4
+#endif
 static int raster_group_for(int tilesM) {
-    static int env = -2;
-    if (env == -2) {
-        const char *e = getenv("FP4_GEMM_RASTER");
-        env = e ? atoi(e) : -1;
-    }
-    const int g = env > 0 ? env : 4;
+    const int g = FP4_GEMM_RASTER_GROUP;
     return g < tilesM ? g : tilesM;
 }
 
@@ -980,14 +977,13 @@ static int num_cus() {
     return n;
 }
 
-// FP4_GEMM_WIDE=0 keeps every product on the 256 x 128 kernel (a tuning aid).
-static bool wide_gemm_enabled() {
-    static int env = -2;
-    if (env == -2) {
-        const char *e = getenv("FP4_GEMM_WIDE");
-        env = e ? atoi(e) : 1;
-    }
-    return env != 0;
+int gemm_kernel_choice(int64_t M, int64_t N, int64_t K, bool f8, int cus) {
+    // wide persistent tiles when K is whole groups of four stages and there are at least two
+    // such tiles per CU (with fewer, the per-tile prologue and epilogue of the large tiles are
+    // left exposed)
+    const int64_t wtiles = ((M + BM - 1) / BM) * ((N + WBN - 1) / WBN);
+    if (!f8 && K % 512 == 0 && cus >= 8 && wtiles >= 2 * (int64_t)cus) return GEMM_WIDE;
+    return GEMM_TILED;
 }
 
 size_t gemm_flag_bytes(int64_t M, int64_t N) {
@@ -1000,29 +996,24 @@ size_t gemm_flag_bytes(int64_t M, int64_t N) {
 static hipError_t launch_gemm_one(const TileArgs &p0, int y_dt, bool acc, bool f8, bool fb, hipStream_t s) {
     TileArgs p = p0;
     const int64_t M = p.M, N = p.N, K = p.K;
-    // wide persistent tiles when there are at least two per CU (with fewer, the per-tile
-    // prologue and epilogue of the large tiles are left exposed)
-    if (!f8 && K % 512 == 0 && wide_gemm_enabled()) {
-        const int cus = num_cus();
-        const int64_t wtiles = ((M + BM - 1) / BM) * ((N + WBN - 1) / WBN);
-        if (cus >= 8 && wtiles >= 2 * (int64_t)cus) {
-            p.tilesN = (int)((N + WBN - 1) / WBN);
-            const int blocks = cus / 8 * 8;
+    const int cus = num_cus();
+    if (gemm_kernel_choice(M, N, K, f8, cus) == GEMM_WIDE) {
+        p.tilesN = (int)((N + WBN - 1) / WBN);
+        const int blocks = cus / 8 * 8;
 #define W3(YD, AO, FBK) hipLaunchKernelGGL((k_fp4_gemm_wide<YD, AO, FBK>), dim3(blocks), dim3(NT), 0, s, p)
-            if (fb) W3(DT_F32, false, true);
-            else if (y_dt == DT_Q16) {
-                if (acc) W3(DT_Q16, true, false);
-                else W3(DT_Q16, false, false);
-            } else if (y_dt == DT_BF16) {
-                if (acc) W3(DT_BF16, true, false);
-                else W3(DT_BF16, false, false);
-            } else {
-                if (acc) W3(DT_F32, true, false);
-                else W3(DT_F32, false, false);
-            }
-#undef W3
-            return hipGetLastError();
+        if (fb) W3(DT_F32, false, true);
+        else if (y_dt == DT_Q16) {
+            if (acc) W3(DT_Q16, true, false);
+            else W3(DT_Q16, false, false);
+        } else if (y_dt == DT_BF16) {
+            if (acc) W3(DT_BF16, true, false);
+            else W3(DT_BF16, false, false);
+        } else {
+            if (acc) W3(DT_F32, true, false);
+            else W3(DT_F32, false, false);
         }
+#undef W3
+        return hipGetLastError();
     }
     const int64_t tiles = (int64_t)p.tilesM * p.tilesN;
     const int blocks = (int)((tiles + 7) / 8 * 8);

@@ -9,8 +9,6 @@
 #include "fp4_common.h"
 #include "fp4_launch.h"
 
-#include <cstdlib>
-
 namespace fp4 {
 
 // ----------------------------------------------------------------------------- zero fill
@@ -585,22 +583,17 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
 }
 
 // Column width of the transposing tile: 128 (256-byte row segments of the input; 3 % faster
-// than 64 on the 16384 x 22016 gradient, equal on the 4096 x 22016 weight).  FP4_QCOLS_TN=64|128
-// overrides (a tuning aid).
-static int qcols_tn() {
-    static int tn = 0;
-    if (!tn) {
-        const char *e = getenv("FP4_QCOLS_TN");
-        const int v = e ? atoi(e) : 0;
-        tn = (v == 64 || v == 128) ? v : 128;
-    }
-    return tn;
-}
+// than 64 on the 16384 x 22016 gradient, equal on the 4096 x 22016 weight).  A compile-time
+// tuning aid: 64 or 128.
+#ifndef FP4_QCOLS_TN
+#define FP4_QCOLS_TN 128
+#endif
+static_assert(FP4_QCOLS_TN == 64 || FP4_QCOLS_TN == 128, "FP4_QCOLS_TN is 64 or 128");
 
 template <int DT, bool RM>
 static void launch_qcols_tile(const void *W, int64_t K, int64_t N, const float *row_mult, const uint32_t *keys,
                               uint8_t *codes, hipStream_t s) {
-    if (qcols_tn() == 128) {
+    if constexpr (FP4_QCOLS_TN == 128) {
         dim3 g((unsigned)((N + 127) / 128), (unsigned)((K + 255) / 256));
         hipLaunchKernelGGL((k_quant_cols<DT, RM, 128>), g, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
     } else {

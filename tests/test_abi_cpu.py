@@ -244,3 +244,21 @@ def test_linear_backward_rejects():
     assert call(wsb=wsb - 1) == EWS
     assert call(dA=C.c_void_p(0x100004)) == EALIGN
     assert call(sA=C.c_void_p(0x100004)) == EALIGN
+
+
+def test_kernel_name_queries():
+    # the selection rule, exported so that a benchmark names what runs
+    L = fp4.lib()
+    assert L.fp4_gemm_kernel_name(16384, 22016, 4096, 256) == b"k_fp4_gemm_wide"
+    assert L.fp4_gemm_kernel_name(8192, 6144, 2048, 256) == b"k_fp4_gemm_wide"   # 768 tiles: 3 per CU
+    assert L.fp4_gemm_kernel_name(8192, 4096, 4096, 256) == b"k_fp4_gemm_wide"   # 512 tiles: 2 per CU
+    assert L.fp4_gemm_kernel_name(8192, 4096, 4096, 257) == b"k_fp4_gemm"        # below 2 per CU
+    assert L.fp4_gemm_kernel_name(16384, 22016, 4160, 256) == b"k_fp4_gemm"      # K not a multiple of 512
+    assert L.fp4_gemm_kernel_name(128, 128, 256, 256) == b"k_fp4_gemm"
+    assert L.fp4_gemm_kernel_name(128, 128, 256, 0) is None
+    assert L.fp4_gemm_kernel_name(128, 127, 256, 256) is None
+    cap = fp4.outlier_capacity(16384, 4096, 0.999)
+    assert L.fp4_comp_kernel_name(16384, cap) == b"k_comp_apply"
+    cap = fp4.outlier_capacity(16384, 13824, 0.99)
+    assert L.fp4_comp_kernel_name(16384, cap) == b"k_comp_block64"
+    assert L.fp4_comp_kernel_name(0, 1) is None

@@ -200,7 +200,7 @@ def test_gemm_accumulator_exact(M, N, K):
 
 # More output tiles than the chip has CUs, ragged in both dimensions, K a multiple of 512: the
 # product then walks several tiles per workgroup (the last two shapes have over 1024 tiles of
-# 256 x 256, so they run on the persistent kernel).  Checked at sampled outputs plus whole
+# 256 x 256, at least two per CU, so they run on the persistent kernel).  Checked at sampled outputs plus whole
 # edge rows and columns.
 @pytest.mark.parametrize("M,N,K,out", [(4200, 4136, 1024, "fp32"), (4352, 4360, 512, "bf16"), (1030, 9000, 2048, "fp32"),
                                        (8192, 8200, 512, "bf16"), (8200, 8192, 1024, "fp32")])
