@@ -1,6 +1,6 @@
 """Benchmark of the FP4 quantized linear forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama7b_gate_up]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload llama7b_gate_up]
 
 A step is one fp4_linear_forward (quantile + clamp + dA, token-wise quantization of A,
 channel-wise quantization of W, FP4 GEMM with dequantization, compensation pass) over one
@@ -109,10 +109,11 @@ def load_traffic(launch_bytes_alg: float):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(A, W, L, rows: int = 32) -> dict:
+def cpu_baseline(A, W, L, rows: int = 256) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload: every
     quantizer step at full size, the accumulator/dequant/compensation on `rows` sampled
-    rows x all N columns, extrapolated linearly to M rows."""
+    rows (the first, the last and seeded others) x all N columns, extrapolated linearly to
+    M rows."""
     import oracle
     from workloads import as_numpy_bits
     Anp, Wnp = as_numpy_bits(A), as_numpy_bits(W)
@@ -123,7 +124,9 @@ def cpu_baseline(A, W, L, rows: int = 32) -> dict:
     Aq, sA = oracle.quant_rows(cl.pop("A_clamped"))
     Wq, sW = oracle.quant_cols(Wnp)
     t1 = time.perf_counter()
-    rs = np.sort(np.random.default_rng(0).choice(M, rows, replace=False))
+    # the first and last rows, and rows - 2 seeded others
+    rest = np.random.default_rng(0).choice(np.arange(1, M - 1), rows - 2, replace=False)
+    rs = np.sort(np.concatenate([[0, M - 1], rest]))
     ms = np.repeat(rs, N).astype(np.int64)
     ns = np.tile(np.arange(N, dtype=np.int64), rows)
     acc = oracle.accumulate_pairs(Aq, Wq, K, ms, ns)
@@ -193,6 +196,30 @@ def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write:
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
+
+
+def mfma_probe(iters: int = 20000) -> dict:
+    """The FP4 matrix-core rate this device sustains with nothing else running (the probe
+    library: one workgroup of four waves per CU, each wave a chain of independent 32x32x64
+    FP4 MFMAs on register operands), and the shader clock its loop ran at (shader-clock
+    counter against the 100 MHz real-time counter)."""
+    L = C.CDLL(os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "libfp4probe.so"))
+    L.fp4_probe_mfma_fp4.restype = C.c_int32
+    L.fp4_probe_mfma_fp4.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clocks = torch.zeros(cus * 4 * 4, dtype=torch.int64, device="cuda")
+    sink = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    run = lambda: L.fp4_probe_mfma_fp4(cus, iters, C.c_void_p(clocks.data_ptr()), C.c_void_p(sink.data_ptr()), st)  # noqa
+    assert run() == 0
+    ms = time_on_stream(run, 3, 1)
+    flops = cus * 4 * iters * 8 * 131072
+    c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
+    ghz = float(np.median((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]) * 0.1))
+    tf = flops / ms / 1e9
+    return {"what": "chains of independent FP4 32x32x64 MFMAs on register operands, one 4-wave workgroup per CU",
+            "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+            "clock_GHz": round(ghz, 3), "peak_at_that_clock_TFLOP/s": round(PEAK_FP4_TFLOPS * ghz / 2.4, 1)}
 
 
 def run_copy(steps: int):
@@ -287,158 +314,183 @@ def run_backward(args):
         "device": torch.cuda.get_device_properties(0).gcnArchName}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama7b_gate_up", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--emu", action="store_true",
-                    help="also time the FP4-on-FP8 emulation of the product (E4M3 expansion + FP8 MFMA) against "
-                         "the native FP4 product on the same codes, both without the dA term")
-    ap.add_argument("--wq", default="per-step", choices=["per-step", "cached", "overlap"],
-                    help="W quantization: inside every forward (the pages' scheme, default); once before the "
-                         "timed steps (fixed inference weights); or on a second stream, each layer's under the "
-                         "previous layer's forward")
-    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic", "fp8codec",
-                                                          "backward"])
-    ap.add_argument("--traffic-dirs", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="--mode traffic: rocprofv3 --pmc output directories of FETCH_SIZE and WRITE_SIZE for "
-                         "the full bench and for --mode copy")
-    args = ap.parse_args()
-    if args.mode == "traffic":
-        write_traffic(*args.traffic_dirs)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this forward is built and "
-              "measured on a single GPU; sharding it over several is a design note, not a run.", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    if args.mode == "copy":
-        run_copy(args.steps)
-        return
-    if args.mode == "fp8codec":
-        run_fp8codec(args.steps, args.warmup)
-        return
-    if args.mode == "backward":
-        run_backward(args)
-        return
+def _rocm_version() -> str | None:
+    try:
+        return open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        return None
 
-    layers = [make_layer(args.workload, li) for li in range(len(WORKLOADS[args.workload].layers))]
-    dev = torch.device("cuda:0")
-    runs = []
-    for A, W, L in layers:
-        Ad, Wd = A.to(dev), W.to(dev)
-        ws = fp4.workspace(Ad, L.N, L.q)
-        Y = torch.empty((L.M, L.N), dtype=torch.bfloat16 if L.out_dtype == "bf16" else torch.float32, device=dev)
-        runs.append((A, W, L, Ad, Wd, ws, Y))
+
+def _smi_clocks() -> str | None:
+    """The current clock levels as rocm-smi reports them (after the timed work), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    lines = [ln.strip() for ln in r.stdout.splitlines() if "clk" in ln.lower() and "(" in ln]
+    return "; ".join(lines[:6]) or None
+
+
+def _pct(xs, p):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), p))
+
+
+def per_step_times(fn, steps: int, warmup: int, nsets: int):
+    """fn(set_index) `steps` times after `warmup` untimed calls, input sets rotated when nsets > 1,
+    with a HIP event on the current stream between consecutive steps.  The timed region is
+    bracketed by device synchronizations.  Returns (per-step ms list, total ms, wall s)."""
+    s = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i % nsets)
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    w0 = time.perf_counter()
+    ev[0].record(s)
+    for i in range(steps):
+        fn(i % nsets)
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)], ev[0].elapsed_time(ev[steps]), wall
 
-    # W's codes and scales, for --wq cached / overlap (per-step quantizes inside the forward)
-    wqs = []
-    for _, _, L, Ad, Wd, ws, Y in runs:
-        wqs.append((torch.empty((L.N, L.K // 2), dtype=torch.uint8, device=dev),
-                    torch.empty(L.N, dtype=torch.float32, device=dev)))
 
-    def quant_w(i):
-        _, _, L, _, Wd, _, _ = runs[i]
-        Wq, sW = wqs[i]
-        fp4._check(fp4.lib().fp4_quantize(fp4._ptr(Wd), fp4._dt(Wd), L.K, L.N, fp4.FP4_PER_COL, None,
-                                          fp4._ptr(Wq), fp4._ptr(sW), fp4._stream(Wd)))
+def _spread(ts: list) -> dict:
+    return {"mean": round(sum(ts) / len(ts), 4), "p10": round(_pct(ts, 10), 4), "p50": round(_pct(ts, 50), 4),
+            "p90": round(_pct(ts, 90), 4), "n": len(ts)}
 
-    def forward_wq(i):
-        _, _, L, Ad, Wd, ws, Y = runs[i]
-        Wq, sW = wqs[i]
-        fp4.linear_forward_wq(Ad, Wd, Wq, sW, L.q, ws=ws, Y=Y)
 
-    main = torch.cuda.current_stream()
+def run_full(args):
+    """The whole forward, per layer of the workload, over inputs resident in HBM: cold-cache
+    steps (two input sets rotated, together larger than the 256 MB memory-side cache) are the
+    primary number; hot-cache steps (one set) and the per-stage breakdown follow."""
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    nsets = 1 if args.hot_only else 2
+    sets, host0 = [], []
+    for r in range(nsets):
+        layers = []
+        for li in range(len(wl.layers)):
+            A, W, L = make_layer(args.workload, li, replica=r)
+            if r == 0:
+                host0.append((A, W, L))
+            Ad, Wd = A.to(dev), W.to(dev)
+            layers.append(dict(A=Ad, W=Wd, L=L, ws=fp4.workspace(Ad, L.N, L.q),
+                               Y=torch.empty((L.M, L.N), dtype=torch.bfloat16 if L.out_dtype == "bf16" else torch.float32,
+                                             device=dev)))
+            if args.wq != "per-step":
+                layers[-1]["Wq"], layers[-1]["sW"] = fp4.quantize_weights(Wd)
+        sets.append(layers)
+    torch.cuda.synchronize()
+    main_s = torch.cuda.current_stream()
     side = torch.cuda.Stream(device=dev)  # default priority
-    if args.wq == "cached":
-        for i in range(len(runs)):
-            quant_w(i)
 
-    def step():
+    def forward(si: int):
+        layers = sets[si]
         if args.wq == "per-step":
-            for _, _, L, Ad, Wd, ws, Y in runs:
-                fp4.linear_forward(Ad, Wd, L.q, ws=ws, Y=Y)
+            for d in layers:
+                fp4.linear_forward(d["A"], d["W"], d["L"].q, ws=d["ws"], Y=d["Y"])
         elif args.wq == "cached":
-            for i in range(len(runs)):
-                forward_wq(i)
-        else:  # overlap: W of layer i+1 is quantized on a second stream under layer i's forward
-            side.wait_stream(main)
+            for d in layers:
+                fp4.linear_forward_wq(d["A"], d["W"], d["Wq"], d["sW"], d["L"].q, ws=d["ws"], Y=d["Y"])
+        else:  # overlap: every layer's W quantized on a second stream, each forward waits for its own
+            side.wait_stream(main_s)
             ready = []
             with torch.cuda.stream(side):
-                for i in range(len(runs)):
-                    quant_w(i)
+                for d in layers:
+                    fp4._check(fp4.lib().fp4_quantize(fp4._ptr(d["W"]), fp4._dt(d["W"]), d["L"].K, d["L"].N,
+                                                      fp4.FP4_PER_COL, None, fp4._ptr(d["Wq"]), fp4._ptr(d["sW"]),
+                                                      fp4._stream(d["W"])))
                     ev = torch.cuda.Event()
                     ev.record(side)
                     ready.append(ev)
-            for i in range(len(runs)):
-                main.wait_event(ready[i])
-                forward_wq(i)
+            for d, ev in zip(layers, ready):
+                main_s.wait_event(ev)
+                fp4.linear_forward_wq(d["A"], d["W"], d["Wq"], d["sW"], d["L"].q, ws=d["ws"], Y=d["Y"])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    e0.record(s)
-    for _ in range(args.steps):
-        step()
-    e1.record(s)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    flops = sum(L.flops for _, _, L, *_ in runs)
-
+    flops = sum(d["L"].flops for d in sets[0])
+    cold, cold_total, wall = per_step_times(forward, args.steps, args.warmup, nsets)
+    ms_step = cold_total / args.steps
     if args.mode == "forward":
         print(json.dumps({"ms_per_step": ms_step}))
         return
+    hot, hot_total, _ = per_step_times(forward, args.steps, args.warmup, 1)
 
-    # The dominant kernel (the GEMM) alone, as the forward launches it: the two-byte
-    # accumulator hand-over (FP4_Q16, with its escape pass, which finds no tile to redo on these
-    # inputs).  Then GEMM + compensation pass together, the pass's time being the difference.
-    gemm_ms, comp_ms, qbytes, cbytes, nnz_total = 0.0, 0.0, 0, 0, 0
+    # the stages of the forward, each between events of its own (hot cache, set 0): the A-side
+    # quantizer, the W-side quantizer, the product (GEMM + escape pass + compensation)
+    names = ("quant_A", "quant_W", "product")
+    stage_ms = {k: [] for k in names}
+
+    def staged(_si: int):
+        rec = []
+        for d in sets[0]:
+            L = d["L"]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(main_s)
+            fp4.forward_quantize(d["A"], None, L.M, L.K, L.N, d["A"].dtype, L.q, d["ws"], stages=fp4.FP4_STAGE_A)
+            ev[1].record(main_s)
+            if args.wq == "per-step":
+                fp4.forward_quantize(None, d["W"], L.M, L.K, L.N, d["A"].dtype, L.q, d["ws"], stages=fp4.FP4_STAGE_W)
+            ev[2].record(main_s)
+            if args.wq == "per-step":
+                fp4.forward_product(d["W"], L.M, L.q, d["ws"], d["Y"])
+            else:
+                fp4.linear_forward_wq(d["A"], d["W"], d["Wq"], d["sW"], L.q, ws=d["ws"], Y=d["Y"])  # not split
+            ev[3].record(main_s)
+            rec.append(ev)
+        staged.last.append(rec)
+    staged.last = []
+    per_step_times(staged, args.steps, args.warmup, 1)
+    for rec in staged.last[args.warmup:]:
+        for k, nm in enumerate(names):
+            stage_ms[nm].append(sum(ev[k].elapsed_time(ev[k + 1]) for ev in rec))
+    quant_a_ms = float(np.median(stage_ms["quant_A"]))
+    quant_w_ms = float(np.median(stage_ms["quant_W"]))
+    product_ms = float(np.median(stage_ms["product"]))
+
+    # the dominant kernel alone, as the forward launches it: the GEMM with the two-byte
+    # accumulator hand-over (FP4_Q16) and its escape pass (which finds no tile to redo here)
+    gemm_ms, nnz_total, qa_bytes, qw_bytes, cbytes = 0.0, 0, 0, 0, 0
     per_layer = []
-    for A, W, L, Ad, Wd, ws, Y in runs:
-        it = fp4.forward_intermediates(ws, L.M, L.K, L.N, A.dtype, L.q)
-        lay = fp4.forward_layout(L.M, L.K, L.N, A.dtype, L.q)
+    for d in sets[0]:
+        L, Ad, Wd, ws, Y = d["L"], d["A"], d["W"], d["ws"], d["Y"]
+        it = fp4.forward_intermediates(ws, L.M, L.K, L.N, Ad.dtype, L.q)
         nnz = int(it["nnz"].item())
         qb = fp4.lib().fp4_gemm_workspace_bytes(L.M, L.N, fp4.FP4_Q16, 0)
-        cb = fp4.lib().fp4_gemm_workspace_bytes(L.M, L.N, fp4._dt(Y), 1)
-        hand = ws[lay.handoff:lay.handoff + max(qb, cb)]
-        assert hand.numel() == max(qb, cb), "workspace has no hand-over region"
-        yq = torch.empty((L.M, L.N), dtype=torch.int16, device=Ad.device)
-        common = (fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K)
+        hand = torch.empty(qb, dtype=torch.uint8, device=dev)
+        yq = torch.empty((L.M, L.N), dtype=torch.int16, device=dev)
         g = lambda: fp4.lib().fp4_gemm(  # noqa: E731
-            *common, None, None, None, 0, None, fp4._dt(Wd), fp4._ptr(yq), fp4.FP4_Q16, None, fp4._ptr(hand), qb,
-            fp4._stream(Ad))
-        gc = lambda: fp4.lib().fp4_gemm(  # noqa: E731
-            *common, fp4._ptr(it["row_ptr"]), fp4._ptr(it["coo_col"]), fp4._ptr(it["coo_val"]), lay.capacity,
-            fp4._ptr(Wd),
-            fp4._dt(Wd), fp4._ptr(Y), fp4._dt(Y), None, fp4._ptr(hand), cb, fp4._stream(Ad))
+            fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K, None, None,
+            None, 0, None, fp4._dt(Wd), fp4._ptr(yq), fp4.FP4_Q16, None, fp4._ptr(hand), qb, fp4._stream(Ad))
         ms_g = time_on_stream(g, args.steps, 2)
-        ms_c = max(time_on_stream(gc, args.steps, 2) - ms_g, 1e-9)
+        del hand, yq
         gemm_ms += ms_g
-        comp_ms += ms_c
-        qb = quantizer_bytes(L.M, L.K, L.N, b_in(A.dtype), nnz, with_w=args.wq != "cached")
-        cb = comp_bytes(L.M, L.N, Y.element_size(), nnz)
-        qbytes += qb
-        cbytes += cb
         nnz_total += nnz
+        bi = b_in(Ad.dtype)
+        qa_bytes += quantizer_bytes(L.M, L.K, L.N, bi, nnz, with_w=False)
+        qw_bytes += quantizer_bytes(L.M, L.K, L.N, bi, nnz) - quantizer_bytes(L.M, L.K, L.N, bi, nnz, with_w=False)
+        cbytes += comp_bytes(L.M, L.N, Y.element_size(), nnz)
         per_layer.append({"layer": L.name, "M": L.M, "K": L.K, "N": L.N, "q": L.q, "nnz": nnz,
-                          "gemm_ms": round(ms_g, 4), "gemm_TFLOP/s": round(L.flops / ms_g / 1e9, 1),
-                          "comp_ms": round(ms_c, 4), "comp_GB/s": round(cb / ms_c / 1e6, 1)})
-
-    quant_ms = max(ms_step - gemm_ms - comp_ms, 1e-9)
+                          "gemm_kernel": gemm_kernel(L.M, L.N, L.K), "gemm_ms": round(ms_g, 4),
+                          "gemm_TFLOP/s": round(L.flops / ms_g / 1e9, 1),
+                          "comp_kernel": fp4.comp_kernel_name(L.M, fp4.outlier_capacity(L.M, L.K, L.q))})
+    if args.wq != "per-step":
+        qw_bytes = 0
+    comp_ms = max(product_ms - gemm_ms, 1e-9)
+    quant_ms = quant_a_ms + quant_w_ms
     gemm_tflops = flops / gemm_ms / 1e9
     fwd_tflops = flops / ms_step / 1e9
-    quant_gbs = qbytes / quant_ms / 1e6
-    first = runs[0][2]
+    first = sets[0][0]["L"]
     traffic = load_traffic(None) if args.workload == "llama7b_gate_up" else None
-    name = first.name if len(runs) == 1 else f"{args.workload}(x{len(runs)} layers)"
+    name = first.name if len(sets[0]) == 1 else f"{args.workload}(x{len(sets[0])} layers)"
+    sha = hashlib.sha256()
+    for A, W, _ in host0:
+        sha.update(A.contiguous().view(torch.uint8).numpy().tobytes() if A.dtype != torch.bfloat16
+                   else A.contiguous().view(torch.int16).numpy().tobytes())
+        sha.update(W.contiguous().view(torch.int16).numpy().tobytes() if W.dtype == torch.bfloat16
+                   else W.contiguous().numpy().tobytes())
+    hbm = lambda b, ms: {"achieved": round(b / ms / 1e6, 1), "frac": round(b / ms / 1e6 / PEAK_HBM_GBS, 4),  # noqa
+                         "ms": round(ms, 4), "algorithmic_bytes": b}
     out = {
         "metric": METRIC,
         "value": round(fwd_tflops, 2),
@@ -453,27 +505,40 @@ def main():
         "dtype": "fp4e2m1 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": name, "M": first.M, "K": first.K, "N": first.N, "in_dtype": first.dtype,
-                   "out_dtype": first.out_dtype, "q": first.q, "layers": len(runs), "w_quant": args.wq,
+                   "out_dtype": first.out_dtype, "q": first.q, "layers": len(sets[0]), "w_quant": args.wq,
                    "parallelism": "none (1 GPU)"},
+        "timing": {"primary": "cold" if nsets == 2 else "hot",
+                   "cold": dict(_spread(cold), what="two seeded input sets rotated step by step (inputs not "
+                                                     "cache-resident); value and ms_per_step are this mean"),
+                   "hot": dict(_spread(hot), what="one input set repeated"),
+                   "hot_TFLOP/s": round(flops / (hot_total / args.steps) / 1e9, 2)},
         "forward_frac_of_fp4_peak": round(fwd_tflops / PEAK_FP4_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": gemm_kernel(first.M, first.N, first.K), "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(gemm_ms, 4)},
-        "compensation": {"bound": "hbm", "kernel": fp4.comp_kernel_name(first.M, fp4.outlier_capacity(first.M, first.K, first.q)), "achieved": round(cbytes / comp_ms / 1e6, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(cbytes / comp_ms / 1e6 / PEAK_HBM_GBS, 4),
-                         "ms": round(comp_ms, 4), "algorithmic_bytes": cbytes},
-        "quantizer": {"bound": "hbm", "achieved": round(quant_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                      "frac": round(quant_gbs / PEAK_HBM_GBS, 4), "ms": round(quant_ms, 4),
-                      "algorithmic_bytes": qbytes},
+        "stages_hot_ms": {"quant_A": round(quant_a_ms, 4), "quant_W": round(quant_w_ms, 4),
+                          "product": round(product_ms, 4), "gemm": round(gemm_ms, 4)},
+        "compensation": dict({"bound": "hbm", "kernel": per_layer[0]["comp_kernel"], "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "how": "product stage minus the GEMM launch, both timed directly"},
+                             **hbm(cbytes, comp_ms)),
+        "quantizer": dict({"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "how": "A-side and W-side stage calls, each between events of its own",
+                           "A": hbm(qa_bytes, quant_a_ms),
+                           "W": hbm(qw_bytes, quant_w_ms) if qw_bytes else None},
+                          **hbm(qa_bytes + qw_bytes, quant_ms)),
         "nnz": nnz_total,
         "layers": per_layer,
         "wall_s_timed": round(wall, 3),
-        "device": torch.cuda.get_device_properties(0).gcnArchName,
+        "env": {"device": torch.cuda.get_device_properties(0).gcnArchName, "rocm": _rocm_version(),
+                "torch": torch.__version__, "input_sha256": sha.hexdigest(), "smi_clocks_after": _smi_clocks()},
     }
+    if not args.no_probe:
+        out["mfma_probe"] = mfma_probe()
     if args.emu:
         emu_ms = nat_ms = 0.0
-        for A, W, L, Ad, Wd, ws, Y in runs:
-            it = fp4.forward_intermediates(ws, L.M, L.K, L.N, A.dtype, L.q)
+        for d in sets[0]:
+            L, Ad, Wd, ws, Y = d["L"], d["A"], d["W"], d["ws"], d["Y"]
+            it = fp4.forward_intermediates(ws, L.M, L.K, L.N, Ad.dtype, L.q)
             common = (fp4._ptr(it["Aq"]), fp4._ptr(it["sA"]), fp4._ptr(it["Wq"]), fp4._ptr(it["sW"]), L.M, L.N, L.K)
             ews = torch.empty(fp4.lib().fp4_gemm_fp8emu_workspace_bytes(L.M, L.N, L.K), dtype=torch.uint8, device=dev)
             emu = lambda: fp4.lib().fp4_gemm_fp8emu(  # noqa: E731
@@ -492,9 +557,54 @@ def main():
             "emulated_frac_of_fp8_peak": round(flops / emu_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
             "speedup_native": round(emu_ms / nat_ms, 3)}
     if not args.no_cpu_baseline:
-        A, W, L = runs[0][0], runs[0][1], runs[0][2]
+        A, W, L = host0[0]
         out["cpu_baseline"] = cpu_baseline(A, W, L)
     print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_gate_up", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the matrix-core issue-rate probe")
+    ap.add_argument("--hot-only", action="store_true", help="one input set only (no cold-cache rotation)")
+    ap.add_argument("--emu", action="store_true",
+                    help="also time the FP4-on-FP8 emulation of the product (E4M3 expansion + FP8 MFMA) against "
+                         "the native FP4 product on the same codes, both without the dA term")
+    ap.add_argument("--wq", default="per-step", choices=["per-step", "cached", "overlap"],
+                    help="W quantization: inside every forward (the pages' scheme, default); once before the "
+                         "timed steps (fixed inference weights); or on a second stream, each layer's under the "
+                         "previous layer's forward")
+    ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic", "fp8codec",
+                                                          "backward", "mfma-peak"])
+    ap.add_argument("--traffic-dirs", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="--mode traffic: rocprofv3 --pmc output directories of FETCH_SIZE and WRITE_SIZE for "
+                         "the full bench and for --mode copy")
+    args = ap.parse_args()
+    if args.mode == "traffic":
+        write_traffic(*args.traffic_dirs)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this forward is built and "
+              "measured on a single GPU; sharding it over several is a design note, not a run.", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.mode == "copy":
+        run_copy(args.steps)
+        return
+    if args.mode == "fp8codec":
+        run_fp8codec(args.steps, args.warmup)
+        return
+    if args.mode == "mfma-peak":
+        print(json.dumps(mfma_probe()))
+        return
+    if args.mode == "backward":
+        run_backward(args)
+        return
+    run_full(args)
 
 
 if __name__ == "__main__":

@@ -225,6 +225,26 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
                               int64_t K, int64_t N, double q, void *Y, int32_t y_dtype,
                               void *workspace, size_t ws_bytes, void *stream);
 
+/* The forward in two stage calls, for callers that time or schedule the stages apart:
+ * fp4_linear_forward(A, W, ...) enqueues exactly fp4_forward_quantize(A, W, ..., FP4_STAGE_A |
+ * FP4_STAGE_W, ...) followed by fp4_forward_product(W, ...) on the same workspace.
+ * fp4_forward_quantize: the quantizer stages, results in the workspace at the fp4_forward_layout
+ *   offsets.  stages is a mask: FP4_STAGE_A = quantile, clamp and dA of A (T, nnz, row_ptr, the
+ *   COO list) and the token-wise codes and scales of A_clamped (QbitAI report, outlier,
+ *   granularity and forward-quantization paragraphs); FP4_STAGE_W = the channel-wise codes and
+ *   scales of W (granularity paragraph).  A (resp. W) may be NULL when its stage is not asked
+ *   for.  Run apart, the W stage takes one more (zero-fill) launch than inside the forward.
+ * fp4_forward_product: the FP4 GEMM with dequantization and the compensation dA . W (GEMM-kernel
+ *   and outlier paragraphs) from the workspace's intermediates (both stages must have run on it
+ *   for the same A, W, q) into Y (M x N of y_dtype); W is the original weight.
+ * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE (also: unknown stage bits),QUANTILE,WORKSPACE,
+ * ALIGN,DEVICE,HIP}. */
+enum { FP4_STAGE_A = 1, FP4_STAGE_W = 2 };
+fp4_status fp4_forward_quantize(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N,
+                                double q, int32_t stages, void *workspace, size_t ws_bytes, void *stream);
+fp4_status fp4_forward_product(const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N, double q, void *Y,
+                               int32_t y_dtype, void *workspace, size_t ws_bytes, void *stream);
+
 /* The same forward with W already quantized: Wq and sW as fp4_quantize(W, FP4_PER_COL)
  * produced them (N x K/2 codes, fp32[N] scales) while W is unchanged, as when the weights
  * of an inference layer are fixed.  The QbitAI report quantizes W at every forward

@@ -24,11 +24,12 @@ LIB_PATH = os.path.join(_HERE, "libfp4lin.so")
 FP4_F32, FP4_BF16 = 0, 1
 FP4_Q16 = 2  # fp4_gemm output only: int16 4*acc with fp32 escapes in the workspace
 FP4_PER_ROW, FP4_PER_COL = 0, 1
+FP4_STAGE_A, FP4_STAGE_W = 1, 2
 
 EXPORTS = (
     "fp4_quantize", "fp4_outlier_capacity", "fp4_outlier_workspace_bytes", "fp4_outlier_clamp",
     "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_forward_layout", "fp4_forward_workspace_bytes", "fp4_linear_forward",
-    "fp4_linear_forward_wq", "fp4_gemm_fp8emu_workspace_bytes", "fp4_gemm_fp8emu",
+    "fp4_linear_forward_wq", "fp4_forward_quantize", "fp4_forward_product", "fp4_gemm_fp8emu_workspace_bytes", "fp4_gemm_fp8emu",
     "fp4_fp8_workspace_bytes", "fp4_fp8_quantize", "fp4_fp8_dequantize",
     "fp4_backward_layout", "fp4_backward_workspace_bytes", "fp4_linear_backward",
     "fp4_gemm_kernel_name", "fp4_comp_kernel_name", "fp4_status_string",
@@ -71,6 +72,8 @@ def lib():
         "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, dbl]),
         "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_linear_forward_wq": (i32, [vp, vp, vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
+        "fp4_forward_quantize": (i32, [vp, vp, i32, i64, i64, i64, dbl, i32, vp, sz, vp]),
+        "fp4_forward_product": (i32, [vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_gemm_fp8emu_workspace_bytes": (sz, [i64, i64, i64]),
         "fp4_fp8_workspace_bytes": (sz, []),
         "fp4_fp8_quantize": (i32, [vp, i32, i64, vp, vp, vp, sz, vp]),
@@ -287,6 +290,25 @@ def linear_forward(A: torch.Tensor, W: torch.Tensor, q: float, out_dtype: torch.
         Y = torch.empty((M, N), dtype=out_dtype, device=A.device)
     _check(lib().fp4_linear_forward(_ptr(A), _ptr(W), _dt(A), M, K, N, float(q), _ptr(Y), _dt(Y), _ptr(ws),
                                     ws.numel(), _stream(A)))
+    return Y
+
+
+def forward_quantize(A: torch.Tensor | None, W: torch.Tensor | None, M: int, K: int, N: int, dtype: torch.dtype,
+                     q: float, ws: torch.Tensor, stages: int = FP4_STAGE_A | FP4_STAGE_W):
+    """The forward's quantizer stages (FP4_STAGE_A and/or FP4_STAGE_W) into the workspace."""
+    _need_cuda(A, W, ws)
+    dt = FP4_BF16 if dtype == torch.bfloat16 else FP4_F32
+    ref = A if A is not None else W
+    _check(lib().fp4_forward_quantize(_ptr(A), _ptr(W), dt, M, K, N, float(q), stages, _ptr(ws), ws.numel(),
+                                      _stream(ref)))
+
+
+def forward_product(W: torch.Tensor, M: int, q: float, ws: torch.Tensor, Y: torch.Tensor):
+    """The forward's product stage (GEMM, dequantization, compensation) from the workspace."""
+    _need_cuda(W, ws, Y)
+    K, N = W.shape
+    _check(lib().fp4_forward_product(_ptr(W), _dt(W), M, K, N, float(q), _ptr(Y), _dt(Y), _ptr(ws), ws.numel(),
+                                     _stream(W)))
     return Y
 
 

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "fp4_host.h"
 #include "fp4_launch.h"
 #include "fp4lin.h"
 
@@ -75,14 +76,20 @@ int64_t capacity_of(int64_t M, int64_t K, double q) {
     return n - 1 - k;
 }
 
+}  // namespace
+
+// ----------------------------------------------------------------------------- shared host helpers
+// (declared in fp4_host.h; the no-alloc entry point in noalloc.hip uses them too)
+namespace fp4 {
+
 // The current device must be gfx950; its CU count sizes the histogram grid.
 struct DevInfo {
     bool known = false;
     bool ok = false;
     int cus = 0;
 };
-std::mutex g_dev_mu;
-DevInfo g_dev[64];
+static std::mutex g_dev_mu;
+static DevInfo g_dev[64];
 
 fp4_status device_check(int *cus) {
     int d = 0;
@@ -100,12 +107,6 @@ fp4_status device_check(int *cus) {
     *cus = info.cus;
     return FP4_OK;
 }
-
-// Scratch of one outlier pass.  [state, hist, hist_lo) is zero-filled per call.
-struct OutlierWs {
-    size_t state, hist, hist_lo, zero_end, rowmax, row_cnt, slots, total;
-    int32_t S;  // staging slots per row
-};
 
 // Slots per row: twice the mean outlier count per row that the capacity bound allows plus
 // a margin, at least 128 (rows vary widely: with log-normal row scales a few rows hold a
@@ -140,8 +141,9 @@ OutlierWs outlier_ws(int64_t M, int64_t K, int32_t dtype, int64_t cap) {
 
 fp4_status hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
 
-// Enqueue the outlier pass: zero, histogram + row maxima, select T, then rows (clamp,
-// optional codes, staging of dA), then the COO scan + scatter.
+// Enqueue the outlier pass: zero (with zero2[0..n_zero2) in the same launch), histogram + row
+// maxima with the select of T in its last workgroup (a second histogram level for fp32), then
+// rows (clamp, optional codes, staging of dA), then the COO list.
 fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, double q, uint8_t *ws,
                         const OutlierWs &w, int cus, float *T, int32_t *coo_row, int32_t *coo_col,
                         float *coo_val, int64_t cap, int32_t *row_ptr, int64_t *nnz, uint8_t *Aq,
@@ -159,8 +161,8 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     const uint64_t k = (uint64_t)std::floor(q * (double)(n - 1));
     hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(ws + w.state), (int64_t)(w.zero_end - w.state) / 4, zero2,
                                n_zero2, s);
-    if (e == hipSuccess) e = launch_hist_rowmax(A, dt, M, K, hist, rowmax, cus, s);
-    if (e == hipSuccess) e = launch_select(A, dt, n, hist, hist_lo, st, T, k, s);
+    if (e == hipSuccess) e = launch_hist_rowmax(A, dt, M, K, hist, rowmax, st, T, k, cus, s);
+    if (e == hipSuccess && dt == DT_F32) e = launch_select_lo(A, n, hist_lo, st, T, s);
     const bool codes = Aq != nullptr;
     if (e == hipSuccess)
         e = launch_quant_rows(A, dt, M, K, codes ? rowmax : nullptr, T, Aq, sA, row_cnt, stg, st,
@@ -170,9 +172,102 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     return hip_status(e);
 }
 
-}  // namespace
+fp4_status outlier_args_check(const void *A, int32_t a_dtype, int64_t M, int64_t K, double q, const float *T,
+                              const int32_t *coo_row, const int32_t *coo_col, const float *coo_val, int64_t capacity,
+                              const int32_t *row_ptr, const int64_t *nnz) {
+    if (!A || !T || !coo_row || !coo_col || !coo_val || !row_ptr || !nnz) return FP4_ERR_NULL;
+    if (!dtype_ok(a_dtype)) return FP4_ERR_DTYPE;
+    if (!mk_ok(M, K)) return FP4_ERR_SHAPE;
+    if (!q_ok(q)) return FP4_ERR_QUANTILE;
+    const int64_t cap = capacity_of(M, K, q);
+    if (cap > COO_MAX) return FP4_ERR_QUANTILE;
+    if (capacity < cap) return FP4_ERR_CAPACITY;
+    if (!aligned16(A) || !aligned16(T) || !aligned16(row_ptr)) return FP4_ERR_ALIGN;
+    return FP4_OK;
+}
+
+fp4_status outlier_clamp_impl(const void *A, int32_t a_dtype, int64_t M, int64_t K, double q, float *T,
+                              int32_t *coo_row, int32_t *coo_col, float *coo_val, int64_t capacity, int32_t *row_ptr,
+                              int64_t *nnz, void *workspace, size_t ws_bytes, void *stream) {
+    fp4_status st = outlier_args_check(A, a_dtype, M, K, q, T, coo_row, coo_col, coo_val, capacity, row_ptr, nnz);
+    if (st != FP4_OK) return st;
+    if (!workspace) return FP4_ERR_NULL;
+    const int64_t cap = capacity_of(M, K, q);
+    const OutlierWs w = outlier_ws(M, K, a_dtype, cap);
+    if (ws_bytes < w.total) return FP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP4_ERR_ALIGN;
+    int cus;
+    st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    // nnz <= cap always (T is the (k+1)-th smallest |a|), so the staging area and the COO
+    // positions are bounded by the computed cap, which the workspace was sized for.
+    return run_outliers(A, a_dtype, M, K, q, static_cast<uint8_t *>(workspace), w, cus, T, coo_row, coo_col, coo_val,
+                        cap, row_ptr, nnz, nullptr, nullptr, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
+}
+
+int64_t outlier_capacity_of(int64_t M, int64_t K, double q) { return capacity_of(M, K, q); }
+
+}  // namespace fp4
 
 namespace {
+// Checks shared by the forward's calls; fills the layout and the CU count.
+fp4_status forward_check(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q, size_t ws_bytes,
+                         const void *workspace, fp4_ws_layout *l, int *cus) {
+    if (!workspace) return FP4_ERR_NULL;
+    if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
+    fp4_status st = fp4_forward_layout(M, K, N, in_dtype, q, l);
+    if (st != FP4_OK) return st;
+    if (ws_bytes < l->total) return FP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP4_ERR_ALIGN;
+    return FP4_OK;
+}
+
+// The forward's quantizer stages into the workspace: FP4_STAGE_A (quantile, clamp, dA, A's
+// codes and scales) and/or FP4_STAGE_W (W's codes and scales).  W's column-maximum keys follow
+// the outlier scratch; they are zeroed in the outlier pass's zero launch when both stages run
+// in one call, else by a launch of their own.
+fp4_status quantize_impl(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N, double q,
+                         int32_t stages, uint8_t *ws, const fp4_ws_layout &l, int cus, hipStream_t s) {
+    const OutlierWs w = outlier_ws(M, K, in_dtype, l.capacity);
+    uint32_t *wkeys = reinterpret_cast<uint32_t *>(ws + l.scratch + w.total);
+    const bool sa = stages & FP4_STAGE_A, sw = stages & FP4_STAGE_W;
+    if (sa) {
+        fp4_status st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, reinterpret_cast<float *>(ws + l.T),
+                                     reinterpret_cast<int32_t *>(ws + l.coo_row),
+                                     reinterpret_cast<int32_t *>(ws + l.coo_col), reinterpret_cast<float *>(ws + l.coo_val),
+                                     l.capacity, reinterpret_cast<int32_t *>(ws + l.row_ptr),
+                                     reinterpret_cast<int64_t *>(ws + l.nnz), ws + l.Aq,
+                                     reinterpret_cast<float *>(ws + l.sA), sw ? wkeys : nullptr, sw ? N : 0, s);
+        if (st != FP4_OK) return st;
+    }
+    if (sw) {
+        hipError_t e = hipSuccess;
+        if (!sa) e = launch_zero(wkeys, N, nullptr, 0, s);
+        if (e == hipSuccess)
+            e = launch_quant_cols(W, dt_of(in_dtype), K, N, reinterpret_cast<float *>(wkeys), ws + l.Wq, true, s, nullptr,
+                                  reinterpret_cast<float *>(ws + l.sW));
+        return hip_status(e);
+    }
+    return FP4_OK;
+}
+
+// The product stage: the accumulator as int16 4*acc (into a bf16 Y itself, else into the
+// workspace) with fp32 escapes (into the workspace, else into the fp32 Y), then
+// Y = Y_main + dA . W from the workspace's intermediates; Wq/sW: W's codes and scales (the
+// workspace's, or a caller's cached ones).
+fp4_status product_impl(const void *W, int32_t in_dtype, const uint8_t *Wq, const float *sW, int64_t M, int64_t K,
+                        int64_t N, void *Y, int32_t y_dtype, uint8_t *ws, const fp4_ws_layout &l, hipStream_t s) {
+    const Q16Bufs b = q16_buffers(Y, y_dtype, ws + l.handoff, M, N);
+    const uint8_t *Aq = ws + l.Aq;
+    const float *sA = reinterpret_cast<const float *>(ws + l.sA);
+    hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, nullptr, s, false, b.esc, b.flags);
+    if (e == hipSuccess)
+        e = launch_comp(b.yq, b.esc, sA, sW, Y, dt_of(y_dtype), M, N, K, reinterpret_cast<const int32_t *>(ws + l.row_ptr),
+                        reinterpret_cast<const int32_t *>(ws + l.coo_col), reinterpret_cast<const float *>(ws + l.coo_val),
+                        W, dt_of(in_dtype), l.capacity, s);
+    return hip_status(e);
+}
+
 // The forward; Wq_in/sW_in: W's codes and scales from an earlier fp4_quantize (W unchanged
 // since), or NULL to quantize W here.
 fp4_status forward_impl(const void *A, const void *W, const uint8_t *Wq_in, const float *sW_in, int32_t in_dtype,
@@ -181,44 +276,19 @@ fp4_status forward_impl(const void *A, const void *W, const uint8_t *Wq_in, cons
     if (!A || !W || !Y || !workspace) return FP4_ERR_NULL;
     if (!dtype_ok(in_dtype) || !dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
     fp4_ws_layout l;
-    fp4_status st = fp4_forward_layout(M, K, N, in_dtype, q, &l);
-    if (st != FP4_OK) return st;
-    if (ws_bytes < l.total) return FP4_ERR_WORKSPACE;
-    if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || !aligned16(workspace)) return FP4_ERR_ALIGN;
     int cus;
+    fp4_status st = forward_check(M, K, N, in_dtype, q, ws_bytes, workspace, &l, &cus);
+    if (st != FP4_OK) return st;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(Y)) return FP4_ERR_ALIGN;
     st = device_check(&cus);
     if (st != FP4_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    float *T = reinterpret_cast<float *>(ws + l.T);
-    int64_t *nnz = reinterpret_cast<int64_t *>(ws + l.nnz);
-    int32_t *row_ptr = reinterpret_cast<int32_t *>(ws + l.row_ptr);
-    int32_t *coo_row = reinterpret_cast<int32_t *>(ws + l.coo_row);
-    int32_t *coo_col = reinterpret_cast<int32_t *>(ws + l.coo_col);
-    float *coo_val = reinterpret_cast<float *>(ws + l.coo_val);
-    uint8_t *Aq = ws + l.Aq;
-    float *sA = reinterpret_cast<float *>(ws + l.sA);
     const bool wq_given = Wq_in != nullptr;
-    const uint8_t *Wq = wq_given ? Wq_in : ws + l.Wq;
-    const float *sW = wq_given ? sW_in : reinterpret_cast<float *>(ws + l.sW);
-    uint32_t *sW_keys = reinterpret_cast<uint32_t *>(ws + l.sW);  // column-max keys, then scales
-    const OutlierWs w = outlier_ws(M, K, in_dtype, l.capacity);
-    // the column-maximum keys of W (kept in the sW region) are zeroed with the outlier scratch
-    st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, T, coo_row, coo_col, coo_val, l.capacity,
-                      row_ptr, nnz, Aq, sA, wq_given ? nullptr : sW_keys, wq_given ? 0 : N, s);
+    st = quantize_impl(A, W, in_dtype, M, K, N, q, wq_given ? FP4_STAGE_A : FP4_STAGE_A | FP4_STAGE_W, ws, l, cus, s);
     if (st != FP4_OK) return st;
-    hipError_t e = hipSuccess;
-    if (!wq_given)
-        e = launch_quant_cols(W, dt_of(in_dtype), K, N, reinterpret_cast<float *>(sW_keys), ws + l.Wq, true, s);
-    // The accumulator as int16 4*acc (into a bf16 Y itself, else into the workspace) with
-    // fp32 escapes (into the workspace, else into the fp32 Y), then Y = Y_main + dA . W
-    const Q16Bufs b = q16_buffers(Y, y_dtype, ws + l.handoff, M, N);
-    if (e == hipSuccess)
-        e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, nullptr, s, false, b.esc, b.flags);
-    if (e == hipSuccess)
-        e = launch_comp(b.yq, b.esc, sA, sW, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(in_dtype),
-                        l.capacity, s);
-    return hip_status(e);
+    return product_impl(W, in_dtype, wq_given ? Wq_in : ws + l.Wq,
+                        wq_given ? sW_in : reinterpret_cast<const float *>(ws + l.sW), M, K, N, Y, y_dtype, ws, l, s);
 }
 
 }  // namespace
@@ -275,23 +345,8 @@ size_t fp4_outlier_workspace_bytes(int64_t M, int64_t K, int32_t a_dtype, double
 fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t K, double q, float *T,
                              int32_t *coo_row, int32_t *coo_col, float *coo_val, int64_t capacity,
                              int32_t *row_ptr, int64_t *nnz, void *workspace, size_t ws_bytes, void *stream) {
-    if (!A || !T || !coo_row || !coo_col || !coo_val || !row_ptr || !nnz || !workspace) return FP4_ERR_NULL;
-    if (!dtype_ok(a_dtype)) return FP4_ERR_DTYPE;
-    if (!mk_ok(M, K)) return FP4_ERR_SHAPE;
-    if (!q_ok(q)) return FP4_ERR_QUANTILE;
-    const int64_t cap = capacity_of(M, K, q);
-    if (cap > COO_MAX) return FP4_ERR_QUANTILE;
-    if (capacity < cap) return FP4_ERR_CAPACITY;
-    const OutlierWs w = outlier_ws(M, K, a_dtype, cap);
-    if (ws_bytes < w.total) return FP4_ERR_WORKSPACE;
-    if (!aligned16(A) || !aligned16(workspace) || !aligned16(T) || !aligned16(row_ptr)) return FP4_ERR_ALIGN;
-    int cus;
-    fp4_status st = device_check(&cus);
-    if (st != FP4_OK) return st;
-    // nnz <= cap always (T is the (k+1)-th smallest |a|), so the staging area and the COO
-    // positions are bounded by the computed cap, which the workspace was sized for.
-    return run_outliers(A, a_dtype, M, K, q, static_cast<uint8_t *>(workspace), w, cus, T, coo_row, coo_col,
-                        coo_val, cap, row_ptr, nnz, nullptr, nullptr, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
+    return fp4::outlier_clamp_impl(A, a_dtype, M, K, q, T, coo_row, coo_col, coo_val, capacity, row_ptr, nnz,
+                                   workspace, ws_bytes, stream);
 }
 
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t with_comp) {
@@ -429,7 +484,7 @@ fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype,
     out->Wq = off; off += align_up((size_t)N * (size_t)(K / 2));
     out->sW = off; off += align_up((size_t)N * 4);
     out->handoff = off; off += q16_ws_bytes(M, N, FP4_BF16);  // the larger of the two hand-overs
-    out->scratch = off; off += outlier_ws(M, K, in_dtype, cap).total;
+    out->scratch = off; off += outlier_ws(M, K, in_dtype, cap).total + align_up((size_t)N * 4);  // + W's keys
     out->total = off;
     out->capacity = cap;
     return FP4_OK;
@@ -443,6 +498,37 @@ size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_d
 fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N,
                               double q, void *Y, int32_t y_dtype, void *workspace, size_t ws_bytes, void *stream) {
     return forward_impl(A, W, nullptr, nullptr, in_dtype, M, K, N, q, Y, y_dtype, workspace, ws_bytes, stream);
+}
+
+fp4_status fp4_forward_quantize(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N,
+                                double q, int32_t stages, void *workspace, size_t ws_bytes, void *stream) {
+    if (stages < 1 || stages > (FP4_STAGE_A | FP4_STAGE_W)) return FP4_ERR_DTYPE;
+    if (((stages & FP4_STAGE_A) && !A) || ((stages & FP4_STAGE_W) && !W)) return FP4_ERR_NULL;
+    fp4_ws_layout l;
+    int cus;
+    fp4_status st = forward_check(M, K, N, in_dtype, q, ws_bytes, workspace, &l, &cus);
+    if (st != FP4_OK) return st;
+    if (((stages & FP4_STAGE_A) && !aligned16(A)) || ((stages & FP4_STAGE_W) && !aligned16(W))) return FP4_ERR_ALIGN;
+    st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    return quantize_impl(A, W, in_dtype, M, K, N, q, stages, static_cast<uint8_t *>(workspace), l, cus,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+fp4_status fp4_forward_product(const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N, double q, void *Y,
+                               int32_t y_dtype, void *workspace, size_t ws_bytes, void *stream) {
+    if (!W || !Y) return FP4_ERR_NULL;
+    if (!dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
+    fp4_ws_layout l;
+    int cus;
+    fp4_status st = forward_check(M, K, N, in_dtype, q, ws_bytes, workspace, &l, &cus);
+    if (st != FP4_OK) return st;
+    if (!aligned16(W) || !aligned16(Y)) return FP4_ERR_ALIGN;
+    st = device_check(&cus);
+    if (st != FP4_OK) return st;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    return product_impl(W, in_dtype, ws + l.Wq, reinterpret_cast<const float *>(ws + l.sW), M, K, N, Y, y_dtype, ws, l,
+                        reinterpret_cast<hipStream_t>(stream));
 }
 
 fp4_status fp4_linear_forward_wq(const void *A, const void *W, const uint8_t *Wq, const float *sW, int32_t in_dtype,

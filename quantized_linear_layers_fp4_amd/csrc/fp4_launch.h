@@ -10,10 +10,12 @@ namespace fp4 {
 
 // Zeroes p1[0..n1) and p2[0..n2) in one launch (n2 may be 0).
 hipError_t launch_zero(uint32_t *p1, int64_t n1, uint32_t *p2, int64_t n2, hipStream_t s);
-hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist,
-                              uint32_t *rowmax_key, int num_cus, hipStream_t s);
-hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint32_t *ghist_lo,
-                         State *st, float *T_out, uint64_t k, hipStream_t s);
+// Histogram of the |A| keys and raw row maxima; the last workgroup to finish selects the bin of
+// rank k (level 1; for bf16 inputs that fixes T).  ghist and st must be zero.
+hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist, uint32_t *rowmax_key,
+                              State *st, float *T_out, uint64_t k, int num_cus, hipStream_t s);
+// Second level of the select for fp32 inputs (ghist_lo zero): fixes T.
+hipError_t launch_select_lo(const void *A, int64_t n, uint32_t *ghist_lo, State *st, float *T_out, hipStream_t s);
 hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const uint32_t *rowmax_key,
                              const float *T_src, uint8_t *codes, float *scales, int32_t *row_cnt,
                              const Staging &stg, State *st, bool emit, bool write_codes, hipStream_t s);
@@ -22,10 +24,13 @@ hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const 
 hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
                       int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val, const void *A, int dt,
                       int64_t K, const float *T_src, hipStream_t s);
-// keys_zeroed: the column-maximum keys (in the scales buffer) were zeroed by an earlier launch.
+// keys_zeroed: the column-maximum keys (in scales_as_keys) were zeroed by an earlier launch.
 // row_mult: NULL, or fp32[K]: quantize fl(row_mult[k] * W[k][n]) instead of W.
+// scales_out: NULL (the scales replace the keys in scales_as_keys, one more launch), or a
+// separate fp32[N] that the quantizing kernel fills itself.
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
-                             uint8_t *codes, bool keys_zeroed, hipStream_t s, const float *row_mult = nullptr);
+                             uint8_t *codes, bool keys_zeroed, hipStream_t s, const float *row_mult = nullptr,
+                             float *scales_out = nullptr);
 // Backward operands: R x C codes (R x C/2 bytes) -> their transpose (C x R/2 bytes), R and C
 // multiples of 32; token-wise quantization of fl(X[r][c] * mult[c]) (C <= 65536); fill.
 hipError_t launch_codes_transpose(const uint8_t *in, int64_t R, int64_t C, uint8_t *out, hipStream_t s);

@@ -21,10 +21,90 @@ __global__ void k_zero_u32(uint32_t *__restrict__ p1, int64_t n1, uint32_t *__re
     }
 }
 
+// ----------------------------------------------------------------------------- select
+// The bin holding rank k (0-based) of a histogram of NB bins, found by the 1024 threads of one
+// workgroup: level 1: k = k_level1 (computed on the host) over the 32768 high bins; level 2:
+// k = st->k_rem over the 65536 low bins of the selected high bin.  final_level says which
+// level fixes T.  Every count and partial sum is at most M*K < 2^32.
+template <int NB>
+__device__ __forceinline__ void select_bin(const uint32_t *__restrict__ hist, State *__restrict__ st, int level,
+                                           int final_level, float *__restrict__ T_out, uint64_t k_level1) {
+    constexpr int PER = NB / 1024;
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t total_s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the thread's PER consecutive bins stay in registers for the search below
+    uint32_t cnts[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(hist + tid * PER + i);
+        cnts[i] = q.x;
+        cnts[i + 1] = q.y;
+        cnts[i + 2] = q.z;
+        cnts[i + 3] = q.w;
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) local += cnts[i];
+    const uint32_t wincl = wave_incl_scan(local, lane);
+    if (lane == 63) wsum[wave] = wincl;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t x = lane < 16 ? wsum[lane] : 0u;
+        const uint32_t xi = wave_incl_scan(x, lane);
+        if (lane < 16) wsum[lane] = xi - x;  // exclusive prefix of the waves
+        if (lane == 15) total_s = xi;
+    }
+    __syncthreads();
+    const uint64_t incl = (uint64_t)wsum[wave] + wincl, excl = incl - local, total = total_s;
+    const uint64_t k = (level == 1) ? k_level1 : st->k_rem;
+    if (excl <= k && k < incl) {
+        // the bin of rank k among the thread's bins: branch-free over the registers
+        uint64_t cum = excl;
+        int bi = PER - 1;
+        uint32_t cnt = cnts[PER - 1];
+        uint64_t before = excl;
+        bool found = false;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const bool here = !found && k < cum + cnts[i];
+            if (here) {
+                bi = i;
+                cnt = cnts[i];
+                before = cum;
+            }
+            found = found || here;
+            cum += cnts[i];
+        }
+        const int b = tid * PER + bi;
+        cum = before;
+        const uint64_t above = total - (cum + cnt);  // entries in later bins
+        if (level == 1) {
+            st->hi_bin = (uint32_t)b;
+            st->hi_count = cnt;
+            st->k_rem = k - cum;
+            st->nnz_hist = above;
+            if (final_level == 1) {
+                st->T_key = (uint32_t)b << 16;
+                st->T = __uint_as_float((uint32_t)b << 16);
+                *T_out = st->T;
+            }
+        } else {
+            const uint32_t key = (st->hi_bin << 16) | (uint32_t)b;
+            st->T_key = key;
+            st->T = __uint_as_float(key);
+            st->nnz_hist += above;
+            *T_out = st->T;
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------- histogram
 // One workgroup of 1024 threads per CU holds a 32768-bin histogram of key >> 16 in LDS
 // (128 KiB); a wave owns one row at a time and also reduces the row's maximum key.
 // Rows [r0, r1) of the block are contiguous.  Non-empty bins are merged with global atomics.
+// (Selecting in the workgroup that merges last, behind a device-scope fence and a ticket, was
+// measured and dropped: on this multi-XCD part the fences took 76 us, the select launch 8.)
 template <int DT>
 __global__ __launch_bounds__(1024) void k_hist_rowmax(const void *__restrict__ A, int64_t M, int64_t K,
                                                       uint32_t *__restrict__ ghist,
@@ -87,6 +167,12 @@ __global__ __launch_bounds__(1024) void k_hist_rowmax(const void *__restrict__ A
     }
 }
 
+// The level-1 select (one workgroup); for bf16 inputs it fixes T.
+__global__ __launch_bounds__(1024) void k_select_hi(const uint32_t *__restrict__ hist, State *__restrict__ st,
+                                                    int final_level, float *__restrict__ T_out, uint64_t k_level1) {
+    select_bin<HIST_BINS>(hist, st, 1, final_level, T_out, k_level1);
+}
+
 // Second level for fp32 inputs: among the entries whose key >> 16 is the selected bin,
 // histogram the low 16 bits (few entries: global atomics).
 __global__ __launch_bounds__(256) void k_hist_lo(const uint32_t *__restrict__ A, int64_t n,
@@ -100,67 +186,10 @@ __global__ __launch_bounds__(256) void k_hist_lo(const uint32_t *__restrict__ A,
     }
 }
 
-// Select the bin holding rank k (0-based) of a histogram of NB bins with one workgroup.
-// level 1: k = k_level1 (computed on the host) over the 32768 high bins; level 2: k = st->k_rem over the 65536 low
-// bins of the selected high bin.  final_level says which level fixes T.
-template <int NB>
-__global__ __launch_bounds__(1024) void k_select(const uint32_t *__restrict__ hist, State *__restrict__ st,
-                                                 int level, int final_level, float *__restrict__ T_out,
-                                                 uint64_t k_level1) {
-    constexpr int PER = NB / 1024;
-    __shared__ uint32_t wsum[16];
-    __shared__ uint32_t total_s;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // every count and partial sum is at most M*K < 2^32
-    uint32_t local = 0;
-#pragma unroll
-    for (int i = 0; i < PER; i += 4) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(hist + tid * PER + i);
-        local += q.x + q.y + q.z + q.w;
-    }
-    const uint32_t wincl = wave_incl_scan(local, lane);
-    if (lane == 63) wsum[wave] = wincl;
-    __syncthreads();
-    if (wave == 0) {
-        const uint32_t x = lane < 16 ? wsum[lane] : 0u;
-        const uint32_t xi = wave_incl_scan(x, lane);
-        if (lane < 16) wsum[lane] = xi - x;  // exclusive prefix of the waves
-        if (lane == 15) total_s = xi;
-    }
-    __syncthreads();
-    const uint64_t incl = (uint64_t)wsum[wave] + wincl, excl = incl - local, total = total_s;
-    const uint64_t k = (level == 1) ? k_level1 : st->k_rem;
-    if (excl <= k && k < incl) {
-        uint64_t cum = excl;
-        int b = tid * PER;
-        for (int i = 0; i < PER; ++i) {
-            uint32_t c = hist[tid * PER + i];
-            if (k < cum + c) {
-                b = tid * PER + i;
-                break;
-            }
-            cum += c;
-        }
-        const uint32_t cnt = hist[b];
-        const uint64_t above = total - (cum + cnt);  // entries in later bins
-        if (level == 1) {
-            st->hi_bin = (uint32_t)b;
-            st->hi_count = cnt;
-            st->k_rem = k - cum;
-            st->nnz_hist = above;
-            if (final_level == 1) {
-                st->T_key = (uint32_t)b << 16;
-                st->T = __uint_as_float((uint32_t)b << 16);
-                *T_out = st->T;
-            }
-        } else {
-            const uint32_t key = (st->hi_bin << 16) | (uint32_t)b;
-            st->T_key = key;
-            st->T = __uint_as_float(key);
-            st->nnz_hist += above;
-            *T_out = st->T;
-        }
-    }
+// The level-2 select of fp32 inputs (one workgroup).
+__global__ __launch_bounds__(1024) void k_select_lo(const uint32_t *__restrict__ hist_lo, State *__restrict__ st,
+                                                    float *__restrict__ T_out) {
+    select_bin<HIST_LO_BINS>(hist_lo, st, 2, 2, T_out, 0);
 }
 
 // ----------------------------------------------------------------------------- rows (A)
@@ -279,7 +308,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, 
                         if (omask & (1u << e)) {
                             const int32_t col = (int32_t)(c * 8 + e);
                             const float val = v[e] - __uint_as_float(sg[e] | tkey);
-                            if (rank < (uint32_t)stg.S) {  // ranks past S: see k_coo_scatter
+                            if (rank < (uint32_t)stg.S) {  // ranks past S: see k_coo_build
                                 SlotEntry se;
                                 se.col = col;
                                 se.val = val;
@@ -300,7 +329,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void *__restrict__ X, 
 
 // ----------------------------------------------------------------------------- COO
 // Exclusive scan of the per-row outlier counts (one workgroup of 1024 threads, 16 rows
-// per thread per pass, wave scans + one cross-wave step).
+// per thread per pass, wave scans + one cross-wave step).  Used ahead of k_coo_build when
+// M is too large for every workgroup of that kernel to sum the counts before its rows.
 __global__ __launch_bounds__(1024) void k_coo_scan(const int32_t *__restrict__ row_cnt, int64_t M,
                                                    int32_t *__restrict__ row_ptr,
                                                    int64_t *__restrict__ nnz_out) {
@@ -363,64 +393,26 @@ __global__ __launch_bounds__(1024) void k_coo_scan(const int32_t *__restrict__ r
     }
 }
 
-// Move each staged entry to row_ptr[row] + rank, one wave per row (ranks below S).
-__global__ __launch_bounds__(256) void k_coo_scatter(Staging stg, const int32_t *__restrict__ row_cnt,
-                                                     const int32_t *__restrict__ row_ptr, int64_t M, int64_t cap,
-                                                     int32_t *__restrict__ coo_row, int32_t *__restrict__ coo_col,
-                                                     float *__restrict__ coo_val) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
-    const int32_t n = min(row_cnt[row], stg.S);
-    const int64_t base = row_ptr[row];
-    for (int32_t j = lane; j < n; j += 64) {
-        const SlotEntry se = stg.slots[row * stg.S + j];
-        const int64_t pos = base + j;
-        if (pos < cap) {
-            if (coo_row) coo_row[pos] = (int32_t)row;
-            coo_col[pos] = se.col;
-            coo_val[pos] = se.val;
-        }
-    }
-}
-
-// Rows with more outliers than staging slots (rare: S is at least 128 and twice the mean count
-// plus a margin).  A workgroup checks 64 rows' counts at once and deals the rows past S to its
-// four waves; for each such row a wave reads the row of A again, ranks its outliers as the
-// quantize pass did (ascending column) and writes those of rank >= S straight to
-// row_ptr[row] + rank.  A kernel of its own: with this code in the quantize kernel (as an
-// atomic overflow list) that kernel took twice as long, and in the scatter kernel every row
-// waited for the few rescans.
+// The outliers of rank >= S of one row that outgrew its staging slots: the row of A is read
+// again, its outliers ranked as the quantize pass ranked them (ascending column), and those of
+// rank >= S written straight to row_ptr[row] + rank.
 template <int DT>
-__global__ __launch_bounds__(256) void k_coo_overflow(int32_t S, const int32_t *__restrict__ row_cnt,
-                                                      const int32_t *__restrict__ row_ptr, int64_t M, int64_t cap,
-                                                      const void *__restrict__ A, int64_t K,
-                                                      const float *__restrict__ T_src, int32_t *__restrict__ coo_row,
-                                                      int32_t *__restrict__ coo_col, float *__restrict__ coo_val) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * 64;  // the workgroup's 64 rows, shared by its 4 waves
-    const int32_t cnt = (r0 + lane < M) ? row_cnt[r0 + lane] : 0;
-    uint64_t todo = __ballot(cnt > S);
-    if (!todo) return;
-    const uint32_t tkey = key_of_f32(__float_as_uint(*T_src));
+__device__ __forceinline__ void coo_overflow_row(int64_t row, int64_t base, int32_t S, int64_t cap,
+                                                 const void *__restrict__ A, int64_t K, uint32_t tkey, int lane,
+                                                 int32_t *__restrict__ coo_row, int32_t *__restrict__ coo_col,
+                                                 float *__restrict__ coo_val) {
     const int64_t nchunk = K / 8;
-    for (int i = 0; todo; ++i) {
-        const int bit = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        if ((i & 3) != wave) continue;  // the group's overflowing rows are dealt to the 4 waves
-        const int64_t row = r0 + bit;
-        const int64_t base = row_ptr[row];
-        uint32_t run = 0;
-        // U chunks of 8 per lane are loaded together: one memory round trip per 512*U elements
-        constexpr int U = 8;
-        for (int64_t cg = 0; cg < nchunk; cg += 64 * U) {
-          float vv[U][8];
-          uint32_t kk[U][8], ss[U][8];
+    uint32_t run = 0;
+    // U chunks of 8 per lane are loaded together: one memory round trip per 512*U elements
+    constexpr int U = 8;
+    for (int64_t cg = 0; cg < nchunk; cg += 64 * U) {
+        float vv[U][8];
+        uint32_t kk[U][8], ss[U][8];
 #pragma unroll
-          for (int u = 0; u < U; ++u)
-              if (cg + u * 64 + lane < nchunk) load8<DT>(A, row * K + (cg + u * 64 + lane) * 8, vv[u], kk[u], ss[u]);
+        for (int u = 0; u < U; ++u)
+            if (cg + u * 64 + lane < nchunk) load8<DT>(A, row * K + (cg + u * 64 + lane) * 8, vv[u], kk[u], ss[u]);
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t c = cg + u * 64 + lane;
             const float *v = vv[u];
             const uint32_t *sg = ss[u];
@@ -450,8 +442,104 @@ __global__ __launch_bounds__(256) void k_coo_overflow(int32_t S, const int32_t *
                 }
             }
             run += total;
-          }
         }
+    }
+}
+
+// The (row, col)-sorted COO list from the staging, one workgroup per 64 rows:
+//   1. PREFIX: the row offset of the workgroup's first row is the sum of the counts before it,
+//      which the workgroup reads itself (at most COO_PREFIX_ROWS counts, from L2), so no
+//      separate scan launch precedes it; otherwise row_ptr was written by k_coo_scan;
+//   2. a wave scan of the 64 counts gives the rows' offsets (row_ptr, and nnz from the last);
+//   3. the 256 threads copy the staged entries (ranks below S) of the 64 rows as one list;
+//   4. rows that outgrew their slots are read again for their ranks >= S.
+constexpr int64_t COO_PREFIX_ROWS = 16384;
+template <int DT, bool PREFIX>
+__global__ __launch_bounds__(256) void k_coo_build(Staging stg, const int32_t *__restrict__ row_cnt,
+                                                   int32_t *__restrict__ row_ptr, int64_t *__restrict__ nnz_out,
+                                                   int64_t M, int64_t cap, int32_t *__restrict__ coo_row,
+                                                   int32_t *__restrict__ coo_col, float *__restrict__ coo_val,
+                                                   const void *__restrict__ A, int64_t K,
+                                                   const float *__restrict__ T_src) {
+    __shared__ uint32_t wsum[4];
+    __shared__ int32_t off_s[64], cnt_s[64], sc_s[65];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    if constexpr (PREFIX) {
+        // row_cnt is 16-byte aligned and r0 a multiple of 64: whole 16-byte groups, at most
+        // COO_PREFIX_ROWS / 1024 of them per thread, all issued before any is added
+        constexpr int PI = (int)(COO_PREFIX_ROWS / 1024);
+        int4 q[PI];
+#pragma unroll
+        for (int u = 0; u < PI; ++u) {
+            const int64_t i = (int64_t)tid * 4 + (int64_t)u * 1024;
+            q[u] = i < r0 ? *reinterpret_cast<const int4 *>(row_cnt + i) : make_int4(0, 0, 0, 0);
+        }
+        uint32_t part = 0;
+#pragma unroll
+        for (int u = 0; u < PI; ++u) part += (uint32_t)q[u].x + (uint32_t)q[u].y + (uint32_t)q[u].z + (uint32_t)q[u].w;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) part += (uint32_t)__shfl_xor((int)part, o, 64);
+        if (lane == 0) wsum[wave] = part;
+        __syncthreads();
+        if (wave == 0) {
+            const uint32_t base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+            const int64_t r = r0 + lane;
+            const uint32_t c = r < M ? (uint32_t)row_cnt[r] : 0u;
+            const uint32_t incl = wave_incl_scan(c, lane);
+            const int32_t off = (int32_t)(base + incl - c);
+            if (r < M) row_ptr[r] = off;
+            if (r == M - 1) {
+                row_ptr[M] = (int32_t)(base + incl);
+                *nnz_out = (int64_t)(base + incl);
+            }
+            off_s[lane] = off;
+            cnt_s[lane] = (int32_t)c;
+        }
+    } else {
+        if (wave == 0) {
+            const int64_t r = r0 + lane;
+            off_s[lane] = r < M ? row_ptr[r] : 0;
+            cnt_s[lane] = r < M ? row_cnt[r] : 0;
+        }
+    }
+    __syncthreads();
+    // staged entries of the 64 rows (ranks below S) as one flat list over the 256 threads: the
+    // row of entry e is found by a binary search in the rows' staged-count prefix
+    if (wave == 0) {
+        const uint32_t st = (uint32_t)min(cnt_s[lane], stg.S);
+        const uint32_t incl = wave_incl_scan(st, lane);
+        sc_s[lane] = (int32_t)(incl - st);
+        if (lane == 63) sc_s[64] = (int32_t)incl;
+    }
+    __syncthreads();
+    for (int32_t e = tid; e < sc_s[64]; e += 256) {
+        int lo = 0, hi = 64;  // the last j with sc_s[j] <= e (rows with no staged entry are skipped)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sc_s[mid] <= e) lo = mid;
+            else hi = mid;
+        }
+        const int32_t t = e - sc_s[lo];
+        const int64_t row = r0 + lo;
+        const SlotEntry se = stg.slots[row * stg.S + t];
+        const int64_t pos = (int64_t)off_s[lo] + t;
+        if (pos < cap) {
+            if (coo_row) coo_row[pos] = (int32_t)row;
+            coo_col[pos] = se.col;
+            coo_val[pos] = se.val;
+        }
+    }
+    // rows past S are rare (S is at least 128 and twice the mean count plus a margin)
+    const uint64_t todo = __ballot(r0 + lane < M && cnt_s[lane] > stg.S);  // the same in every wave
+    if (!todo) return;
+    const uint32_t tkey = key_of_f32(__float_as_uint(*T_src));
+    uint64_t t = todo;
+    for (int i = 0; t; ++i) {
+        const int bit = __builtin_ctzll(t);
+        t &= t - 1;
+        if ((i & 3) != wave) continue;  // dealt to the four waves in turn
+        coo_overflow_row<DT>(r0 + bit, off_s[bit], stg.S, cap, A, K, tkey, lane, coo_row, coo_col, coo_val);
     }
 }
 
@@ -519,11 +607,13 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
 // transposed: Wq[n][k/2].  Loads: TN/8 threads per row (16 bytes = 8 columns each), two rows
 // (k, k+1) per thread per pass so each output byte (pair of k) is formed in registers; the
 // transpose goes through a TN x 128-byte LDS tile, written out as 128-byte rows of Wq.
+// scales_out: NULL, or fp32[N] (a buffer other than the keys) that the workgroups of the first
+// tile row fill with the dequantization scales of their columns.
 template <int DT, bool RM, int TN>
 __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, int64_t K, int64_t N,
                                                     const float *__restrict__ row_mult,
                                                     const uint32_t *__restrict__ colmax_key,
-                                                    uint8_t *__restrict__ codes) {
+                                                    uint8_t *__restrict__ codes, float *__restrict__ scales_out) {
     constexpr int TPR = TN / 8;         // threads per row
     constexpr int RPP = 256 / TPR;      // row pairs per pass
     constexpr int PASSES = 128 / RPP;   // 128 row pairs = 256 rows per tile
@@ -535,7 +625,10 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
     const int64_t n0 = (int64_t)blockIdx.x * TN, k0 = (int64_t)blockIdx.y * 256;
     if (tid < TN) {
         float r = 0.0f, s;
-        if (n0 + tid < N) vector_scale(__uint_as_float(colmax_key[n0 + tid]), r, s);
+        if (n0 + tid < N) {
+            vector_scale(__uint_as_float(colmax_key[n0 + tid]), r, s);
+            if (scales_out && blockIdx.y == 0) scales_out[n0 + tid] = s;
+        }
         rs[tid] = r;
     }
     __syncthreads();
@@ -592,13 +685,13 @@ static_assert(FP4_QCOLS_TN == 64 || FP4_QCOLS_TN == 128, "FP4_QCOLS_TN is 64 or 
 
 template <int DT, bool RM>
 static void launch_qcols_tile(const void *W, int64_t K, int64_t N, const float *row_mult, const uint32_t *keys,
-                              uint8_t *codes, hipStream_t s) {
+                              uint8_t *codes, float *scales_out, hipStream_t s) {
     if constexpr (FP4_QCOLS_TN == 128) {
         dim3 g((unsigned)((N + 127) / 128), (unsigned)((K + 255) / 256));
-        hipLaunchKernelGGL((k_quant_cols<DT, RM, 128>), g, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+        hipLaunchKernelGGL((k_quant_cols<DT, RM, 128>), g, dim3(256), 0, s, W, K, N, row_mult, keys, codes, scales_out);
     } else {
         dim3 g((unsigned)((N + 63) / 64), (unsigned)((K + 255) / 256));
-        hipLaunchKernelGGL((k_quant_cols<DT, RM, 64>), g, dim3(256), 0, s, W, K, N, row_mult, keys, codes);
+        hipLaunchKernelGGL((k_quant_cols<DT, RM, 64>), g, dim3(256), 0, s, W, K, N, row_mult, keys, codes, scales_out);
     }
 }
 
@@ -625,25 +718,21 @@ hipError_t launch_zero(uint32_t *p1, int64_t n1, uint32_t *p2, int64_t n2, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist,
-                              uint32_t *rowmax_key, int num_cus, hipStream_t s) {
+hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist, uint32_t *rowmax_key,
+                              State *st, float *T_out, uint64_t k, int num_cus, hipStream_t s) {
     int blocks = (int)(M < (int64_t)num_cus ? M : (int64_t)num_cus);
     if (dt == DT_BF16)
         hipLaunchKernelGGL(k_hist_rowmax<DT_BF16>, dim3(blocks), dim3(1024), 0, s, A, M, K, ghist, rowmax_key);
     else
         hipLaunchKernelGGL(k_hist_rowmax<DT_F32>, dim3(blocks), dim3(1024), 0, s, A, M, K, ghist, rowmax_key);
+    hipLaunchKernelGGL(k_select_hi, dim3(1), dim3(1024), 0, s, ghist, st, dt == DT_BF16 ? 1 : 2, T_out, (uint64_t)k);
     return hipGetLastError();
 }
 
-hipError_t launch_select(const void *A, int dt, int64_t n, uint32_t *ghist, uint32_t *ghist_lo,
-                         State *st, float *T_out, uint64_t k, hipStream_t s) {
-    const int final_level = (dt == DT_BF16) ? 1 : 2;
-    hipLaunchKernelGGL(k_select<HIST_BINS>, dim3(1), dim3(1024), 0, s, ghist, st, 1, final_level, T_out, k);
-    if (dt == DT_F32) {
-        hipLaunchKernelGGL(k_hist_lo, dim3(blocks_for(n, 256, 2048)), dim3(256), 0, s,
-                           (const uint32_t *)A, n, st, ghist_lo);
-        hipLaunchKernelGGL(k_select<HIST_LO_BINS>, dim3(1), dim3(1024), 0, s, ghist_lo, st, 2, 2, T_out, k);
-    }
+hipError_t launch_select_lo(const void *A, int64_t n, uint32_t *ghist_lo, State *st, float *T_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_hist_lo, dim3(blocks_for(n, 256, 2048)), dim3(256), 0, s, (const uint32_t *)A, n, st,
+                       ghist_lo);
+    hipLaunchKernelGGL(k_select_lo, dim3(1), dim3(1024), 0, s, ghist_lo, st, T_out);
     return hipGetLastError();
 }
 
@@ -674,21 +763,26 @@ hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const 
 hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
                       int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val, const void *A, int dt,
                       int64_t K, const float *T_src, hipStream_t s) {
-    hipLaunchKernelGGL(k_coo_scan, dim3(1), dim3(1024), 0, s, row_cnt, M, row_ptr, nnz_out);
-    hipLaunchKernelGGL(k_coo_scatter, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, stg, row_cnt, row_ptr, M, cap,
-                       coo_row, coo_col, coo_val);
-    const dim3 go((unsigned)((M + 63) / 64));  // 64 rows per workgroup
-    if (dt == DT_BF16)
-        hipLaunchKernelGGL(k_coo_overflow<DT_BF16>, go, dim3(256), 0, s, stg.S, row_cnt, row_ptr, M, cap, A, K, T_src,
-                           coo_row, coo_col, coo_val);
-    else
-        hipLaunchKernelGGL(k_coo_overflow<DT_F32>, go, dim3(256), 0, s, stg.S, row_cnt, row_ptr, M, cap, A, K, T_src,
-                           coo_row, coo_col, coo_val);
+    const dim3 grid((unsigned)((M + 63) / 64)), block(256);  // 64 rows per workgroup
+    const bool prefix = M <= COO_PREFIX_ROWS;
+    if (!prefix) hipLaunchKernelGGL(k_coo_scan, dim3(1), dim3(1024), 0, s, row_cnt, M, row_ptr, nnz_out);
+#define CB(DT, PF)                                                                                              \
+    hipLaunchKernelGGL((k_coo_build<DT, PF>), grid, block, 0, s, stg, row_cnt, row_ptr, nnz_out, M, cap, coo_row, \
+                       coo_col, coo_val, A, K, T_src)
+    if (dt == DT_BF16) {
+        if (prefix) CB(DT_BF16, true);
+        else CB(DT_BF16, false);
+    } else {
+        if (prefix) CB(DT_F32, true);
+        else CB(DT_F32, false);
+    }
+#undef CB
     return hipGetLastError();
 }
 
 hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float *scales_as_keys,
-                             uint8_t *codes, bool keys_zeroed, hipStream_t s, const float *row_mult) {
+                             uint8_t *codes, bool keys_zeroed, hipStream_t s, const float *row_mult,
+                             float *scales_out) {
     uint32_t *keys = reinterpret_cast<uint32_t *>(scales_as_keys);
     if (!keys_zeroed) {
         hipError_t e = launch_zero(keys, N, nullptr, 0, s);
@@ -699,7 +793,7 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
 #define QC(DT, RM)                                                                                         \
     do {                                                                                                   \
         hipLaunchKernelGGL((k_colmax<DT, RM>), g1, dim3(256), 0, s, W, K, N, rows_per_block, row_mult, keys); \
-        launch_qcols_tile<DT, RM>(W, K, N, row_mult, keys, codes, s);                                       \
+        launch_qcols_tile<DT, RM>(W, K, N, row_mult, keys, codes, scales_out, s);                           \
     } while (0)
     if (dt == DT_BF16) {
         if (row_mult) QC(DT_BF16, true);
@@ -709,7 +803,7 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
         else QC(DT_F32, false);
     }
 #undef QC
-    hipLaunchKernelGGL(k_col_scales, dim3(blocks_for(N, 256, 1 << 20)), dim3(256), 0, s, keys, N);
+    if (!scales_out) hipLaunchKernelGGL(k_col_scales, dim3(blocks_for(N, 256, 1 << 20)), dim3(256), 0, s, keys, N);
     return hipGetLastError();
 }
 
@@ -717,11 +811,11 @@ hipError_t launch_quant_cols_keyed(const void *W, int dt, int64_t K, int64_t N, 
                                    uint8_t *codes, const float *row_mult, hipStream_t s) {
     uint32_t *keys = reinterpret_cast<uint32_t *>(scales_as_keys);
     if (dt == DT_BF16) {
-        if (row_mult) launch_qcols_tile<DT_BF16, true>(W, K, N, row_mult, keys, codes, s);
-        else launch_qcols_tile<DT_BF16, false>(W, K, N, row_mult, keys, codes, s);
+        if (row_mult) launch_qcols_tile<DT_BF16, true>(W, K, N, row_mult, keys, codes, nullptr, s);
+        else launch_qcols_tile<DT_BF16, false>(W, K, N, row_mult, keys, codes, nullptr, s);
     } else {
-        if (row_mult) launch_qcols_tile<DT_F32, true>(W, K, N, row_mult, keys, codes, s);
-        else launch_qcols_tile<DT_F32, false>(W, K, N, row_mult, keys, codes, s);
+        if (row_mult) launch_qcols_tile<DT_F32, true>(W, K, N, row_mult, keys, codes, nullptr, s);
+        else launch_qcols_tile<DT_F32, false>(W, K, N, row_mult, keys, codes, nullptr, s);
     }
     hipLaunchKernelGGL(k_col_scales, dim3(blocks_for(N, 256, 1 << 20)), dim3(256), 0, s, keys, N);
     return hipGetLastError();

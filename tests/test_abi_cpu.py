@@ -107,6 +107,33 @@ def test_linear_forward_wq_rejects():
     assert call(wsb=lay.total - 1) == EWS
 
 
+def test_forward_stage_calls_reject():
+    """The two stage calls of the forward check their stage mask, the pointers of the stages
+    asked for, and everything the whole forward checks."""
+    L = fp4.lib()
+    lay = fp4.WsLayout()
+    assert L.fp4_forward_layout(64, 128, 64, fp4.FP4_BF16, 0.99, C.byref(lay)) == OK
+    quant = lambda **kw: L.fp4_forward_quantize(  # noqa: E731
+        kw.get("A", FAKE), kw.get("W", FAKE), fp4.FP4_BF16, 64, kw.get("K", 128), 64, kw.get("q", 0.99),
+        kw.get("stages", 3), kw.get("ws", FAKE), kw.get("wsb", lay.total), None)
+    assert quant(stages=0) == EDTYPE and quant(stages=4) == EDTYPE
+    assert quant(A=None) == ENULL and quant(W=None) == ENULL
+    assert quant(ws=None) == ENULL
+    assert quant(K=100) == ESHAPE
+    assert quant(q=1.5) == EQ
+    assert quant(wsb=lay.total - 1) == EWS
+    assert quant(A=C.c_void_p(0x100004)) == EALIGN
+    assert quant(A=C.c_void_p(0x100004), stages=fp4.FP4_STAGE_W) != EALIGN  # A unused: then the device check
+    prod = lambda **kw: L.fp4_forward_product(  # noqa: E731
+        kw.get("W", FAKE), fp4.FP4_BF16, 64, kw.get("K", 128), 64, 0.99, kw.get("Y", FAKE), kw.get("ydt", 1),
+        FAKE, kw.get("wsb", lay.total), None)
+    assert prod(W=None) == ENULL and prod(Y=None) == ENULL
+    assert prod(ydt=9) == EDTYPE
+    assert prod(K=100) == ESHAPE
+    assert prod(wsb=16) == EWS
+    assert prod(Y=C.c_void_p(0x100002)) == EALIGN
+
+
 def test_fp8_codec_rejects():
     L = fp4.lib()
     wsb = L.fp4_fp8_workspace_bytes()
@@ -262,3 +289,4 @@ def test_kernel_name_queries():
     cap = fp4.outlier_capacity(16384, 13824, 0.99)
     assert L.fp4_comp_kernel_name(16384, cap) == b"k_comp_block64"
     assert L.fp4_comp_kernel_name(0, 1) is None
+

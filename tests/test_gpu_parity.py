@@ -496,6 +496,37 @@ def test_forward_with_cached_weights(dtype, M, K, N, q, out):
         assert_y_close(to_np(Y2), ref["Y"], ref["denom"])
 
 
+@pytest.mark.parametrize("order", ["A_then_W", "W_then_A", "both"])
+@pytest.mark.parametrize("dtype,M,K,N,q,out", [("bf16", 300, 512, 264, 0.99, torch.bfloat16),
+                                               ("fp32", 130, 256, 72, 0.95, torch.float32)])
+def test_forward_in_stage_calls(dtype, M, K, N, q, out, order):
+    """fp4_forward_quantize (A and W stages, in either order or together) + fp4_forward_product
+    give the same bits as fp4_linear_forward, intermediates included."""
+    _say(f"forward stages {order} {dtype} {M}x{K}x{N}")
+    A, W = make_custom(M, K, N, dtype=dtype, seed=23)
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    ws1 = fp4.workspace(Ad, N, q)
+    Y1 = fp4.linear_forward(Ad, Wd, q, out_dtype=out, ws=ws1)
+    ws2 = torch.full_like(ws1, 0x5A)  # stale contents must not matter
+    if order == "both":
+        fp4.forward_quantize(Ad, Wd, M, K, N, A.dtype, q, ws2)
+    else:
+        stages = [fp4.FP4_STAGE_A, fp4.FP4_STAGE_W] if order == "A_then_W" else [fp4.FP4_STAGE_W, fp4.FP4_STAGE_A]
+        for st in stages:
+            fp4.forward_quantize(Ad if st == fp4.FP4_STAGE_A else None, Wd if st == fp4.FP4_STAGE_W else None,
+                                 M, K, N, A.dtype, q, ws2, stages=st)
+    Y2 = fp4.forward_product(Wd, M, q, ws2, torch.empty_like(Y1))
+    torch.cuda.synchronize()
+    bits = torch.int16 if out == torch.bfloat16 else torch.int32
+    assert torch.equal(Y1.view(bits), Y2.view(bits))
+    i1 = fp4.forward_intermediates(ws1, M, K, N, A.dtype, q)
+    i2 = fp4.forward_intermediates(ws2, M, K, N, A.dtype, q)
+    nnz = int(i1["nnz"].item())
+    for k in ("T", "nnz", "row_ptr", "coo_col", "coo_val", "Aq", "sA", "Wq", "sW"):
+        a, b = (i1[k][:nnz], i2[k][:nnz]) if k.startswith("coo") else (i1[k], i2[k])
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), k
+
+
 # ----------------------------------------------------------------------------- FP8 gradient codec
 def test_fp8_encoder_sweep():
     """With amax = 448 the multiplier is exactly 1, so the codes are the encoder itself on
@@ -576,6 +607,32 @@ def _sample_pairs(rng, M, N, row_ptr, count=3000):
     return np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
 
 
+def _wide_tile_origin(lg, tilesM, tilesN, group=4):
+    """(row, col) origin of logical tile lg of the persistent 256 x 256 GEMM: groups of `group`
+    tile-rows swept across all tile-columns, column by column."""
+    g = min(group, tilesM)
+    grp = lg // (g * tilesN)
+    first_m = grp * g
+    gm = min(g, tilesM - first_m)
+    ig = lg - grp * g * tilesN
+    return (first_m + ig % gm) * 256, (ig // gm) * 256
+
+
+def _whole_tiles(M, N, cus):
+    """Output tiles compared whole at full size: the first tile, the last (ragged) one, and the
+    first and last tile of the first and the last XCD's contiguous range of the persistent
+    walk (the first tile of a range is a workgroup's first, whose last pairs are stored during
+    its next tile; the last ends a walk and stores at once)."""
+    assert fp4.gemm_kernel_name(M, N, 4096, cus) == "k_fp4_gemm_wide"
+    tilesM, tilesN = -(-M // 256), -(-N // 256)
+    tiles = tilesM * tilesN
+    tpx = -(-tiles // 8)
+    lgs = {0, tiles - 1, tpx - 1, 7 * tpx, tiles - 1}
+    out = {_wide_tile_origin(lg, tilesM, tilesN) for lg in lgs if lg < tiles}
+    out.add(((tilesM - 1) * 256, (tilesN - 1) * 256))
+    return sorted(out)
+
+
 FULL = [(w, li) for w in ("llama1.3b_qkv", "llama7b_gate_up", "llama13b_down", "llama7b_block")
         for li in range(len(WORKLOADS[w].layers))]
 
@@ -627,6 +684,21 @@ def test_forward_full_size(wl, li):
     if L.out_dtype == "bf16":
         assert_bf16_close(to_np(Y.view(-1)[idx]), r_y, denom)
     _say(f"  sampled acc bit-exact, Y max rel err {err:.3e}")
+    # whole 256 x 256 output tiles of the launch the benchmark times
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for (m0, n0) in _whole_tiles(M, N, cus):
+        rows, cols = np.arange(m0, min(m0 + 256, M)), np.arange(n0, min(n0 + 256, N))
+        tm, tn = np.repeat(rows, cols.size).astype(np.int64), np.tile(cols, rows.size).astype(np.int64)
+        t_acc = acc[m0:m0 + rows.size, n0:n0 + cols.size].cpu().numpy().reshape(-1)
+        r_acc = oracle.accumulate_pairs(Aq, Wq, K, tm, tn)
+        assert np.array_equal(t_acc, r_acc), (m0, n0)
+        r_y, denom = oracle.output_pairs(r_acc, sA, sW, tm, tn, cl["row_ptr"], cl["coo_col"], cl["coo_val"], Wnp)
+        assert_y_close(Y32[m0:m0 + rows.size, n0:n0 + cols.size].cpu().numpy().reshape(-1), r_y, denom,
+                       what=f"Y tile ({m0},{n0})")
+        if L.out_dtype == "bf16":
+            assert_bf16_close(to_np(Y[m0:m0 + rows.size, n0:n0 + cols.size]).reshape(-1), r_y, denom,
+                              what=f"Y(bf16) tile ({m0},{n0})")
+    _say(f"  whole tiles {_whole_tiles(M, N, cus)} match")
 
 
 @pytest.mark.parametrize("out,M,K", [("bf16", 8192, 512), ("fp32", 8192, 512), ("bf16", 8200, 1024)])
@@ -757,7 +829,7 @@ def test_backward_zero_gradient_rows_and_columns():
     _check_backward_small(A, W, torch.zeros_like(dY), 0.99, torch.float32)
 
 
-BWD_FULL = [("llama1.3b_qkv", 0), ("llama7b_gate_up", 0)]
+BWD_FULL = [("llama1.3b_qkv", 0), ("llama7b_gate_up", 0), ("llama13b_down", 0)]
 
 
 @pytest.mark.parametrize("wl,li", BWD_FULL, ids=[f"{w}-{WORKLOADS[w].layers[li].name}" for w, li in BWD_FULL])

@@ -1,6 +1,7 @@
 """The seeded input generator: its draws stay fixed, and each workload has the shape and
 the value structure its recipe states (no GPU, no oracle: the generator holds none of the
 method's arithmetic)."""
+import dataclasses
 import hashlib
 
 import numpy as np
@@ -40,7 +41,12 @@ def test_table_shapes_fit_the_library_limits():
             assert L.N % 8 == 0 and L.M * L.K < 2**32
             assert 0.0 < L.q < 1.0
         names.add(wl.seed_id)
-    assert len(names) == len(WORKLOADS)  # distinct random streams
+    # distinct random streams, except the chain's second-quantile variant, which reuses the
+    # chain's inputs on purpose
+    assert len(names) == len(WORKLOADS) - 1
+    q999, chain = WORKLOADS["llama7b_block_q999"], WORKLOADS["llama7b_block"]
+    assert q999.seed_id == chain.seed_id
+    assert [dataclasses.replace(L, q=0.99) for L in q999.layers] == list(chain.layers)
 
 
 def test_sparse_outliers_structure():
@@ -72,3 +78,16 @@ def test_weights_std(name):
     L = WORKLOADS[name].layers[0]
     W = workloads._normal(workloads._rng(WORKLOADS[name].seed_id, 0, 2), (min(L.K, 512), L.N), std=L.w_std)
     assert abs(float(W.std()) / L.w_std - 1.0) < 0.02
+
+
+def test_replicas_are_distinct_draws_of_the_same_recipe():
+    """Replica 1 (the benchmark's second, cache-cold input set) has the shapes and dtypes of
+    replica 0 and different values; replica 0 is unchanged by the replica argument."""
+    A0, W0, L = make_layer("llama1.3b_qkv", 0)
+    A0b, W0b, _ = make_layer("llama1.3b_qkv", 0, replica=0)
+    A1, W1, _ = make_layer("llama1.3b_qkv", 0, replica=1)
+    assert torch.equal(A0, A0b) and torch.equal(W0, W0b)
+    assert A1.shape == A0.shape and A1.dtype == A0.dtype and W1.shape == W0.shape
+    assert not torch.equal(A0, A1) and not torch.equal(W0, W1)
+    # same recipe: the same 8 outlier channels are not required, but the scale is
+    assert abs(float(W1.float().std()) - float(W0.float().std())) < 1e-3
