@@ -73,7 +73,8 @@ enum {
     FP4_ERR_WORKSPACE = 6, /* workspace smaller than the size query returns */
     FP4_ERR_DEVICE = 7,    /* current HIP device is not gfx950 */
     FP4_ERR_HIP = 8,       /* a HIP runtime call or launch failed */
-    FP4_ERR_ALIGN = 9      /* a pointer is not 16-byte aligned */
+    FP4_ERR_ALIGN = 9,     /* a pointer is not 16-byte aligned */
+    FP4_ERR_SCRATCH = 10   /* the problem needs more than the no-alloc entry point's fixed scratch */
 };
 enum { FP4_F32 = 0, FP4_BF16 = 1 };          /* element types of A, W, X, Y */
 /* Output type of fp4_gemm only (no compensation term): the exact accumulator in two bytes.
@@ -127,6 +128,22 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
                              float *T, int32_t *coo_row, int32_t *coo_col, float *coo_val,
                              int64_t capacity, int32_t *row_ptr, int64_t *nnz, void *workspace,
                              size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): fp4_outlier_clamp without a workspace argument.
+ * The scratch is a fixed array of FP4_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on
+ * each GPU it runs on until the process ends.
+ * A problem whose scratch (fp4_outlier_workspace_bytes) exceeds it is rejected with
+ * FP4_ERR_SCRATCH before anything is enqueued; e.g. a bf16 16384 x 13824 input at q = 0.99
+ * needs 38 MB.  Outputs, results and the other statuses are those of fp4_outlier_clamp; the
+ * call allocates, frees and memsets nothing (the scratch is cleared by a fill kernel).  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one GPU (different
+ * streams, or host threads) race and must be serialized by the caller; calls on one stream
+ * are ordered. */
+#define FP4_NOALLOC_SCRATCH_BYTES (64u << 20)
+fp4_status fp4_outlier_clamp_noalloc(const void *A, int32_t a_dtype, int64_t M, int64_t K, double q,
+                                     float *T, int32_t *coo_row, int32_t *coo_col, float *coo_val,
+                                     int64_t capacity, int32_t *row_ptr, int64_t *nnz, void *stream);
 
 /* Host-only: workspace bytes fp4_gemm needs: with the compensation term about M * N * 4 for
  * a bf16 Y (the fp32 escapes of the two-byte hand-over; the accumulators go through Y

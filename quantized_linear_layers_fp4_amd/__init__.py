@@ -28,6 +28,7 @@ FP4_STAGE_A, FP4_STAGE_W = 1, 2
 
 EXPORTS = (
     "fp4_quantize", "fp4_outlier_capacity", "fp4_outlier_workspace_bytes", "fp4_outlier_clamp",
+    "fp4_outlier_clamp_noalloc",
     "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_forward_layout", "fp4_forward_workspace_bytes", "fp4_linear_forward",
     "fp4_linear_forward_wq", "fp4_forward_quantize", "fp4_forward_product", "fp4_gemm_fp8emu_workspace_bytes", "fp4_gemm_fp8emu",
     "fp4_fp8_workspace_bytes", "fp4_fp8_quantize", "fp4_fp8_dequantize",
@@ -66,6 +67,7 @@ def lib():
         "fp4_outlier_capacity": (i64, [i64, i64, dbl]),
         "fp4_outlier_workspace_bytes": (sz, [i64, i64, i32, dbl]),
         "fp4_outlier_clamp": (i32, [vp, i32, i64, i64, dbl, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]),
+        "fp4_outlier_clamp_noalloc": (i32, [vp, i32, i64, i64, dbl, vp, vp, vp, vp, i64, vp, vp, vp]),
         "fp4_gemm_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "fp4_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, sz, vp]),
         "fp4_forward_layout": (i32, [i64, i64, i64, i32, dbl, C.POINTER(WsLayout)]),

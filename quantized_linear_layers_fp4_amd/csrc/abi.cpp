@@ -307,6 +307,7 @@ const char *fp4_status_string(fp4_status s) {
     case FP4_ERR_DEVICE: return "current HIP device is not gfx950";
     case FP4_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case FP4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP4_ERR_SCRATCH: return "the problem needs more scratch than the no-alloc entry point holds";
     default: return "unknown status";
     }
 }

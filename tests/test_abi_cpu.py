@@ -12,7 +12,7 @@ import quantized_linear_layers_fp4_amd as fp4
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp4lin.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EQ, ECAP, EWS, EDEV, EHIP, EALIGN = range(10)
+OK, ENULL, ESHAPE, EDTYPE, EQ, ECAP, EWS, EDEV, EHIP, EALIGN, ESCRATCH = range(11)
 FAKE = C.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
 
 
@@ -290,3 +290,24 @@ def test_kernel_name_queries():
     assert L.fp4_comp_kernel_name(16384, cap) == b"k_comp_block64"
     assert L.fp4_comp_kernel_name(0, 1) is None
 
+
+def test_outlier_clamp_noalloc_rejects():
+    """The no-allocation variant checks what fp4_outlier_clamp checks, and rejects a problem
+    whose scratch exceeds its fixed array with FP4_ERR_SCRATCH, before any HIP call."""
+    L = fp4.lib()
+    call = lambda **kw: L.fp4_outlier_clamp_noalloc(  # noqa: E731
+        kw.get("A", FAKE), fp4.FP4_BF16, kw.get("M", 64), kw.get("K", 128), kw.get("q", 0.99), FAKE, FAKE, FAKE,
+        FAKE, kw.get("cap", 1 << 20), kw.get("row_ptr", FAKE), FAKE, None)
+    assert call(A=None) == ENULL
+    assert call(K=100) == ESHAPE
+    assert call(q=float("nan")) == EQ
+    assert call(cap=0) == ECAP
+    assert call(row_ptr=C.c_void_p(0x100004)) == EALIGN
+    big_m, big_k = 65535, 65536  # q = 0.99: 1320 staging slots per row, far beyond 64 MiB
+    need = L.fp4_outlier_workspace_bytes(big_m, big_k, fp4.FP4_BF16, 0.99)
+    assert need > (64 << 20)
+    assert call(M=big_m, K=big_k, cap=fp4.outlier_capacity(big_m, big_k, 0.99)) == ESCRATCH
+    assert L.fp4_status_string(ESCRATCH) != L.fp4_status_string(99)
+    # the workload shapes fit
+    for (m, k, q) in [(16384, 4096, 0.999), (16384, 13824, 0.99), (8192, 11008, 0.99)]:
+        assert L.fp4_outlier_workspace_bytes(m, k, fp4.FP4_BF16, q) <= (64 << 20)
