@@ -6,7 +6,8 @@
  * FP4 matrix peak.  This probe measures what the matrix cores of the present device actually
  * sustain when they do nothing else: every wave issues a long chain of independent
  * V_MFMA_SCALE_F32_32X32X64_F8F6F4 instructions on FP4 operands held in registers (no memory
- * traffic inside the timed loop), and reads the shader clock counter and the constant-rate
+ * traffic inside the timed loop; the unscaled form with unit block scales, as the GEMM
+ * issues it), and reads the shader clock counter and the constant-rate
  * real-time counter before and after, so the caller can derive the clock the loop ran at.
  *
  * Not part of the forward: only the benchmark calls it.

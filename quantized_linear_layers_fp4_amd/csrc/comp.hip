@@ -185,6 +185,104 @@ __global__ __launch_bounds__(256) void k_comp_apply(CompArgs a, int chunks, int 
     comp_task<YDT, WDT, CC>(a, row, chunk, lane);
 }
 
+// R consecutive rows of one 512-column chunk per wave (lane l owns the 8 columns 8l .. of the
+// chunk in every row).  A single task is a chain of three dependent memory round trips (the
+// CSR offsets, then the row's entries, then their W row segments); here the R rows'
+// accumulator codes, the chunk's column scales and the R + 1 offsets are requested together,
+// then the rows' entries with one load per lane, then the W segments of up to CB entries of
+// every row at once, so one chain serves R rows.  Each row's entries are still added in
+// ascending k, one fp32 fma each, from Y_main: the results are those of k_comp_apply.
+template <int YDT, int WDT, int R, int CBR>
+__device__ __forceinline__ void comp_rows(const CompArgs &a, int r0, int chunk, int lane) {
+    constexpr int CC = 8;
+    const int N = a.N, M = a.M;
+    const int col = chunk * (64 * CC) + lane * CC;
+    const bool active = col < N;  // N % 8 == 0: a lane's columns are in range together
+    const int32_t rp = a.row_ptr[min(r0 + min(lane, R), M)];
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.sW), 0, N * 4, 0x00020000);
+    v4i qv[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int row = min(r0 + i, M - 1);
+        const __amdgpu_buffer_rsrc_t rsQ =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t *>(a.Yq) + (size_t)row * N, 0, N * 2, 0x00020000);
+        qv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsQ, col * 2, 0, 2);
+    }
+    v4i swv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) swv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16 * h, 0, 0);
+    float sa[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) sa[i] = a.sA[min(r0 + i, M - 1)];
+    int32_t eb[R + 1];
+#pragma unroll
+    for (int i = 0; i <= R; ++i) eb[i] = __builtin_amdgcn_readlane(rp, i);
+    float y[R][CC];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        decode_ymain<CC>(qv[i], swv, sa[i], active, a.esc + (size_t)min(r0 + i, M - 1) * N, col, y[i]);
+
+    constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t rsW =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.W), 0, (int)((int64_t)a.K * N * ESZ), 0x00020000);
+    const uint32_t row_bytes = (uint32_t)N * ESZ;
+    const uint32_t lane_off = (uint32_t)col * ESZ;
+    const int32_t e0 = eb[0], total = eb[R] - eb[0];
+    for (int32_t base = 0; base < total; base += 64) {  // 64 entries of the rows per window
+        int32_t kk = 0;
+        float dd = 0.0f;
+        if (base + lane < total) {
+            kk = a.coo_col[e0 + base + lane];
+            dd = a.coo_val[e0 + base + lane];
+        }
+        int lo[R], n[R], nmax = 0;  // row i's entries in this window: indices lo[i] .. lo[i] + n[i]
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            lo[i] = max(eb[i] - e0 - base, 0);
+            n[i] = max(min(eb[i + 1] - e0 - base, 64) - lo[i], 0);
+            nmax = max(nmax, n[i]);
+        }
+        for (int s0 = 0; s0 < nmax; s0 += CBR) {
+            v4i w[R][CBR][2];
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int u = 0; u < CBR; ++u) {
+                    const bool on = s0 + u < n[i];  // wave-uniform
+                    const uint32_t k = (uint32_t)__builtin_amdgcn_readlane(kk, on ? lo[i] + s0 + u : 0);
+                    load_seg<WDT, CC>(rsW, k * row_bytes + lane_off, on, w[i][u]);
+                }
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int u = 0; u < CBR; ++u) {
+                    if (s0 + u < n[i]) {  // wave-uniform; ascending k within row i
+                        const float d = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int32_t, dd), lo[i] + s0 + u));
+#pragma unroll
+                        for (int c = 0; c < CC; ++c) y[i][c] = __builtin_fmaf(d, seg_elem<WDT>(w[i][u], c), y[i][c]);
+                    }
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        if (active && r0 + i < M) store_y<YDT, CC>(a.Y, (size_t)(r0 + i) * N + col, y[i]);
+}
+
+// Tasks (chunk, group of R rows), chunk-major, dealt to the XCDs in contiguous ranges.
+template <int YDT, int WDT, int R, int CBR>
+__global__ __launch_bounds__(256) void k_comp_rows(CompArgs a, int chunks, int per_xcd) {
+    const int lane = threadIdx.x & 63;
+    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    const int64_t task = (int64_t)logical * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int groups = (a.M + R - 1) / R;
+    if (task >= (int64_t)chunks * groups) return;  // whole wave
+    const int chunk = (int)(task / groups);
+    const int g = (int)(task - (int64_t)chunk * groups);
+    comp_rows<YDT, WDT, R, CBR>(a, g * R, chunk, lane);
+}
+
 // Many entries per row: one wave per (block of 8 rows, chunk of 64 columns) task, lane
 // 8r + g on row r of the block and columns 8g .. 8g+7 of the chunk.  The waves an XCD runs
 // at once then gather from a W strip 64 columns wide (K x 128 bytes of bf16, 1.8 MB for
@@ -294,6 +392,25 @@ static hipError_t launch_comp_tasks(const CompArgs &a, int y_dt, int w_dt, hipSt
     const int per_xcd = (int)((blocks + 7) / 8);
     const dim3 grid((unsigned)per_xcd * 8u), block(256);
 #define C(YD, WD) hipLaunchKernelGGL((k_comp_apply<YD, WD, CC>), grid, block, 0, s, a, chunks, per_xcd)
+    if (y_dt == DT_BF16) {
+        if (w_dt == DT_BF16) C(DT_BF16, DT_BF16);
+        else C(DT_BF16, DT_F32);
+    } else {
+        if (w_dt == DT_BF16) C(DT_F32, DT_BF16);
+        else C(DT_F32, DT_F32);
+    }
+#undef C
+    return hipGetLastError();
+}
+
+template <int R, int CBR>
+static hipError_t launch_comp_rows(const CompArgs &a, int y_dt, int w_dt, hipStream_t s) {
+    const int chunks = (int)((a.N + 511) / 512);
+    const int64_t tasks = (int64_t)chunks * ((a.M + R - 1) / R);
+    const int64_t blocks = (tasks + 3) / 4;
+    const int per_xcd = (int)((blocks + 7) / 8);
+    const dim3 grid((unsigned)per_xcd * 8u), block(256);
+#define C(YD, WD) hipLaunchKernelGGL((k_comp_rows<YD, WD, R, CBR>), grid, block, 0, s, a, chunks, per_xcd)
     if (y_dt == DT_BF16) {
         if (w_dt == DT_BF16) C(DT_BF16, DT_BF16);
         else C(DT_BF16, DT_F32);

@@ -40,7 +40,11 @@ constexpr int BM = 256, BN = 128, NW = 4, NT = 64 * NW;
 constexpr int BKB = 64;                    // bytes of K per row per stage (128 codes)
 constexpr int OPA = BM * BKB;              // A tile per stage: 16 KiB
 constexpr int STB = (BM + BN) * BKB;       // A then B: 24 KiB per stage buffer
-constexpr int UNIT_SCALE = 0x7F7F7F7F;     // E8M0 127 = 2^0 in every byte
+// Block scales of the MFMA: 0 in both scale operands selects the unscaled form of the
+// instruction (V_MFMA_F32_32X32X64_F8F6F4, unit scales).  Its results equal those with explicit
+// E8M0 unit scales (127 in every byte), and it issues faster: 32.7 against 34.4 cycles per
+// MFMA in a chain of independent FP4 MFMAs on one box, at a 4 % higher clock.
+constexpr int UNIT_SCALE = 0;
 constexpr int BUF_FLAGS = 0x00020000;      // raw buffer descriptor word 3 (gfx9 family)
 constexpr int OOB = 0x7FFFFFF0;            // an offset past every buffer: the load returns 0
 

@@ -13,6 +13,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int CHAINS = 8;  // independent accumulators: enough to keep the matrix pipe full
+// Scale operands 0: the unscaled form of the instruction (unit block scales), the form the FP4
+// GEMM issues.
 
 __global__ __launch_bounds__(256, 1) void k_probe_mfma_fp4(int iters, uint64_t *__restrict__ clocks,
                                                            float *__restrict__ sink) {
@@ -36,8 +38,7 @@ __global__ __launch_bounds__(256, 1) void k_probe_mfma_fp4(int iters, uint64_t *
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int c = 0; c < CHAINS; ++c)
-            acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 4, 4, 0, 0x7F7F7F7F, 0,
-                                                                      0x7F7F7F7F);
+            acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 4, 4, 0, 0, 0, 0);
     }
     // the end stamps wait for the last results
     float s = 0.0f;
