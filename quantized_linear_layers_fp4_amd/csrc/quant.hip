@@ -465,6 +465,11 @@ __global__ __launch_bounds__(256) void k_coo_build(Staging stg, const int32_t *_
     __shared__ int32_t off_s[64], cnt_s[64], sc_s[65];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t r0 = (int64_t)blockIdx.x * 64;
+    // wave 0's lanes hold the counts of the workgroup's 64 rows; their load is issued together
+    // with the prefix loads (one memory round trip for both)
+    const int64_t rl = r0 + lane;
+    const uint32_t c = (wave == 0 && rl < M) ? (uint32_t)row_cnt[rl] : 0u;
+    uint32_t base = 0;
     if constexpr (PREFIX) {
         // row_cnt is 16-byte aligned and r0 a multiple of 64: whole 16-byte groups, at most
         // COO_PREFIX_ROWS / 1024 of them per thread, all issued before any is added
@@ -482,37 +487,31 @@ __global__ __launch_bounds__(256) void k_coo_build(Staging stg, const int32_t *_
         for (int o = 32; o > 0; o >>= 1) part += (uint32_t)__shfl_xor((int)part, o, 64);
         if (lane == 0) wsum[wave] = part;
         __syncthreads();
-        if (wave == 0) {
-            const uint32_t base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-            const int64_t r = r0 + lane;
-            const uint32_t c = r < M ? (uint32_t)row_cnt[r] : 0u;
-            const uint32_t incl = wave_incl_scan(c, lane);
-            const int32_t off = (int32_t)(base + incl - c);
-            if (r < M) row_ptr[r] = off;
-            if (r == M - 1) {
+        base = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    }
+    if (wave == 0) {
+        const uint32_t incl = wave_incl_scan(c, lane);
+        int32_t off;
+        if constexpr (PREFIX) {
+            off = (int32_t)(base + incl - c);
+            if (rl < M) row_ptr[rl] = off;
+            if (rl == M - 1) {
                 row_ptr[M] = (int32_t)(base + incl);
                 *nnz_out = (int64_t)(base + incl);
             }
-            off_s[lane] = off;
-            cnt_s[lane] = (int32_t)c;
+        } else {
+            off = rl < M ? row_ptr[rl] : 0;
         }
-    } else {
-        if (wave == 0) {
-            const int64_t r = r0 + lane;
-            off_s[lane] = r < M ? row_ptr[r] : 0;
-            cnt_s[lane] = r < M ? row_cnt[r] : 0;
-        }
+        off_s[lane] = off;
+        cnt_s[lane] = (int32_t)c;
+        // the rows' staged entries (ranks below S) as one flat list: its prefix
+        const uint32_t st = min(c, (uint32_t)stg.S);
+        const uint32_t sincl = wave_incl_scan(st, lane);
+        sc_s[lane] = (int32_t)(sincl - st);
+        if (lane == 63) sc_s[64] = (int32_t)sincl;
     }
     __syncthreads();
-    // staged entries of the 64 rows (ranks below S) as one flat list over the 256 threads: the
-    // row of entry e is found by a binary search in the rows' staged-count prefix
-    if (wave == 0) {
-        const uint32_t st = (uint32_t)min(cnt_s[lane], stg.S);
-        const uint32_t incl = wave_incl_scan(st, lane);
-        sc_s[lane] = (int32_t)(incl - st);
-        if (lane == 63) sc_s[64] = (int32_t)incl;
-    }
-    __syncthreads();
+    // the row of entry e is found by a binary search in the rows' staged-count prefix
     for (int32_t e = tid; e < sc_s[64]; e += 256) {
         int lo = 0, hi = 64;  // the last j with sc_s[j] <= e (rows with no staged entry are skipped)
         while (hi - lo > 1) {
@@ -604,9 +603,12 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
 }
 
 // Quantize a 256 (k) x TN (n) tile of W with the finished column maxima and write it
-// transposed: Wq[n][k/2].  Loads: TN/8 threads per row (16 bytes = 8 columns each), two rows
-// (k, k+1) per thread per pass so each output byte (pair of k) is formed in registers; the
-// transpose goes through a TN x 128-byte LDS tile, written out as 128-byte rows of Wq.
+// transposed: Wq[n][k/2].  Loads: TN/8 threads per row (16 bytes = 8 columns each); each thread
+// takes 8 consecutive rows (4 pairs of k) of its 8 columns, so it forms 4 output bytes of each
+// column in a register and writes them to LDS as one dword.  The transpose tile holds a column's
+// 128 bytes (256 values of k) as 32 dwords; dword j of column c sits at j ^ 4*((c/8) % 8), which
+// spreads a wave's writes over all banks (two lanes per bank) and keeps each 16-byte group whole
+// for the read-out, which writes 128-byte rows of Wq.
 // scales_out: NULL, or fp32[N] (a buffer other than the keys) that the workgroups of the first
 // tile row fill with the dequantization scales of their columns.
 template <int DT, bool RM, int TN>
@@ -615,12 +617,12 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
                                                     const uint32_t *__restrict__ colmax_key,
                                                     uint8_t *__restrict__ codes, float *__restrict__ scales_out) {
     constexpr int TPR = TN / 8;         // threads per row
-    constexpr int RPP = 256 / TPR;      // row pairs per pass
-    constexpr int PASSES = 128 / RPP;   // 128 row pairs = 256 rows per tile
+    constexpr int GPP = 256 / TPR;      // groups of 8 rows per pass
+    constexpr int PASSES = 32 / GPP;    // 32 groups of 8 rows = 256 rows per tile
     constexpr int TPN = 256 / TN;       // threads per output row
-    constexpr int BPT = 128 / TPN;      // output bytes per thread
+    constexpr int DPT = 32 / TPN;       // output dwords per thread
     __shared__ float rs[TN];
-    __shared__ uint8_t tile[TN][128 + 4];
+    __shared__ __attribute__((aligned(16))) uint32_t tile[TN][32];
     const int tid = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * TN, k0 = (int64_t)blockIdx.y * 256;
     if (tid < TN) {
@@ -634,42 +636,41 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
     __syncthreads();
     const int c8 = tid % TPR;         // columns n0 + 8*c8 .. +7
     const int64_t col = n0 + c8 * 8;
+    const int swz = 4 * (c8 & 7);     // the dword swizzle of the thread's columns
     float r8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) r8[e] = rs[c8 * 8 + e];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-        const int j = tid / TPR + RPP * p;  // row pair: rows 2j, 2j+1 of the tile
-        const int64_t k = k0 + 2 * j;
-        uint32_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (col < N && k < K) {  // K % 32 == 0: both rows of a pair are in range together
-            float v0[8], v1[8];
-            uint32_t key0[8], key1[8];
-            load8_rm<DT, RM>(W, row_mult, k, N, col, v0, key0);
-            load8_rm<DT, RM>(W, row_mult, k + 1, N, col, v1, key1);
+        const int jj = tid / TPR + GPP * p;  // rows 8*jj .. 8*jj+7 of the tile: output dword jj
+        const int64_t k = k0 + 8 * jj;
+        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (col < N && k < K) {  // K % 32 == 0: the 8 rows are in range together
+            float v[8][8];
+            uint32_t key[8][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = e2m1_pack2<0>(0u, v0[e] * r8[e], v1[e] * r8[e]) & 0xFFu;
+            for (int q = 0; q < 8; ++q) load8_rm<DT, RM>(W, row_mult, k + q, N, col, v[q], key[q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    w[e] |= (e2m1_pack2<0>(0u, v[2 * q][e] * r8[e], v[2 * q + 1][e] * r8[e]) & 0xFFu) << (8 * q);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tile[c8 * 8 + e][j] = (uint8_t)b[e];
+        for (int e = 0; e < 8; ++e) tile[c8 * 8 + e][jj ^ swz] = w[e];
     }
     __syncthreads();
-    // write out: n = tid / TPN, BPT bytes (2*BPT values of k) per thread
+    // write out: n = tid / TPN, DPT dwords (8*DPT values of k) per thread
     const int nl = tid / TPN, part = tid % TPN;
     const int64_t n = n0 + nl;
-    const int64_t kb = k0 / 2 + part * BPT;  // byte offset within the row of Wq
+    const int rswz = 4 * ((nl >> 3) & 7);
+    const int64_t kb = k0 / 2 + part * DPT * 4;  // byte offset within the row of Wq
     if (n < N) {
 #pragma unroll
-        for (int h = 0; h < BPT / 16; ++h) {
+        for (int h = 0; h < DPT / 4; ++h) {
             if (kb + h * 16 < K / 2) {
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int o = part * BPT + h * 16 + i * 4;
-                    w[i] = (uint32_t)tile[nl][o] | ((uint32_t)tile[nl][o + 1] << 8) |
-                           ((uint32_t)tile[nl][o + 2] << 16) | ((uint32_t)tile[nl][o + 3] << 24);
-                }
-                *reinterpret_cast<uint4 *>(codes + n * (K / 2) + kb + h * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+                const uint4 q = *reinterpret_cast<const uint4 *>(&tile[nl][(part * DPT + 4 * h) ^ rswz]);
+                *reinterpret_cast<uint4 *>(codes + n * (K / 2) + kb + h * 16) = q;
             }
         }
     }

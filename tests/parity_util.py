@@ -24,6 +24,9 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray, denom: np.ndarray, what: str = "Y"):
+    """Checks |Y_gpu - Y_ref| <= REL * denom element by element (denom = |Y_main| + the row's
+    sum |delta_k * W[k][n]|, the scale of the forward error of the compensation sum in any
+    order) and returns the largest err / denom."""
     err = np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64))
     bound = REL * denom
     bad = np.nonzero(err > bound)
@@ -32,6 +35,20 @@ def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray, denom: np.ndarray, what
         raise AssertionError(f"{what}: {bad[0].size} entries beyond tolerance; first at {i}: gpu={y_gpu[i]!r} "
                              f"ref={y_ref[i]!r} denom={denom[i]!r}")
     return float((err / np.maximum(denom, 1e-300)).max()) if err.size else 0.0
+
+
+def plain_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
+    """The plain relative error max |Y_gpu - Y_ref| / |Y_ref| over the entries with
+    |Y_ref| >= 1e-3 * rms(Y_ref) (entries near zero, where Y_main and the compensation cancel,
+    are left out: there only the tolerance above is meaningful).  Reported beside it."""
+    r = y_ref.astype(np.float64).reshape(-1)
+    g = y_gpu.astype(np.float64).reshape(-1)
+    if r.size == 0:
+        return 0.0
+    keep = np.abs(r) >= 1e-3 * np.sqrt(np.mean(r * r))
+    if not keep.any():
+        return 0.0
+    return float((np.abs(g[keep] - r[keep]) / np.abs(r[keep])).max())
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
