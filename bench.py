@@ -87,10 +87,9 @@ def _kernel_is(name: str):
 
 
 def _gemm_main(name: str):
-    """The GEMM launch proper among rocprofv3 kernel names: `name` without its escape-pass
-    instantiation (the last template argument true)."""
-    is_k = _kernel_is(name)
-    return lambda n: is_k(n) and not n.split("(")[0].rstrip().endswith("true>")
+    """The GEMM launch among rocprofv3 kernel names: the kernel `name` (the escape kernel that
+    follows a two-byte product is another kernel, k_q16_escapes)."""
+    return _kernel_is(name)
 
 
 def gemm_src_sha() -> str:
@@ -375,9 +374,9 @@ def run_full(args):
             if r == 0:
                 host0.append((A, W, L))
             Ad, Wd = A.to(dev), W.to(dev)
-            layers.append(dict(A=Ad, W=Wd, L=L, ws=fp4.workspace(Ad, L.N, L.q),
-                               Y=torch.empty((L.M, L.N), dtype=torch.bfloat16 if L.out_dtype == "bf16" else torch.float32,
-                                             device=dev)))
+            ydt = torch.bfloat16 if L.out_dtype == "bf16" else torch.float32
+            layers.append(dict(A=Ad, W=Wd, L=L, ws=fp4.workspace(Ad, L.N, L.q, ydt),
+                               Y=torch.empty((L.M, L.N), dtype=ydt, device=dev)))
             if args.wq != "per-step":
                 layers[-1]["Wq"], layers[-1]["sW"] = fp4.quantize_weights(Wd)
         sets.append(layers)
@@ -417,7 +416,7 @@ def run_full(args):
     hot, hot_total, _ = per_step_times(forward, args.steps, args.warmup, 1)
 
     # the stages of the forward, each between events of its own (hot cache, set 0): the A-side
-    # quantizer, the W-side quantizer, the product (GEMM + escape pass + compensation)
+    # quantizer, the W-side quantizer, the product (GEMM + compensation + escape kernel)
     names = ("quant_A", "quant_W", "product")
     stage_ms = {k: [] for k in names}
 
@@ -449,7 +448,7 @@ def run_full(args):
     product_ms = float(np.median(stage_ms["product"]))
 
     # the dominant kernel alone, as the forward launches it: the GEMM with the two-byte
-    # accumulator hand-over (FP4_Q16) and its escape pass (which finds no tile to redo here)
+    # accumulator hand-over (FP4_Q16) and its escape kernel (which finds no block to redo here)
     gemm_ms, nnz_total, qa_bytes, qw_bytes, cbytes = 0.0, 0, 0, 0, 0
     per_layer = []
     for d in sets[0]:

@@ -78,11 +78,13 @@ enum {
 };
 enum { FP4_F32 = 0, FP4_BF16 = 1 };          /* element types of A, W, X, Y */
 /* Output type of fp4_gemm only (no compensation term): the exact accumulator in two bytes.
- * Element (m, n) is the int16 4*acc (acc is a multiple of 1/4), except in the output tiles
- * (256 x 128 or 256 x 256, as the library tiles the shape) that hold some |acc| > 8191.75:
- * there every element is -32768 and the workspace holds fl(fl(acc*sA)*sW) as fp32 at
- * element (m, n) (those tiles are recomputed by a second launch).  This is how the GEMM hands its result to the compensation pass
- * inside fp4_gemm and fp4_linear_forward. */
+ * Element (m, n) is the int16 4*acc (acc is a multiple of 1/4), except in escaped blocks:
+ * aligned 128-row x 64-column blocks (rows 128i.., columns 64j..), each lying in an aligned
+ * 128 x 128 block that holds some |acc| > 8191.75, and covering every such element.  There
+ * every element is -32768 and the workspace holds fl(fl(acc*sA)*sW) as fp32 at element
+ * (m, n) (those blocks are recomputed by a second kernel).  This is how the GEMM hands its
+ * result to the compensation pass inside fp4_gemm and fp4_linear_forward, where the escaped
+ * blocks are instead written straight to Y. */
 enum { FP4_Q16 = 2 };
 enum { FP4_PER_ROW = 0, FP4_PER_COL = 1 };   /* token-wise (A) / channel-wise (W) */
 
@@ -145,12 +147,11 @@ fp4_status fp4_outlier_clamp_noalloc(const void *A, int32_t a_dtype, int64_t M, 
                                      float *T, int32_t *coo_row, int32_t *coo_col, float *coo_val,
                                      int64_t capacity, int32_t *row_ptr, int64_t *nnz, void *stream);
 
-/* Host-only: workspace bytes fp4_gemm needs: with the compensation term about M * N * 4 for
- * a bf16 Y (the fp32 escapes of the two-byte hand-over; the accumulators go through Y
- * itself) and about M * N * 2 for an fp32 Y (the accumulators; the escapes go through Y);
- * for y_dtype FP4_Q16 (no compensation term) about M * N * 4 (the escapes); each plus 4 bytes
- * per 256 x 128 output block (flags of the escape pass); else 0 (also 0 for invalid
- * arguments). */
+/* Host-only: workspace bytes fp4_gemm needs: with the compensation term, one byte per
+ * 128 x 64 output block (the map of escaped blocks) for a bf16 Y (the two-byte hand-over
+ * goes through Y itself), plus M * N * 2 for an fp32 Y (the hand-over); for y_dtype FP4_Q16
+ * (no compensation term) M * N * 4 (the fp32 escapes) plus the map; else 0 (also 0 for
+ * invalid arguments).  Each part is rounded up to 256 bytes. */
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t with_comp);
 
 /* The FP4 GEMM with dequantization, plus the sparse compensation term (QbitAI report,
@@ -168,9 +169,11 @@ size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t w
  *   workspace, ws_bytes: device scratch of at least fp4_gemm_workspace_bytes() bytes
  *            (may be NULL when that is 0).  With dA the GEMM hands its accumulator to the
  *            compensation pass as FP4_Q16 elements (in Y for a bf16 Y, in the workspace for
- *            an fp32 Y) with the escapes in the other buffer; the pass rebuilds
- *            Y_main = fl(fl(acc*sA)*sW) bit for bit from them.
- * Two kernels run on the stream: the GEMM, then (with dA) the compensation pass.
+ *            an fp32 Y) with the map of escaped blocks in the workspace; the pass rebuilds
+ *            Y_main = fl(fl(acc*sA)*sW) bit for bit from them, and the escaped blocks are
+ *            recomputed from the codes and written with the same arithmetic.
+ * Kernels run on the stream in order: the GEMM; then, for FP4_Q16, the escape kernel; with
+ * dA, the compensation pass and the escape kernel.
  * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,WORKSPACE,ALIGN,DEVICE,HIP}. */
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW,
                     int64_t M, int64_t N, int64_t K, const int32_t *row_ptr,
@@ -219,24 +222,28 @@ struct fp4_ws_layout {
     size_t row_ptr;               /* int32[M+1] */
     size_t coo_row, coo_col, coo_val; /* capacity entries each */
     size_t Aq, sA, Wq, sW;        /* codes and scales */
-    size_t handoff;               /* the GEMM's hand-over to the compensation pass (fp32
-                                     escapes for a bf16 Y, int16 accumulators for an fp32
-                                     Y; see FP4_Q16) and the escape pass's flags */
+    size_t handoff;               /* the GEMM's hand-over to the compensation pass (the int16
+                                     accumulators for an fp32 Y, nothing for a bf16 Y, which
+                                     holds them itself; see FP4_Q16) and the map of escaped
+                                     blocks.  It is the last region of the workspace: every
+                                     other offset is the same for both Y types. */
     size_t scratch;               /* internal */
     int64_t capacity;             /* fp4_outlier_capacity(M, K, q) */
 };
 
-/* Host-only: workspace layout / size of fp4_linear_forward (returns FP4_OK or an
- * argument error; size 0 on error). */
-fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q,
+/* Host-only: workspace layout / size of fp4_linear_forward for Y of y_dtype (returns FP4_OK
+ * or an argument error; size 0 on error). */
+fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, int32_t y_dtype, double q,
                               struct fp4_ws_layout *out);
-size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q);
+size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_dtype, int32_t y_dtype,
+                                   double q);
 
 /* The whole forward of one FP4 linear layer (QbitAI report, forward-quantization and
  * outlier paragraphs): quantile and clamp of A with dA, token-wise quantization of
  * A_clamped, channel-wise quantization of W, FP4 GEMM, dequantization, compensation.
  *   A  M x K, W  K x N, both of in_dtype; Y  M x N of y_dtype (out)
- *   workspace: at least fp4_forward_workspace_bytes() bytes (layout: fp4_forward_layout).
+ *   workspace: at least fp4_forward_workspace_bytes(..., y_dtype, q) bytes (layout:
+ *            fp4_forward_layout).
  * Returns FP4_OK or FP4_ERR_{NULL,SHAPE,DTYPE,QUANTILE,WORKSPACE,ALIGN,DEVICE,HIP}. */
 fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, int64_t M,
                               int64_t K, int64_t N, double q, void *Y, int32_t y_dtype,
@@ -251,6 +258,8 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
  *   granularity and forward-quantization paragraphs); FP4_STAGE_W = the channel-wise codes and
  *   scales of W (granularity paragraph).  A (resp. W) may be NULL when its stage is not asked
  *   for.  Run apart, the W stage takes one more (zero-fill) launch than inside the forward.
+ *   It uses the workspace up to the layout's handoff offset, which is the same for both Y
+ *   types, and needs at least that many bytes.
  * fp4_forward_product: the FP4 GEMM with dequantization and the compensation dA . W (GEMM-kernel
  *   and outlier paragraphs) from the workspace's intermediates (both stages must have run on it
  *   for the same A, W, q) into Y (M x N of y_dtype); W is the original weight.

@@ -70,8 +70,8 @@ def lib():
         "fp4_outlier_clamp_noalloc": (i32, [vp, i32, i64, i64, dbl, vp, vp, vp, vp, i64, vp, vp, vp]),
         "fp4_gemm_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "fp4_gemm": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, i64, vp, i32, vp, i32, vp, vp, sz, vp]),
-        "fp4_forward_layout": (i32, [i64, i64, i64, i32, dbl, C.POINTER(WsLayout)]),
-        "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, dbl]),
+        "fp4_forward_layout": (i32, [i64, i64, i64, i32, i32, dbl, C.POINTER(WsLayout)]),
+        "fp4_forward_workspace_bytes": (sz, [i64, i64, i64, i32, i32, dbl]),
         "fp4_linear_forward": (i32, [vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_linear_forward_wq": (i32, [vp, vp, vp, vp, i32, i64, i64, i64, dbl, vp, i32, vp, sz, vp]),
         "fp4_forward_quantize": (i32, [vp, vp, i32, i64, i64, i64, dbl, i32, vp, sz, vp]),
@@ -215,7 +215,8 @@ def gemm(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor,
 def gemm_q16(Aq: torch.Tensor, sA: torch.Tensor, Wq: torch.Tensor, sW: torch.Tensor, K: int,
              acc_out: bool = False):
     """The exact accumulator in two bytes (FP4_Q16): (Yq int16 M x N, esc fp32 M x N), where
-    Yq = 4*acc when |acc| <= 8191.75, else -32768 with esc = fl(fl(acc*sA)*sW) there."""
+    Yq = 4*acc, except in the escaped 128 x 64 blocks (those around some |acc| > 8191.75):
+    there Yq = -32768 and esc = fl(fl(acc*sA)*sW)."""
     _need_cuda(Aq, sA, Wq, sW)
     M, N = Aq.shape[0], Wq.shape[0]
     Yq = torch.empty((M, N), dtype=torch.int16, device=Aq.device)
@@ -264,16 +265,19 @@ def fp8_dequantize(codes: torch.Tensor, scale: torch.Tensor, out_dtype: torch.dt
     return Y
 
 
-def forward_layout(M: int, K: int, N: int, dtype: torch.dtype, q: float) -> WsLayout:
+def forward_layout(M: int, K: int, N: int, dtype: torch.dtype, q: float,
+                   out_dtype: torch.dtype | None = None) -> WsLayout:
+    """The forward workspace's layout for inputs of dtype and Y of out_dtype (default: dtype)."""
     lay = WsLayout()
-    _check(lib().fp4_forward_layout(M, K, N, _out_dtype_code(dtype), float(q), C.byref(lay)))
+    _check(lib().fp4_forward_layout(M, K, N, _out_dtype_code(dtype), _out_dtype_code(out_dtype or dtype), float(q),
+                                    C.byref(lay)))
     return lay
 
 
-def workspace(A: torch.Tensor, N: int, q: float) -> torch.Tensor:
-    """A workspace tensor sized for linear_forward(A, W (K x N), q)."""
+def workspace(A: torch.Tensor, N: int, q: float, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """A workspace tensor sized for linear_forward(A, W (K x N), q, out_dtype)."""
     M, K = A.shape
-    lay = forward_layout(M, K, N, A.dtype, q)
+    lay = forward_layout(M, K, N, A.dtype, q, out_dtype)
     return torch.empty(lay.total, dtype=torch.uint8, device=A.device)
 
 
@@ -287,7 +291,7 @@ def linear_forward(A: torch.Tensor, W: torch.Tensor, q: float, out_dtype: torch.
     N = W.shape[1]
     out_dtype = out_dtype or A.dtype
     if ws is None:
-        ws = workspace(A, N, q)
+        ws = workspace(A, N, q, out_dtype)
     if Y is None:
         Y = torch.empty((M, N), dtype=out_dtype, device=A.device)
     _check(lib().fp4_linear_forward(_ptr(A), _ptr(W), _dt(A), M, K, N, float(q), _ptr(Y), _dt(Y), _ptr(ws),
@@ -335,7 +339,7 @@ def linear_forward_wq(A: torch.Tensor, W: torch.Tensor, Wq: torch.Tensor, sW: to
     N = W.shape[1]
     out_dtype = out_dtype or A.dtype
     if ws is None:
-        ws = workspace(A, N, q)
+        ws = workspace(A, N, q, out_dtype)
     if Y is None:
         Y = torch.empty((M, N), dtype=out_dtype, device=A.device)
     _check(lib().fp4_linear_forward_wq(_ptr(A), _ptr(W), _ptr(Wq), _ptr(sW), _dt(A), M, K, N, float(q), _ptr(Y),

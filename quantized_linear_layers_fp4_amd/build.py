@@ -24,7 +24,7 @@ PROBE_SOURCES = ["probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "quant.hip", "gemm.hip", "comp.hip", "emu.hip", "fp8codec.hip", "bwd.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "gemm.hip", "comp.hip", "escape.hip", "emu.hip", "fp8codec.hip", "bwd.hip", "noalloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -37,33 +37,50 @@ bool gemm_ok(int64_t M, int64_t N, int64_t K) { return mk_ok(M, K) && n_ok(N) &&
 bool wcomp_ok(int64_t N, int64_t K, int32_t w_dtype) {
     return K * N * (w_dtype == FP4_BF16 ? 2 : 4) <= (int64_t)0x7FFFFFFF;
 }
-// Where the GEMM's two-byte accumulators, their fp32 escapes and the escape pass's tile
-// flags go on the way to a compensated Y (or to an FP4_Q16 output): a bf16 Y (and an
-// FP4_Q16 output) holds the accumulators itself and the workspace the escapes (M*N*4 bytes);
-// an fp32 Y holds the escapes and the workspace the accumulators (M*N*2 bytes).  The flags
-// follow in the workspace.
-size_t q16_main_bytes(int64_t M, int64_t N, int32_t y_dtype) {
-    return align_up((size_t)M * (size_t)N * (y_dtype == FP4_F32 ? 2 : 4));
+// Where the GEMM's two-byte accumulators and its map of escaped blocks go.  On the way to a
+// compensated Y (comp): into a bf16 Y itself, or into the workspace (M*N*2 bytes) for an fp32
+// Y; the escaped blocks are then written by the escape kernel, so no fp32 values are kept.
+// As the standalone FP4_Q16 output: into Y, with the fp32 escape buffer (M*N*4 bytes) in the
+// workspace.  The map follows in the workspace.
+size_t q16_main_bytes(int64_t M, int64_t N, int32_t y_dtype, bool comp) {
+    if (!comp) return align_up((size_t)M * (size_t)N * 4);
+    return y_dtype == FP4_F32 ? align_up((size_t)M * (size_t)N * 2) : 0;
 }
-size_t q16_ws_bytes(int64_t M, int64_t N, int32_t y_dtype) {
-    return q16_main_bytes(M, N, y_dtype) + align_up(gemm_flag_bytes(M, N));
+size_t q16_ws_bytes(int64_t M, int64_t N, int32_t y_dtype, bool comp) {
+    return q16_main_bytes(M, N, y_dtype, comp) + align_up(esc_map_bytes(M, N));
 }
 struct Q16Bufs {
     int16_t *yq;
-    float *esc;
-    uint8_t *flags;
+    float *esc;  // standalone FP4_Q16 output only
+    uint8_t *emap;
 };
-Q16Bufs q16_buffers(void *Y, int32_t y_dtype, uint8_t *ws, int64_t M, int64_t N) {
+Q16Bufs q16_buffers(void *Y, int32_t y_dtype, uint8_t *ws, int64_t M, int64_t N, bool comp) {
     Q16Bufs b;
-    if (y_dtype == FP4_F32) {
+    b.esc = nullptr;
+    if (comp && y_dtype == FP4_F32) {
         b.yq = reinterpret_cast<int16_t *>(ws);
-        b.esc = static_cast<float *>(Y);
     } else {
         b.yq = static_cast<int16_t *>(Y);
-        b.esc = reinterpret_cast<float *>(ws);
+        if (!comp) b.esc = reinterpret_cast<float *>(ws);
     }
-    b.flags = ws + q16_main_bytes(M, N, y_dtype);
+    b.emap = ws + q16_main_bytes(M, N, y_dtype, comp);
     return b;
+}
+// The compensated product: the GEMM's two-byte hand-over and map, the compensation pass over
+// the blocks that the hand-over holds, and the escape kernel over the others.
+hipError_t launch_product_comp(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
+                               int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
+                               const float *coo_val, int64_t capacity, const void *W, int32_t w_dtype, void *Y,
+                               int32_t y_dtype, float *acc_out, uint8_t *ws, hipStream_t s) {
+    const Q16Bufs b = q16_buffers(Y, y_dtype, ws, M, N, true);
+    hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, acc_out, s, false, b.emap);
+    if (e == hipSuccess)
+        e = launch_comp(b.yq, b.emap, sA, sW, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype),
+                        capacity, s);
+    if (e == hipSuccess)
+        e = launch_escapes_comp(Aq, sA, Wq, sW, M, N, K, b.emap, row_ptr, coo_col, coo_val, W, dt_of(w_dtype), Y,
+                                dt_of(y_dtype), s);
+    return e;
 }
 
 // The COO list of dA is indexed with int32 (row_ptr), and the kernels address it with
@@ -211,13 +228,15 @@ int64_t outlier_capacity_of(int64_t M, int64_t K, double q) { return capacity_of
 
 namespace {
 // Checks shared by the forward's calls; fills the layout and the CU count.
-fp4_status forward_check(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q, size_t ws_bytes,
-                         const void *workspace, fp4_ws_layout *l, int *cus) {
+// need_product: the product stage runs (the workspace must hold the whole layout for y_dtype);
+// else only the quantizer stages, which use the part before the hand-over.
+fp4_status forward_check(int64_t M, int64_t K, int64_t N, int32_t in_dtype, int32_t y_dtype, double q,
+                         size_t ws_bytes, const void *workspace, bool need_product, fp4_ws_layout *l, int *cus) {
     if (!workspace) return FP4_ERR_NULL;
-    if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
-    fp4_status st = fp4_forward_layout(M, K, N, in_dtype, q, l);
+    if (!dtype_ok(in_dtype) || !dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
+    fp4_status st = fp4_forward_layout(M, K, N, in_dtype, y_dtype, q, l);
     if (st != FP4_OK) return st;
-    if (ws_bytes < l->total) return FP4_ERR_WORKSPACE;
+    if (ws_bytes < (need_product ? l->total : l->handoff)) return FP4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FP4_ERR_ALIGN;
     return FP4_OK;
 }
@@ -251,21 +270,16 @@ fp4_status quantize_impl(const void *A, const void *W, int32_t in_dtype, int64_t
     return FP4_OK;
 }
 
-// The product stage: the accumulator as int16 4*acc (into a bf16 Y itself, else into the
-// workspace) with fp32 escapes (into the workspace, else into the fp32 Y), then
-// Y = Y_main + dA . W from the workspace's intermediates; Wq/sW: W's codes and scales (the
+// The product stage: Y = Y_main + dA . W from the workspace's intermediates, through the
+// two-byte hand-over in the layout's handoff region; Wq/sW: W's codes and scales (the
 // workspace's, or a caller's cached ones).
 fp4_status product_impl(const void *W, int32_t in_dtype, const uint8_t *Wq, const float *sW, int64_t M, int64_t K,
                         int64_t N, void *Y, int32_t y_dtype, uint8_t *ws, const fp4_ws_layout &l, hipStream_t s) {
-    const Q16Bufs b = q16_buffers(Y, y_dtype, ws + l.handoff, M, N);
-    const uint8_t *Aq = ws + l.Aq;
-    const float *sA = reinterpret_cast<const float *>(ws + l.sA);
-    hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, nullptr, s, false, b.esc, b.flags);
-    if (e == hipSuccess)
-        e = launch_comp(b.yq, b.esc, sA, sW, Y, dt_of(y_dtype), M, N, K, reinterpret_cast<const int32_t *>(ws + l.row_ptr),
-                        reinterpret_cast<const int32_t *>(ws + l.coo_col), reinterpret_cast<const float *>(ws + l.coo_val),
-                        W, dt_of(in_dtype), l.capacity, s);
-    return hip_status(e);
+    return hip_status(launch_product_comp(
+        ws + l.Aq, reinterpret_cast<const float *>(ws + l.sA), Wq, sW, M, N, K,
+        reinterpret_cast<const int32_t *>(ws + l.row_ptr), reinterpret_cast<const int32_t *>(ws + l.coo_col),
+        reinterpret_cast<const float *>(ws + l.coo_val), l.capacity, W, in_dtype, Y, y_dtype, nullptr,
+        ws + l.handoff, s));
 }
 
 // The forward; Wq_in/sW_in: W's codes and scales from an earlier fp4_quantize (W unchanged
@@ -277,7 +291,7 @@ fp4_status forward_impl(const void *A, const void *W, const uint8_t *Wq_in, cons
     if (!dtype_ok(in_dtype) || !dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
     fp4_ws_layout l;
     int cus;
-    fp4_status st = forward_check(M, K, N, in_dtype, q, ws_bytes, workspace, &l, &cus);
+    fp4_status st = forward_check(M, K, N, in_dtype, y_dtype, q, ws_bytes, workspace, true, &l, &cus);
     if (st != FP4_OK) return st;
     if (!aligned16(A) || !aligned16(W) || !aligned16(Y)) return FP4_ERR_ALIGN;
     st = device_check(&cus);
@@ -352,9 +366,9 @@ fp4_status fp4_outlier_clamp(const void *A, int32_t a_dtype, int64_t M, int64_t 
 
 size_t fp4_gemm_workspace_bytes(int64_t M, int64_t N, int32_t y_dtype, int32_t with_comp) {
     if (M < 1 || !n_ok(N)) return 0;
-    if (y_dtype == FP4_Q16) return with_comp ? 0 : q16_ws_bytes(M, N, y_dtype);
+    if (y_dtype == FP4_Q16) return with_comp ? 0 : q16_ws_bytes(M, N, y_dtype, false);
     if (!dtype_ok(y_dtype) || !with_comp) return 0;
-    return q16_ws_bytes(M, N, y_dtype);
+    return q16_ws_bytes(M, N, y_dtype, true);
 }
 
 fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
@@ -380,16 +394,15 @@ fp4_status fp4_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const
     if (st != FP4_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (q16) {
-        const Q16Bufs b = q16_buffers(Y, y_dtype, static_cast<uint8_t *>(workspace), M, N);
-        return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, acc_out, s, false, b.esc, b.flags));
+        const Q16Bufs b = q16_buffers(Y, y_dtype, static_cast<uint8_t *>(workspace), M, N, false);
+        hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, acc_out, s, false, b.emap);
+        if (e == hipSuccess) e = launch_escapes_q16(Aq, sA, Wq, sW, M, N, K, b.emap, b.yq, b.esc, s);
+        return hip_status(e);
     }
     if (!comp) return hip_status(launch_gemm(Aq, sA, Wq, sW, M, N, K, Y, dt_of(y_dtype), acc_out, s));
-    const Q16Bufs b = q16_buffers(Y, y_dtype, static_cast<uint8_t *>(workspace), M, N);
-    hipError_t e = launch_gemm(Aq, sA, Wq, sW, M, N, K, b.yq, DT_Q16, acc_out, s, false, b.esc, b.flags);
-    if (e == hipSuccess)
-        e = launch_comp(b.yq, b.esc, sA, sW, Y, dt_of(y_dtype), M, N, K, row_ptr, coo_col, coo_val, W, dt_of(w_dtype),
-                        capacity > 0 ? capacity : 0, s);
-    return hip_status(e);
+    return hip_status(launch_product_comp(Aq, sA, Wq, sW, M, N, K, row_ptr, coo_col, coo_val,
+                                          capacity > 0 ? capacity : 0, W, w_dtype, Y, y_dtype, acc_out,
+                                          static_cast<uint8_t *>(workspace), s));
 }
 
 const char *fp4_gemm_kernel_name(int64_t M, int64_t N, int64_t K, int32_t num_cus) {
@@ -463,11 +476,11 @@ fp4_status fp4_gemm_fp8emu(const uint8_t *Aq, const float *sA, const uint8_t *Wq
     return hip_status(e);
 }
 
-fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q,
+fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype, int32_t y_dtype, double q,
                               struct fp4_ws_layout *out) {
     if (!out) return FP4_ERR_NULL;
     std::memset(out, 0, sizeof(*out));
-    if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
+    if (!dtype_ok(in_dtype) || !dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
     if (!gemm_ok(M, N, K) || !wcomp_ok(N, K, in_dtype)) return FP4_ERR_SHAPE;
     if (!q_ok(q)) return FP4_ERR_QUANTILE;
     const int64_t cap = capacity_of(M, K, q);
@@ -484,16 +497,16 @@ fp4_status fp4_forward_layout(int64_t M, int64_t K, int64_t N, int32_t in_dtype,
     out->sA = off; off += align_up((size_t)M * 4);
     out->Wq = off; off += align_up((size_t)N * (size_t)(K / 2));
     out->sW = off; off += align_up((size_t)N * 4);
-    out->handoff = off; off += q16_ws_bytes(M, N, FP4_BF16);  // the larger of the two hand-overs
     out->scratch = off; off += outlier_ws(M, K, in_dtype, cap).total + align_up((size_t)N * 4);  // + W's keys
+    out->handoff = off; off += q16_ws_bytes(M, N, y_dtype, true);  // last: the only part that depends on Y's type
     out->total = off;
     out->capacity = cap;
     return FP4_OK;
 }
 
-size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_dtype, double q) {
+size_t fp4_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t in_dtype, int32_t y_dtype, double q) {
     fp4_ws_layout l;
-    return fp4_forward_layout(M, K, N, in_dtype, q, &l) == FP4_OK ? l.total : 0;
+    return fp4_forward_layout(M, K, N, in_dtype, y_dtype, q, &l) == FP4_OK ? l.total : 0;
 }
 
 fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N,
@@ -507,7 +520,8 @@ fp4_status fp4_forward_quantize(const void *A, const void *W, int32_t in_dtype, 
     if (((stages & FP4_STAGE_A) && !A) || ((stages & FP4_STAGE_W) && !W)) return FP4_ERR_NULL;
     fp4_ws_layout l;
     int cus;
-    fp4_status st = forward_check(M, K, N, in_dtype, q, ws_bytes, workspace, &l, &cus);
+    // the quantizer stages' part of the layout is the same for every Y type
+    fp4_status st = forward_check(M, K, N, in_dtype, FP4_BF16, q, ws_bytes, workspace, false, &l, &cus);
     if (st != FP4_OK) return st;
     if (((stages & FP4_STAGE_A) && !aligned16(A)) || ((stages & FP4_STAGE_W) && !aligned16(W))) return FP4_ERR_ALIGN;
     st = device_check(&cus);
@@ -522,7 +536,7 @@ fp4_status fp4_forward_product(const void *W, int32_t in_dtype, int64_t M, int64
     if (!dtype_ok(y_dtype)) return FP4_ERR_DTYPE;
     fp4_ws_layout l;
     int cus;
-    fp4_status st = forward_check(M, K, N, in_dtype, q, ws_bytes, workspace, &l, &cus);
+    fp4_status st = forward_check(M, K, N, in_dtype, y_dtype, q, ws_bytes, workspace, true, &l, &cus);
     if (st != FP4_OK) return st;
     if (!aligned16(W) || !aligned16(Y)) return FP4_ERR_ALIGN;
     st = device_check(&cus);

@@ -2,8 +2,9 @@
 // paragraph of the QbitAI report on "Optimizing Large Language Model Training Using FP4
 // Quantization": the entries clamped away from A are kept as a sparse matrix and their
 // product with the weights is added back).  They run after the FP4 GEMM, which hands over
-// its exact accumulator as two-byte integers 4*acc (fp32 escapes for |acc| > 8191.75); the
-// pass rebuilds the dequantized product Y_main = fl(fl(acc*sA)*sW) bit for bit and writes
+// its exact accumulator as two-byte integers 4*acc (the 128 x 64 blocks where some
+// |acc| > 8191.75 does not fit are marked in a map; the pass leaves them to the escape
+// kernel, escape.hip, which computes them with the same arithmetic); the pass rebuilds the dequantized product Y_main = fl(fl(acc*sA)*sW) bit for bit and writes
 // Y = Y_main + dA . W in the output type, rounded once, the entries added in ascending k with
 // one fp32 fma each.  The two-byte hand-over halves the bytes that an fp32 Y_main would cost
 // on both sides of the pass.
@@ -56,25 +57,15 @@ __device__ __forceinline__ float seg_elem(const v4i (&raw)[2], int c) {
 }
 
 // Decodes the lane's CC int16 accumulator codes q (packed in qv) into Y_main: acc = q / 4
-// exactly, Y_main = fl(fl(acc * sA) * sW) as the GEMM's own epilogue rounds it; escaped
-// elements take their fp32 value from er (the row's escape values).  Yq may be Y itself
-// (bf16 Y) and esc may be Y itself (fp32 Y): every lane reads exactly the bytes it later
-// writes, and no other lane touches them.
+// exactly, Y_main = fl(fl(acc * sA) * sW) as the GEMM's own epilogue rounds it.  Yq may be Y
+// itself (bf16 Y): every lane reads exactly the bytes it later writes, and no other lane
+// touches them.
 template <int CC>
-__device__ __forceinline__ void decode_ymain(const v4i &qv, const v4i (&swv)[2], float sa, bool active,
-                                             const float *er, int col, float (&y)[CC]) {
-    bool escaped = false;
+__device__ __forceinline__ void decode_ymain(const v4i &qv, const v4i (&swv)[2], float sa, float (&y)[CC]) {
 #pragma unroll
     for (int i = 0; i < CC; ++i) {
         const int q = (int)(int16_t)(((uint32_t)qv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-        escaped |= q == Q16_ESC;
         y[i] = ((float)q * 0.25f * sa) * __int_as_float(swv[i >> 2][i & 3]);
-    }
-    if (__builtin_amdgcn_ballot_w64(escaped)) {  // |acc| > Q16_MAX_ACC somewhere in the wave
-#pragma unroll
-        for (int i = 0; i < CC; ++i)
-            if (active && (int)(int16_t)(((uint32_t)qv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) == Q16_ESC)
-                y[i] = er[col + i];
     }
 }
 
@@ -99,7 +90,8 @@ __device__ __forceinline__ void store_y(void *Y, size_t off, const float (&y)[CC
 
 struct CompArgs {
     const int16_t *Yq;
-    const float *esc;
+    const uint8_t *emap;  // the GEMM's map of escaped ESC_ROWS x ESC_COLS blocks, cellsN per row
+    int cellsN;
     const float *sA, *sW;
     void *Y;
     int M, N, K;
@@ -113,7 +105,7 @@ template <int YDT, int WDT, int CC>
 __device__ __forceinline__ void comp_task(const CompArgs &a, int row, int chunk, int lane) {
     const int N = a.N;
     const int col = chunk * (64 * CC) + lane * CC;
-    const bool active = col < N;  // N % 8 == 0: a lane's columns are in range together
+    const bool inside = col < N;  // N % 8 == 0: a lane's columns are in range together
     // The row's CSR offsets (lane l loads row_ptr[row + (l & 1)]), the lane's accumulator
     // codes and column scales, issued together; the codes and scales go through
     // descriptors, so a lane past N reads zeros.
@@ -132,10 +124,13 @@ __device__ __forceinline__ void comp_task(const CompArgs &a, int row, int chunk,
 #pragma unroll
     for (int h = 0; h < CC / 4; ++h) swv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16 * h, 0, 0);
     const float sa = a.sA[row];
+    // a lane's CC columns lie in one block of the map (CC divides ESC_COLS)
+    uint8_t escaped = 0;
+    if (inside) escaped = a.emap[(size_t)(row / ESC_ROWS) * a.cellsN + col / ESC_COLS];
     const int32_t e0 = __builtin_amdgcn_readlane(rp, 0);
     const int32_t e1 = __builtin_amdgcn_readlane(rp, 1);
     float y[CC];
-    decode_ymain<CC>(qv, swv, sa, active, a.esc + (size_t)row * N, col, y);
+    decode_ymain<CC>(qv, swv, sa, y);
 
     // W through a buffer descriptor.  Offsets are unsigned 32-bit: K*N*ESZ < 2^31, so the
     // largest (a lane past N on the last row of W) stays below 2^32 and reads zeros; such a
@@ -171,7 +166,7 @@ __device__ __forceinline__ void comp_task(const CompArgs &a, int row, int chunk,
             }
         }
     }
-    if (active) store_y<YDT, CC>(a.Y, (size_t)row * N + col, y);
+    if (inside && !escaped) store_y<YDT, CC>(a.Y, (size_t)row * N + col, y);
 }
 
 template <int YDT, int WDT, int CC>
@@ -183,104 +178,6 @@ __global__ __launch_bounds__(256) void k_comp_apply(CompArgs a, int chunks, int 
     const int chunk = (int)(task / a.M);
     const int row = (int)(task - (int64_t)chunk * a.M);
     comp_task<YDT, WDT, CC>(a, row, chunk, lane);
-}
-
-// R consecutive rows of one 512-column chunk per wave (lane l owns the 8 columns 8l .. of the
-// chunk in every row).  A single task is a chain of three dependent memory round trips (the
-// CSR offsets, then the row's entries, then their W row segments); here the R rows'
-// accumulator codes, the chunk's column scales and the R + 1 offsets are requested together,
-// then the rows' entries with one load per lane, then the W segments of up to CB entries of
-// every row at once, so one chain serves R rows.  Each row's entries are still added in
-// ascending k, one fp32 fma each, from Y_main: the results are those of k_comp_apply.
-template <int YDT, int WDT, int R, int CBR>
-__device__ __forceinline__ void comp_rows(const CompArgs &a, int r0, int chunk, int lane) {
-    constexpr int CC = 8;
-    const int N = a.N, M = a.M;
-    const int col = chunk * (64 * CC) + lane * CC;
-    const bool active = col < N;  // N % 8 == 0: a lane's columns are in range together
-    const int32_t rp = a.row_ptr[min(r0 + min(lane, R), M)];
-    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.sW), 0, N * 4, 0x00020000);
-    v4i qv[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const int row = min(r0 + i, M - 1);
-        const __amdgpu_buffer_rsrc_t rsQ =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<int16_t *>(a.Yq) + (size_t)row * N, 0, N * 2, 0x00020000);
-        qv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsQ, col * 2, 0, 2);
-    }
-    v4i swv[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) swv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16 * h, 0, 0);
-    float sa[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) sa[i] = a.sA[min(r0 + i, M - 1)];
-    int32_t eb[R + 1];
-#pragma unroll
-    for (int i = 0; i <= R; ++i) eb[i] = __builtin_amdgcn_readlane(rp, i);
-    float y[R][CC];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-        decode_ymain<CC>(qv[i], swv, sa[i], active, a.esc + (size_t)min(r0 + i, M - 1) * N, col, y[i]);
-
-    constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
-    const __amdgpu_buffer_rsrc_t rsW =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.W), 0, (int)((int64_t)a.K * N * ESZ), 0x00020000);
-    const uint32_t row_bytes = (uint32_t)N * ESZ;
-    const uint32_t lane_off = (uint32_t)col * ESZ;
-    const int32_t e0 = eb[0], total = eb[R] - eb[0];
-    for (int32_t base = 0; base < total; base += 64) {  // 64 entries of the rows per window
-        int32_t kk = 0;
-        float dd = 0.0f;
-        if (base + lane < total) {
-            kk = a.coo_col[e0 + base + lane];
-            dd = a.coo_val[e0 + base + lane];
-        }
-        int lo[R], n[R], nmax = 0;  // row i's entries in this window: indices lo[i] .. lo[i] + n[i]
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            lo[i] = max(eb[i] - e0 - base, 0);
-            n[i] = max(min(eb[i + 1] - e0 - base, 64) - lo[i], 0);
-            nmax = max(nmax, n[i]);
-        }
-        for (int s0 = 0; s0 < nmax; s0 += CBR) {
-            v4i w[R][CBR][2];
-#pragma unroll
-            for (int i = 0; i < R; ++i)
-#pragma unroll
-                for (int u = 0; u < CBR; ++u) {
-                    const bool on = s0 + u < n[i];  // wave-uniform
-                    const uint32_t k = (uint32_t)__builtin_amdgcn_readlane(kk, on ? lo[i] + s0 + u : 0);
-                    load_seg<WDT, CC>(rsW, k * row_bytes + lane_off, on, w[i][u]);
-                }
-#pragma unroll
-            for (int i = 0; i < R; ++i)
-#pragma unroll
-                for (int u = 0; u < CBR; ++u) {
-                    if (s0 + u < n[i]) {  // wave-uniform; ascending k within row i
-                        const float d = __builtin_bit_cast(
-                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int32_t, dd), lo[i] + s0 + u));
-#pragma unroll
-                        for (int c = 0; c < CC; ++c) y[i][c] = __builtin_fmaf(d, seg_elem<WDT>(w[i][u], c), y[i][c]);
-                    }
-                }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-        if (active && r0 + i < M) store_y<YDT, CC>(a.Y, (size_t)(r0 + i) * N + col, y[i]);
-}
-
-// Tasks (chunk, group of R rows), chunk-major, dealt to the XCDs in contiguous ranges.
-template <int YDT, int WDT, int R, int CBR>
-__global__ __launch_bounds__(256) void k_comp_rows(CompArgs a, int chunks, int per_xcd) {
-    const int lane = threadIdx.x & 63;
-    const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    const int64_t task = (int64_t)logical * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int groups = (a.M + R - 1) / R;
-    if (task >= (int64_t)chunks * groups) return;  // whole wave
-    const int chunk = (int)(task / groups);
-    const int g = (int)(task - (int64_t)chunk * groups);
-    comp_rows<YDT, WDT, R, CBR>(a, g * R, chunk, lane);
 }
 
 // Many entries per row: one wave per (block of 8 rows, chunk of 64 columns) task, lane
@@ -306,7 +203,7 @@ __global__ __launch_bounds__(256) void k_comp_block64(CompArgs a, int nrb, int p
     const int r = lane >> 3, g = lane & 7;
     const int row = r0 + r;
     const int col = chunk * 64 + g * CC;
-    const bool active = row < M && col < N;  // N % 8 == 0: a lane's columns are in range together
+    const bool inside = row < M && col < N;  // N % 8 == 0: a lane's columns are in range together
     const int rowc = min(row, M - 1);
 
     const int32_t rp = a.row_ptr[min(r0 + (lane & 15), M)];
@@ -317,13 +214,16 @@ __global__ __launch_bounds__(256) void k_comp_block64(CompArgs a, int nrb, int p
     for (int o = 8; o < 64; o <<= 1) nmax = max(nmax, __shfl_xor(nmax, o));
 
     const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.sW), 0, N * 4, 0x00020000);
-    const v4i qv = active ? *reinterpret_cast<const v4i *>(a.Yq + (size_t)rowc * N + col) : v4i{0, 0, 0, 0};
+    const v4i qv = inside ? *reinterpret_cast<const v4i *>(a.Yq + (size_t)rowc * N + col) : v4i{0, 0, 0, 0};
+    uint8_t escaped = 0;
+    if (inside) escaped = a.emap[(size_t)(row / ESC_ROWS) * a.cellsN + col / ESC_COLS];
+    const bool active = inside && !escaped;
     v4i swv[2];
     swv[0] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4, 0, 0);
     swv[1] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16, 0, 0);
     const float sa = a.sA[rowc];
     float y[CC];
-    decode_ymain<CC>(qv, swv, sa, active, a.esc + (size_t)rowc * N, col, y);
+    decode_ymain<CC>(qv, swv, sa, y);
 
     constexpr int ESZ = (WDT == DT_BF16) ? 2 : 4;
     const __amdgpu_buffer_rsrc_t rsW =
@@ -403,31 +303,13 @@ static hipError_t launch_comp_tasks(const CompArgs &a, int y_dt, int w_dt, hipSt
     return hipGetLastError();
 }
 
-template <int R, int CBR>
-static hipError_t launch_comp_rows(const CompArgs &a, int y_dt, int w_dt, hipStream_t s) {
-    const int chunks = (int)((a.N + 511) / 512);
-    const int64_t tasks = (int64_t)chunks * ((a.M + R - 1) / R);
-    const int64_t blocks = (tasks + 3) / 4;
-    const int per_xcd = (int)((blocks + 7) / 8);
-    const dim3 grid((unsigned)per_xcd * 8u), block(256);
-#define C(YD, WD) hipLaunchKernelGGL((k_comp_rows<YD, WD, R, CBR>), grid, block, 0, s, a, chunks, per_xcd)
-    if (y_dt == DT_BF16) {
-        if (w_dt == DT_BF16) C(DT_BF16, DT_BF16);
-        else C(DT_BF16, DT_F32);
-    } else {
-        if (w_dt == DT_BF16) C(DT_F32, DT_BF16);
-        else C(DT_F32, DT_F32);
-    }
-#undef C
-    return hipGetLastError();
-}
-
 int comp_kernel_choice(int64_t M, int64_t capacity) { return capacity > 64 * M ? COMP_BLOCK64 : COMP_CHUNK; }
 
-hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y, int y_dt,
+hipError_t launch_comp(const int16_t *Yq, const uint8_t *emap, const float *sA, const float *sW, void *Y, int y_dt,
                        int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s) {
-    const CompArgs a{Yq, esc, sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
+    const int cellsN = (int)((N + ESC_COLS - 1) / ESC_COLS);
+    const CompArgs a{Yq, emap, cellsN, sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
     // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
     // gathers, and the 8-row x 64-column blocks keep each XCD's W strip in its L2
     if (comp_kernel_choice(M, capacity) == COMP_BLOCK64) return launch_comp_block64(a, y_dt, w_dt, s);

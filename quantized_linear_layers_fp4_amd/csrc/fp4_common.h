@@ -10,10 +10,13 @@ namespace fp4 {
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q16 = 2 };
 
 // DT_Q16: the GEMM's accumulator handed to the compensation pass in two bytes.  The FP4
-// products are multiples of 1/4 and their fp32 sum is exact, so 4*acc is an integer; when
-// |4*acc| <= 32767 it is stored as int16, otherwise the element holds Q16_ESC and the
-// dequantized value fl(fl(acc*sA)*sW) goes, in fp32, to the same position of an escape
-// buffer.  Either way the pass recovers Y_main bit for bit.
+// products are multiples of 1/4 and their fp32 sum is exact, so 4*acc is an integer, stored
+// as int16 when |acc| <= Q16_MAX_ACC.  The GEMM also writes a map with one byte per aligned
+// ESC_ROWS x ESC_COLS output block, set for the blocks of a wave block that holds a larger
+// |acc|; the escape kernel (escape.hip) recomputes those blocks and the compensation pass
+// skips them.  As the standalone two-byte output, escaped elements hold Q16_ESC and an fp32
+// buffer their fl(fl(acc*sA)*sW).
+constexpr int ESC_ROWS = 128, ESC_COLS = 64;
 constexpr int Q16_ESC = -32768;
 constexpr float Q16_MAX_ACC = 8191.75f;  // largest |acc| stored inline
 // fl(acc * 4 + 1.5 * 2^23) is exact for |4*acc| < 2^22 and its low 16 bits are 4*acc as int16

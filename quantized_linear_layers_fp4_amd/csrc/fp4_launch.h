@@ -50,16 +50,26 @@ hipError_t launch_quant_cols_keyed(const void *W, int dt, int64_t K, int64_t N, 
                                    uint8_t *codes, const float *row_mult, hipStream_t s);
 
 // FP4 GEMM + dequantization: Y = fl(fl(acc * sA) * sW) in y_dt.  With y_dt == DT_Q16, Y
-// receives the accumulator as int16 4*acc, and a second launch (the escape pass) recomputes
-// in fp32 the tiles that hold some |acc| > Q16_MAX_ACC: their fl(fl(acc*sA)*sW) goes to esc
-// (fp32[M*N]) and their int16 elements become Q16_ESC.  flags: gemm_flag_bytes(M, N) bytes
-// of device scratch (written by the first launch, read by the second).
+// receives the accumulator as int16 4*acc, and emap (esc_map_bytes(M, N) bytes) the map of
+// the ESC_ROWS x ESC_COLS blocks where some |acc| > Q16_MAX_ACC left it out of range (every
+// byte is written).
 // acc_out: NULL or fp32[M*N].
 // f8: Aq (M x K) and Wq (N x K) hold E4M3 bytes, one K value each (the emulation path).
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
                        int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8 = false,
-                       float *esc = nullptr, uint8_t *flags = nullptr);
-size_t gemm_flag_bytes(int64_t M, int64_t N);
+                       uint8_t *emap = nullptr);
+size_t esc_map_bytes(int64_t M, int64_t N);
+// The escaped blocks of a DT_Q16 product (emap as launch_gemm wrote it), recomputed from the
+// codes.  launch_escapes_q16: as the standalone two-byte output, fl(fl(acc*sA)*sW) into esc
+// (fp32[M*N]) and Q16_ESC into their elements of Yq.  launch_escapes_comp: the final
+// Y = Y_main + dA . W in y_dt for those blocks, with the compensation pass's arithmetic (the
+// pass itself skips them).
+hipError_t launch_escapes_q16(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
+                              int64_t N, int64_t K, const uint8_t *emap, int16_t *Yq, float *esc, hipStream_t s);
+hipError_t launch_escapes_comp(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
+                               int64_t N, int64_t K, const uint8_t *emap, const int32_t *row_ptr,
+                               const int32_t *coo_col, const float *coo_val, const void *W, int w_dt, void *Y,
+                               int y_dt, hipStream_t s);
 // The GEMM kernel launch_gemm picks for a shape on a device with `cus` compute units.
 enum : int { GEMM_TILED = 0, GEMM_WIDE = 1 };
 int gemm_kernel_choice(int64_t M, int64_t N, int64_t K, bool f8, int cus);
@@ -72,14 +82,14 @@ hipError_t launch_fp8_dequantize(const uint8_t *codes, int64_t n, const float *s
 // input bytes -> 2 * n_bytes output bytes.
 hipError_t launch_e2m1_to_e4m3(const uint8_t *codes, int64_t n_bytes, uint8_t *out, hipStream_t s);
 // Y = Y_main + dA . W, accumulated in fp32 in ascending k from Y_main, rounded once to y_dt.
-// Y_main comes from the GEMM's DT_Q16 output (Yq, esc) and the scales sA, sW.  Yq may be a
-// bf16 Y itself, esc may be an fp32 Y itself.  capacity: what the dA list was sized for
-// (picks the kernel shape only; 0 if unknown).
+// Y_main comes from the GEMM's DT_Q16 output Yq and the scales sA, sW; the blocks that emap
+// marks are left alone (launch_escapes_comp writes them).  Yq may be a bf16 Y itself.
+// capacity: what the dA list was sized for (picks the kernel shape only; 0 if unknown).
 // The compensation kernel launch_comp picks: chunk tasks up to 64 entries per row on average
 // (capacity / M), 8-row blocks beyond.
 enum : int { COMP_CHUNK = 0, COMP_BLOCK64 = 1 };
 int comp_kernel_choice(int64_t M, int64_t capacity);
-hipError_t launch_comp(const int16_t *Yq, const float *esc, const float *sA, const float *sW, void *Y, int y_dt,
+hipError_t launch_comp(const int16_t *Yq, const uint8_t *emap, const float *sA, const float *sW, void *Y, int y_dt,
                        int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s);
 

@@ -18,8 +18,8 @@
 // Epilogue: Y = fl(fl(acc * sA) * sW); each wave reorders its result tiles through a
 // private patch of LDS so that the stores are 16 bytes per lane along rows.  In front of the
 // sparse compensation dA . W (a separate kernel, comp.hip) the output is instead the exact
-// accumulator as the int16 4*acc (DT_Q16), with a second, flagged launch (FB) that recomputes
-// in fp32 the tiles where it does not fit; the compensation pass rebuilds Y_main from it.
+// accumulator as the int16 4*acc (DT_Q16), with a map of the 128 x 64 output blocks where it
+// does not fit (escape.hip recomputes those); the compensation pass rebuilds Y_main from it.
 //
 // Large products (K a multiple of 512 and at least two 256 x 256 tiles per CU) run on a
 // second, persistent kernel with 256 x 256 tiles (see "wide tiles" below); both compute the
@@ -58,8 +58,9 @@ struct TileArgs {
     int M, N, K;
     void *Y;
     float *acc_out;
-    int16_t *yq;     // FB: the DT_Q16 output whose escaped blocks are marked
-    uint8_t *flags;  // DT_Q16 / FB: per tile and wave, 1 when the wave's block holds |acc| > Q16_MAX_ACC
+    uint8_t *emap;   // DT_Q16: one byte per 128 x 64 output block (row-major, cellsN per row),
+                     // 1 when the wave block it lies in holds some |acc| > Q16_MAX_ACC
+    int cellsM, cellsN;
     int tilesM, tilesN, raster_group;
 };
 
@@ -174,22 +175,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-}
-
-// The escape pass of a DT_Q16 product (FB kernels): after a tile's fp32 epilogue has
-// written fl(fl(acc*sA)*sW) to the escape buffer, every int16 element of the wave's
-// 128 x 32*NJ result block (rows rbase.., columns cbase..) becomes Q16_ESC, 16 bytes per
-// lane along rows.
-template <int NJ>
-__device__ __forceinline__ void q16_fill_esc(int16_t *Yq, int lane, int rbase, int cbase, int M, int N, bool full) {
-    constexpr int CPR = 4 * NJ;  // 16-byte chunks per row
-    const int pat = (int)(((uint32_t)(uint16_t)Q16_ESC << 16) | (uint16_t)Q16_ESC);
-#pragma unroll
-    for (int k = 0; k < 2 * CPR; ++k) {  // 128 rows x CPR chunks, 64 per instruction
-        const int c = k * 64 + lane, grow = rbase + c / CPR, gcol = cbase + (c % CPR) * 8;
-        if (full || (grow < M && gcol < N))
-            __builtin_nontemporal_store(v4i{pat, pat, pat, pat}, reinterpret_cast<v4i *>(Yq + (size_t)grow * N + gcol));
-    }
 }
 
 // The epilogue of two side-by-side 32 x 32 tiles (rows row0.., columns col0.. and col0+32..)
@@ -323,9 +308,7 @@ __device__ __forceinline__ void pair_store(const uint32_t (&pk)[16], uint16_t *P
     }
 }
 // F8: the operands are E4M3 bytes (one K value per byte) instead of packed E2M1 codes.
-// FB: the escape pass of a DT_Q16 product (YDT = DT_F32 into the escape buffer): only the
-// tiles whose flags the DT_Q16 launch set are computed.
-template <int YDT, bool ACCOUT, bool KFULL, bool F8, bool FB>
+template <int YDT, bool ACCOUT, bool KFULL, bool F8>
 __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     // two-byte outputs run on the transposed product (swapped MFMA operands, see epi_pair_t)
     constexpr bool TR = YDT != DT_F32 && !F8;
@@ -344,9 +327,6 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     const int per_xcd = gridDim.x / 8;
     const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (logical >= p.tilesM * p.tilesN) return;
-    if constexpr (FB) {
-        if (!reinterpret_cast<const uint32_t *>(p.flags)[logical]) return;
-    }
     const int group = logical / (p.raster_group * p.tilesN);
     const int first_m = group * p.raster_group;
     const int gm = min(p.raster_group, p.tilesM - first_m);
@@ -552,10 +532,10 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
-    if constexpr (YDT == DT_Q16) {
-        if (lane == 0) p.flags[logical * 4 + wave] = qesc ? 1 : 0;
+    if constexpr (YDT == DT_Q16) {  // the wave's 128 x 64 block is one cell of the map
+        const int cm = m0 / 128 + wm, cn = n0 / 64 + wn;
+        if (lane == 0 && cm < p.cellsM && cn < p.cellsN) p.emap[(size_t)cm * p.cellsN + cn] = qesc ? 1 : 0;
     }
-    if constexpr (FB) q16_fill_esc<2>(p.yq, lane, m0 + wm * 128, n0 + wn * 64, M, N, full);
 }
 
 // ----------------------------------------------------------------------------- wide tiles
@@ -584,8 +564,7 @@ struct WBook {
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     \
     } while (0)
 
-// FB as in k_fp4_gemm: the escape pass, on the flagged tiles of the workgroup's walk only.
-template <int YDT, bool ACCOUT, bool FB>
+template <int YDT, bool ACCOUT>
 __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sb0[WSTB];
     __shared__ __attribute__((aligned(16))) uint8_t sb1[WSTB];
@@ -603,21 +582,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int tpx = (tiles + 7) / 8;
     const int hi = min((xcd + 1) * tpx, tiles);
-    // FB: the next tile of the walk at or after lg that the DT_Q16 launch flagged (64 of the
-    // walk's flags per round trip, one per lane)
-    auto flagged = [&](int lg) {
-        if constexpr (FB) {
-            const uint32_t *f = reinterpret_cast<const uint32_t *>(p.flags);
-            while (lg < hi) {
-                const int mine = lg + lane * per_xcd_wg;
-                const uint64_t b = __builtin_amdgcn_ballot_w64(mine < hi && f[mine] != 0);
-                if (b) return lg + (int)__builtin_ctzll(b) * per_xcd_wg;
-                lg += 64 * per_xcd_wg;
-            }
-        }
-        return lg;
-    };
-    int logical = flagged(xcd * tpx + slot);
+    int logical = xcd * tpx + slot;
     if (logical >= hi) return;
 
     auto origin = [&](int lg, int &m0, int &n0) {
@@ -741,7 +706,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     };
 
     for (int tt = 0;; ++tt) {
-        const int nlog = flagged(logical + per_xcd_wg);
+        const int nlog = logical + per_xcd_wg;
         const bool has_next = nlog < hi;
         int nm0 = m0, nn0 = n0, noffA[4], noffB[4];
         if (has_next) origin(nlog, nm0, nn0);
@@ -929,7 +894,10 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
         }
         if constexpr (YDT == DT_Q16) {
             qesc = __builtin_amdgcn_ballot_w64(qmx > Q16_MAX_ACC) != 0;
-            if (lane == 0) p.flags[logical * 4 + wave] = qesc ? 1 : 0;
+            // the wave's 128 x 128 block is two cells of the map
+            const int cm = m0 / 128 + wm, cn = n0 / 64 + 2 * wn;
+            if (lane < 2 && cm < p.cellsM && cn + lane < p.cellsN)
+                p.emap[(size_t)cm * p.cellsN + cn + lane] = qesc ? 1 : 0;
         }
         if constexpr (DEFER) {
             pr0 = m0 + wm * 128;
@@ -942,7 +910,6 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
                 for (int pp = 0; pp < ND; ++pp) flush_pair(pk[pp], pp);
             }
         }
-        if constexpr (FB) q16_fill_esc<4>(p.yq, lane, m0 + wm * 128, n0 + wn * 128, M, N, full);
         bk[(tt + 1) & 1].sA[tid] = nbA;
         bk[(tt + 1) & 1].sW[tid] = nbW;
         if (!has_next) break;
@@ -992,60 +959,45 @@ int gemm_kernel_choice(int64_t M, int64_t N, int64_t K, bool f8, int cus) {
     return GEMM_TILED;
 }
 
-size_t gemm_flag_bytes(int64_t M, int64_t N) {
-    // one byte per wave and tile of the 256 x 128 kernel, which has the most tiles
-    return (size_t)4 * (size_t)((M + BM - 1) / BM) * (size_t)((N + BN - 1) / BN);
-}
-
-// One launch of the product.  FB: the escape pass of a DT_Q16 product (fp32 into Y = the
-// escape buffer, flagged tiles only).
-static hipError_t launch_gemm_one(const TileArgs &p0, int y_dt, bool acc, bool f8, bool fb, hipStream_t s) {
+// One launch of the product.
+static hipError_t launch_gemm_one(const TileArgs &p0, int y_dt, bool acc, bool f8, hipStream_t s) {
     TileArgs p = p0;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int cus = num_cus();
     if (gemm_kernel_choice(M, N, K, f8, cus) == GEMM_WIDE) {
         p.tilesN = (int)((N + WBN - 1) / WBN);
         const int blocks = cus / 8 * 8;
-#define W3(YD, AO, FBK) hipLaunchKernelGGL((k_fp4_gemm_wide<YD, AO, FBK>), dim3(blocks), dim3(NT), 0, s, p)
-        if (fb) W3(DT_F32, false, true);
-        else if (y_dt == DT_Q16) {
-            if (acc) W3(DT_Q16, true, false);
-            else W3(DT_Q16, false, false);
+#define W2(YD, AO) hipLaunchKernelGGL((k_fp4_gemm_wide<YD, AO>), dim3(blocks), dim3(NT), 0, s, p)
+        if (y_dt == DT_Q16) {
+            if (acc) W2(DT_Q16, true);
+            else W2(DT_Q16, false);
         } else if (y_dt == DT_BF16) {
-            if (acc) W3(DT_BF16, true, false);
-            else W3(DT_BF16, false, false);
+            if (acc) W2(DT_BF16, true);
+            else W2(DT_BF16, false);
         } else {
-            if (acc) W3(DT_F32, true, false);
-            else W3(DT_F32, false, false);
+            if (acc) W2(DT_F32, true);
+            else W2(DT_F32, false);
         }
-#undef W3
+#undef W2
         return hipGetLastError();
     }
     const int64_t tiles = (int64_t)p.tilesM * p.tilesN;
     const int blocks = (int)((tiles + 7) / 8 * 8);
     const bool kfull = f8 ? (K % 64 == 0) : (K % 128 == 0);  // every stage whole
-#define G3(YD, AO, KF, F, FBK) hipLaunchKernelGGL((k_fp4_gemm<YD, AO, KF, F, FBK>), dim3(blocks), dim3(NT), 0, s, p)
-#define G2(YD, AO, F)                               \
-    do {                                            \
-        if (kfull) G3(YD, AO, true, F, false);      \
-        else G3(YD, AO, false, F, false);           \
+#define G3(YD, AO, KF, F) hipLaunchKernelGGL((k_fp4_gemm<YD, AO, KF, F>), dim3(blocks), dim3(NT), 0, s, p)
+#define G2(YD, AO, F)                        \
+    do {                                     \
+        if (kfull) G3(YD, AO, true, F);      \
+        else G3(YD, AO, false, F);           \
     } while (0)
 #define G1(YD, AO)                  \
     do {                            \
         if (f8) G2(YD, AO, true);   \
         else G2(YD, AO, false);     \
     } while (0)
-    if (fb) {  // never F8
-        if (kfull) G3(DT_F32, false, true, false, true);
-        else G3(DT_F32, false, false, false, true);
-    } else if (y_dt == DT_Q16) {  // never F8
-        if (kfull) {
-            if (acc) G3(DT_Q16, true, true, false, false);
-            else G3(DT_Q16, false, true, false, false);
-        } else {
-            if (acc) G3(DT_Q16, true, false, false, false);
-            else G3(DT_Q16, false, false, false, false);
-        }
+    if (y_dt == DT_Q16) {  // never F8
+        if (acc) G2(DT_Q16, true, false);
+        else G2(DT_Q16, false, false);
     } else if (y_dt == DT_BF16) {
         if (acc) G1(DT_BF16, true);
         else G1(DT_BF16, false);
@@ -1060,9 +1012,9 @@ static hipError_t launch_gemm_one(const TileArgs &p0, int y_dt, bool acc, bool f
 }
 
 hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M,
-                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8, float *esc,
-                       uint8_t *flags) {
-    if (y_dt == DT_Q16 && (f8 || !esc || !flags)) return hipErrorInvalidValue;
+                       int64_t N, int64_t K, void *Y, int y_dt, float *acc_out, hipStream_t s, bool f8,
+                       uint8_t *emap) {
+    if (y_dt == DT_Q16 && (f8 || !emap)) return hipErrorInvalidValue;
     TileArgs p;
     p.Aq = Aq;
     p.Wq = Wq;
@@ -1073,18 +1025,13 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
     p.K = (int)K;
     p.Y = Y;
     p.acc_out = acc_out;
-    p.yq = nullptr;
-    p.flags = flags;
+    p.emap = emap;
+    p.cellsM = (int)((M + ESC_ROWS - 1) / ESC_ROWS);
+    p.cellsN = (int)((N + ESC_COLS - 1) / ESC_COLS);
     p.tilesM = (int)((M + BM - 1) / BM);
     p.tilesN = (int)((N + BN - 1) / BN);
     p.raster_group = raster_group_for(p.tilesM);
-    hipError_t e = launch_gemm_one(p, y_dt, acc_out != nullptr, f8, false, s);
-    if (e != hipSuccess || y_dt != DT_Q16) return e;
-    // the escape pass: the tiles whose accumulators left the int16 range, again in fp32
-    p.Y = esc;
-    p.yq = static_cast<int16_t *>(Y);
-    p.acc_out = nullptr;
-    return launch_gemm_one(p, DT_F32, false, false, true, s);
+    return launch_gemm_one(p, y_dt, acc_out != nullptr, f8, s);
 }
 
 }  // namespace fp4

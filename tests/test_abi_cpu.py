@@ -49,20 +49,41 @@ def test_capacity_matches_oracle():
     assert L.fp4_outlier_capacity(10, 32, 1.5) == -1
 
 
-def test_forward_layout_is_disjoint_and_aligned():
+@pytest.mark.parametrize("ydt", [fp4.FP4_BF16, fp4.FP4_F32])
+def test_forward_layout_is_disjoint_and_aligned(ydt):
+    """Regions in order, 256-byte aligned and disjoint; the hand-over is last and the only
+    part that depends on Y's type: the escape map alone for a bf16 Y (which holds the two-byte
+    accumulators itself), plus the int16 accumulators for an fp32 Y."""
     lay = fp4.WsLayout()
     L = fp4.lib()
-    assert L.fp4_forward_layout(300, 512, 264, fp4.FP4_BF16, 0.99, C.byref(lay)) == OK
+    assert L.fp4_forward_layout(300, 512, 264, fp4.FP4_BF16, ydt, 0.99, C.byref(lay)) == OK
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    emap = up(3 * 5)  # one byte per 128 x 64 output block
+    hand = emap + (up(300 * 264 * 2) if ydt == fp4.FP4_F32 else 0)
     cap = lay.capacity
     parts = [(lay.T, 4), (lay.nnz, 8), (lay.row_ptr, 301 * 4), (lay.coo_row, cap * 4), (lay.coo_col, cap * 4),
              (lay.coo_val, cap * 4), (lay.Aq, 300 * 256), (lay.sA, 300 * 4), (lay.Wq, 264 * 256),
-             (lay.sW, 264 * 4), (lay.handoff, 300 * 264 * 4), (lay.scratch, 1)]
+             (lay.sW, 264 * 4), (lay.scratch, 1), (lay.handoff, hand)]
     parts.sort()
     for (a, na), (b, _) in zip(parts, parts[1:]):
         assert a % 256 == 0 and a + na <= b
-    assert parts[-1][0] < lay.total
-    assert L.fp4_forward_workspace_bytes(300, 512, 264, fp4.FP4_BF16, 0.99) == lay.total
-    assert L.fp4_forward_workspace_bytes(300, 500, 264, fp4.FP4_BF16, 0.99) == 0
+    assert parts[-1][0] == lay.handoff and lay.total == lay.handoff + hand
+    other = fp4.WsLayout()
+    assert L.fp4_forward_layout(300, 512, 264, fp4.FP4_BF16, 1 - ydt, 0.99, C.byref(other)) == OK
+    names = ("T", "nnz", "row_ptr", "coo_row", "coo_col", "coo_val", "Aq", "sA", "Wq", "sW", "handoff", "scratch")
+    assert all(getattr(lay, n) == getattr(other, n) for n in names)
+    assert L.fp4_forward_workspace_bytes(300, 512, 264, fp4.FP4_BF16, ydt, 0.99) == lay.total
+    assert L.fp4_forward_workspace_bytes(300, 500, 264, fp4.FP4_BF16, ydt, 0.99) == 0
+    assert L.fp4_forward_workspace_bytes(300, 512, 264, fp4.FP4_BF16, 2, 0.99) == 0  # FP4_Q16 is no Y type here
+
+
+def test_forward_workspace_of_the_gate_up_layer():
+    """With a bf16 Y the forward's hand-over is only the escape map: the workspace of the
+    16384 x 4096 x 22016 layer is its codes, scales, dA list and scratch (under 0.13 GB)."""
+    L = fp4.lib()
+    total = L.fp4_forward_workspace_bytes(16384, 4096, 22016, fp4.FP4_BF16, fp4.FP4_BF16, 0.999)
+    codes = 16384 * 2048 + 22016 * 2048
+    assert codes < total < 0.13e9
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -96,7 +117,7 @@ def test_linear_forward_wq_rejects():
     forward checks."""
     L = fp4.lib()
     lay = fp4.WsLayout()
-    assert L.fp4_forward_layout(64, 128, 64, fp4.FP4_BF16, 0.99, C.byref(lay)) == OK
+    assert L.fp4_forward_layout(64, 128, 64, fp4.FP4_BF16, fp4.FP4_BF16, 0.99, C.byref(lay)) == OK
     call = lambda **kw: L.fp4_linear_forward_wq(  # noqa: E731
         FAKE, FAKE, kw.get("Wq", FAKE), kw.get("sW", FAKE), fp4.FP4_BF16, 64, kw.get("K", 128), 64, 0.99, FAKE,
         fp4.FP4_BF16, FAKE, kw.get("wsb", lay.total), None)
@@ -112,7 +133,7 @@ def test_forward_stage_calls_reject():
     asked for, and everything the whole forward checks."""
     L = fp4.lib()
     lay = fp4.WsLayout()
-    assert L.fp4_forward_layout(64, 128, 64, fp4.FP4_BF16, 0.99, C.byref(lay)) == OK
+    assert L.fp4_forward_layout(64, 128, 64, fp4.FP4_BF16, fp4.FP4_F32, 0.99, C.byref(lay)) == OK
     quant = lambda **kw: L.fp4_forward_quantize(  # noqa: E731
         kw.get("A", FAKE), kw.get("W", FAKE), fp4.FP4_BF16, 64, kw.get("K", 128), 64, kw.get("q", 0.99),
         kw.get("stages", 3), kw.get("ws", FAKE), kw.get("wsb", lay.total), None)
@@ -121,7 +142,8 @@ def test_forward_stage_calls_reject():
     assert quant(ws=None) == ENULL
     assert quant(K=100) == ESHAPE
     assert quant(q=1.5) == EQ
-    assert quant(wsb=lay.total - 1) == EWS
+    assert quant(wsb=lay.handoff - 1) == EWS  # the quantizer stages use the part before the hand-over
+    assert quant(wsb=lay.handoff) not in (EWS, OK)  # past the argument checks (no GPU here)
     assert quant(A=C.c_void_p(0x100004)) == EALIGN
     assert quant(A=C.c_void_p(0x100004), stages=fp4.FP4_STAGE_W) != EALIGN  # A unused: then the device check
     prod = lambda **kw: L.fp4_forward_product(  # noqa: E731
@@ -131,6 +153,9 @@ def test_forward_stage_calls_reject():
     assert prod(ydt=9) == EDTYPE
     assert prod(K=100) == ESHAPE
     assert prod(wsb=16) == EWS
+    # an fp32 Y needs the int16 hand-over in the workspace, a bf16 Y only the escape map
+    small = L.fp4_forward_workspace_bytes(64, 128, 64, fp4.FP4_BF16, fp4.FP4_BF16, 0.99)
+    assert small < lay.total and prod(ydt=0, wsb=small) == EWS and prod(ydt=1, wsb=small) != EWS
     assert prod(Y=C.c_void_p(0x100002)) == EALIGN
 
 
@@ -192,9 +217,9 @@ def test_gemm_rejects():
     assert g(rp=FAKE) == ENULL            # partial compensation arguments
     assert g(rp=FAKE, cc=FAKE) == ENULL
     assert g(rp=FAKE, cc=FAKE, cv=FAKE) == ENULL  # compensation without W
-    assert g(**comp) == ENULL             # bf16 Y with compensation needs the escape workspace
+    assert g(**comp) == ENULL             # bf16 Y with compensation needs the escape map
     need = {d: L.fp4_gemm_workspace_bytes(64, 64, d, int(d != 2)) for d in (0, 1, 2)}
-    assert need[1] > 64 * 64 * 4 and need[0] > 64 * 64 * 2 and need[2] > 64 * 64 * 4
+    assert need[1] == 256 and need[0] == 64 * 64 * 2 + 256 and need[2] == 64 * 64 * 4 + 256
     assert g(**comp, ws=FAKE, wsb=need[1] - 1) == EWS
     assert g(**comp, ws=C.c_void_p(0x100008), wsb=need[1]) == EALIGN
     assert g(**comp, ydt=0) == ENULL      # so does an fp32 Y (the int16 accumulators)
@@ -213,12 +238,12 @@ def test_gemm_rejects():
 def test_gemm_workspace_bytes():
     L = fp4.lib()
     up = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    flags = up(4 * 2 * 3)  # a byte per wave of each 256 x 128 tile: 2 x 3 tiles
-    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 1) == up(300 * 264 * 4) + flags  # fp32 escapes
+    emap = up(3 * 5)  # one byte per 128 x 64 output block: 3 x 5 blocks
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 1) == emap  # the accumulators go through Y
     assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_BF16, 0) == 0
-    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 1) == up(300 * 264 * 2) + flags   # int16 accumulators
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 1) == up(300 * 264 * 2) + emap   # int16 accumulators
     assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_F32, 0) == 0
-    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_Q16, 0) == up(300 * 264 * 4) + flags   # fp32 escapes
+    assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_Q16, 0) == up(300 * 264 * 4) + emap   # fp32 escapes
     assert L.fp4_gemm_workspace_bytes(300, 264, fp4.FP4_Q16, 1) == 0   # no dA term on the raw hand-over
     assert L.fp4_gemm_workspace_bytes(0, 264, fp4.FP4_BF16, 1) == 0
     assert L.fp4_gemm_workspace_bytes(300, 100, fp4.FP4_BF16, 1) == 0

@@ -306,11 +306,11 @@ def _escape_codes(rng, M, N, K, rows, cols):
     return Aq, Wq
 
 
-def _check_q16(Yq, esc, acc, sA, sW, block=(256, 128)):
+def _check_q16(Yq, esc, acc, sA, sW):
     """The FP4_Q16 contract element by element: the int16 4*acc, or -32768 with esc holding
-    fl(fl(acc*sA)*sW) in fp32; every |acc| > 8191.75 is escaped, and escapes stay inside the
-    output tiles (256 x 128 or 256 x 256) that hold such an accumulator.  Returns the number of
-    escaped elements."""
+    fl(fl(acc*sA)*sW) in fp32; every |acc| > 8191.75 is escaped, escapes come in whole aligned
+    128 x 64 blocks (clipped at the edges), and each escaped block lies in an aligned 128 x 128
+    block that holds such an accumulator.  Returns the number of escaped elements."""
     yq = Yq.cpu().numpy().astype(np.int64)
     a = acc.cpu().numpy()
     escaped = yq == -32768
@@ -322,12 +322,15 @@ def _check_q16(Yq, esc, acc, sA, sW, block=(256, 128)):
         ymain = (a[escaped] * sA[np.nonzero(escaped)[0]]).astype(np.float32) * sW[np.nonzero(escaped)[1]]
         assert np.array_equal(e[escaped], ymain.astype(np.float32))
         M, N = a.shape
-        bm, bn = block
-        hot = np.zeros(((M + bm - 1) // bm, (N + bn - 1) // bn), dtype=bool)
-        r, c = np.nonzero(big)
-        hot[r // bm, c // bn] = True
-        r, c = np.nonzero(escaped)
-        assert np.all(hot[r // bm, c // bn])
+        cm, cn = (M + 127) // 128, (N + 127) // 128 * 2  # 128 x 64 cells, whole 128 x 128 blocks
+        pad = lambda x: np.pad(x, ((0, cm * 128 - M), (0, cn * 64 - N)))  # noqa: E731
+        inside = pad(np.ones_like(escaped)).reshape(cm, 128, cn, 64)
+        cells = pad(escaped).reshape(cm, 128, cn, 64)
+        esc_cell = cells.any(axis=(1, 3))
+        assert np.all((cells | ~inside).all(axis=(1, 3))[esc_cell])  # whole cells
+        hot = pad(big).reshape(cm, 128, cn // 2, 128).any(axis=(1, 3))
+        r, c = np.nonzero(esc_cell)
+        assert np.all(hot[r, c // 2])
     return int(escaped.sum())
 
 
@@ -352,8 +355,8 @@ def test_gemm_q16_handover(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(8192, 8192, 512), (8200, 8192, 1024)])
 def test_gemm_q16_handover_wide(M, N, K):
-    """The same contract on the persistent 256 x 256 kernel (1024 or more tiles), its escape
-    pass recomputing only the flagged tiles.  K = 1024 (eight K-stages) is the first depth at
+    """The same contract on the persistent 256 x 256 kernel (1024 or more tiles), the escape
+    kernel recomputing only the marked blocks.  K = 1024 (eight K-stages) is the first depth at
     which a tile's last pairs are stored under the next tile's first steps; M = 8200 adds a
     ragged row of tiles."""
     _say(f"gemm q16 wide {M}x{N}x{K}")
@@ -369,7 +372,7 @@ def test_gemm_q16_handover_wide(M, N, K):
     ns = np.concatenate([rng.integers(0, N, 20000), np.tile(np.arange(N), len(rows))])
     g = acc.view(-1)[torch.from_numpy(ms * N + ns).to(DEV)].cpu().numpy()
     assert np.array_equal(g, oracle.accumulate_pairs(Aq, Wq, K, ms, ns))
-    n_esc = _check_q16(Yq, esc, acc, sA, sW, block=(256, 256))
+    n_esc = _check_q16(Yq, esc, acc, sA, sW)
     assert n_esc > 0
 
 
@@ -392,9 +395,9 @@ def test_forward_rows_of_every_length(dtype, out):
 
 @pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("bf16", "fp32"), ("fp32", "fp32")])
 def test_forward_with_escaped_accumulators(dtype, out):
-    """Rows of A and columns of W that quantize to +6 everywhere give acc = 36 K = 18432:
-    the GEMM hands those tiles over in fp32 (the workspace for a bf16 Y, Y itself for an fp32
-    Y) and the compensation pass must still produce the oracle's Y."""
+    """Rows of A and columns of W that quantize to +6 everywhere give acc = 36 K = 18432, past
+    the two-byte hand-over: the GEMM marks those blocks, the compensation pass skips them and
+    the escape kernel writes their Y from the codes; the whole Y must still be the oracle's."""
     _say(f"forward escapes {dtype} out={out}")
     A, W = make_custom(300, 512, 264, dtype=dtype, seed=21)
     A[5:8] = 1.0
@@ -408,7 +411,7 @@ def _check_forward_small(A, W, q, out_dtype):
     M, K = A.shape
     N = W.shape[1]
     Ad, Wd = A.to(DEV), W.to(DEV)
-    ws = fp4.workspace(Ad, N, q)
+    ws = fp4.workspace(Ad, N, q, out_dtype)
     Y = fp4.linear_forward(Ad, Wd, q, out_dtype=out_dtype, ws=ws)
     torch.cuda.synchronize()
     inter = fp4.forward_intermediates(ws, M, K, N, A.dtype, q)
@@ -463,7 +466,7 @@ def test_forward_is_deterministic():
     A, W = make_custom(1024, 2048, 1032, dtype="bf16", seed=9, kind="student_t")
     Ad, Wd = A.to(DEV), W.to(DEV)
     q = 0.99
-    ws1, ws2 = fp4.workspace(Ad, 1032, q).zero_(), fp4.workspace(Ad, 1032, q).zero_()
+    ws1, ws2 = fp4.workspace(Ad, 1032, q, torch.float32).zero_(), fp4.workspace(Ad, 1032, q, torch.float32).zero_()
     Y1 = fp4.linear_forward(Ad, Wd, q, out_dtype=torch.float32, ws=ws1)
     Y2 = fp4.linear_forward(Ad, Wd, q, out_dtype=torch.float32, ws=ws2)
     torch.cuda.synchronize()
@@ -505,7 +508,7 @@ def test_forward_in_stage_calls(dtype, M, K, N, q, out, order):
     _say(f"forward stages {order} {dtype} {M}x{K}x{N}")
     A, W = make_custom(M, K, N, dtype=dtype, seed=23)
     Ad, Wd = A.to(DEV), W.to(DEV)
-    ws1 = fp4.workspace(Ad, N, q)
+    ws1 = fp4.workspace(Ad, N, q, out)
     Y1 = fp4.linear_forward(Ad, Wd, q, out_dtype=out, ws=ws1)
     ws2 = torch.full_like(ws1, 0x5A)  # stale contents must not matter
     if order == "both":
@@ -646,7 +649,7 @@ def test_forward_full_size(wl, li):
     A, W, _ = make_layer(wl, li)
     M, K, N = L.M, L.K, L.N
     Ad, Wd = A.to(DEV), W.to(DEV)
-    ws = fp4.workspace(Ad, N, L.q)
+    ws = fp4.workspace(Ad, N, L.q, _dt(L.out_dtype))
     Y = fp4.linear_forward(Ad, Wd, L.q, out_dtype=_dt(L.out_dtype), ws=ws)
     inter = fp4.forward_intermediates(ws, M, K, N, A.dtype, L.q)
     nnz = int(inter["nnz"].item())
@@ -706,10 +709,10 @@ def test_forward_full_size(wl, li):
 def test_forward_escapes_wide(out, M, K):
     """The forward on the persistent 256 x 256 GEMM (M x K x 8192: 1024 tiles or more) with
     accumulators past the two-byte range (rows of A and channels of W quantizing to +-6
-    everywhere: acc = +-36 K): its escape pass recomputes those tiles in fp32 and the
-    compensation pass takes them from there (the workspace for a bf16 Y, Y for an fp32 Y).
-    Intermediates in full; the accumulator and Y at sampled outputs, all of them in the
-    escaped tiles' rows.  K = 1024 with M = 8200: deferred stores and a ragged row of tiles."""
+    everywhere: acc = +-36 K): the escape kernel writes the marked blocks' Y from the codes,
+    the compensation pass the rest.  Intermediates in full; the accumulator and Y at sampled
+    outputs (many in the escaped rows) and over a whole escaped 128 x 128 block.  K = 1024 with
+    M = 8200: deferred stores and a ragged row of tiles."""
     N = 8192
     _say(f"forward escapes wide {M}x{K}x{N} out={out}")
     A, W = make_custom(M, K, N, dtype="bf16", seed=41)
@@ -720,7 +723,7 @@ def test_forward_escapes_wide(out, M, K):
         W[:, c] = 0.02 if c != 4100 else -0.02
     q = 0.99
     Ad, Wd = A.to(DEV), W.to(DEV)
-    ws = fp4.workspace(Ad, N, q)
+    ws = fp4.workspace(Ad, N, q, _dt(out))
     Y = fp4.linear_forward(Ad, Wd, q, out_dtype=_dt(out), ws=ws)
     inter = fp4.forward_intermediates(ws, M, K, N, A.dtype, q)
     Anp, Wnp = oracle_inputs(A, W)
@@ -738,8 +741,10 @@ def test_forward_escapes_wide(out, M, K):
     assert np.array_equal(to_np(inter["Wq"]), Wq) and np.array_equal(to_np(inter["sW"]), sW)
     rng = np.random.default_rng(43)
     ms, ns = _sample_pairs(rng, M, N, cl["row_ptr"])
-    ms = np.concatenate([ms, np.repeat(rows, 600), np.repeat(rows, len(cols))])
-    ns = np.concatenate([ns, rng.integers(0, N, 600 * len(rows)), np.tile(cols, len(rows))])
+    b0, c0 = rows[1] // 128 * 128, cols[1] // 128 * 128  # the aligned block around an escape
+    bm, bn = np.meshgrid(np.arange(b0, b0 + 128), np.arange(c0, c0 + 128), indexing="ij")
+    ms = np.concatenate([ms, np.repeat(rows, 600), np.repeat(rows, len(cols)), bm.reshape(-1)])
+    ns = np.concatenate([ns, rng.integers(0, N, 600 * len(rows)), np.tile(cols, len(rows)), bn.reshape(-1)])
     r_acc = oracle.accumulate_pairs(Aq, Wq, K, ms, ns)
     assert np.abs(r_acc).max() > 8191.75  # the sample holds escaped accumulators
     r_y, denom = oracle.output_pairs(r_acc, sA, sW, ms, ns, cl["row_ptr"], cl["coo_col"], cl["coo_val"], Wnp)
@@ -755,7 +760,7 @@ def test_forward_escapes_wide(out, M, K):
 def _fwd_codes_gpu(Ad, Wd, q):
     M, K = Ad.shape
     N = Wd.shape[1]
-    ws = fp4.workspace(Ad, N, q)
+    ws = fp4.workspace(Ad, N, q, torch.float32)
     fp4.linear_forward(Ad, Wd, q, out_dtype=torch.float32, ws=ws)
     return fp4.forward_intermediates(ws, M, K, N, Ad.dtype, q)
 
