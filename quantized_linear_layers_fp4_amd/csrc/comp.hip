@@ -90,8 +90,8 @@ __device__ __forceinline__ void store_y(void *Y, size_t off, const float (&y)[CC
 
 struct CompArgs {
     const int16_t *Yq;
-    const uint8_t *emap;  // the GEMM's map of escaped ESC_ROWS x ESC_COLS blocks, cellsN per row
-    int cellsN;
+    const uint8_t *emap;  // the GEMM's map of escaped ESC_ROWS x ESC_COLS blocks, mapN bytes per row
+    int mapN;
     const float *sA, *sW;
     void *Y;
     int M, N, K;
@@ -124,9 +124,15 @@ __device__ __forceinline__ void comp_task(const CompArgs &a, int row, int chunk,
 #pragma unroll
     for (int h = 0; h < CC / 4; ++h) swv[h] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4 + 16 * h, 0, 0);
     const float sa = a.sA[row];
-    // a lane's CC columns lie in one block of the map (CC divides ESC_COLS)
-    uint8_t escaped = 0;
-    if (inside) escaped = a.emap[(size_t)(row / ESC_ROWS) * a.cellsN + col / ESC_COLS];
+    // the map bytes under the chunk: one aligned word per wave (a uniform, scalar load); a lane's
+    // CC columns lie in one block (CC divides ESC_COLS)
+    constexpr int BPC = 64 * CC / ESC_COLS;  // blocks per chunk
+    static_assert(BPC == 8 || BPC == 4, "map word");
+    const size_t moff = (size_t)(row / ESC_ROWS) * a.mapN + (size_t)chunk * BPC;
+    uint64_t mw;
+    if constexpr (BPC == 8) mw = *reinterpret_cast<const uint64_t *>(a.emap + moff);
+    else mw = *reinterpret_cast<const uint32_t *>(a.emap + moff);
+    const bool escaped = ((mw >> (8 * (lane * CC / ESC_COLS))) & 0xFF) != 0;
     const int32_t e0 = __builtin_amdgcn_readlane(rp, 0);
     const int32_t e1 = __builtin_amdgcn_readlane(rp, 1);
     float y[CC];
@@ -215,8 +221,11 @@ __global__ __launch_bounds__(256) void k_comp_block64(CompArgs a, int nrb, int p
 
     const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.sW), 0, N * 4, 0x00020000);
     const v4i qv = inside ? *reinterpret_cast<const v4i *>(a.Yq + (size_t)rowc * N + col) : v4i{0, 0, 0, 0};
-    uint8_t escaped = 0;
-    if (inside) escaped = a.emap[(size_t)(row / ESC_ROWS) * a.cellsN + col / ESC_COLS];
+    // the task's 8 rows and 64 columns are one block of the map: its byte from the aligned word
+    // that holds it (a uniform, scalar load; the map's row stride is a multiple of 8)
+    const size_t mi = (size_t)(r0 / ESC_ROWS) * a.mapN + chunk;
+    const uint32_t mword = *reinterpret_cast<const uint32_t *>(a.emap + (mi & ~(size_t)3));
+    const bool escaped = ((mword >> (8 * (mi & 3))) & 0xFF) != 0;
     const bool active = inside && !escaped;
     v4i swv[2];
     swv[0] = __builtin_amdgcn_raw_buffer_load_b128(rsS, col * 4, 0, 0);
@@ -308,8 +317,7 @@ int comp_kernel_choice(int64_t M, int64_t capacity) { return capacity > 64 * M ?
 hipError_t launch_comp(const int16_t *Yq, const uint8_t *emap, const float *sA, const float *sW, void *Y, int y_dt,
                        int64_t M, int64_t N, int64_t K, const int32_t *row_ptr, const int32_t *coo_col,
                        const float *coo_val, const void *W, int w_dt, int64_t capacity, hipStream_t s) {
-    const int cellsN = (int)((N + ESC_COLS - 1) / ESC_COLS);
-    const CompArgs a{Yq, emap, cellsN, sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
+    const CompArgs a{Yq, emap, esc_map_stride(N), sA, sW, Y, (int)M, (int)N, (int)K, row_ptr, coo_col, coo_val, W};
     // the list's capacity bounds the mean entries per row; past 64 the pass is bound by its
     // gathers, and the 8-row x 64-column blocks keep each XCD's W strip in its L2
     if (comp_kernel_choice(M, capacity) == COMP_BLOCK64) return launch_comp_block64(a, y_dt, w_dt, s);

@@ -30,8 +30,8 @@ struct EscArgs {
     const uint8_t *Aq, *Wq;  // M x K/2 and N x K/2 E2M1 codes, two per byte, low nibble first
     const float *sA, *sW;
     int M, N, K;
-    const uint8_t *emap;  // cellsM x cellsN, one byte per ESC_ROWS x ESC_COLS block
-    int cellsM, cellsN;
+    const uint8_t *emap;  // cellsM rows of mapN bytes, one per ESC_ROWS x ESC_COLS block (cellsN used)
+    int cellsM, cellsN, mapN;
     int16_t *Yq;  // ESC_Q16: the two-byte output, and its fp32 escape buffer
     float *esc;
     const int32_t *row_ptr, *coo_col;  // ESC_COMP: dA (CSR offsets, columns, values), W, Y
@@ -122,17 +122,18 @@ __global__ __launch_bounds__(256) void k_q16_escapes(EscArgs a) {
     __shared__ int list[256];
     __shared__ int count;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cells = a.cellsM * a.cellsN;
+    const int cells = a.cellsM * a.mapN;
     for (int base = blockIdx.x * 256; base < cells; base += gridDim.x * 256) {
         if (tid == 0) count = 0;
         __syncthreads();
         const int c = base + tid;
-        if (c < cells && a.emap[c]) list[atomicAdd(&count, 1)] = c;  // LDS: at most 256 entries
+        // the row padding past cellsN is never written: not a block
+        if (c < cells && c % a.mapN < a.cellsN && a.emap[c]) list[atomicAdd(&count, 1)] = c;  // LDS: <= 256
         __syncthreads();
         const int n = count;
         for (int i = 0; i < n; ++i) {
             const int cell = list[i];
-            const int r0 = (cell / a.cellsN) * ESC_ROWS + 32 * wave, c0 = (cell % a.cellsN) * ESC_COLS;
+            const int r0 = (cell / a.mapN) * ESC_ROWS + 32 * wave, c0 = (cell % a.mapN) * ESC_COLS;
             if (r0 < a.M) {  // wave-uniform
                 v16f acc[2];
                 block_acc(a, r0, c0, lane, acc);
@@ -143,9 +144,7 @@ __global__ __launch_bounds__(256) void k_q16_escapes(EscArgs a) {
     }
 }
 
-size_t esc_map_bytes(int64_t M, int64_t N) {
-    return (size_t)((M + ESC_ROWS - 1) / ESC_ROWS) * (size_t)((N + ESC_COLS - 1) / ESC_COLS);
-}
+size_t esc_map_bytes(int64_t M, int64_t N) { return (size_t)((M + ESC_ROWS - 1) / ESC_ROWS) * esc_map_stride(N); }
 
 static EscArgs esc_args(const uint8_t *Aq, const float *sA, const uint8_t *Wq, const float *sW, int64_t M, int64_t N,
                         int64_t K, const uint8_t *emap) {
@@ -160,13 +159,14 @@ static EscArgs esc_args(const uint8_t *Aq, const float *sA, const uint8_t *Wq, c
     a.emap = emap;
     a.cellsM = (int)((M + ESC_ROWS - 1) / ESC_ROWS);
     a.cellsN = (int)((N + ESC_COLS - 1) / ESC_COLS);
+    a.mapN = esc_map_stride(N);
     return a;
 }
 
 // one round of 256 map bytes per workgroup covers the map with up to 4096 workgroups; larger
 // maps take further rounds
 static dim3 esc_grid(const EscArgs &a) {
-    const int64_t rounds = ((int64_t)a.cellsM * a.cellsN + 255) / 256;
+    const int64_t rounds = ((int64_t)a.cellsM * a.mapN + 255) / 256;
     return dim3((unsigned)(rounds < 4096 ? rounds : 4096));
 }
 

@@ -17,6 +17,9 @@ enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q16 = 2 };
 // skips them.  As the standalone two-byte output, escaped elements hold Q16_ESC and an fp32
 // buffer their fl(fl(acc*sA)*sW).
 constexpr int ESC_ROWS = 128, ESC_COLS = 64;
+// Row stride of the map in bytes: a multiple of 8, so the eight blocks under a 512-column chunk
+// are one aligned 8-byte word (the padding bytes are never written or read as blocks).
+__host__ __device__ inline int esc_map_stride(int64_t N) { return (int)((N + 8 * ESC_COLS - 1) / (8 * ESC_COLS)) * 8; }
 constexpr int Q16_ESC = -32768;
 constexpr float Q16_MAX_ACC = 8191.75f;  // largest |acc| stored inline
 // fl(acc * 4 + 1.5 * 2^23) is exact for |4*acc| < 2^22 and its low 16 bits are 4*acc as int16

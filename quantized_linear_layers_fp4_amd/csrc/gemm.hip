@@ -58,9 +58,9 @@ struct TileArgs {
     int M, N, K;
     void *Y;
     float *acc_out;
-    uint8_t *emap;   // DT_Q16: one byte per 128 x 64 output block (row-major, cellsN per row),
+    uint8_t *emap;   // DT_Q16: one byte per 128 x 64 output block (row-major, stride mapN),
                      // 1 when the wave block it lies in holds some |acc| > Q16_MAX_ACC
-    int cellsM, cellsN;
+    int cellsM, cellsN, mapN;
     int tilesM, tilesN, raster_group;
 };
 
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(NT, 2) void k_fp4_gemm(TileArgs p) {
     }
     if constexpr (YDT == DT_Q16) {  // the wave's 128 x 64 block is one cell of the map
         const int cm = m0 / 128 + wm, cn = n0 / 64 + wn;
-        if (lane == 0 && cm < p.cellsM && cn < p.cellsN) p.emap[(size_t)cm * p.cellsN + cn] = qesc ? 1 : 0;
+        if (lane == 0 && cm < p.cellsM && cn < p.cellsN) p.emap[(size_t)cm * p.mapN + cn] = qesc ? 1 : 0;
     }
 }
 
@@ -897,7 +897,7 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
             // the wave's 128 x 128 block is two cells of the map
             const int cm = m0 / 128 + wm, cn = n0 / 64 + 2 * wn;
             if (lane < 2 && cm < p.cellsM && cn + lane < p.cellsN)
-                p.emap[(size_t)cm * p.cellsN + cn + lane] = qesc ? 1 : 0;
+                p.emap[(size_t)cm * p.mapN + cn + lane] = qesc ? 1 : 0;
         }
         if constexpr (DEFER) {
             pr0 = m0 + wm * 128;
@@ -1028,6 +1028,7 @@ hipError_t launch_gemm(const uint8_t *Aq, const float *sA, const uint8_t *Wq, co
     p.emap = emap;
     p.cellsM = (int)((M + ESC_ROWS - 1) / ESC_ROWS);
     p.cellsN = (int)((N + ESC_COLS - 1) / ESC_COLS);
+    p.mapN = esc_map_stride(N);
     p.tilesM = (int)((M + BM - 1) / BM);
     p.tilesN = (int)((N + BN - 1) / BN);
     p.raster_group = raster_group_for(p.tilesM);
