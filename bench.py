@@ -221,6 +221,31 @@ def mfma_probe(iters: int = 20000) -> dict:
             "clock_GHz": round(ghz, 3), "peak_at_that_clock_TFLOP/s": round(PEAK_FP4_TFLOPS * ghz / 2.4, 1)}
 
 
+def vendor_gemm(M: int, N: int, K: int, ours_ms: float | None = None) -> dict:
+    """A same-box reference for the FP4 GEMM: torch._scaled_mm on MX-FP4 operands (which PyTorch
+    for ROCm hands to hipBLASLt on gfx950) at the same M, N, K, with random codes, E8M0 block
+    scales of 32 all equal to 1 and a bf16 output.  Not part of the forward; recorded beside it."""
+    what = ("torch._scaled_mm, MX-FP4 operands (float4_e2m1fn_x2, E8M0 block scales of 32, all 1), bf16 out, "
+            "same M, N, K, random codes")
+    try:
+        dev = torch.device("cuda:0")
+        g = torch.Generator(device=dev).manual_seed(20250128)
+        a = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g)
+        b = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g)
+        a, b = a.view(torch.float4_e2m1fn_x2), b.view(torch.float4_e2m1fn_x2)
+        sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        f = lambda: torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.bfloat16)  # noqa: E731
+        f()
+        ms = time_on_stream(f, 20, 3)
+    except Exception as ex:  # noqa: BLE001 - a reference only: report why it is absent
+        return {"what": what, "error": repr(ex)[:300]}
+    out = {"what": what, "ms": round(ms, 4), "TFLOP/s": round(2.0 * M * N * K / ms / 1e9, 1)}
+    if ours_ms:
+        out["ours_over_vendor_speed"] = round(ms / ours_ms, 3)
+    return out
+
+
 def run_copy(steps: int):
     """Plain 1 GiB device copy: the calibration kernel for the HBM byte counters."""
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -533,6 +558,8 @@ def run_full(args):
     }
     if not args.no_probe:
         out["mfma_probe"] = mfma_probe()
+        L0 = sets[0][0]["L"]
+        out["vendor_gemm"] = vendor_gemm(L0.M, L0.N, L0.K, gemm_ms if len(sets[0]) == 1 else None)
     if args.emu:
         emu_ms = nat_ms = 0.0
         for d in sets[0]:
@@ -568,7 +595,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_gate_up", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-probe", action="store_true", help="skip the matrix-core issue-rate probe")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the matrix-core issue-rate probe and the vendor GEMM reference")
     ap.add_argument("--hot-only", action="store_true", help="one input set only (no cold-cache rotation)")
     ap.add_argument("--emu", action="store_true",
                     help="also time the FP4-on-FP8 emulation of the product (E4M3 expansion + FP8 MFMA) against "
@@ -578,7 +606,7 @@ def main():
                          "timed steps (fixed inference weights); or on a second stream, each layer's under the "
                          "previous layer's forward")
     ap.add_argument("--mode", default="full", choices=["full", "copy", "forward", "traffic", "fp8codec",
-                                                          "backward", "mfma-peak"])
+                                                          "backward", "mfma-peak", "vendor-gemm"])
     ap.add_argument("--traffic-dirs", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="--mode traffic: rocprofv3 --pmc output directories of FETCH_SIZE and WRITE_SIZE for "
                          "the full bench and for --mode copy")
@@ -599,6 +627,10 @@ def main():
         return
     if args.mode == "mfma-peak":
         print(json.dumps(mfma_probe()))
+        return
+    if args.mode == "vendor-gemm":
+        L = WORKLOADS[args.workload].layers[0]
+        print(json.dumps(vendor_gemm(L.M, L.N, L.K)))
         return
     if args.mode == "backward":
         run_backward(args)
