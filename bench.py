@@ -246,6 +246,16 @@ def vendor_gemm(M: int, N: int, K: int, ours_ms: float | None = None) -> dict:
     return out
 
 
+def hbm_copy_probe(steps: int = 10) -> dict:
+    """The device-to-device copy rate of this machine (1 GiB, read + write bytes over the time): what
+    a bandwidth-bound pass can reach here, beside the published 8 TB/s."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = time_on_stream(lambda: dst.copy_(src), steps, 2)
+    del src, dst
+    return {"what": "1 GiB device copy", "ms": round(ms, 4), "GB/s": round(2 * (1 << 30) / ms / 1e6, 1)}
+
+
 def run_copy(steps: int):
     """Plain 1 GiB device copy: the calibration kernel for the HBM byte counters."""
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -537,6 +547,8 @@ def run_full(args):
                    "hot": dict(_spread(hot), what="one input set repeated"),
                    "hot_TFLOP/s": round(flops / (hot_total / args.steps) / 1e9, 2)},
         "forward_frac_of_fp4_peak": round(fwd_tflops / PEAK_FP4_TFLOPS, 4),
+        # the product stage (GEMM, compensation and escape scan): 2MNK over its own time
+        "product_stage_frac_of_fp4_peak": round(flops / product_ms / 1e9 / PEAK_FP4_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": gemm_kernel(first.M, first.N, first.K), "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(gemm_ms, 4)},
@@ -558,6 +570,12 @@ def run_full(args):
     }
     if not args.no_probe:
         out["mfma_probe"] = mfma_probe()
+        out["hbm_copy"] = hbm_copy_probe()
+        # each bound against what this machine sustains (the probes) besides the published peaks
+        out["roofline"]["frac_of_probe_peak"] = round(gemm_tflops / out["mfma_probe"]["TFLOP/s"], 4)
+        cp = out["hbm_copy"]["GB/s"]
+        for k in ("compensation", "quantizer"):
+            out[k]["frac_of_copy_rate"] = round(out[k]["achieved"] / cp, 4)
         L0 = sets[0][0]["L"]
         out["vendor_gemm"] = vendor_gemm(L0.M, L0.N, L0.K, gemm_ms if len(sets[0]) == 1 else None)
     if args.emu:
