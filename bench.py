@@ -450,37 +450,41 @@ def run_full(args):
         return
     hot, hot_total, _ = per_step_times(forward, args.steps, args.warmup, 1)
 
-    # the stages of the forward, each between events of its own (hot cache, set 0): the A-side
-    # quantizer, the W-side quantizer, the product (GEMM + compensation + escape kernel)
-    names = ("quant_A", "quant_W", "product")
-    stage_ms = {k: [] for k in names}
+    # the stages of the forward, each between events of its own (hot cache, set 0): the
+    # quantizer as the forward calls it (A and W in one call, whose W passes share launches
+    # with the A side's), then the product (GEMM + compensation + escape kernel); with cached
+    # weight codes the whole cached-weight forward is the second stage (not split)
+    def stage_times(parts):
+        recs = []
 
-    def staged(_si: int):
-        rec = []
-        for d in sets[0]:
-            L = d["L"]
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            ev[0].record(main_s)
-            fp4.forward_quantize(d["A"], None, L.M, L.K, L.N, d["A"].dtype, L.q, d["ws"], stages=fp4.FP4_STAGE_A)
-            ev[1].record(main_s)
-            if args.wq == "per-step":
-                fp4.forward_quantize(None, d["W"], L.M, L.K, L.N, d["A"].dtype, L.q, d["ws"], stages=fp4.FP4_STAGE_W)
-            ev[2].record(main_s)
-            if args.wq == "per-step":
-                fp4.forward_product(d["W"], L.M, L.q, d["ws"], d["Y"])
-            else:
-                fp4.linear_forward_wq(d["A"], d["W"], d["Wq"], d["sW"], L.q, ws=d["ws"], Y=d["Y"])  # not split
-            ev[3].record(main_s)
-            rec.append(ev)
-        staged.last.append(rec)
-    staged.last = []
-    per_step_times(staged, args.steps, args.warmup, 1)
-    for rec in staged.last[args.warmup:]:
-        for k, nm in enumerate(names):
-            stage_ms[nm].append(sum(ev[k].elapsed_time(ev[k + 1]) for ev in rec))
-    quant_a_ms = float(np.median(stage_ms["quant_A"]))
-    quant_w_ms = float(np.median(stage_ms["quant_W"]))
-    product_ms = float(np.median(stage_ms["product"]))
+        def step(_si: int):
+            rec = []
+            for d in sets[0]:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+                ev[0].record(main_s)
+                for k, f in enumerate(parts):
+                    f(d)
+                    ev[k + 1].record(main_s)
+                rec.append(ev)
+            recs.append(rec)
+        per_step_times(step, args.steps, args.warmup, 1)
+        return [float(np.median([sum(ev[k].elapsed_time(ev[k + 1]) for ev in rec) for rec in recs[args.warmup:]]))
+                for k in range(len(parts))]
+
+    def q_call(stages):
+        return lambda d: fp4.forward_quantize(d["A"] if stages & fp4.FP4_STAGE_A else None,
+                                              d["W"] if stages & fp4.FP4_STAGE_W else None, d["L"].M, d["L"].K,
+                                              d["L"].N, d["A"].dtype, d["L"].q, d["ws"], stages=stages)
+    per_step_w = args.wq == "per-step"
+    if per_step_w:
+        second = lambda d: fp4.forward_product(d["W"], d["L"].M, d["L"].q, d["ws"], d["Y"])  # noqa: E731
+    else:
+        second = lambda d: fp4.linear_forward_wq(d["A"], d["W"], d["Wq"], d["sW"], d["L"].q,  # noqa: E731
+                                                 ws=d["ws"], Y=d["Y"])
+    quant_ms, product_ms = stage_times([q_call(fp4.FP4_STAGE_A | (fp4.FP4_STAGE_W if per_step_w else 0)), second])
+    # each side of the quantizer in a call of its own (its own launches), for the split
+    quant_a_ms, quant_w_ms = stage_times([q_call(fp4.FP4_STAGE_A), q_call(fp4.FP4_STAGE_W)]) if per_step_w \
+        else (quant_ms, None)
 
     # the dominant kernel alone, as the forward launches it: the GEMM with the two-byte
     # accumulator hand-over (FP4_Q16) and its escape kernel (which finds no block to redo here)
@@ -511,7 +515,6 @@ def run_full(args):
     if args.wq != "per-step":
         qw_bytes = 0
     comp_ms = max(product_ms - gemm_ms, 1e-9)
-    quant_ms = quant_a_ms + quant_w_ms
     gemm_tflops = flops / gemm_ms / 1e9
     fwd_tflops = flops / ms_step / 1e9
     first = sets[0][0]["L"]
@@ -552,15 +555,17 @@ def run_full(args):
         "roofline": {"bound": "mfma", "kernel": gemm_kernel(first.M, first.N, first.K), "achieved": round(gemm_tflops, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic, "ms_per_launch": round(gemm_ms, 4)},
-        "stages_hot_ms": {"quant_A": round(quant_a_ms, 4), "quant_W": round(quant_w_ms, 4),
-                          "product": round(product_ms, 4), "gemm": round(gemm_ms, 4)},
+        "stages_hot_ms": {"quantizer": round(quant_ms, 4), "product": round(product_ms, 4), "gemm": round(gemm_ms, 4),
+                          "quant_A_alone": round(quant_a_ms, 4),
+                          "quant_W_alone": round(quant_w_ms, 4) if quant_w_ms is not None else None},
         "compensation": dict({"bound": "hbm", "kernel": per_layer[0]["comp_kernel"], "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "how": "product stage minus the GEMM launch, both timed directly"},
                              **hbm(cbytes, comp_ms)),
         "quantizer": dict({"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "how": "A-side and W-side stage calls, each between events of its own",
-                           "A": hbm(qa_bytes, quant_a_ms),
-                           "W": hbm(qw_bytes, quant_w_ms) if qw_bytes else None},
+                           "how": "the forward's quantizer stage call (A and W in one call, its own launches), "
+                                  "between events of its own; A_alone / W_alone: each side in a call of its own",
+                           "A_alone": hbm(qa_bytes, quant_a_ms),
+                           "W_alone": hbm(qw_bytes, quant_w_ms) if qw_bytes else None},
                           **hbm(qa_bytes + qw_bytes, quant_ms)),
         "nnz": nnz_total,
         "layers": per_layer,

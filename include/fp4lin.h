@@ -257,7 +257,8 @@ fp4_status fp4_linear_forward(const void *A, const void *W, int32_t in_dtype, in
  *   COO list) and the token-wise codes and scales of A_clamped (QbitAI report, outlier,
  *   granularity and forward-quantization paragraphs); FP4_STAGE_W = the channel-wise codes and
  *   scales of W (granularity paragraph).  A (resp. W) may be NULL when its stage is not asked
- *   for.  Run apart, the W stage takes one more (zero-fill) launch than inside the forward.
+ *   for.  Asked for together (as the forward does), W's two passes share launches with the A
+ *   side's select and COO build; the W stage alone takes three launches of its own.
  *   It uses the workspace up to the layout's handoff offset, which is the same for both Y
  *   types, and needs at least that many bytes.
  * fp4_forward_product: the FP4 GEMM with dequantization and the compensation dA . W (GEMM-kernel

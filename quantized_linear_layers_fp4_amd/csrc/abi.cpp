@@ -158,13 +158,13 @@ OutlierWs outlier_ws(int64_t M, int64_t K, int32_t dtype, int64_t cap) {
 
 fp4_status hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
 
-// Enqueue the outlier pass: zero (with zero2[0..n_zero2) in the same launch), histogram + row
-// maxima with the select of T in its last workgroup (a second histogram level for fp32), then
-// rows (clamp, optional codes, staging of dA), then the COO list.
+// Enqueue the outlier pass: zero, histogram + row maxima, the select of T (a second histogram
+// level for fp32), then rows (clamp, optional codes, staging of dA), then the COO list.  With
+// wside, W's column maxima run in the select's launch and its quantize pass in the COO build's.
 fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, double q, uint8_t *ws,
                         const OutlierWs &w, int cus, float *T, int32_t *coo_row, int32_t *coo_col,
                         float *coo_val, int64_t cap, int32_t *row_ptr, int64_t *nnz, uint8_t *Aq,
-                        float *sA, uint32_t *zero2, int64_t n_zero2, hipStream_t s) {
+                        float *sA, const WSide *wside, hipStream_t s) {
     State *st = reinterpret_cast<State *>(ws + w.state);
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + w.hist);
     uint32_t *hist_lo = reinterpret_cast<uint32_t *>(ws + w.hist_lo);
@@ -176,16 +176,17 @@ fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, doub
     const int dt = dt_of(dtype);
     const int64_t n = M * K;
     const uint64_t k = (uint64_t)std::floor(q * (double)(n - 1));
-    hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(ws + w.state), (int64_t)(w.zero_end - w.state) / 4, zero2,
-                               n_zero2, s);
-    if (e == hipSuccess) e = launch_hist_rowmax(A, dt, M, K, hist, rowmax, st, T, k, cus, s);
+    hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(ws + w.state), (int64_t)(w.zero_end - w.state) / 4,
+                               wside ? wside->keys : nullptr, wside ? wside->N : 0, s);
+    if (e == hipSuccess) e = launch_hist_rowmax(A, dt, M, K, hist, rowmax, cus, s);
+    if (e == hipSuccess) e = launch_select_hi(hist, dt, st, T, k, wside, s);
     if (e == hipSuccess && dt == DT_F32) e = launch_select_lo(A, n, hist_lo, st, T, s);
     const bool codes = Aq != nullptr;
     if (e == hipSuccess)
         e = launch_quant_rows(A, dt, M, K, codes ? rowmax : nullptr, T, Aq, sA, row_cnt, stg, st,
                               /*emit=*/true, /*write_codes=*/codes, s);
     if (e == hipSuccess)
-        e = launch_coo(row_cnt, M, row_ptr, nnz, stg, cap, coo_row, coo_col, coo_val, A, dt, K, T, s);
+        e = launch_coo(row_cnt, M, row_ptr, nnz, stg, cap, coo_row, coo_col, coo_val, A, dt, K, T, wside, s);
     return hip_status(e);
 }
 
@@ -219,7 +220,7 @@ fp4_status outlier_clamp_impl(const void *A, int32_t a_dtype, int64_t M, int64_t
     // nnz <= cap always (T is the (k+1)-th smallest |a|), so the staging area and the COO
     // positions are bounded by the computed cap, which the workspace was sized for.
     return run_outliers(A, a_dtype, M, K, q, static_cast<uint8_t *>(workspace), w, cus, T, coo_row, coo_col, coo_val,
-                        cap, row_ptr, nnz, nullptr, nullptr, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
+                        cap, row_ptr, nnz, nullptr, nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
 }
 
 int64_t outlier_capacity_of(int64_t M, int64_t K, double q) { return capacity_of(M, K, q); }
@@ -243,25 +244,23 @@ fp4_status forward_check(int64_t M, int64_t K, int64_t N, int32_t in_dtype, int3
 
 // The forward's quantizer stages into the workspace: FP4_STAGE_A (quantile, clamp, dA, A's
 // codes and scales) and/or FP4_STAGE_W (W's codes and scales).  W's column-maximum keys follow
-// the outlier scratch; they are zeroed in the outlier pass's zero launch when both stages run
-// in one call, else by a launch of their own.
+// the outlier scratch.  When both stages run in one call, W's passes share the outlier pass's
+// launches (its keys zeroed in the zero fill); alone, W takes a zero fill and its two passes.
 fp4_status quantize_impl(const void *A, const void *W, int32_t in_dtype, int64_t M, int64_t K, int64_t N, double q,
                          int32_t stages, uint8_t *ws, const fp4_ws_layout &l, int cus, hipStream_t s) {
     const OutlierWs w = outlier_ws(M, K, in_dtype, l.capacity);
     uint32_t *wkeys = reinterpret_cast<uint32_t *>(ws + l.scratch + w.total);
     const bool sa = stages & FP4_STAGE_A, sw = stages & FP4_STAGE_W;
     if (sa) {
-        fp4_status st = run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, reinterpret_cast<float *>(ws + l.T),
-                                     reinterpret_cast<int32_t *>(ws + l.coo_row),
-                                     reinterpret_cast<int32_t *>(ws + l.coo_col), reinterpret_cast<float *>(ws + l.coo_val),
-                                     l.capacity, reinterpret_cast<int32_t *>(ws + l.row_ptr),
-                                     reinterpret_cast<int64_t *>(ws + l.nnz), ws + l.Aq,
-                                     reinterpret_cast<float *>(ws + l.sA), sw ? wkeys : nullptr, sw ? N : 0, s);
-        if (st != FP4_OK) return st;
+        WSide wside{W, dt_of(in_dtype), K, N, wkeys, ws + l.Wq, reinterpret_cast<float *>(ws + l.sW)};
+        return run_outliers(A, in_dtype, M, K, q, ws + l.scratch, w, cus, reinterpret_cast<float *>(ws + l.T),
+                            reinterpret_cast<int32_t *>(ws + l.coo_row), reinterpret_cast<int32_t *>(ws + l.coo_col),
+                            reinterpret_cast<float *>(ws + l.coo_val), l.capacity,
+                            reinterpret_cast<int32_t *>(ws + l.row_ptr), reinterpret_cast<int64_t *>(ws + l.nnz),
+                            ws + l.Aq, reinterpret_cast<float *>(ws + l.sA), sw ? &wside : nullptr, s);
     }
     if (sw) {
-        hipError_t e = hipSuccess;
-        if (!sa) e = launch_zero(wkeys, N, nullptr, 0, s);
+        hipError_t e = launch_zero(wkeys, N, nullptr, 0, s);
         if (e == hipSuccess)
             e = launch_quant_cols(W, dt_of(in_dtype), K, N, reinterpret_cast<float *>(wkeys), ws + l.Wq, true, s, nullptr,
                                   reinterpret_cast<float *>(ws + l.sW));

@@ -10,6 +10,8 @@
 
 namespace fp4 {
 
+struct WSide;  // fp4_launch.h
+
 // The current device must be gfx950; *cus receives its compute-unit count (cached per device).
 fp4_status device_check(int *cus);
 
@@ -38,10 +40,11 @@ fp4_status outlier_clamp_impl(const void *A, int32_t a_dtype, int64_t M, int64_t
                               int64_t *nnz, void *workspace, size_t ws_bytes, void *stream);
 
 // Enqueue the outlier pass on scratch ws (layout w).  Aq/sA: NULL, or A_clamped's codes and
-// scales written in the same pass; zero2[0..n_zero2): zeroed in the pass's zero-fill launch.
+// scales written in the same pass.  wside: NULL, or W's quantization, done in the pass's
+// launches (its keys zeroed in the zero fill, its two passes beside the select and the COO build).
 fp4_status run_outliers(const void *A, int32_t dtype, int64_t M, int64_t K, double q, uint8_t *ws,
                         const OutlierWs &w, int cus, float *T, int32_t *coo_row, int32_t *coo_col,
                         float *coo_val, int64_t cap, int32_t *row_ptr, int64_t *nnz, uint8_t *Aq,
-                        float *sA, uint32_t *zero2, int64_t n_zero2, hipStream_t s);
+                        float *sA, const WSide *wside, hipStream_t s);
 
 }  // namespace fp4

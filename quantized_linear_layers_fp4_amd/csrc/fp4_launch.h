@@ -10,10 +10,24 @@ namespace fp4 {
 
 // Zeroes p1[0..n1) and p2[0..n2) in one launch (n2 may be 0).
 hipError_t launch_zero(uint32_t *p1, int64_t n1, uint32_t *p2, int64_t n2, hipStream_t s);
-// Histogram of the |A| keys and raw row maxima; the last workgroup to finish selects the bin of
-// rank k (level 1; for bf16 inputs that fixes T).  ghist and st must be zero.
+// The W side of the forward's quantizer when it shares launches with the A side: K x N W (the
+// A side's dtype), its column-maximum keys (zeroed before), codes (N x K/2) and scales (N).
+struct WSide {
+    const void *W;
+    int dt;
+    int64_t K, N;
+    uint32_t *keys;
+    uint8_t *codes;
+    float *scales;
+};
+
+// Histogram of the |A| keys and raw row maxima (ghist zero).
 hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist, uint32_t *rowmax_key,
-                              State *st, float *T_out, uint64_t k, int num_cus, hipStream_t s);
+                              int num_cus, hipStream_t s);
+// Level 1 of the select: the bin of rank k (st zero); for bf16 inputs it fixes T.  w: NULL, or
+// W's column maxima, computed in the same launch.
+hipError_t launch_select_hi(const uint32_t *ghist, int dt, State *st, float *T_out, uint64_t k, const WSide *w,
+                            hipStream_t s);
 // Second level of the select for fp32 inputs (ghist_lo zero): fixes T.
 hipError_t launch_select_lo(const void *A, int64_t n, uint32_t *ghist_lo, State *st, float *T_out, hipStream_t s);
 hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const uint32_t *rowmax_key,
@@ -21,9 +35,10 @@ hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const 
                              const Staging &stg, State *st, bool emit, bool write_codes, hipStream_t s);
 // Exclusive scan of the row counts into row_ptr / nnz, then the staged entries (and, for rows
 // that outgrew their slots, a second read of those rows of A) into the (row, col)-sorted list.
+// w: NULL, or W's codes and scales from its finished column maxima, in the same launch.
 hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
                       int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val, const void *A, int dt,
-                      int64_t K, const float *T_src, hipStream_t s);
+                      int64_t K, const float *T_src, const WSide *w, hipStream_t s);
 // keys_zeroed: the column-maximum keys (in scales_as_keys) were zeroed by an earlier launch.
 // row_mult: NULL, or fp32[K]: quantize fl(row_mult[k] * W[k][n]) instead of W.
 // scales_out: NULL (the scales replace the keys in scales_as_keys, one more launch), or a

@@ -22,14 +22,66 @@ __global__ void k_zero_u32(uint32_t *__restrict__ p1, int64_t n1, uint32_t *__re
 }
 
 // ----------------------------------------------------------------------------- select
-// The bin holding rank k (0-based) of a histogram of NB bins, found by the 1024 threads of one
-// workgroup: level 1: k = k_level1 (computed on the host) over the 32768 high bins; level 2:
-// k = st->k_rem over the 65536 low bins of the selected high bin.  final_level says which
-// level fixes T.  Every count and partial sum is at most M*K < 2^32.
-template <int NB>
-__device__ __forceinline__ void select_bin(const uint32_t *__restrict__ hist, State *__restrict__ st, int level,
-                                           int final_level, float *__restrict__ T_out, uint64_t k_level1) {
-    constexpr int PER = NB / 1024;
+// Level 1 (the 32768 high bins, rank k computed on the host) by one workgroup of 256 threads:
+// thread t sums bins [128t, 128t + 128), a scan over the threads finds the one whose range
+// holds rank k, and wave 0 then finds the bin among those 128 (two per lane).  For bf16
+// inputs the bin fixes T; for fp32 inputs it leaves the rank within the bin to level 2.  Every
+// count and partial sum is at most M*K < 2^32.  It needs no more than 256 threads and a few
+// registers, so it can run as one workgroup of a launch that does other work.
+__device__ __forceinline__ void select_hi_256(const uint32_t *__restrict__ hist, State *__restrict__ st,
+                                              int final_level, float *__restrict__ T_out, uint64_t k) {
+    constexpr int PER = HIST_BINS / 256;
+    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t sel_s[2];  // the thread whose bins hold rank k, and the count before them
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint4 *src = reinterpret_cast<const uint4 *>(hist + tid * PER);
+    uint32_t local = 0;
+    for (int r = 0; r < PER / 4; r += 8) {
+        uint4 q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = src[r + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) local += q[u].x + q[u].y + q[u].z + q[u].w;
+    }
+    const uint32_t wincl = wave_incl_scan(local, lane);
+    if (lane == 63) wsum[wave] = wincl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const uint64_t total = (uint64_t)wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    const uint64_t incl = (uint64_t)before + wincl, excl = incl - local;
+    if (excl <= k && k < incl) {  // exactly one thread: k < total
+        sel_s[0] = (uint32_t)tid;
+        sel_s[1] = (uint32_t)excl;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int t = (int)sel_s[0];
+    const uint2 p = reinterpret_cast<const uint2 *>(hist + t * PER)[lane];
+    const uint32_t pc = p.x + p.y;
+    const uint64_t pex = (uint64_t)sel_s[1] + wave_incl_scan(pc, lane) - pc;  // entries before bin t*PER + 2*lane
+    if (pex <= k && k < pex + pc) {
+        const bool first = k < pex + p.x;
+        const uint32_t b = (uint32_t)(t * PER + 2 * lane + (first ? 0 : 1));
+        const uint32_t cnt = first ? p.x : p.y;
+        const uint64_t cum = first ? pex : pex + p.x;
+        st->hi_bin = b;
+        st->hi_count = cnt;
+        st->k_rem = k - cum;
+        st->nnz_hist = total - (cum + cnt);  // entries in later bins
+        if (final_level == 1) {
+            st->T_key = b << 16;
+            st->T = __uint_as_float(b << 16);
+            *T_out = st->T;
+        }
+    }
+}
+
+// Level 2 for fp32 inputs: rank st->k_rem among the 65536 low bins of the selected high bin,
+// found by the 1024 threads of one workgroup; it fixes T.
+__device__ __forceinline__ void select_lo_1024(const uint32_t *__restrict__ hist, State *__restrict__ st,
+                                               float *__restrict__ T_out) {
+    constexpr int PER = HIST_LO_BINS / 1024;
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t total_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -57,7 +109,7 @@ __device__ __forceinline__ void select_bin(const uint32_t *__restrict__ hist, St
     }
     __syncthreads();
     const uint64_t incl = (uint64_t)wsum[wave] + wincl, excl = incl - local, total = total_s;
-    const uint64_t k = (level == 1) ? k_level1 : st->k_rem;
+    const uint64_t k = st->k_rem;
     if (excl <= k && k < incl) {
         // the bin of rank k among the thread's bins: branch-free over the registers
         uint64_t cum = excl;
@@ -76,26 +128,13 @@ __device__ __forceinline__ void select_bin(const uint32_t *__restrict__ hist, St
             found = found || here;
             cum += cnts[i];
         }
-        const int b = tid * PER + bi;
-        cum = before;
-        const uint64_t above = total - (cum + cnt);  // entries in later bins
-        if (level == 1) {
-            st->hi_bin = (uint32_t)b;
-            st->hi_count = cnt;
-            st->k_rem = k - cum;
-            st->nnz_hist = above;
-            if (final_level == 1) {
-                st->T_key = (uint32_t)b << 16;
-                st->T = __uint_as_float((uint32_t)b << 16);
-                *T_out = st->T;
-            }
-        } else {
-            const uint32_t key = (st->hi_bin << 16) | (uint32_t)b;
-            st->T_key = key;
-            st->T = __uint_as_float(key);
-            st->nnz_hist += above;
-            *T_out = st->T;
-        }
+        const uint32_t b = (uint32_t)(tid * PER + bi);
+        const uint64_t above = total - (before + cnt);  // entries in later bins
+        const uint32_t key = (st->hi_bin << 16) | b;
+        st->T_key = key;
+        st->T = __uint_as_float(key);
+        st->nnz_hist += above;
+        *T_out = st->T;
     }
 }
 
@@ -167,10 +206,10 @@ __global__ __launch_bounds__(1024) void k_hist_rowmax(const void *__restrict__ A
     }
 }
 
-// The level-1 select (one workgroup); for bf16 inputs it fixes T.
-__global__ __launch_bounds__(1024) void k_select_hi(const uint32_t *__restrict__ hist, State *__restrict__ st,
-                                                    int final_level, float *__restrict__ T_out, uint64_t k_level1) {
-    select_bin<HIST_BINS>(hist, st, 1, final_level, T_out, k_level1);
+// The level-1 select alone (one workgroup of 256 threads).
+__global__ __launch_bounds__(256) void k_select_hi(const uint32_t *__restrict__ hist, State *__restrict__ st,
+                                                   int final_level, float *__restrict__ T_out, uint64_t k_level1) {
+    select_hi_256(hist, st, final_level, T_out, k_level1);
 }
 
 // Second level for fp32 inputs: among the entries whose key >> 16 is the selected bin,
@@ -189,7 +228,7 @@ __global__ __launch_bounds__(256) void k_hist_lo(const uint32_t *__restrict__ A,
 // The level-2 select of fp32 inputs (one workgroup).
 __global__ __launch_bounds__(1024) void k_select_lo(const uint32_t *__restrict__ hist_lo, State *__restrict__ st,
                                                     float *__restrict__ T_out) {
-    select_bin<HIST_LO_BINS>(hist_lo, st, 2, 2, T_out, 0);
+    select_lo_1024(hist_lo, st, T_out);
 }
 
 // ----------------------------------------------------------------------------- rows (A)
@@ -404,7 +443,8 @@ __device__ __forceinline__ void coo_overflow_row(int64_t row, int64_t base, int3
     const int64_t nchunk = K / 8;
     uint32_t run = 0;
     // U chunks of 8 per lane are loaded together: one memory round trip per 512*U elements
-    constexpr int U = 8;
+    // (rows this long are rare; a small U keeps the registers of the COO build low)
+    constexpr int U = 2;
     for (int64_t cg = 0; cg < nchunk; cg += 64 * U) {
         float vv[U][8];
         uint32_t kk[U][8], ss[U][8];
@@ -455,16 +495,15 @@ __device__ __forceinline__ void coo_overflow_row(int64_t row, int64_t base, int3
 //   4. rows that outgrew their slots are read again for their ranks >= S.
 constexpr int64_t COO_PREFIX_ROWS = 16384;
 template <int DT, bool PREFIX>
-__global__ __launch_bounds__(256) void k_coo_build(Staging stg, const int32_t *__restrict__ row_cnt,
-                                                   int32_t *__restrict__ row_ptr, int64_t *__restrict__ nnz_out,
-                                                   int64_t M, int64_t cap, int32_t *__restrict__ coo_row,
-                                                   int32_t *__restrict__ coo_col, float *__restrict__ coo_val,
-                                                   const void *__restrict__ A, int64_t K,
-                                                   const float *__restrict__ T_src) {
+__device__ __forceinline__ void coo_block(Staging stg, const int32_t *__restrict__ row_cnt,
+                                          int32_t *__restrict__ row_ptr, int64_t *__restrict__ nnz_out, int64_t M,
+                                          int64_t cap, int32_t *__restrict__ coo_row, int32_t *__restrict__ coo_col,
+                                          float *__restrict__ coo_val, const void *__restrict__ A, int64_t K,
+                                          const float *__restrict__ T_src, int bx) {
     __shared__ uint32_t wsum[4];
     __shared__ int32_t off_s[64], cnt_s[64], sc_s[65];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)bx * 64;
     // wave 0's lanes hold the counts of the workgroup's 64 rows; their load is issued together
     // with the prefix loads (one memory round trip for both)
     const int64_t rl = r0 + lane;
@@ -472,17 +511,20 @@ __global__ __launch_bounds__(256) void k_coo_build(Staging stg, const int32_t *_
     uint32_t base = 0;
     if constexpr (PREFIX) {
         // row_cnt is 16-byte aligned and r0 a multiple of 64: whole 16-byte groups, at most
-        // COO_PREFIX_ROWS / 1024 of them per thread, all issued before any is added
-        constexpr int PI = (int)(COO_PREFIX_ROWS / 1024);
-        int4 q[PI];
-#pragma unroll
-        for (int u = 0; u < PI; ++u) {
-            const int64_t i = (int64_t)tid * 4 + (int64_t)u * 1024;
-            q[u] = i < r0 ? *reinterpret_cast<const int4 *>(row_cnt + i) : make_int4(0, 0, 0, 0);
-        }
+        // COO_PREFIX_ROWS / 1024 of them per thread, in two rounds of loads issued together
+        constexpr int PI = (int)(COO_PREFIX_ROWS / 1024), PH = PI / 2;
         uint32_t part = 0;
+#pragma unroll 1
+        for (int h = 0; h < PI / PH; ++h) {
+            int4 q[PH];
 #pragma unroll
-        for (int u = 0; u < PI; ++u) part += (uint32_t)q[u].x + (uint32_t)q[u].y + (uint32_t)q[u].z + (uint32_t)q[u].w;
+            for (int u = 0; u < PH; ++u) {
+                const int64_t i = (int64_t)tid * 4 + (int64_t)(h * PH + u) * 1024;
+                q[u] = i < r0 ? *reinterpret_cast<const int4 *>(row_cnt + i) : make_int4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < PH; ++u) part += (uint32_t)q[u].x + (uint32_t)q[u].y + (uint32_t)q[u].z + (uint32_t)q[u].w;
+        }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) part += (uint32_t)__shfl_xor((int)part, o, 64);
         if (lane == 0) wsum[wave] = part;
@@ -542,6 +584,16 @@ __global__ __launch_bounds__(256) void k_coo_build(Staging stg, const int32_t *_
     }
 }
 
+template <int DT, bool PREFIX>
+__global__ __launch_bounds__(256) void k_coo_build(Staging stg, const int32_t *__restrict__ row_cnt,
+                                                   int32_t *__restrict__ row_ptr, int64_t *__restrict__ nnz_out,
+                                                   int64_t M, int64_t cap, int32_t *__restrict__ coo_row,
+                                                   int32_t *__restrict__ coo_col, float *__restrict__ coo_val,
+                                                   const void *__restrict__ A, int64_t K,
+                                                   const float *__restrict__ T_src) {
+    coo_block<DT, PREFIX>(stg, row_cnt, row_ptr, nnz_out, M, cap, coo_row, coo_col, coo_val, A, K, T_src, blockIdx.x);
+}
+
 // ----------------------------------------------------------------------------- columns (W)
 // Row k of the matrix as quantized: the input itself, or (RM) fl(row_mult[k] * x), the
 // form the backward quantizes per column.
@@ -561,15 +613,15 @@ __device__ __forceinline__ void load8_rm(const void *__restrict__ W, const float
 }
 
 // Column maxima of K x N W (keys), merged with atomicMax into colmax_key (zeroed before).
-// Block: 256 threads = 4 waves over the same 512 columns (8 per lane), rows split by wave.
+// Tile (bx, by): 256 threads = 4 waves over the same 512 columns (8 per lane), rows split by wave.
 template <int DT, bool RM>
-__global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int64_t K, int64_t N,
-                                                int rows_per_block, const float *__restrict__ row_mult,
-                                                uint32_t *__restrict__ colmax_key) {
+__device__ __forceinline__ void colmax_tile(const void *__restrict__ W, int64_t K, int64_t N, int rows_per_block,
+                                            const float *__restrict__ row_mult, uint32_t *__restrict__ colmax_key,
+                                            int bx, int by) {
     __shared__ uint32_t red[4][512];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t col = (int64_t)blockIdx.x * 512 + lane * 8;
-    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t col = (int64_t)bx * 512 + lane * 8;
+    const int64_t r0 = (int64_t)by * rows_per_block;
     const int64_t r1 = min(K, r0 + rows_per_block);
     uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (col < N) {
@@ -597,9 +649,16 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
     __syncthreads();
     for (int i = threadIdx.x; i < 512; i += 256) {
         uint32_t m = max(max(red[0][i], red[1][i]), max(red[2][i], red[3][i]));
-        int64_t c = (int64_t)blockIdx.x * 512 + i;
+        int64_t c = (int64_t)bx * 512 + i;
         if (c < N && m) atomicMax(&colmax_key[c], m);
     }
+}
+
+template <int DT, bool RM>
+__global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int64_t K, int64_t N,
+                                                int rows_per_block, const float *__restrict__ row_mult,
+                                                uint32_t *__restrict__ colmax_key) {
+    colmax_tile<DT, RM>(W, K, N, rows_per_block, row_mult, colmax_key, blockIdx.x, blockIdx.y);
 }
 
 // Quantize a 256 (k) x TN (n) tile of W with the finished column maxima and write it
@@ -612,10 +671,10 @@ __global__ __launch_bounds__(256) void k_colmax(const void *__restrict__ W, int6
 // scales_out: NULL, or fp32[N] (a buffer other than the keys) that the workgroups of the first
 // tile row fill with the dequantization scales of their columns.
 template <int DT, bool RM, int TN>
-__global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, int64_t K, int64_t N,
-                                                    const float *__restrict__ row_mult,
-                                                    const uint32_t *__restrict__ colmax_key,
-                                                    uint8_t *__restrict__ codes, float *__restrict__ scales_out) {
+__device__ __forceinline__ void qcols_tile(const void *__restrict__ W, int64_t K, int64_t N,
+                                           const float *__restrict__ row_mult,
+                                           const uint32_t *__restrict__ colmax_key, uint8_t *__restrict__ codes,
+                                           float *__restrict__ scales_out, int bx, int by) {
     constexpr int TPR = TN / 8;         // threads per row
     constexpr int GPP = 256 / TPR;      // groups of 8 rows per pass
     constexpr int PASSES = 32 / GPP;    // 32 groups of 8 rows = 256 rows per tile
@@ -624,12 +683,12 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
     __shared__ float rs[TN];
     __shared__ __attribute__((aligned(16))) uint32_t tile[TN][32];
     const int tid = threadIdx.x;
-    const int64_t n0 = (int64_t)blockIdx.x * TN, k0 = (int64_t)blockIdx.y * 256;
+    const int64_t n0 = (int64_t)bx * TN, k0 = (int64_t)by * 256;
     if (tid < TN) {
         float r = 0.0f, s;
         if (n0 + tid < N) {
             vector_scale(__uint_as_float(colmax_key[n0 + tid]), r, s);
-            if (scales_out && blockIdx.y == 0) scales_out[n0 + tid] = s;
+            if (scales_out && by == 0) scales_out[n0 + tid] = s;
         }
         rs[tid] = r;
     }
@@ -676,6 +735,14 @@ __global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, 
     }
 }
 
+template <int DT, bool RM, int TN>
+__global__ __launch_bounds__(256) void k_quant_cols(const void *__restrict__ W, int64_t K, int64_t N,
+                                                    const float *__restrict__ row_mult,
+                                                    const uint32_t *__restrict__ colmax_key,
+                                                    uint8_t *__restrict__ codes, float *__restrict__ scales_out) {
+    qcols_tile<DT, RM, TN>(W, K, N, row_mult, colmax_key, codes, scales_out, blockIdx.x, blockIdx.y);
+}
+
 // Column width of the transposing tile: 128 (256-byte row segments of the input; 3 % faster
 // than 64 on the 16384 x 22016 gradient, equal on the 4096 x 22016 weight).  A compile-time
 // tuning aid: 64 or 128.
@@ -706,6 +773,42 @@ __global__ void k_col_scales(uint32_t *__restrict__ colmax_key_then_scale, int64
     }
 }
 
+// ----------------------------------------------------------------------------- shared launches
+// When the forward quantizes A and W in one call, the W side's two passes share launches with
+// the A side's latency-bound steps, which are independent of them: the level-1 select (one
+// workgroup) runs beside W's column maxima, and the COO build beside W's quantize pass.  Each
+// workgroup takes one part by its index (a uniform branch), so both parts keep their own
+// tiling; the short A-side workgroups come first in the dispatch order.
+constexpr int COLMAX_ROWS = 256;  // rows of W per column-maximum workgroup
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_select_colmax(const uint32_t *__restrict__ hist, State *__restrict__ st,
+                                                       int final_level, float *__restrict__ T_out, uint64_t k_level1,
+                                                       WSide w, int gx) {
+    if (blockIdx.x == 0) {
+        select_hi_256(hist, st, final_level, T_out, k_level1);
+        return;
+    }
+    const int b = (int)blockIdx.x - 1;
+    colmax_tile<DT, false>(w.W, w.K, w.N, COLMAX_ROWS, nullptr, w.keys, b % gx, b / gx);
+}
+
+template <int DT, bool PREFIX>
+__global__ __launch_bounds__(256) void k_coo_qcols(Staging stg, const int32_t *__restrict__ row_cnt,
+                                                   int32_t *__restrict__ row_ptr, int64_t *__restrict__ nnz_out,
+                                                   int64_t M, int64_t cap, int32_t *__restrict__ coo_row,
+                                                   int32_t *__restrict__ coo_col, float *__restrict__ coo_val,
+                                                   const void *__restrict__ A, int64_t K,
+                                                   const float *__restrict__ T_src, int ncoo, WSide w, int gx) {
+    if ((int)blockIdx.x < ncoo) {
+        coo_block<DT, PREFIX>(stg, row_cnt, row_ptr, nnz_out, M, cap, coo_row, coo_col, coo_val, A, K, T_src,
+                              blockIdx.x);
+        return;
+    }
+    const int b = (int)blockIdx.x - ncoo;
+    qcols_tile<DT, false, FP4_QCOLS_TN>(w.W, w.K, w.N, nullptr, w.keys, w.codes, w.scales, b % gx, b / gx);
+}
+
 // ----------------------------------------------------------------------------- launchers
 static inline int blocks_for(int64_t n, int threads, int cap) {
     int64_t b = (n + threads - 1) / threads;
@@ -720,13 +823,28 @@ hipError_t launch_zero(uint32_t *p1, int64_t n1, uint32_t *p2, int64_t n2, hipSt
 }
 
 hipError_t launch_hist_rowmax(const void *A, int dt, int64_t M, int64_t K, uint32_t *ghist, uint32_t *rowmax_key,
-                              State *st, float *T_out, uint64_t k, int num_cus, hipStream_t s) {
+                              int num_cus, hipStream_t s) {
     int blocks = (int)(M < (int64_t)num_cus ? M : (int64_t)num_cus);
     if (dt == DT_BF16)
         hipLaunchKernelGGL(k_hist_rowmax<DT_BF16>, dim3(blocks), dim3(1024), 0, s, A, M, K, ghist, rowmax_key);
     else
         hipLaunchKernelGGL(k_hist_rowmax<DT_F32>, dim3(blocks), dim3(1024), 0, s, A, M, K, ghist, rowmax_key);
-    hipLaunchKernelGGL(k_select_hi, dim3(1), dim3(1024), 0, s, ghist, st, dt == DT_BF16 ? 1 : 2, T_out, (uint64_t)k);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_hi(const uint32_t *ghist, int dt, State *st, float *T_out, uint64_t k, const WSide *w,
+                            hipStream_t s) {
+    const int final_level = dt == DT_BF16 ? 1 : 2;
+    if (!w) {
+        hipLaunchKernelGGL(k_select_hi, dim3(1), dim3(256), 0, s, ghist, st, final_level, T_out, k);
+        return hipGetLastError();
+    }
+    const int gx = (int)((w->N + 511) / 512), gy = (int)((w->K + COLMAX_ROWS - 1) / COLMAX_ROWS);
+    const dim3 grid((unsigned)(1 + gx * gy));
+    if (w->dt == DT_BF16)
+        hipLaunchKernelGGL(k_select_colmax<DT_BF16>, grid, dim3(256), 0, s, ghist, st, final_level, T_out, k, *w, gx);
+    else
+        hipLaunchKernelGGL(k_select_colmax<DT_F32>, grid, dim3(256), 0, s, ghist, st, final_level, T_out, k, *w, gx);
     return hipGetLastError();
 }
 
@@ -763,10 +881,27 @@ hipError_t launch_quant_rows(const void *X, int dt, int64_t R, int64_t C, const 
 
 hipError_t launch_coo(const int32_t *row_cnt, int64_t M, int32_t *row_ptr, int64_t *nnz_out, const Staging &stg,
                       int64_t cap, int32_t *coo_row, int32_t *coo_col, float *coo_val, const void *A, int dt,
-                      int64_t K, const float *T_src, hipStream_t s) {
-    const dim3 grid((unsigned)((M + 63) / 64)), block(256);  // 64 rows per workgroup
+                      int64_t K, const float *T_src, const WSide *w, hipStream_t s) {
+    const int ncoo = (int)((M + 63) / 64);  // 64 rows per workgroup
     const bool prefix = M <= COO_PREFIX_ROWS;
     if (!prefix) hipLaunchKernelGGL(k_coo_scan, dim3(1), dim3(1024), 0, s, row_cnt, M, row_ptr, nnz_out);
+    if (w) {
+        const int gx = (int)((w->N + FP4_QCOLS_TN - 1) / FP4_QCOLS_TN), gy = (int)((w->K + 255) / 256);
+        const dim3 grid((unsigned)(ncoo + gx * gy));
+#define CQ(DT, PF)                                                                                              \
+    hipLaunchKernelGGL((k_coo_qcols<DT, PF>), grid, dim3(256), 0, s, stg, row_cnt, row_ptr, nnz_out, M, cap, coo_row, \
+                       coo_col, coo_val, A, K, T_src, ncoo, *w, gx)
+        if (dt == DT_BF16) {
+            if (prefix) CQ(DT_BF16, true);
+            else CQ(DT_BF16, false);
+        } else {
+            if (prefix) CQ(DT_F32, true);
+            else CQ(DT_F32, false);
+        }
+#undef CQ
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)ncoo), block(256);
 #define CB(DT, PF)                                                                                              \
     hipLaunchKernelGGL((k_coo_build<DT, PF>), grid, block, 0, s, stg, row_cnt, row_ptr, nnz_out, M, cap, coo_row, \
                        coo_col, coo_val, A, K, T_src)
@@ -789,7 +924,7 @@ hipError_t launch_quant_cols(const void *W, int dt, int64_t K, int64_t N, float 
         hipError_t e = launch_zero(keys, N, nullptr, 0, s);
         if (e != hipSuccess) return e;
     }
-    const int rows_per_block = 256;
+    const int rows_per_block = COLMAX_ROWS;
     dim3 g1((unsigned)((N + 511) / 512), (unsigned)((K + rows_per_block - 1) / rows_per_block));
 #define QC(DT, RM)                                                                                         \
     do {                                                                                                   \

@@ -132,6 +132,8 @@ OUT_CASES = [
     ("bf16", 1000, 4096, 0.999, "normal_sparse_outliers"), ("fp32", 128, 256, 0.99, "normal_sparse_outliers"),
     ("fp32", 333, 512, 0.9, "student_t"), ("bf16", 17, 64, 0.0, "plain"), ("bf16", 40, 96, 1.0, "plain"),
     ("fp32", 9, 32, 0.5, "plain"), ("bf16", 2000, 2048, 0.5, "student_t"),
+    # more rows than one COO workgroup sums for its own offset: the row offsets come from a scan
+    ("bf16", 16400, 64, 0.99, "student_t"),
 ]
 
 
@@ -445,6 +447,9 @@ def test_forward_tiny():
     ("bf16", 300, 512, 264, 0.99, "fp32"), ("bf16", 513, 1056, 776, 0.999, "bf16"),
     ("fp32", 257, 288, 136, 0.95, "fp32"), ("bf16", 1, 32, 8, 0.5, "fp32"), ("bf16", 64, 64, 64, 1.0, "bf16"),
     ("bf16", 520, 2048, 264, 0.9, "fp32"),
+    # more rows than one COO workgroup sums for its own offset (the scan launch, then the COO
+    # build beside W's quantize pass)
+    ("bf16", 16400, 64, 72, 0.99, "bf16"), ("fp32", 16448, 96, 40, 0.995, "fp32"),
 ])
 def test_forward_small(dtype, M, K, N, q, out):
     _say(f"forward {dtype} {M}x{K}x{N} q={q} out={out}")
