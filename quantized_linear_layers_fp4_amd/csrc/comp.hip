@@ -253,24 +253,31 @@ __global__ __launch_bounds__(256) void k_comp_block64(CompArgs a, int nrb, int p
     };
     int32_t kk, dd;
     load_ent(0, kk, dd);
-    for (int e = 0; e < nmax; e += 8) {
+    // an escaped block is written by the escape kernel: no entry to walk
+    const int32_t nwalk = escaped ? 0 : nmax;
+    for (int e = 0; e < nwalk; e += 8) {
+        // lane 8r + g turns row r's entry e + g into the byte offset of its W row once (past the
+        // row: 2^31, past the buffer, which reads zeros; K*N*ESZ < 2^31), and the row's lanes
+        // take the eight offsets by lane permutes
+        const uint32_t ko = e + g < n ? (uint32_t)kk * row_bytes : 0x80000000u;
         v4i w[8][2];
         float d[8];
+        uint32_t off[8];
+        // all sixteen permutes first, so the eight W loads go out back to back
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint32_t k = (uint32_t)__shfl(kk, (lane & ~7) + u);
-            d[u] = __int_as_float(__shfl(dd, (lane & ~7) + u));
-            const uint32_t off = (e + u < n && active) ? k * row_bytes + lane_off : 0x80000000u;  // K*N*ESZ < 2^31
-            load_seg<WDT, CC>(rsW, off, true, w[u]);
-        }
+        for (int u = 0; u < 8; ++u) off[u] = (uint32_t)__shfl((int)ko, (lane & ~7) + u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) d[u] = __int_as_float(__shfl(dd, (lane & ~7) + u));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load_seg<WDT, CC>(rsW, off[u] + lane_off, true, w[u]);
         load_ent(e + 8, kk, dd);
+        // ascending k.  An entry past the row has d = 0 and reads W as zeros, and fma(0, 0, y)
+        // is y exactly (y is never -0: it starts as +0 or nonzero, and an exact cancellation
+        // rounds to +0), so every lane runs every step without a branch.
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (e + u < n) {  // per row; ascending k
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int c = 0; c < CC; ++c) y[c] = __builtin_fmaf(d[u], seg_elem<WDT>(w[u], c), y[c]);
-            }
-        }
+            for (int c = 0; c < CC; ++c) y[c] = __builtin_fmaf(d[u], seg_elem<WDT>(w[u], c), y[c]);
     }
     if (active) store_y<YDT, CC>(a.Y, (size_t)row * N + col, y);
 }
