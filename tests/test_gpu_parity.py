@@ -457,6 +457,38 @@ def test_forward_small(dtype, M, K, N, q, out):
     _check_forward_small(A, W, q, _dt(out))
 
 
+def _random_forward_cases(n: int = 24, seed: int = 2024):
+    """Seeded random shapes within the limits (K % 32 == 0, N % 8 == 0), sized for the oracle:
+    ragged against every tile (256-row and 128/256-column GEMM tiles, 64-row COO groups,
+    512-column compensation chunks, 128 x 64 escape blocks), both dtypes and output types, and
+    quantiles from 0 to 1; a quantile below 0.95 at K >= 640 gives more than 64 entries per row,
+    so those cases take the 8-row block compensation."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.integers(1, 1200))
+        K = 32 * int(rng.integers(1, 48))
+        N = 8 * int(rng.integers(1, 160))
+        while M * K * N > 1.5e8:
+            M = max(1, M // 2)
+        q = float(rng.choice([0.0, 0.5, 0.9, 0.97, 0.99, 0.999, 1.0]))
+        dtype = str(rng.choice(["bf16", "fp32"]))
+        out = str(rng.choice(["bf16", "fp32"])) if dtype == "bf16" else "fp32"
+        kind = str(rng.choice(["normal_sparse_outliers", "student_t", "plain"]))
+        cases.append((i, dtype, M, K, N, q, out, kind))
+    return cases
+
+
+@pytest.mark.parametrize("i,dtype,M,K,N,q,out,kind", _random_forward_cases(),
+                         ids=lambda v: str(v) if not isinstance(v, float) else f"q{v}")
+def test_forward_random_shapes(i, dtype, M, K, N, q, out, kind):
+    """Every intermediate (T, nnz, row_ptr, the COO list, Aq, sA, Wq, sW) bit-exact and Y within
+    tolerance, on seeded random shapes."""
+    _say(f"forward random #{i} {dtype} {M}x{K}x{N} q={q} out={out} {kind}")
+    A, W = make_custom(M, K, N, dtype=dtype, seed=500 + i, kind=kind)
+    _check_forward_small(A, W, q, _dt(out))
+
+
 def test_forward_zero_rows_and_columns():
     _say("forward zero rows/cols")
     A, W = make_custom(96, 256, 72, dtype="bf16", seed=3)
