@@ -408,6 +408,33 @@ def test_forward_with_escaped_accumulators(dtype, out):
     _check_forward_small(A, W, 0.99, _dt(out))
 
 
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("fp32", "fp32")])
+def test_forward_heavy_row_in_escaped_block(dtype, out):
+    """A row with many dA entries inside an escaped block.  Row 130 holds 70 planted outliers
+    (+80) and 1.0 elsewhere, and against W's column 40 (0.02 everywhere) its accumulator is past
+    the two-byte range: its compensation task (a chain of 70 entries, nine groups of W segments)
+    must leave that escaped 128 x 64 block to the escape kernel, which walks the same 70 entries,
+    and write the rest of its chunk; row 3 carries 78 entries in a block that does not escape."""
+    _say(f"forward heavy row in an escaped block {dtype} out={out}")
+    M, K, N = 300, 1024, 264
+    A, W = make_custom(M, K, N, dtype=dtype, seed=61)
+    rng = np.random.default_rng(7)
+    A[130] = 1.0
+    for r in (130, 3):
+        cols = rng.choice(K, 70, replace=False)
+        A[r, cols] = 80.0
+    W[:, 40] = 0.02
+    q = 0.99
+    assert fp4.outlier_capacity(M, K, q) <= 64 * M  # the 512-column chunk tasks
+    _check_forward_small(A, W, q, _dt(out))
+    Anp, Wnp = oracle_inputs(A, W)
+    cl = oracle.clamp_coo(Anp, oracle.abs_quantile(Anp, q), want_clamped=True, cap=oracle.capacity(M, K, q))
+    assert np.diff(cl["row_ptr"])[[3, 130]].min() > 64
+    Aq = oracle.quant_rows(cl["A_clamped"])[0]
+    Wq = oracle.quant_cols(Wnp)[0]
+    assert abs(oracle.accumulate(Aq[130:131], Wq[40:41], K)[0, 0]) > 8191.75  # that block escaped
+
+
 # ----------------------------------------------------------------------------- forward
 def _check_forward_small(A, W, q, out_dtype):
     M, K = A.shape
