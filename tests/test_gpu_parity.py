@@ -878,6 +878,37 @@ def test_backward_small(dtype, M, K, N, out):
     _check_backward_small(A, W, dY, 0.99, _dt(out))
 
 
+def _random_backward_cases(n: int = 16, seed: int = 4242):
+    """Seeded random shapes for the backward: M, K and N multiples of 32 (the two contractions
+    need M and N so); ragged against the GEMM tiles in every output dimension, both dtypes and
+    output types, N from 32 to about 26k (a bf16 dY up to 24576 takes the fused row pass, an fp32
+    one the separate passes)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = 32 * int(rng.integers(1, 24))
+        K = 32 * int(rng.integers(1, 40))
+        N = 32 * int(rng.integers(1, 900 if i % 2 else 40))
+        while M * K * N > 1.2e8:  # keep N, shrink the others
+            if K > 32:
+                K = max(32, (K // 2) // 32 * 32)
+            else:
+                M = max(32, (M // 2) // 32 * 32)
+        dtype = str(rng.choice(["bf16", "fp32"]))
+        out = str(rng.choice(["bf16", "fp32"]))
+        cases.append((i, dtype, M, K, N, out))
+    return cases
+
+
+@pytest.mark.parametrize("i,dtype,M,K,N,out", _random_backward_cases())
+def test_backward_random_shapes(i, dtype, M, K, N, out):
+    """Gq, sG, Hq, sH, WqT, AqT, dA and dW bit-exact on seeded random shapes."""
+    _say(f"backward random #{i} {dtype} M={M} K={K} N={N} -> {out}")
+    A, W = make_custom(M, K, N, dtype=dtype, seed=700 + i)
+    dY = make_custom_grad(M, N, dtype=dtype, seed=700 + i)
+    _check_backward_small(A, W, dY, 0.99, _dt(out))
+
+
 def test_backward_one_product():
     # dA alone allows any M; dW alone allows N % 8 == 0
     _say("backward dA only (M=300), dW only (N=264)")
