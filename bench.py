@@ -34,6 +34,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak (5.0 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_llama7b_gate_up.json")
 GEMM_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "gemm.hip")
+COMP_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "comp.hip")
 
 
 def b_in(dtype: torch.dtype) -> int:
@@ -96,16 +97,21 @@ def gemm_src_sha() -> str:
     return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(launch_bytes_alg: float):
-    """HBM bytes per GEMM launch from the committed rocprofv3 --pmc summary, if it was
-    taken on the current GEMM source; else None."""
+def comp_src_sha() -> str:
+    return hashlib.sha256(open(COMP_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(launch_bytes_alg: float, what: str = "gemm"):
+    """HBM bytes per launch of the GEMM (what="gemm") or of the compensation pass (what="comp")
+    from the committed rocprofv3 --pmc summary, if it was taken on the current source of that
+    kernel; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_src_sha") != gemm_src_sha():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    if what == "gemm":
+        return rec.get("hbm_bytes_per_launch") if rec.get("gemm_src_sha") == gemm_src_sha() else None
+    return rec.get("comp_hbm_bytes_per_launch") if rec.get("comp_src_sha") == comp_src_sha() else None
 
 
 def cpu_baseline(A, W, L, rows: int = 256) -> dict:
@@ -169,7 +175,8 @@ def _counter_per_dispatch(d: str, counter: str, kernel_pred) -> float:
 def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write: str):
     """HBM bytes per GEMM launch (and per k_comp_apply launch) on the 7B gate+up shape:
     FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the bytes a plain 1 GiB copy moves
-    per unit of the same counter.  Written with the hash of the GEMM source it was measured on."""
+    per unit of the same counter.  Written with the hashes of the GEMM and compensation sources
+    it was measured on."""
     # the GEMM kernel the library picked for this shape: the one present in the counters
     kname = "k_fp4_gemm_wide"
     try:
@@ -182,7 +189,8 @@ def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write:
     c_f = _counter_per_dispatch(copy_fetch, "FETCH_SIZE", is_copy)
     c_w = _counter_per_dispatch(copy_write, "WRITE_SIZE", is_copy)
     f_fetch, f_write = (1 << 30) / c_f, (1 << 30) / c_w
-    rec = {"gemm_src_sha": gemm_src_sha(), "workload": "llama7b_gate_up", "gemm_kernel": kname,
+    rec = {"gemm_src_sha": gemm_src_sha(), "comp_src_sha": comp_src_sha(), "workload": "llama7b_gate_up",
+           "gemm_kernel": kname,
            "copy_fetch_size": c_f, "copy_write_size": c_w,
            "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write}
     for name, pred in (("gemm", is_gemm), ("comp", is_comp)):
@@ -519,6 +527,7 @@ def run_full(args):
     fwd_tflops = flops / ms_step / 1e9
     first = sets[0][0]["L"]
     traffic = load_traffic(None) if args.workload == "llama7b_gate_up" else None
+    comp_traffic = load_traffic(None, "comp") if args.workload == "llama7b_gate_up" else None
     name = first.name if len(sets[0]) == 1 else f"{args.workload}(x{len(sets[0])} layers)"
     sha = hashlib.sha256()
     for A, W, _ in host0:
@@ -559,7 +568,11 @@ def run_full(args):
                           "quant_A_alone": round(quant_a_ms, 4),
                           "quant_W_alone": round(quant_w_ms, 4) if quant_w_ms is not None else None},
         "compensation": dict({"bound": "hbm", "kernel": per_layer[0]["comp_kernel"], "peak": PEAK_HBM_GBS,
-                              "unit": "GB/s", "how": "product stage minus the GEMM launch, both timed directly"},
+                              "unit": "GB/s", "how": "product stage minus the GEMM launch, both timed directly",
+                              # counted HBM bytes of one k_comp_apply launch (rocprofv3 FETCH_SIZE +
+                              # WRITE_SIZE, scaled by a plain copy's counts), and that over its time
+                              "traffic": comp_traffic,
+                              "traffic_GB/s": round(comp_traffic / comp_ms / 1e6, 1) if comp_traffic else None},
                              **hbm(cbytes, comp_ms)),
         "quantizer": dict({"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "how": "the forward's quantizer stage call (A and W in one call, its own launches), "
