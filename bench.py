@@ -35,6 +35,9 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak (5.0 PFLOP/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_llama7b_gate_up.json")
 GEMM_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "gemm.hip")
 COMP_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "comp.hip")
+QUANT_SRC = os.path.join(ROOT, "quantized_linear_layers_fp4_amd", "csrc", "quant.hip")
+# the forward's quantizer launches (both sides in one stage call)
+QUANT_KERNELS = ("k_zero_u32", "k_hist_rowmax", "k_select_colmax", "k_quant_rows", "k_coo_qcols")
 
 
 def b_in(dtype: torch.dtype) -> int:
@@ -87,6 +90,11 @@ def _kernel_is(name: str):
     return lambda n: n.replace("void ", "").startswith(f"fp4::{name}<")
 
 
+def _kernel_named(name: str):
+    """Predicate on rocprofv3 kernel names: the kernel `name`, templated or not."""
+    return lambda n: n.replace("void ", "").startswith((f"fp4::{name}<", f"fp4::{name}("))
+
+
 def _gemm_main(name: str):
     """The GEMM launch among rocprofv3 kernel names: the kernel `name` (the escape kernel that
     follows a two-byte product is another kernel, k_q16_escapes)."""
@@ -101,16 +109,22 @@ def comp_src_sha() -> str:
     return hashlib.sha256(open(COMP_SRC, "rb").read()).hexdigest()[:16]
 
 
+def quant_src_sha() -> str:
+    return hashlib.sha256(open(QUANT_SRC, "rb").read()).hexdigest()[:16]
+
+
 def load_traffic(launch_bytes_alg: float, what: str = "gemm"):
-    """HBM bytes per launch of the GEMM (what="gemm") or of the compensation pass (what="comp")
-    from the committed rocprofv3 --pmc summary, if it was taken on the current source of that
-    kernel; else None."""
+    """HBM bytes per launch of the GEMM (what="gemm"), of the compensation pass (what="comp"), or
+    per quantizer stage call (what="quant", the sum over its launches) from the committed
+    rocprofv3 --pmc summary, if it was taken on the current source of those kernels; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if what == "gemm":
         return rec.get("hbm_bytes_per_launch") if rec.get("gemm_src_sha") == gemm_src_sha() else None
+    if what == "quant":
+        return rec.get("quant_hbm_bytes_per_call") if rec.get("quant_src_sha") == quant_src_sha() else None
     return rec.get("comp_hbm_bytes_per_launch") if rec.get("comp_src_sha") == comp_src_sha() else None
 
 
@@ -175,8 +189,8 @@ def _counter_per_dispatch(d: str, counter: str, kernel_pred) -> float:
 def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write: str):
     """HBM bytes per GEMM launch (and per k_comp_apply launch) on the 7B gate+up shape:
     FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the bytes a plain 1 GiB copy moves
-    per unit of the same counter.  Written with the hashes of the GEMM and compensation sources
-    it was measured on."""
+    per unit of the same counter, and the same summed over the forward's quantizer launches.
+    Written with the hashes of the GEMM, compensation and quantizer sources it was measured on."""
     # the GEMM kernel the library picked for this shape: the one present in the counters
     kname = "k_fp4_gemm_wide"
     try:
@@ -200,6 +214,11 @@ def write_traffic(gemm_fetch: str, gemm_write: str, copy_fetch: str, copy_write:
         rec.update({f"{pre}fetch_size_per_launch": fs, f"{pre}write_size_per_launch": ws,
                     f"{pre}hbm_read_bytes_per_launch": fs * f_fetch, f"{pre}hbm_write_bytes_per_launch": ws * f_write,
                     f"{pre}hbm_bytes_per_launch": round(fs * f_fetch + ws * f_write)})
+    qf = sum(_counter_per_dispatch(gemm_fetch, "FETCH_SIZE", _kernel_named(k)) for k in QUANT_KERNELS)
+    qw = sum(_counter_per_dispatch(gemm_write, "WRITE_SIZE", _kernel_named(k)) for k in QUANT_KERNELS)
+    rec.update({"quant_src_sha": quant_src_sha(), "quant_kernels": list(QUANT_KERNELS),
+                "quant_hbm_read_bytes_per_call": qf * f_fetch, "quant_hbm_write_bytes_per_call": qw * f_write,
+                "quant_hbm_bytes_per_call": round(qf * f_fetch + qw * f_write)})
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
@@ -528,6 +547,7 @@ def run_full(args):
     first = sets[0][0]["L"]
     traffic = load_traffic(None) if args.workload == "llama7b_gate_up" else None
     comp_traffic = load_traffic(None, "comp") if args.workload == "llama7b_gate_up" else None
+    quant_traffic = load_traffic(None, "quant") if args.workload == "llama7b_gate_up" and per_step_w else None
     name = first.name if len(sets[0]) == 1 else f"{args.workload}(x{len(sets[0])} layers)"
     sha = hashlib.sha256()
     for A, W, _ in host0:
@@ -578,7 +598,10 @@ def run_full(args):
                            "how": "the forward's quantizer stage call (A and W in one call, its own launches), "
                                   "between events of its own; A_alone / W_alone: each side in a call of its own",
                            "A_alone": hbm(qa_bytes, quant_a_ms),
-                           "W_alone": hbm(qw_bytes, quant_w_ms) if qw_bytes else None},
+                           "W_alone": hbm(qw_bytes, quant_w_ms) if qw_bytes else None,
+                           # counted HBM bytes of the stage call's launches (W read twice), and over its time
+                           "traffic": quant_traffic,
+                           "traffic_GB/s": round(quant_traffic / quant_ms / 1e6, 1) if quant_traffic else None},
                           **hbm(qa_bytes + qw_bytes, quant_ms)),
         "nnz": nnz_total,
         "layers": per_layer,
