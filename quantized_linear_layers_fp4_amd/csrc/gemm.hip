@@ -2,11 +2,11 @@
 // (QbitAI report on "Optimizing Large Language Model Training Using FP4 Quantization":
 // GEMM-kernel paragraph for the FP4 tiled product, granularity paragraph for the row/column
 // scales that factor out of the K-sum).  The pages' kernel emulates FP4 on FP8 tensor cores and reduces in
-// FP16; here the CDNA4 matrix cores multiply E2M1 operands natively (unit E8M0 block
-// scales) and accumulate in fp32, which is exact for these operands.
+// FP16; here the CDNA4 matrix cores multiply E2M1 operands natively (the F8F6F4 MFMA in its
+// unscaled form, i.e. unit block scales) and accumulate in fp32, which is exact for these operands.
 //
 // Workgroup: 4 waves (one per SIMD) own a 256 x 128 output tile; wave (wm, wn) owns rows
-// 128*wm.. and columns 64*wn.. as 4 x 2 tiles of V_MFMA_SCALE_F32_32X32X64_F8F6F4.  Two
+// 128*wm.. and columns 64*wn.. as 4 x 2 tiles of V_MFMA_F32_32X32X64_F8F6F4.  Two
 // workgroups share a CU (73.5 KiB of LDS each), so one's epilogue and barriers run under
 // the other's matrix work.  K advances 128 codes (64 bytes per row) per stage.  Operand
 // tiles travel from global memory straight into one of three LDS stage buffers (buffer
