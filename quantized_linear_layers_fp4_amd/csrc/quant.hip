@@ -45,6 +45,10 @@ __device__ __forceinline__ void select_hi_256(const uint32_t *__restrict__ hist,
     }
     const uint32_t wincl = wave_incl_scan(local, lane);
     if (lane == 63) wsum[wave] = wincl;
+    if (tid == 0) {  // a default in range, should the histogram not hold rank k (it always does)
+        sel_s[0] = 0;
+        sel_s[1] = 0;
+    }
     __syncthreads();
     uint32_t before = 0;
     for (int w = 0; w < wave; ++w) before += wsum[w];
