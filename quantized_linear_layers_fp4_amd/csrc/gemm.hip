@@ -713,9 +713,11 @@ __global__ __launch_bounds__(NT, 1) void k_fp4_gemm_wide(TileArgs p) {
     // DT_Q16 outputs: the last ND pairs of a tile are packed in registers and stored during the
     // next tile's first steps, under its MFMAs (the bf16 epilogue stores at once: deferring it spills)
     constexpr bool DEFER = YDT == DT_Q16;
-    // pairs deferred (the tile's last ND; the others are stored at once).  2, 4 and 6 measured
-    // within noise of each other on four layer shapes with the unscaled MFMA; 8 spills.
+    // pairs deferred (the tile's last ND; the others are stored at once).  The next tile's first
+    // two steps flush exactly four (two each), so ND is 4 here; with the flushes spread to match,
+    // 2, 4 and 6 measured within noise of each other on four layer shapes, and 8 spills.
     constexpr int ND = 4;
+    static_assert(ND == 4, "the first two steps of a tile flush four deferred pairs");
     uint32_t pk[ND][16];
     bool pend = false;
     int pr0 = 0, pc0 = 0;
