@@ -539,6 +539,28 @@ def test_forward_is_deterministic():
     assert torch.equal(ws1[: lay.scratch], ws2[: lay.scratch])
 
 
+def test_forward_is_deterministic_wide():
+    """The same on the persistent 256 x 256 GEMM (1056 tiles, a ragged last tile column, the two-byte
+    hand-over with deferred stores and loads carried from one step to the next): five forwards,
+    each Y and each workspace's results bitwise equal to the first's."""
+    M, K, N, q = 8192, 4096, 8200, 0.999
+    _say(f"determinism wide {M}x{K}x{N}")
+    A, W = make_custom(M, K, N, dtype="bf16", seed=29, kind="student_t")
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    assert fp4.gemm_kernel_name(M, N, K, torch.cuda.get_device_properties(0).multi_processor_count) == "k_fp4_gemm_wide"
+    lay = fp4.forward_layout(M, K, N, A.dtype, q)
+    # zeroed: parts of the results region (the COO arrays past nnz) are not written
+    ws0 = fp4.workspace(Ad, N, q, torch.bfloat16).zero_()
+    Y0 = fp4.linear_forward(Ad, Wd, q, out_dtype=torch.bfloat16, ws=ws0).clone()
+    r0 = ws0[: lay.scratch].clone()
+    ws, Y = fp4.workspace(Ad, N, q, torch.bfloat16).zero_(), torch.empty_like(Y0)
+    for _ in range(4):
+        fp4.linear_forward(Ad, Wd, q, out_dtype=torch.bfloat16, ws=ws, Y=Y)
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y0.view(torch.int16))
+        assert torch.equal(ws[: lay.scratch], r0)
+
+
 @pytest.mark.parametrize("dtype,M,K,N,q,out", [
     ("bf16", 300, 512, 264, 0.99, torch.bfloat16),
     ("fp32", 130, 256, 72, 0.95, torch.float32),
